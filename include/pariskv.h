@@ -1,0 +1,171 @@
+/*
+ * pariskv.h -- C ABI of the MI355X (gfx950) ParisKV decode path.
+ *
+ * ParisKV ("ParisKV: Fast and Drift-Robust KV-Cache Retrieval for Long-Context
+ * LLMs") keeps the full KV cache, encodes every key of the retrieval zone into
+ * compact metadata (sign-pattern bucket ids, 4-bit sign+magnitude codes and a
+ * calibration scale per subspace), and at every decode step retrieves the
+ * top-k keys for the current query coarse-to-fine on the GPU before running
+ * attention over sink + local + update buffer + the retrieved keys.
+ *
+ * Terms used below:
+ *   d      head dimension (128)           B   subspaces (16)     m  coordinates per subspace (8)
+ *   unit   one (batch, kv head) sequence  G   query heads per kv head (grouped-query attention)
+ *   cap    capacity in tokens per unit    N   tokens currently held per unit
+ *
+ * Memory layouts (row-major, innermost last):
+ *   K / V store   [batch][n_kv_heads][cap][d]      kv_dtype, caller-owned
+ *   q             [batch][n_q_heads][d]            kv_dtype; query head h belongs to kv head h / G
+ *   k_new, v_new  [batch][n_kv_heads][d]           kv_dtype
+ *   sel           [batch][n_kv_heads][top_k]       int32 token positions, ascending
+ *   sel_n         [batch][n_kv_heads]              int32 number of valid entries of sel
+ *   out           [batch][n_q_heads][d]            float32
+ * All device pointers must be 16-byte aligned; rows are contiguous.
+ *
+ * Streams: every call that launches work takes a hipStream_t (passed as
+ * void*, NULL = the null stream) and returns without synchronising.  Errors
+ * found by host-side validation are returned before anything is launched and
+ * leave the context unchanged.  A device fault surfaces as PK_ERR_HIP from a
+ * later call.  A context is not thread-safe; calls on one context must be
+ * issued from one host thread in order.
+ */
+#ifndef PARISKV_H
+#define PARISKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PK_OK = 0,
+    PK_ERR_INVALID = -1,      /* bad argument or configuration                      */
+    PK_ERR_NO_DEVICE = -2,    /* no usable gfx950 device                            */
+    PK_ERR_OOM = -3,          /* device allocation failed                           */
+    PK_ERR_CAPACITY = -4,     /* the token would exceed the context's capacity      */
+    PK_ERR_HIP = -5,          /* a HIP runtime call failed (launch or earlier fault) */
+    PK_ERR_UNSUPPORTED = -6   /* valid, but not a configuration this library builds */
+} pk_status;
+
+typedef enum { PK_F32 = 0, PK_BF16 = 1 } pk_dtype;
+
+/* Where the caller's K/V store lives.  PK_MEM_HOST_MAPPED: pinned host memory
+ * mapped into the device address space; attention then reads retrieved rows
+ * over the host link, as in the page's UVA offloading. */
+typedef enum { PK_MEM_DEVICE = 0, PK_MEM_HOST_MAPPED = 1 } pk_mem;
+
+/* Method parameters.  ParisKV page: "Analytic centroids" (B, m), "Coarse
+ * candidate generation" (rho, vote weights, candidate fraction), "Sliding-window
+ * update mechanism" (zones).  Supported: head_dim 128, n_sub 16, sub_dim 8. */
+typedef struct {
+    int32_t head_dim;          /* d = 128                                             */
+    int32_t n_sub;             /* B = 16                                              */
+    int32_t sub_dim;           /* m = 8 (256 sign-pattern centroids per subspace)     */
+    int32_t rho;               /* centroids picked per subspace and query head, 1..8  */
+    uint8_t vote_weight[8];    /* vote of a rank-r pick (r = 0 is the best), 1..255   */
+    int32_t coarse_permille;   /* candidates kept = max(top_k, ceil(p * N_r / 1000)), capped at N_r */
+    int32_t top_k;             /* keys retrieved per unit, >= 1                       */
+    int32_t n_sink;            /* first tokens always attended                        */
+    int32_t n_local;           /* most recent tokens always attended                  */
+    int32_t buf_tokens;        /* update buffer U (0 = static context, no appends)    */
+    uint64_t sign_bits[2];     /* SRHT diagonal: D_jj = -1 where bit j is set         */
+} pk_config;
+
+typedef struct pk_ctx pk_ctx;  /* opaque; owned by the library */
+
+/* Create a context over the caller's K/V store.
+ * Owns: the per-key metadata (16 B of bucket ids and a 128 B record of codes
+ * and scales per token), the window counters and all scratch.  The caller
+ * keeps ownership of k_store / v_store, which must outlive the context.
+ * Requires n_q_heads = G * n_kv_heads with 1 <= G <= 16, G * max(weight) <= 255,
+ * buf_tokens <= n_local.  Allocates device memory and synchronises the device.
+ * Errors: PK_ERR_INVALID, PK_ERR_UNSUPPORTED, PK_ERR_NO_DEVICE, PK_ERR_OOM. */
+pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                    int64_t capacity, pk_dtype kv_dtype, void* k_store, void* v_store,
+                    pk_mem store_mem, pk_ctx** out);
+
+/* Free the context (synchronises the device).  NULL is ignored. */
+void pk_destroy(pk_ctx* ctx);
+
+/* Prefill.  The caller has written n_tokens tokens of every unit into the
+ * store.  Sets the window (sink = first n_sink tokens, local = last n_local,
+ * retrieval in between, empty buffer) and encodes every retrieval-zone key:
+ * SRHT rotation, bucket id per subspace, 4-bit code per coordinate, scale w
+ * per subspace.  ParisKV page: "Normalization and rotation", "Coarse candidate
+ * generation", "Quantization", "Calibration" (w is computed at prefill).
+ * Errors: PK_ERR_INVALID (n_tokens < 1), PK_ERR_CAPACITY (n_tokens > cap). */
+pk_status pk_encode_keys(pk_ctx* ctx, int64_t n_tokens, void* stream);
+
+/* Decode append: write one new token per unit (device k_new / v_new) at
+ * position N, into the update buffer.  If the previous step filled the buffer
+ * (U tokens), first move the oldest local tokens into the retrieval zone and
+ * encode them on the device, and promote the buffer to local.  ParisKV page:
+ * "Sliding-window update mechanism".
+ * Errors: PK_ERR_INVALID (buf_tokens == 0 or NULL input), PK_ERR_CAPACITY. */
+pk_status pk_append_decode_keys(pk_ctx* ctx, const void* k_new, const void* v_new, void* stream);
+
+/* Retrieval for the current queries q (device).  Per unit: rotate the G
+ * queries, pick the top-rho centroids per subspace, score every retrieval-zone
+ * key by its summed collision votes, keep the top candidates, rerank them with
+ * the RSQ-IP estimate  sum_g ||q_g|| sum_b w_b <v_b, q~_b>  and write the top-k
+ * positions to sel (ascending) and their count to sel_n.  Ties go to the lower
+ * token position.  ParisKV page: "Coarse candidate generation",
+ * "Candidate reranking (RSQ-IP)", "Estimation".
+ * Errors: PK_ERR_INVALID (NULL pointer, or no prefill yet). */
+pk_status pk_retrieve(pk_ctx* ctx, const void* q, int32_t* sel, int32_t* sel_n, void* stream);
+
+/* Sparse GQA decode attention of q over sink + local + update buffer + the
+ * sel_n[u] positions in sel (any positions of the retrieval zone, e.g. those
+ * pk_retrieve wrote).  out = softmax(q k^T / sqrt(d)) V over that set, float32.
+ * ParisKV page: "Problem definition" (attention over a top-k subset), "UVA
+ * offloading" (retrieved rows may live in host memory).
+ * Errors: PK_ERR_INVALID (NULL pointer, or no prefill yet). */
+pk_status pk_sparse_attend(pk_ctx* ctx, const void* q, const int32_t* sel, const int32_t* sel_n,
+                           float* out, void* stream);
+
+/* Host only, no device needed.  The sign+3-bit magnitude codebook for sub_dim
+ * m: the Lloyd-Max quantiser of |u_j| for u uniform on the unit sphere of R^m
+ * (u_j^2 ~ Beta(1/2, (m-1)/2), the page's Beta prior).  levels[n_levels]
+ * = fp32 levels, sq_thresholds[n_levels-1] = fp32(t^2) of the thresholds.
+ * ParisKV page: "Quantization".  Errors: PK_ERR_INVALID (m < 2, n_levels != 8, NULL). */
+pk_status pk_codebook(int32_t sub_dim, int32_t n_levels, float* levels, float* sq_thresholds);
+
+/* Human-readable name of a status code (static string). */
+const char* pk_status_string(pk_status s);
+
+/* Current window of the context (same for every unit), host-side mirror. */
+pk_status pk_get_window(const pk_ctx* ctx, int64_t* n_tokens, int64_t* sink_end, int64_t* r_end,
+                        int64_t* buf);
+
+/* Per-stage kernel timing.  While enabled, every kernel the context launches
+ * is bracketed by HIP events recorded on the stream it runs on.
+ * pk_profile_read synchronises those events and returns, per stage, the
+ * summed duration in milliseconds and the number of launches since the last
+ * enable (arrays of PK_STAGE_COUNT entries).  Errors: PK_ERR_INVALID. */
+enum { PK_STAGE_ENCODE = 0, PK_STAGE_APPEND = 1, PK_STAGE_QPREP = 2, PK_STAGE_SCAN = 3,
+       PK_STAGE_RERANK = 4, PK_STAGE_ATTEND = 5, PK_STAGE_COUNT = 6 };
+pk_status pk_profile_enable(pk_ctx* ctx, int32_t on);
+pk_status pk_profile_read(pk_ctx* ctx, double* ms, int64_t* launches);
+
+/* Debug read-back for tests: copies an internal buffer to host memory and
+ * synchronises the stream.  `bytes` must equal the size reported by
+ * pk_debug_size for `what`.
+ *   PK_DBG_IDS     uint8  [units][cap][B]           bucket ids
+ *   PK_DBG_REC     uint8  [units][cap][128]         64 B nibbles (coord 2i in low half of byte i) + float32 w[B]
+ *   PK_DBG_LUT     uint8  [units][B][256]           vote table of the last pk_retrieve
+ *   PK_DBG_SCORES  uint16 [units][cap]              coarse score of retrieval position sink_end + i
+ *   PK_DBG_CAND    int32  [units][cmax]             candidate positions (ascending), first n_cand valid
+ *   PK_DBG_EST     float  [units][cmax]             RSQ-IP estimate of each candidate
+ *   PK_DBG_NCAND   int32  [units][4]                {threshold score, ties taken, n_cand, k_eff}  */
+enum { PK_DBG_IDS = 0, PK_DBG_REC = 1, PK_DBG_LUT = 2, PK_DBG_SCORES = 3, PK_DBG_CAND = 4,
+       PK_DBG_EST = 5, PK_DBG_NCAND = 6 };
+size_t pk_debug_size(const pk_ctx* ctx, int32_t what);
+pk_status pk_debug_copy(pk_ctx* ctx, int32_t what, void* host_dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARISKV_H */

@@ -1,0 +1,431 @@
+// Host side of the C ABI: validation, ownership, the window mirror and launch
+// sequencing.  Every step of the decode path runs in the HIP kernels; this
+// file only decides sizes and launches them in stream order.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "pariskv.h"
+#include "pk_device.hpp"
+#include "pk_launch.hpp"
+
+using pk::CodeTables;
+
+struct pk_ctx {
+    pk_config cfg;
+    int batch = 0, n_kv = 0, n_q = 0, G = 0, units = 0;
+    int64_t cap = 0;
+    pk_dtype dt = PK_BF16;
+    void* K = nullptr;
+    void* V = nullptr;
+    pk_mem mem = PK_MEM_DEVICE;
+    int device = 0;
+    CodeTables tab{};
+    // window mirror (identical for every unit)
+    bool prefilled = false;
+    int64_t n = 0, sink_end = 0, r_end = 0, buf = 0;
+    // sizes
+    int nbins = 0, max_chunks = 0, max_splits = 0;
+    int64_t cmax = 0;
+    // device buffers
+    uint8_t* ids = nullptr;       // [units][cap][16]
+    uint8_t* rec = nullptr;       // [units][cap][128]
+    uint8_t* lut = nullptr;       // [units][16][256]
+    float* ysum = nullptr;        // [units][128]
+    uint16_t* scores = nullptr;   // [units][cap]
+    uint32_t* bhist = nullptr;    // [units][max_chunks][nbins]
+    int32_t* meta = nullptr;      // [units][4]
+    int32_t* off = nullptr;       // [units][max_chunks][2]
+    int32_t* cand_pos = nullptr;  // [units][cmax]
+    float* cand_est = nullptr;    // [units][cmax]
+    uint32_t* tickets = nullptr;  // [3][units]
+    float* part = nullptr;        // [units][max_splits][G][130]
+    // optional per-stage timing
+    bool profiling = false;
+    struct Mark {
+        int stage;
+        hipEvent_t a, b;
+    };
+    std::vector<Mark> marks;
+    std::vector<hipEvent_t> event_pool;
+};
+
+namespace {
+
+bool g_verbose = std::getenv("PK_VERBOSE") != nullptr;
+
+pk_status hip_fail(hipError_t e, const char* what) {
+    if (g_verbose) std::fprintf(stderr, "pariskv: %s: %s\n", what, hipGetErrorString(e));
+    return e == hipErrorOutOfMemory ? PK_ERR_OOM : PK_ERR_HIP;
+}
+
+#define PK_HIP(call)                                      \
+    do {                                                  \
+        hipError_t e_ = (call);                           \
+        if (e_ != hipSuccess) return hip_fail(e_, #call); \
+    } while (0)
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+hipEvent_t take_event(pk_ctx* c) {
+    if (!c->event_pool.empty()) {
+        hipEvent_t e = c->event_pool.back();
+        c->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one launch with events when profiling is on.
+struct StageTimer {
+    pk_ctx* c;
+    int stage;
+    hipStream_t st;
+    hipEvent_t a = nullptr;
+    StageTimer(pk_ctx* c_, int stage_, hipStream_t st_) : c(c_), stage(stage_), st(st_) {
+        if (c->profiling && (a = take_event(c)) != nullptr) (void)hipEventRecord(a, st);
+    }
+    ~StageTimer() {
+        if (!a) return;
+        hipEvent_t b = take_event(c);
+        if (!b) {
+            c->event_pool.push_back(a);
+            return;
+        }
+        (void)hipEventRecord(b, st);
+        c->marks.push_back({stage, a, b});
+    }
+};
+
+int64_t coarse_count(int64_t n_r, int permille, int top_k) {
+    const int64_t frac = ceil_div((int64_t)permille * n_r, 1000);
+    int64_t c = frac > top_k ? frac : top_k;
+    return c < n_r ? c : n_r;
+}
+
+int choose_chunk(int units, int64_t n_r) {
+    int chunk = 256;
+    while (chunk < 8192 && (int64_t)units * ceil_div(n_r, chunk) > 2048) chunk *= 2;
+    return chunk;
+}
+
+size_t dtype_size(pk_dtype d) { return d == PK_F32 ? 4 : 2; }
+
+void release_events(pk_ctx* c) {
+    for (auto& m : c->marks) {
+        c->event_pool.push_back(m.a);
+        c->event_pool.push_back(m.b);
+    }
+    c->marks.clear();
+}
+
+void free_all(pk_ctx* c) {
+    release_events(c);
+    for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
+    c->event_pool.clear();
+    void* bufs[] = {c->ids, c->rec,      c->lut,      c->ysum,    c->scores, c->bhist,
+                    c->meta, c->off,     c->cand_pos, c->cand_est, c->tickets, c->part};
+    for (void* p : bufs)
+        if (p) (void)hipFree(p);
+}
+
+pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capacity, int* G_out,
+                          int* nbins_out) {
+    if (!cfg || n_kv < 1 || n_q < 1 || capacity < 1) return PK_ERR_INVALID;
+    if (cfg->head_dim != 128 || cfg->n_sub != 16 || cfg->sub_dim != 8) return PK_ERR_UNSUPPORTED;
+    if (cfg->rho < 1 || cfg->rho > pk::kRhoMax) return PK_ERR_INVALID;
+    if (cfg->coarse_permille < 1 || cfg->coarse_permille > 1000) return PK_ERR_INVALID;
+    if (cfg->top_k < 1 || cfg->n_sink < 0 || cfg->n_local < 0 || cfg->buf_tokens < 0)
+        return PK_ERR_INVALID;
+    if (cfg->buf_tokens > 0 && cfg->buf_tokens > cfg->n_local) return PK_ERR_INVALID;
+    if (n_q % n_kv != 0) return PK_ERR_INVALID;
+    const int G = n_q / n_kv;
+    if (G < 1 || G > 16) return PK_ERR_INVALID;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return PK_ERR_UNSUPPORTED;
+    int wmax = 0;
+    for (int r = 0; r < cfg->rho; ++r) {
+        if (cfg->vote_weight[r] < 1) return PK_ERR_INVALID;
+        if (cfg->vote_weight[r] > wmax) wmax = cfg->vote_weight[r];
+    }
+    if (G * wmax > 255) return PK_ERR_INVALID;
+    const int nbins = cfg->n_sub * G * wmax + 1;
+    if (nbins > pk::kMaxBins) return PK_ERR_UNSUPPORTED;
+    if (capacity > (int64_t)1 << 24) return PK_ERR_UNSUPPORTED;
+    *G_out = G;
+    *nbins_out = nbins;
+    return PK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pk_status_string(pk_status s) {
+    switch (s) {
+        case PK_OK: return "ok";
+        case PK_ERR_INVALID: return "invalid argument";
+        case PK_ERR_NO_DEVICE: return "no gfx950 device";
+        case PK_ERR_OOM: return "device out of memory";
+        case PK_ERR_CAPACITY: return "capacity exceeded";
+        case PK_ERR_HIP: return "HIP runtime error";
+        case PK_ERR_UNSUPPORTED: return "unsupported configuration";
+    }
+    return "unknown status";
+}
+
+pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
+                    int64_t capacity, pk_dtype kv_dtype, void* k_store, void* v_store,
+                    pk_mem store_mem, pk_ctx** out) {
+    if (!out) return PK_ERR_INVALID;
+    *out = nullptr;
+    if (batch < 1 || !k_store || !v_store) return PK_ERR_INVALID;
+    if (kv_dtype != PK_F32 && kv_dtype != PK_BF16) return PK_ERR_INVALID;
+    if (store_mem != PK_MEM_DEVICE && store_mem != PK_MEM_HOST_MAPPED) return PK_ERR_INVALID;
+    int G = 0, nbins = 0;
+    pk_status st = validate_config(cfg, n_kv_heads, n_q_heads, capacity, &G, &nbins);
+    if (st != PK_OK) return st;
+    if ((reinterpret_cast<uintptr_t>(k_store) | reinterpret_cast<uintptr_t>(v_store)) & 15)
+        return PK_ERR_INVALID;
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return PK_ERR_NO_DEVICE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_NO_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PK_ERR_NO_DEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return PK_ERR_NO_DEVICE;
+
+    pk_ctx* c = new (std::nothrow) pk_ctx();
+    if (!c) return PK_ERR_OOM;
+    c->cfg = *cfg;
+    c->batch = batch;
+    c->n_kv = n_kv_heads;
+    c->n_q = n_q_heads;
+    c->G = G;
+    c->units = batch * n_kv_heads;
+    c->cap = capacity;
+    c->dt = kv_dtype;
+    c->K = k_store;
+    c->V = v_store;
+    c->mem = store_mem;
+    c->device = dev;
+    c->nbins = nbins;
+    if (pk_codebook(cfg->sub_dim, 8, c->tab.levels, c->tab.sq_thr) != PK_OK) {
+        delete c;
+        return PK_ERR_INVALID;
+    }
+    c->max_chunks = (int)std::min<int64_t>(pk::kMaxChunks, ceil_div(capacity, 256));
+    c->cmax = coarse_count(capacity, cfg->coarse_permille, cfg->top_k);
+    if (c->cmax < 1) c->cmax = 1;
+    c->max_splits = (int)ceil_div((int64_t)cfg->n_sink + cfg->n_local + cfg->buf_tokens + cfg->top_k,
+                                  pk::attend_split());
+
+    const int64_t U = c->units;
+    struct Alloc {
+        void** p;
+        size_t bytes;
+    } allocs[] = {
+        {(void**)&c->ids, (size_t)(U * capacity * pk::kSub)},
+        {(void**)&c->rec, (size_t)(U * capacity * pk::kRec)},
+        {(void**)&c->lut, (size_t)(U * pk::kSub * 256)},
+        {(void**)&c->ysum, (size_t)(U * pk::kD * 4)},
+        {(void**)&c->scores, (size_t)(U * capacity * 2)},
+        {(void**)&c->bhist, (size_t)(U * c->max_chunks * (int64_t)nbins * 4)},
+        {(void**)&c->meta, (size_t)(U * 4 * 4)},
+        {(void**)&c->off, (size_t)(U * c->max_chunks * 2 * 4)},
+        {(void**)&c->cand_pos, (size_t)(U * c->cmax * 4)},
+        {(void**)&c->cand_est, (size_t)(U * c->cmax * 4)},
+        {(void**)&c->tickets, (size_t)(3 * U * 4)},
+        {(void**)&c->part, (size_t)(U * c->max_splits * (int64_t)G * (pk::kD + 2) * 4)},
+    };
+    for (auto& a : allocs) {
+        if (hipMalloc(a.p, a.bytes) != hipSuccess) {
+            free_all(c);
+            delete c;
+            return PK_ERR_OOM;
+        }
+    }
+    if (hipMemset(c->tickets, 0, 3 * U * 4) != hipSuccess ||
+        hipMemset(c->meta, 0, U * 16) != hipSuccess ||
+        hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        free_all(c);
+        delete c;
+        return PK_ERR_HIP;
+    }
+    *out = c;
+    return PK_OK;
+}
+
+void pk_destroy(pk_ctx* ctx) {
+    if (!ctx) return;
+    (void)hipDeviceSynchronize();
+    free_all(ctx);
+    delete ctx;
+}
+
+pk_status pk_get_window(const pk_ctx* c, int64_t* n_tokens, int64_t* sink_end, int64_t* r_end,
+                        int64_t* buf) {
+    if (!c) return PK_ERR_INVALID;
+    if (n_tokens) *n_tokens = c->n;
+    if (sink_end) *sink_end = c->sink_end;
+    if (r_end) *r_end = c->r_end;
+    if (buf) *buf = c->buf;
+    return PK_OK;
+}
+
+pk_status pk_encode_keys(pk_ctx* c, int64_t n_tokens, void* stream) {
+    if (!c || n_tokens < 1) return PK_ERR_INVALID;
+    if (n_tokens > c->cap) return PK_ERR_CAPACITY;
+    const int64_t sink_end = std::min<int64_t>(c->cfg.n_sink, n_tokens);
+    const int64_t r_end = std::max<int64_t>(sink_end, n_tokens - c->cfg.n_local);
+    StageTimer tm(c, PK_STAGE_ENCODE, (hipStream_t)stream);
+    PK_HIP(pk::launch_encode(c->dt == PK_BF16, c->K, c->cap, c->units, sink_end, r_end - sink_end,
+                             c->ids, c->rec, c->cfg.sign_bits, c->tab, (hipStream_t)stream));
+    c->n = n_tokens;
+    c->sink_end = sink_end;
+    c->r_end = r_end;
+    c->buf = 0;
+    c->prefilled = true;
+    return PK_OK;
+}
+
+pk_status pk_append_decode_keys(pk_ctx* c, const void* k_new, const void* v_new, void* stream) {
+    if (!c || !k_new || !v_new) return PK_ERR_INVALID;
+    if (!c->prefilled || c->cfg.buf_tokens == 0) return PK_ERR_INVALID;
+    if (c->n + 1 > c->cap) return PK_ERR_CAPACITY;
+    const hipStream_t st = (hipStream_t)stream;
+    if (c->buf >= c->cfg.buf_tokens) {
+        // the previous step filled the buffer: oldest local tokens -> retrieval (encoded),
+        // buffer -> local
+        const int64_t local = c->n - c->buf - c->r_end;
+        const int64_t move = std::max<int64_t>(0, local + c->buf - c->cfg.n_local);
+        StageTimer tm(c, PK_STAGE_ENCODE, st);
+        if (move > 0)
+            PK_HIP(pk::launch_encode(c->dt == PK_BF16, c->K, c->cap, c->units, c->r_end, move,
+                                     c->ids, c->rec, c->cfg.sign_bits, c->tab, st));
+        c->r_end += move;
+        c->buf = 0;
+    }
+    const int64_t row = (int64_t)pk::kD * dtype_size(c->dt);
+    {
+        StageTimer tm(c, PK_STAGE_APPEND, st);
+        PK_HIP(pk::launch_append(k_new, v_new, c->K, c->V, row, c->cap, c->n, c->units, st));
+    }
+    c->n += 1;
+    c->buf += 1;
+    return PK_OK;
+}
+
+pk_status pk_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, void* stream) {
+    if (!c || !q || !sel || !sel_n) return PK_ERR_INVALID;
+    if (!c->prefilled) return PK_ERR_INVALID;
+    const hipStream_t st = (hipStream_t)stream;
+    const bool bf16 = c->dt == PK_BF16;
+    {
+        StageTimer tm(c, PK_STAGE_QPREP, st);
+        PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
+                                c->cfg.vote_weight, c->lut, c->ysum, st));
+    }
+    const int64_t n_r = c->r_end - c->sink_end;
+    if (n_r <= 0) {
+        PK_HIP(pk::launch_empty_select(c->units, sel_n, c->meta, st));
+        return PK_OK;
+    }
+    const int64_t C = coarse_count(n_r, c->cfg.coarse_permille, c->cfg.top_k);
+    const int chunk = choose_chunk(c->units, n_r);
+    const int n_chunks = (int)ceil_div(n_r, chunk);
+    uint32_t* t_scan = c->tickets;
+    uint32_t* t_rerank = c->tickets + c->units;
+    {
+        StageTimer tm(c, PK_STAGE_SCAN, st);
+        PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
+                               c->max_chunks, c->lut, c->scores, c->bhist, c->nbins, t_scan,
+                               c->meta, c->off, C, c->cfg.top_k, st));
+    }
+    StageTimer tm(c, PK_STAGE_RERANK, st);
+    PK_HIP(pk::launch_rerank(chunk, c->scores, c->rec, c->cap, c->units, c->sink_end, n_r, n_chunks,
+                             c->max_chunks, c->meta, c->off, c->ysum, c->tab, c->cand_pos,
+                             c->cand_est, c->cmax, t_rerank, c->cfg.top_k, sel, sel_n, st));
+    return PK_OK;
+}
+
+pk_status pk_sparse_attend(pk_ctx* c, const void* q, const int32_t* sel, const int32_t* sel_n,
+                           float* out, void* stream) {
+    if (!c || !q || !sel || !sel_n || !out) return PK_ERR_INVALID;
+    if (!c->prefilled) return PK_ERR_INVALID;
+    const int64_t hot = c->sink_end + (c->n - c->r_end);
+    const int n_splits = (int)ceil_div(hot + c->cfg.top_k, pk::attend_split());
+    if (n_splits > c->max_splits) return PK_ERR_INVALID;
+    StageTimer tm(c, PK_STAGE_ATTEND, (hipStream_t)stream);
+    PK_HIP(pk::launch_attend(c->dt == PK_BF16, c->G, c->K, c->V, c->cap, c->units, q, c->sink_end,
+                             c->r_end, c->n, sel, sel_n, c->cfg.top_k, n_splits, c->part,
+                             c->tickets + 2 * c->units, out, (hipStream_t)stream));
+    return PK_OK;
+}
+
+pk_status pk_profile_enable(pk_ctx* c, int32_t on) {
+    if (!c) return PK_ERR_INVALID;
+    if (hipDeviceSynchronize() != hipSuccess) return PK_ERR_HIP;
+    release_events(c);
+    c->profiling = on != 0;
+    return PK_OK;
+}
+
+pk_status pk_profile_read(pk_ctx* c, double* ms, int64_t* launches) {
+    if (!c || !ms || !launches) return PK_ERR_INVALID;
+    for (int i = 0; i < PK_STAGE_COUNT; ++i) {
+        ms[i] = 0.0;
+        launches[i] = 0;
+    }
+    for (auto& m : c->marks) {
+        PK_HIP(hipEventSynchronize(m.b));
+        float t = 0.0f;
+        PK_HIP(hipEventElapsedTime(&t, m.a, m.b));
+        ms[m.stage] += t;
+        launches[m.stage] += 1;
+    }
+    return PK_OK;
+}
+
+size_t pk_debug_size(const pk_ctx* c, int32_t what) {
+    if (!c) return 0;
+    const size_t U = (size_t)c->units, cap = (size_t)c->cap;
+    switch (what) {
+        case PK_DBG_IDS: return U * cap * pk::kSub;
+        case PK_DBG_REC: return U * cap * pk::kRec;
+        case PK_DBG_LUT: return U * pk::kSub * 256;
+        case PK_DBG_SCORES: return U * cap * 2;
+        case PK_DBG_CAND: return U * (size_t)c->cmax * 4;
+        case PK_DBG_EST: return U * (size_t)c->cmax * 4;
+        case PK_DBG_NCAND: return U * 16;
+    }
+    return 0;
+}
+
+pk_status pk_debug_copy(pk_ctx* c, int32_t what, void* host_dst, size_t bytes, void* stream) {
+    if (!c || !host_dst) return PK_ERR_INVALID;
+    const size_t need = pk_debug_size(c, what);
+    if (need == 0 || bytes != need) return PK_ERR_INVALID;
+    const void* src = nullptr;
+    switch (what) {
+        case PK_DBG_IDS: src = c->ids; break;
+        case PK_DBG_REC: src = c->rec; break;
+        case PK_DBG_LUT: src = c->lut; break;
+        case PK_DBG_SCORES: src = c->scores; break;
+        case PK_DBG_CAND: src = c->cand_pos; break;
+        case PK_DBG_EST: src = c->cand_est; break;
+        case PK_DBG_NCAND: src = c->meta; break;
+    }
+    const hipStream_t st = (hipStream_t)stream;
+    PK_HIP(hipMemcpyAsync(host_dst, src, bytes, hipMemcpyDeviceToHost, st));
+    PK_HIP(hipStreamSynchronize(st));
+    return PK_OK;
+}
+
+}  // extern "C"

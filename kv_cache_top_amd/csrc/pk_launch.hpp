@@ -1,0 +1,36 @@
+// Kernel launchers (host side), one per kernel family.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pk {
+
+struct CodeTables;
+
+hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64_t p0,
+                         int64_t count, uint8_t* ids, uint8_t* rec, const uint64_t sign[2],
+                         const CodeTables& tab, hipStream_t st);
+hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
+                        int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
+                        hipStream_t st);
+hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
+                         int64_t row_bytes, int64_t cap, int64_t pos, int units, hipStream_t st);
+hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
+                       int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
+                       uint16_t* scores, uint32_t* bhist, int nbins, uint32_t* tickets,
+                       int32_t* meta, int32_t* off, int64_t C, int top_k, hipStream_t st);
+hipError_t launch_rerank(int chunk, const uint16_t* scores, const uint8_t* rec, int64_t cap,
+                         int units, int64_t sink_end, int64_t n_r, int n_chunks, int max_chunks,
+                         const int32_t* meta, const int32_t* off, const float* ysum,
+                         const CodeTables& tab, int32_t* cand_pos, float* cand_est, int64_t cmax,
+                         uint32_t* tickets, int top_k, int32_t* sel, int32_t* sel_n,
+                         hipStream_t st);
+hipError_t launch_empty_select(int units, int32_t* sel_n, int32_t* meta, hipStream_t st);
+int attend_split();
+hipError_t launch_attend(bool bf16, int G, const void* K, const void* V, int64_t cap, int units,
+                         const void* q, int64_t sink_end, int64_t r_end, int64_t n_tok,
+                         const int32_t* sel, const int32_t* sel_n, int top_k, int n_splits,
+                         float* part, uint32_t* tickets, float* out, hipStream_t st);
+
+}  // namespace pk

@@ -1,0 +1,140 @@
+"""Python front end of the ParisKV decode path on MI355X.
+
+`ParisKV` owns a library context over a K/V store.  torch allocates the store
+and the outputs and supplies the current HIP stream; every computation runs
+in libpariskv.so's kernels.  There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _native as nat
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_DT = {torch.float32: nat.PK_F32, torch.bfloat16: nat.PK_BF16}
+
+
+class ParisKV:
+    """One layer's KV cache with ParisKV retrieval.
+
+    Stores are [batch, n_kv, capacity, 128] in `dtype`; pass your own (device,
+    or pinned host memory with host_mapped=True) or let the class allocate
+    device ones.  Queries are [batch, n_q, 128] in the same dtype.
+    """
+
+    def __init__(self, *, batch: int, n_kv: int, n_q: int, capacity: int,
+                 dtype: torch.dtype = torch.bfloat16, config: nat.PkConfig | None = None,
+                 k_store: torch.Tensor | None = None, v_store: torch.Tensor | None = None,
+                 host_mapped: bool = False, device: str | torch.device = "cuda", **cfg_kw):
+        if not torch.cuda.is_available():
+            raise RuntimeError("ParisKV needs a ROCm GPU (gfx950); no device is visible")
+        if dtype not in _DT:
+            raise ValueError(f"unsupported dtype {dtype}")
+        self.cfg = config if config is not None else nat.make_config(**cfg_kw)
+        self.batch, self.n_kv, self.n_q, self.capacity, self.dtype = batch, n_kv, n_q, capacity, dtype
+        self.group = n_q // n_kv
+        shape = (batch, n_kv, capacity, 128)
+        if k_store is None:
+            k_store = torch.empty(shape, dtype=dtype, device=device)
+        if v_store is None:
+            v_store = torch.empty(shape, dtype=dtype, device=device)
+        for t in (k_store, v_store):
+            if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
+                raise ValueError(f"store must be a contiguous {dtype} tensor of shape {shape}")
+        self.K, self.V = k_store, v_store
+        self.device = torch.device(device)
+        self._ctx = ctypes.c_void_p()
+        nat.check(nat.lib.pk_create(ctypes.byref(self.cfg), batch, n_kv, n_q, capacity, _DT[dtype],
+                                    _ptr(k_store), _ptr(v_store),
+                                    nat.PK_MEM_HOST_MAPPED if host_mapped else nat.PK_MEM_DEVICE,
+                                    ctypes.byref(self._ctx)), "pk_create")
+
+    # -- lifecycle ---------------------------------------------------------
+    def close(self) -> None:
+        if self._ctx:
+            nat.lib.pk_destroy(self._ctx)
+            self._ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- the four calls of the decode path ----------------------------------
+    def encode_keys(self, n_tokens: int, stream=None) -> None:
+        nat.check(nat.lib.pk_encode_keys(self._ctx, n_tokens, _stream(stream)), "pk_encode_keys")
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+        self._check_rows(k_new, (self.batch, self.n_kv, 128))
+        self._check_rows(v_new, (self.batch, self.n_kv, 128))
+        nat.check(nat.lib.pk_append_decode_keys(self._ctx, _ptr(k_new), _ptr(v_new), _stream(stream)),
+                  "pk_append_decode_keys")
+
+    def retrieve(self, q: torch.Tensor, sel: torch.Tensor | None = None,
+                 sel_n: torch.Tensor | None = None, stream=None):
+        self._check_rows(q, (self.batch, self.n_q, 128))
+        if sel is None:
+            sel = torch.empty((self.batch, self.n_kv, self.cfg.top_k), dtype=torch.int32, device=q.device)
+        if sel_n is None:
+            sel_n = torch.empty((self.batch, self.n_kv), dtype=torch.int32, device=q.device)
+        nat.check(nat.lib.pk_retrieve(self._ctx, _ptr(q), _ptr(sel), _ptr(sel_n), _stream(stream)),
+                  "pk_retrieve")
+        return sel, sel_n
+
+    def sparse_attend(self, q: torch.Tensor, sel: torch.Tensor, sel_n: torch.Tensor,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        self._check_rows(q, (self.batch, self.n_q, 128))
+        if sel.dtype != torch.int32 or tuple(sel.shape) != (self.batch, self.n_kv, self.cfg.top_k):
+            raise ValueError("sel must be int32 [batch, n_kv, top_k]")
+        if sel_n.dtype != torch.int32 or tuple(sel_n.shape) != (self.batch, self.n_kv):
+            raise ValueError("sel_n must be int32 [batch, n_kv]")
+        if out is None:
+            out = torch.empty((self.batch, self.n_q, 128), dtype=torch.float32, device=q.device)
+        nat.check(nat.lib.pk_sparse_attend(self._ctx, _ptr(q), _ptr(sel), _ptr(sel_n), _ptr(out),
+                                           _stream(stream)), "pk_sparse_attend")
+        return out
+
+    def step(self, q: torch.Tensor, stream=None):
+        """Retrieve then attend; returns (out, sel, sel_n)."""
+        sel, sel_n = self.retrieve(q, stream=stream)
+        return self.sparse_attend(q, sel, sel_n, stream=stream), sel, sel_n
+
+    # -- introspection -------------------------------------------------------
+    def window(self):
+        vals = [ctypes.c_int64() for _ in range(4)]
+        nat.check(nat.lib.pk_get_window(self._ctx, *[ctypes.byref(v) for v in vals]), "pk_get_window")
+        return tuple(v.value for v in vals)   # (n_tokens, sink_end, r_end, buf)
+
+    _DBG_DTYPE = {nat.PK_DBG_IDS: np.uint8, nat.PK_DBG_REC: np.uint8, nat.PK_DBG_LUT: np.uint8,
+                  nat.PK_DBG_SCORES: np.uint16, nat.PK_DBG_CAND: np.int32, nat.PK_DBG_EST: np.float32,
+                  nat.PK_DBG_NCAND: np.int32}
+
+    def debug(self, what: int, stream=None) -> np.ndarray:
+        n = nat.lib.pk_debug_size(self._ctx, what)
+        buf = np.empty(n, np.uint8)
+        nat.check(nat.lib.pk_debug_copy(self._ctx, what, buf.ctypes.data_as(ctypes.c_void_p), n,
+                                        _stream(stream)), "pk_debug_copy")
+        arr = buf.view(self._DBG_DTYPE[what])
+        units = self.batch * self.n_kv
+        return arr.reshape(units, -1)
+
+    def _check_rows(self, t: torch.Tensor, shape):
+        if tuple(t.shape) != shape or t.dtype != self.dtype or not t.is_contiguous():
+            raise ValueError(f"expected a contiguous {self.dtype} tensor of shape {shape}, "
+                             f"got {tuple(t.shape)} {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError("inputs must be device tensors")

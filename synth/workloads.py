@@ -64,6 +64,9 @@ class Workload:
     V: np.ndarray
     Q: np.ndarray            # float32 [batch, n_kv*group, d]
     planted: np.ndarray | None = None   # int64 [batch, n_kv, n_plant] positions
+    planted_dir: np.ndarray | None = None  # float64 [batch, n_kv, d] unit directions
+    seed: int = 0
+    layer: int = 0
 
     @property
     def n_units(self) -> int:
@@ -122,6 +125,7 @@ def _build(name, batch, n_kv, group, N, dtype, params, seed, layer, n_outlier,
     V = np.empty((batch, n_kv, N, d), np.float32)
     Q = np.empty((batch, n_kv * group, d), np.float32)
     planted = np.empty((batch, n_kv, n_plant), np.int64) if n_plant else None
+    pdir = np.empty((batch, n_kv, d), np.float64) if n_plant else None
 
     def one(u):
         b, h = divmod(u, n_kv)
@@ -146,6 +150,7 @@ def _build(name, batch, n_kv, group, N, dtype, params, seed, layer, n_outlier,
                 q64[g] = np.linalg.norm(q64[g]) * (plant_cos * uhat + math.sqrt(1 - plant_cos**2) * e)
             q = q64.astype(np.float32)
             planted[b, h] = pos
+            pdir[b, h] = uhat
         if dtype == "bf16":
             k, v, q = round_bf16(k), round_bf16(v), round_bf16(q)
         K[b, h] = k
@@ -155,7 +160,7 @@ def _build(name, batch, n_kv, group, N, dtype, params, seed, layer, n_outlier,
     with ThreadPoolExecutor(max(1, threads)) as ex:
         list(ex.map(one, range(units)))
     return Workload(name, batch, n_kv, group, N, dtype, params, sign_bits(seed, layer),
-                    K, V, Q, planted)
+                    K, V, Q, planted, pdir, seed, layer)
 
 
 # ---------------------------------------------------------------------------
@@ -221,3 +226,29 @@ def decode_stream(w: Workload, n_steps: int, drift_sigma: float = 2.0, seed: int
         Vn[:, b, h] = v
         Qn[:, b, h * w.group:(h + 1) * w.group] = q
     return Kn, Vn, Qn
+
+
+def query_pool(w: Workload, n: int, plant_cos: float = 0.3) -> np.ndarray:
+    """n further query sets drawn with the workload's recipe (new draws, same
+    channel scales; planted workloads: new noisy copies of the planted
+    direction).  float32 [n, batch, n_kv*G, d]."""
+    d = w.params.head_dim
+    out = np.empty((n, w.batch, w.n_kv * w.group, d), np.float32)
+    for u in range(w.n_units):
+        b, h = divmod(u, w.n_kv)
+        s_k = _channel_scales(_rng(w.seed, w.layer, u, _S_SCALE), d, 4 if w.dtype == "bf16" else 0)
+        r = _rng(w.seed, w.layer, u, 1000 + _S_QUERY)
+        q = r.standard_normal((n, w.group, d)) * s_k
+        if w.planted_dir is not None:
+            uhat = w.planted_dir[b, h]
+            for i in range(n):
+                for g in range(w.group):
+                    e = r.standard_normal(d)
+                    e -= (e @ uhat) * uhat
+                    e /= np.linalg.norm(e)
+                    q[i, g] = np.linalg.norm(q[i, g]) * (plant_cos * uhat +
+                                                         math.sqrt(1 - plant_cos**2) * e)
+        if w.dtype == "bf16":
+            q = round_bf16(q)
+        out[:, b, h * w.group:(h + 1) * w.group] = q
+    return out

@@ -1,0 +1,183 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI on a
+synthetic workload and compare every stage with the oracle (per unit)."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from oracle import pariskv as ok
+from oracle.codebook import spec_tables
+
+LEVELS, SQ_T = spec_tables()
+
+# acceptance bars
+W_RTOL = 1e-6          # calibration scale (fp32 on both sides; derivation in the design notes)
+EST_RTOL = 1e-4        # RSQ-IP estimate, relative to the sum of the absolute terms
+ATT_TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(wl):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def make_ctx(wl, capacity=None, **override):
+    from kv_cache_top_amd import ParisKV
+    p = wl.params
+    kw = dict(rho=p.rho, vote_weights=p.vote_weights, coarse_permille=p.coarse_permille,
+              top_k=p.top_k, n_sink=p.n_sink, n_local=p.n_local, buf_tokens=p.buf_tokens,
+              sign_bits=tuple(int(x) for x in wl.sign_bits))
+    kw.update(override)
+    cap = capacity or wl.n_tokens
+    dt = torch_dtype(wl)
+    pkv = ParisKV(batch=wl.batch, n_kv=wl.n_kv, n_q=wl.n_kv * wl.group, capacity=cap, dtype=dt, **kw)
+    N = wl.n_tokens
+    pkv.K[:, :, :N].copy_(torch.from_numpy(wl.K).to(dt))
+    pkv.V[:, :, :N].copy_(torch.from_numpy(wl.V).to(dt))
+    return pkv
+
+
+def queries(wl, Q=None):
+    Q = wl.Q if Q is None else Q
+    return torch.from_numpy(np.ascontiguousarray(Q)).to(torch_dtype(wl)).cuda()
+
+
+def unit_view(wl, u):
+    b, h = divmod(u, wl.n_kv)
+    return wl.K[b, h], wl.V[b, h], wl.Q[b, h * wl.group:(h + 1) * wl.group]
+
+
+def est_scale(nib, w, Qg, signs):
+    """sum_g sum_b |w_b <v_b, (R q_g)_b>|: the magnitude the estimate error is measured against."""
+    v = ok.dequantize(ok.unpack_nibbles(nib, 16, 8), LEVELS)
+    R = ok.srht_matrix(signs)
+    w = np.asarray(w, np.float64)
+    s = np.zeros(v.shape[0])
+    for q in np.atleast_2d(np.asarray(Qg, np.float64)):
+        y = (R @ q).reshape(16, 8)
+        s += np.sum(np.abs(w * np.einsum("nbj,bj->nb", v, y)), axis=1)
+    return s
+
+
+class UnitReport:
+    def __init__(self):
+        self.lines = []
+
+    def add(self, s):
+        self.lines.append(s)
+
+
+def check_encode(wl, pkv, units, ids_all=None, rec_all=None):
+    """ids and nibbles bit-exact, w within W_RTOL, for the retrieval zone of `units`."""
+    n, sink_end, r_end, _ = pkv.window()
+    ids_all = pkv.debug(0) if ids_all is None else ids_all
+    rec_all = pkv.debug(1) if rec_all is None else rec_all
+    s = wl.signs()
+    out = {}
+    for u in units:
+        K, _, _ = unit_view(wl, u)
+        pos = np.arange(sink_end, r_end)
+        i_o, n_o, w_o = ok.encode_keys(K[pos], s, LEVELS, SQ_T)
+        ids_g = ids_all[u].reshape(-1, 16)[pos]
+        rec_g = rec_all[u].reshape(-1, 128)[pos]
+        nib_g = rec_g[:, :64]
+        w_g = rec_g[:, 64:].copy().view(np.float32)
+        assert np.array_equal(ids_g, i_o), f"unit {u}: bucket ids differ at {np.argwhere(ids_g != i_o)[:5]}"
+        assert np.array_equal(nib_g, n_o), f"unit {u}: nibbles differ at {np.argwhere(nib_g != n_o)[:5]}"
+        rel = np.abs(w_g.astype(np.float64) - w_o) / np.maximum(np.abs(w_o), 1e-30)
+        assert np.all(rel <= W_RTOL), f"unit {u}: w rel err {rel.max():.3g}"
+        out[u] = (i_o, n_o, w_o)
+    return out
+
+
+def check_retrieval(wl, pkv, units, sel, sel_n, enc):
+    """LUT, scores, candidates bit-exact; estimates within EST_RTOL; fine sets by the tie rule.
+    Returns per-unit oracle results."""
+    n, sink_end, r_end, _ = pkv.window()
+    lut = pkv.debug(2)
+    scores = pkv.debug(3)
+    cand = pkv.debug(4)
+    est = pkv.debug(5)
+    meta = pkv.debug(6)
+    sel = sel.cpu().numpy().reshape(wl.n_units, -1)
+    sel_n = sel_n.cpu().numpy().reshape(-1)
+    s = wl.signs()
+    p = wl.params
+    res = {}
+    for u in units:
+        K, V, Qg = unit_view(wl, u)
+        i_o, n_o, w_o = enc[u]
+        pos = np.arange(sink_end, r_end)
+        N_r = pos.size
+        L, _ = ok.vote_table(Qg, s, p.rho, p.vote_weights)
+        assert np.array_equal(lut[u].reshape(16, 256).astype(np.int64), L.astype(np.int64)), \
+            f"unit {u}: vote table differs"
+        sc_o = ok.coarse_scores(i_o, L) if N_r else np.zeros(0, np.int64)
+        assert np.array_equal(scores[u][:N_r].astype(np.int64), sc_o), f"unit {u}: coarse scores differ"
+        C = ok.coarse_count(N_r, p.coarse_permille, p.top_k)
+        assert meta[u][2] == C, f"unit {u}: C {meta[u][2]} != {C}"
+        cand_o = ok.top_by_key(sc_o, pos, C)
+        assert np.array_equal(cand[u][:C], cand_o), f"unit {u}: coarse candidate set differs"
+        rel = cand_o - sink_end
+        e_o = ok.rsq_ip(n_o[rel], w_o[rel], Qg, s, LEVELS) if C else np.zeros(0)
+        scale = est_scale(n_o[rel], w_o[rel], Qg, s) if C else np.zeros(0)
+        err = np.abs(est[u][:C].astype(np.float64) - e_o)
+        assert np.all(err <= EST_RTOL * np.maximum(scale, 1e-30)), \
+            f"unit {u}: est rel err {np.max(err / np.maximum(scale, 1e-30)):.3g}"
+        k_eff = min(p.top_k, C)
+        assert sel_n[u] == k_eff, f"unit {u}: sel_n {sel_n[u]} != {k_eff}"
+        sel_g = sel[u][:k_eff]
+        assert np.all(np.diff(sel_g) > 0), f"unit {u}: sel not strictly ascending"
+        sel_o = ok.top_by_key(e_o, cand_o, k_eff)
+        diff = np.setxor1d(sel_g, sel_o)
+        if diff.size:
+            kth = np.sort(e_o)[::-1][k_eff - 1]
+            idx = np.searchsorted(cand_o, diff)
+            assert np.all(np.isin(diff, cand_o)), f"unit {u}: selected a non-candidate"
+            near = np.abs(e_o[idx] - kth) <= EST_RTOL * np.maximum(scale[idx], 1e-30)
+            assert np.all(near), f"unit {u}: fine sets differ beyond ties: {diff[~near][:5]}"
+        res[u] = dict(sel_o=sel_o, sel_g=sel_g, cand=cand_o, est=e_o, n_diff=int(diff.size))
+    return res
+
+
+def check_attention(wl, pkv, units, sel, sel_n, out, tol=None):
+    """GPU output vs the oracle's attention over hot + the GPU's own selection."""
+    n, sink_end, r_end, _ = pkv.window()
+    sel = sel.cpu().numpy().reshape(wl.n_units, -1)
+    sel_n = sel_n.cpu().numpy().reshape(-1)
+    out = out.cpu().numpy().reshape(wl.n_units, wl.group, 128)
+    tol = ATT_TOL[wl.dtype] if tol is None else tol
+    worst = 0.0
+    for u in units:
+        K, V, Qg = unit_view(wl, u)
+        hot = np.concatenate([np.arange(0, sink_end), np.arange(r_end, n)])
+        A = np.concatenate([hot, sel[u][:sel_n[u]]])
+        ref = ok.sparse_attention(Qg, K[:n], V[:n], A)
+        e = float(np.max(np.abs(out[u] - ref)))
+        worst = max(worst, e)
+        assert e <= tol, f"unit {u}: attention max-abs err {e:.3g} > {tol}"
+    return worst
+
+
+def recall_report(wl, pkv, units, sel, sel_n):
+    n, sink_end, r_end, _ = pkv.window()
+    sel = sel.cpu().numpy().reshape(wl.n_units, -1)
+    sel_n = sel_n.cpu().numpy().reshape(-1)
+    rec, planted = [], []
+    for u in units:
+        K, _, Qg = unit_view(wl, u)
+        pos = np.arange(sink_end, r_end)
+        ref = ok.exact_topk(K, Qg, pos, wl.params.top_k)
+        rec.append(ok.recall(sel[u][:sel_n[u]], ref))
+        if wl.planted is not None:
+            b, h = divmod(u, wl.n_kv)
+            pl = wl.planted[b, h]
+            planted.append(np.isin(pl, sel[u][:sel_n[u]]).mean())
+    return float(np.mean(rec)), (float(np.mean(planted)) if planted else None)

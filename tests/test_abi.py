@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, validates its arguments before touching a device, and computes the
+same codebook as the oracle (bit-exact fp32 tables)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT
+
+nat = pytest.importorskip("kv_cache_top_amd._native", reason="libpariskv.so not built")
+from oracle.codebook import spec_tables  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "pariskv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pk_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    fns = declared_functions()
+    for name in ("pk_encode_keys", "pk_append_decode_keys", "pk_retrieve", "pk_sparse_attend"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(nat.LIB_PATH)
+    missing = [f for f in declared_functions() if not hasattr(lib, f)]
+    assert not missing, missing
+    assert set(declared_functions()) == set(nat.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    for s in range(-6, 1):
+        assert nat.lib.pk_status_string(s)
+    assert nat.lib.pk_status_string(-99) == b"unknown status"
+
+
+def test_library_codebook_matches_oracle_bit_exact():
+    for m in (4, 8, 16):
+        lv, th = nat.codebook(m)
+        c32, T32 = spec_tables(m)
+        assert np.array_equal(lv.view(np.uint32), c32.view(np.uint32))
+        assert np.array_equal(th.view(np.uint32), T32.view(np.uint32))
+
+
+def test_codebook_rejects_bad_arguments():
+    lv = (ctypes.c_float * 8)()
+    th = (ctypes.c_float * 7)()
+    assert nat.lib.pk_codebook(1, 8, lv, th) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_codebook(8, 4, lv, th) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_codebook(8, 8, None, th) == nat.PK_ERR_INVALID
+
+
+def _create(cfg, batch=1, n_kv=8, n_q=32, cap=1000, dtype=nat.PK_BF16, k=16, v=16, mem=0):
+    ctx = ctypes.c_void_p()
+    st = nat.lib.pk_create(ctypes.byref(cfg) if cfg is not None else None, batch, n_kv, n_q, cap,
+                           dtype, ctypes.c_void_p(k), ctypes.c_void_p(v), mem, ctypes.byref(ctx))
+    return st, ctx
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("head_dim", 64, nat.PK_ERR_UNSUPPORTED),
+    ("n_sub", 8, nat.PK_ERR_UNSUPPORTED),
+    ("sub_dim", 16, nat.PK_ERR_UNSUPPORTED),
+    ("rho", 0, nat.PK_ERR_INVALID),
+    ("rho", 9, nat.PK_ERR_INVALID),
+    ("coarse_permille", 0, nat.PK_ERR_INVALID),
+    ("coarse_permille", 1001, nat.PK_ERR_INVALID),
+    ("top_k", 0, nat.PK_ERR_INVALID),
+    ("n_sink", -1, nat.PK_ERR_INVALID),
+    ("buf_tokens", 600, nat.PK_ERR_INVALID),     # larger than n_local
+])
+def test_create_validates_config(field, value, expect):
+    cfg = nat.make_config()
+    setattr(cfg, field, value)
+    st, ctx = _create(cfg)
+    assert st == expect and not ctx.value
+
+
+def test_create_validates_shapes_and_pointers():
+    cfg = nat.make_config()
+    assert _create(None)[0] == nat.PK_ERR_INVALID
+    assert _create(cfg, batch=0)[0] == nat.PK_ERR_INVALID
+    assert _create(cfg, n_q=30)[0] == nat.PK_ERR_INVALID          # not a multiple of n_kv
+    assert _create(cfg, n_q=8 * 3)[0] == nat.PK_ERR_UNSUPPORTED   # G = 3
+    assert _create(cfg, n_q=8 * 32)[0] == nat.PK_ERR_INVALID      # G = 32
+    assert _create(cfg, cap=0)[0] == nat.PK_ERR_INVALID
+    assert _create(cfg, cap=(1 << 24) + 1)[0] == nat.PK_ERR_UNSUPPORTED
+    assert _create(cfg, dtype=7)[0] == nat.PK_ERR_INVALID
+    assert _create(cfg, k=0)[0] == nat.PK_ERR_INVALID
+    assert _create(cfg, k=24)[0] == nat.PK_ERR_INVALID            # not 16-byte aligned
+    assert _create(cfg, mem=5)[0] == nat.PK_ERR_INVALID
+    big = nat.make_config(vote_weights=(200, 1, 1, 1))
+    assert _create(big)[0] == nat.PK_ERR_INVALID                  # G * weight > 255
+    zero = nat.make_config(vote_weights=(4, 3, 0, 1))
+    assert _create(zero)[0] == nat.PK_ERR_INVALID
+
+
+def test_calls_reject_null_context():
+    p = ctypes.c_void_p(16)
+    assert nat.lib.pk_encode_keys(None, 10, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_append_decode_keys(None, p, p, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_retrieve(None, p, p, p, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_sparse_attend(None, p, p, p, p, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_debug_copy(None, 0, p, 1, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_debug_size(None, 0) == 0
+    nat.lib.pk_destroy(None)
+
+
+def test_no_device_is_reported_without_a_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, ctx = _create(nat.make_config())
+    assert st == nat.PK_ERR_NO_DEVICE and not ctx.value

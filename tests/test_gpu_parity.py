@@ -1,0 +1,174 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: bucket ids, nibbles, vote tables, coarse scores and candidate sets
+bit-exact; w within 1e-6 relative; RSQ-IP estimates within 1e-4 of the sum of
+absolute terms; fine sets identical except for members whose oracle estimate
+ties the k-th within that tolerance; attention within 2e-2 (bf16) / 1e-5
+(fp32) max-abs, against the oracle's attention over the same set.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pariskv as ok
+from synth import workloads as W
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import kv_cache_top_amd  # noqa: F401  (fails loudly when the library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+def _full_check(wl, units=None, capacity=None, tag=""):
+    units = list(range(wl.n_units)) if units is None else units
+    gc.log(f"[{tag}] {wl.name} N={wl.n_tokens} units={len(units)}/{wl.n_units}")
+    pkv = gc.make_ctx(wl, capacity=capacity)
+    pkv.encode_keys(wl.n_tokens)
+    q = gc.queries(wl)
+    sel, sel_n = pkv.retrieve(q)
+    out = pkv.sparse_attend(q, sel, sel_n)
+    torch.cuda.synchronize()
+    enc = gc.check_encode(wl, pkv, units)
+    res = gc.check_retrieval(wl, pkv, units, sel, sel_n, enc)
+    err = gc.check_attention(wl, pkv, units, sel, sel_n, out)
+    rec, planted = gc.recall_report(wl, pkv, units, sel, sel_n)
+    nd = sum(r["n_diff"] for r in res.values())
+    gc.log(f"[{tag}] ok: attention max-abs {err:.3g}, fine-set tie swaps {nd}, "
+           f"recall@k {rec:.3f}" + (f", planted recall {planted:.3f}" if planted is not None else ""))
+    return pkv, sel, sel_n, out
+
+
+def test_single_head_4k_f32():
+    _full_check(W.single_head_f32(), tag="single-head")
+
+
+def test_gqa_ragged_small():
+    # several scan chunks per unit and a ragged tail; batch 2 x 8 kv heads
+    _full_check(W.gqa_bf16(N=20011, batch=2, top_k=512), tag="ragged")
+
+
+def test_gqa_32k():
+    _full_check(W.gqa_bf16(N=32768), tag="gqa-32k")
+
+
+def test_gqa_128k_batch4_planted():
+    wl = W.gqa_128k_planted()
+    pkv, sel, sel_n, out = _full_check(wl, units=[0, 13, 31], tag="gqa-128k")
+    # every unit: k ascending positions inside the retrieval zone
+    n, sink_end, r_end, _ = pkv.window()
+    s = sel.cpu().numpy().reshape(wl.n_units, -1)
+    assert np.all(sel_n.cpu().numpy() == wl.params.top_k)
+    assert np.all(np.diff(s, axis=1) > 0) and s.min() >= sink_end and s.max() < r_end
+    assert torch.isfinite(out).all()
+
+
+def test_all_keys_kept_is_full_attention():
+    wl = W.gqa_bf16(N=3000, top_k=4096, permille=1000, n_local=64)
+    pkv = gc.make_ctx(wl)
+    pkv.encode_keys(wl.n_tokens)
+    q = gc.queries(wl)
+    sel, sel_n = pkv.retrieve(q)
+    out = pkv.sparse_attend(q, sel, sel_n).cpu().numpy()
+    assert np.all(sel_n.cpu().numpy() == 3000 - 4 - 64)
+    for u in range(wl.n_units):
+        K, V, Qg = gc.unit_view(wl, u)
+        ref = ok.sparse_attention(Qg, K, V, np.arange(3000))
+        assert np.max(np.abs(out.reshape(8, 4, 128)[u] - ref)) <= 2e-2
+
+
+def test_empty_retrieval_zone():
+    wl = W.gqa_bf16(N=300)                # shorter than sink + local
+    pkv = gc.make_ctx(wl)
+    pkv.encode_keys(300)
+    q = gc.queries(wl)
+    sel, sel_n = pkv.retrieve(q)
+    out = pkv.sparse_attend(q, sel, sel_n).cpu().numpy().reshape(8, 4, 128)
+    assert np.all(sel_n.cpu().numpy() == 0)
+    for u in range(8):
+        K, V, Qg = gc.unit_view(wl, u)
+        assert np.max(np.abs(out[u] - ok.sparse_attention(Qg, K, V, np.arange(300)))) <= 2e-2
+
+
+def test_retrieval_zone_smaller_than_k():
+    _full_check(W.gqa_bf16(N=1000), tag="short")
+
+
+def test_single_token_context():
+    wl = W.single_head_f32(N=1)
+    pkv = gc.make_ctx(wl)
+    pkv.encode_keys(1)
+    q = gc.queries(wl)
+    sel, sel_n = pkv.retrieve(q)
+    out = pkv.sparse_attend(q, sel, sel_n).cpu().numpy()
+    assert sel_n.item() == 0
+    assert np.max(np.abs(out[0, 0] - wl.V[0, 0, 0])) <= 1e-6
+
+
+def test_decode_window_append_evict():
+    """Appends through several buffer fills: the window mirror follows the oracle's,
+    evicted keys are encoded exactly like a prefill encode, and sampled steps match."""
+    T, N0 = 200, 4096
+    wl = W.gqa_bf16(N=N0, top_k=256, n_local=128, buf_tokens=64)
+    Kn, Vn, Qn = W.decode_stream(wl, T)
+    pkv = gc.make_ctx(wl, capacity=N0 + T)
+    pkv.encode_keys(N0)
+    win = ok.Window(N0, 4, 128, 64)
+    dt = gc.torch_dtype(wl)
+    Kall = np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2)
+    Vall = np.concatenate([wl.V, np.moveaxis(Vn, 0, 2)], axis=2)
+    full = W.Workload(wl.name, wl.batch, wl.n_kv, wl.group, N0 + T, wl.dtype, wl.params,
+                      wl.sign_bits, Kall, Vall, wl.Q)
+    check_at = {0, 63, 64, 65, 127, 128, 199}
+    for t in range(T):
+        pkv.append(torch.from_numpy(Kn[t]).to(dt).cuda(), torch.from_numpy(Vn[t]).to(dt).cuda())
+        win.append()
+        assert pkv.window() == (win.n, win.sink_end, win.r_end, win.buf)
+        q = torch.from_numpy(Qn[t]).to(dt).cuda()
+        sel, sel_n = pkv.retrieve(q)
+        out = pkv.sparse_attend(q, sel, sel_n)
+        if t in check_at:
+            torch.cuda.synchronize()
+            full.Q = Qn[t]
+            units = [0, 5]
+            enc = gc.check_encode(full, pkv, units)
+            gc.check_retrieval(full, pkv, units, sel, sel_n, enc)
+            gc.check_attention(full, pkv, units, sel, sel_n, out)
+            gc.log(f"[decode] step {t}: window {pkv.window()} ok")
+        win.end_step()
+
+
+def test_deterministic():
+    wl = W.gqa_bf16(N=20011, top_k=512)
+    pkv = gc.make_ctx(wl)
+    pkv.encode_keys(wl.n_tokens)
+    q = gc.queries(wl)
+    runs = []
+    for _ in range(2):
+        sel, sel_n = pkv.retrieve(q)
+        out = pkv.sparse_attend(q, sel, sel_n)
+        torch.cuda.synchronize()
+        runs.append((sel.cpu().numpy(), out.cpu().numpy(), pkv.debug(5).copy()))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1].view(np.uint32), runs[1][1].view(np.uint32))
+    assert np.array_equal(runs[0][2].view(np.uint32), runs[1][2].view(np.uint32))
+
+
+def test_append_past_capacity_is_rejected():
+    from kv_cache_top_amd import PkError
+    wl = W.gqa_bf16(N=1000, buf_tokens=16, n_local=64)
+    pkv = gc.make_ctx(wl, capacity=1001)
+    pkv.encode_keys(1000)
+    dt = gc.torch_dtype(wl)
+    k = torch.zeros((1, 8, 128), dtype=dt, device="cuda")
+    pkv.append(k, k)
+    before = pkv.window()
+    with pytest.raises(PkError):
+        pkv.append(k, k)
+    assert pkv.window() == before
