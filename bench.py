@@ -16,7 +16,6 @@ the timed region.
 from __future__ import annotations
 
 import argparse
-import ctypes
 import json
 import math
 import os
@@ -92,10 +91,7 @@ class Layer:
     def step(self):
         i = self.t % self.pool
         self.t += 1
-        c = self.ctx
-        c.append(self.kn[i], self.vn[i])
-        c.retrieve(self.q[i], self.sel, self.sel_n)
-        c.sparse_attend(self.q[i], self.sel, self.sel_n, self.out)
+        self.ctx.decode_step(self.kn[i], self.vn[i], self.q[i], self.sel, self.sel_n, self.out)
 
 
 def counts(layer):
@@ -181,13 +177,10 @@ def main():
     # prefill encode of every layer (timed per layer, reported separately)
     enc_ms = []
     for L in layers:
-        nat.lib.pk_profile_enable(L.ctx._ctx, 1)
+        L.ctx.profile(True)
         L.ctx.encode_keys(L.wl.n_tokens)
-        ms = (ctypes.c_double * 6)()
-        ln = (ctypes.c_int64 * 6)()
-        nat.lib.pk_profile_read(L.ctx._ctx, ms, ln)
-        enc_ms.append(ms[0])
-        nat.lib.pk_profile_enable(L.ctx._ctx, 0)
+        enc_ms.append(L.ctx.profile_read()["encode"][0])
+        L.ctx.profile(False)
     torch.cuda.synchronize()
 
     nl = len(layers)
@@ -211,7 +204,7 @@ def main():
 
     # profiled pass: per-stage kernel durations from HIP events on the launch stream
     for L in layers:
-        nat.lib.pk_profile_enable(L.ctx._ctx, 1)
+        L.ctx.profile(True)
     sums = {k: 0.0 for k in ("scan", "rerank", "attend")}
     base = args.warmup + args.steps
     for i in range(args.profile_steps):
@@ -221,19 +214,17 @@ def main():
             sums[k] += c[k]
         L.step()
     torch.cuda.synchronize()
-    stage_ms = np.zeros(6)
-    stage_n = np.zeros(6, np.int64)
+    stage_ms = {k: 0.0 for k in nat.STAGES}
+    stage_n = {k: 0 for k in nat.STAGES}
     for L in layers:
-        ms = (ctypes.c_double * 6)()
-        ln = (ctypes.c_int64 * 6)()
-        nat.check(nat.lib.pk_profile_read(L.ctx._ctx, ms, ln), "pk_profile_read")
-        stage_ms += np.array(ms[:])
-        stage_n += np.array(ln[:])
-        nat.lib.pk_profile_enable(L.ctx._ctx, 0)
+        for k, (ms, n) in L.ctx.profile_read().items():
+            stage_ms[k] += ms
+            stage_n[k] += n
+        L.ctx.profile(False)
     stages = {}
-    for i, name in enumerate(nat.STAGES):
-        if stage_n[i]:
-            stages[name] = {"launches": int(stage_n[i]), "avg_us": 1e3 * stage_ms[i] / stage_n[i]}
+    for name in nat.STAGES:
+        if stage_n[name]:
+            stages[name] = {"launches": stage_n[name], "avg_us": 1e3 * stage_ms[name] / stage_n[name]}
     n_prof = args.profile_steps
 
     def gbs(name):

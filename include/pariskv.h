@@ -79,8 +79,9 @@ typedef struct pk_ctx pk_ctx;  /* opaque; owned by the library */
  * Owns: the per-key metadata (16 B of bucket ids and a 128 B record of codes
  * and scales per token), the window counters and all scratch.  The caller
  * keeps ownership of k_store / v_store, which must outlive the context.
- * Requires n_q_heads = G * n_kv_heads with 1 <= G <= 16, G * max(weight) <= 255,
- * buf_tokens <= n_local.  Allocates device memory and synchronises the device.
+ * Requires n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8} (other G up to 16
+ * are valid but PK_ERR_UNSUPPORTED), G * max(weight) <= 255, buf_tokens <=
+ * n_local, capacity <= 2^24.  Allocates device memory and synchronises the device.
  * Errors: PK_ERR_INVALID, PK_ERR_UNSUPPORTED, PK_ERR_NO_DEVICE, PK_ERR_OOM. */
 pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
                     int64_t capacity, pk_dtype kv_dtype, void* k_store, void* v_store,
@@ -125,6 +126,14 @@ pk_status pk_retrieve(pk_ctx* ctx, const void* q, int32_t* sel, int32_t* sel_n, 
 pk_status pk_sparse_attend(pk_ctx* ctx, const void* q, const int32_t* sel, const int32_t* sel_n,
                            float* out, void* stream);
 
+/* One whole decode step: pk_append_decode_keys(k_new, v_new) followed by
+ * pk_retrieve(q) and pk_sparse_attend(q) over the retrieved set, with the
+ * append carried out by the retrieval's first kernel.  Same arguments,
+ * layouts and results as the three calls in that order.
+ * Errors: as pk_append_decode_keys; a PK_ERR_HIP leaves the context unusable. */
+pk_status pk_decode_step(pk_ctx* ctx, const void* k_new, const void* v_new, const void* q,
+                         int32_t* sel, int32_t* sel_n, float* out, void* stream);
+
 /* Host only, no device needed.  The sign+3-bit magnitude codebook for sub_dim
  * m: the Lloyd-Max quantiser of |u_j| for u uniform on the unit sphere of R^m
  * (u_j^2 ~ Beta(1/2, (m-1)/2), the page's Beta prior).  levels[n_levels]
@@ -145,7 +154,8 @@ pk_status pk_get_window(const pk_ctx* ctx, int64_t* n_tokens, int64_t* sink_end,
  * summed duration in milliseconds and the number of launches since the last
  * enable (arrays of PK_STAGE_COUNT entries).  Errors: PK_ERR_INVALID. */
 enum { PK_STAGE_ENCODE = 0, PK_STAGE_APPEND = 1, PK_STAGE_QPREP = 2, PK_STAGE_SCAN = 3,
-       PK_STAGE_RERANK = 4, PK_STAGE_ATTEND = 5, PK_STAGE_COUNT = 6 };
+       PK_STAGE_RERANK = 4, PK_STAGE_FINE = 5, PK_STAGE_ATTEND = 6, PK_STAGE_COMBINE = 7,
+       PK_STAGE_COUNT = 8 };
 pk_status pk_profile_enable(pk_ctx* ctx, int32_t on);
 pk_status pk_profile_read(pk_ctx* ctx, double* ms, int64_t* launches);
 

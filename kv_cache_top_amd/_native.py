@@ -17,7 +17,7 @@ PK_OK, PK_ERR_INVALID, PK_ERR_NO_DEVICE, PK_ERR_OOM, PK_ERR_CAPACITY, PK_ERR_HIP
     PK_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 PK_F32, PK_BF16 = 0, 1
 PK_MEM_DEVICE, PK_MEM_HOST_MAPPED = 0, 1
-STAGES = ("encode", "append", "qprep", "scan", "rerank", "attend")
+STAGES = ("encode", "append", "qprep", "scan", "rerank", "fine", "attend", "combine")
 (PK_DBG_IDS, PK_DBG_REC, PK_DBG_LUT, PK_DBG_SCORES, PK_DBG_CAND, PK_DBG_EST,
  PK_DBG_NCAND) = range(7)
 
@@ -50,6 +50,8 @@ SIGNATURES = {
     "pk_retrieve": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "pk_sparse_attend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p]),
+    "pk_decode_step": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p]),
     "pk_codebook": (_i32, [_i32, _i32, ctypes.POINTER(ctypes.c_float),
                            ctypes.POINTER(ctypes.c_float)]),
     "pk_status_string": (ctypes.c_char_p, [_i32]),
@@ -62,10 +64,25 @@ SIGNATURES = {
 }
 
 
+def _preload_torch_hip_runtime():
+    """The library takes torch's device pointers and streams, so the process
+    must hold one HIP runtime: torch's.  Its bundled libamdhip64 has the same
+    soname as the system one, so loading it first (globally) makes the
+    dynamic linker bind libpariskv.so to it."""
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.origin:
+        return
+    hip = os.path.join(os.path.dirname(spec.origin), "lib", "libamdhip64.so")
+    if os.path.exists(hip):
+        ctypes.CDLL(hip, mode=ctypes.RTLD_GLOBAL)
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                           "(python kv_cache_top_amd/build.py)")
+    _preload_torch_hip_runtime()
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

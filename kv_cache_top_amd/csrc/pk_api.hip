@@ -31,17 +31,16 @@ struct pk_ctx {
     int nbins = 0, max_chunks = 0, max_splits = 0;
     int64_t cmax = 0;
     // device buffers
-    uint8_t* ids = nullptr;       // [units][cap][16]
-    uint8_t* rec = nullptr;       // [units][cap][128]
-    uint8_t* lut = nullptr;       // [units][16][256]
-    float* ysum = nullptr;        // [units][128]
-    uint16_t* scores = nullptr;   // [units][cap]
-    uint32_t* bhist = nullptr;    // [units][max_chunks][nbins]
+    uint8_t* ids = nullptr;       // [units][cap][16]   bucket ids
+    uint8_t* rec = nullptr;       // [units][cap][128]  nibbles + w
+    uint8_t* lut = nullptr;       // [units][16][256]   vote table
+    float* ysum = nullptr;        // [units][128]       sum of rotated queries
+    uint16_t* scores = nullptr;   // [units][cap]       coarse scores (retrieval offset)
+    uint32_t* hist = nullptr;     // [units][nbins]     coarse-score histogram
+    uint16_t* ge = nullptr;       // [units][max_chunks][nbins] per-chunk #{score >= s}
     int32_t* meta = nullptr;      // [units][4]
-    int32_t* off = nullptr;       // [units][max_chunks][2]
     int32_t* cand_pos = nullptr;  // [units][cmax]
     float* cand_est = nullptr;    // [units][cmax]
-    uint32_t* tickets = nullptr;  // [3][units]
     float* part = nullptr;        // [units][max_splits][G][130]
     // optional per-stage timing
     bool profiling = false;
@@ -108,6 +107,8 @@ int64_t coarse_count(int64_t n_r, int permille, int top_k) {
     return c < n_r ? c : n_r;
 }
 
+// Chunk of retrieval-zone keys per scan/rerank block: the smallest power of
+// two in [256, 8192] that keeps the grid at <= 2048 blocks.
 int choose_chunk(int units, int64_t n_r) {
     int chunk = 256;
     while (chunk < 8192 && (int64_t)units * ceil_div(n_r, chunk) > 2048) chunk *= 2;
@@ -128,8 +129,8 @@ void free_all(pk_ctx* c) {
     release_events(c);
     for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
     c->event_pool.clear();
-    void* bufs[] = {c->ids, c->rec,      c->lut,      c->ysum,    c->scores, c->bhist,
-                    c->meta, c->off,     c->cand_pos, c->cand_est, c->tickets, c->part};
+    void* bufs[] = {c->ids,  c->rec, c->lut,  c->ysum,     c->scores,  c->hist,
+                    c->ge,   c->meta, c->cand_pos, c->cand_est, c->part};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
 }
@@ -156,8 +157,85 @@ pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capac
     const int nbins = cfg->n_sub * G * wmax + 1;
     if (nbins > pk::kMaxBins) return PK_ERR_UNSUPPORTED;
     if (capacity > (int64_t)1 << 24) return PK_ERR_UNSUPPORTED;
+    const int64_t attended = (int64_t)cfg->n_sink + cfg->n_local + cfg->buf_tokens + cfg->top_k;
+    if (ceil_div(attended, pk::attend_split()) > pk::attend_max_splits()) return PK_ERR_UNSUPPORTED;
     *G_out = G;
     *nbins_out = nbins;
+    return PK_OK;
+}
+
+// Oldest local tokens to move into the retrieval zone before the next append
+// (zero unless the previous step filled the update buffer).
+int64_t pending_eviction(const pk_ctx* c) {
+    if (c->cfg.buf_tokens == 0 || c->buf < c->cfg.buf_tokens) return 0;
+    const int64_t local = c->n - c->buf - c->r_end;
+    return std::max<int64_t>(0, local + c->buf - c->cfg.n_local);
+}
+
+// Encodes the evicted tokens and updates the mirror.  Call only when the
+// buffer is full.
+pk_status evict(pk_ctx* c, hipStream_t st) {
+    const int64_t move = pending_eviction(c);
+    if (move > 0) {
+        StageTimer tm(c, PK_STAGE_ENCODE, st);
+        PK_HIP(pk::launch_encode(c->dt == PK_BF16, c->K, c->cap, c->units, c->r_end, move, c->ids,
+                                 c->rec, c->cfg.sign_bits, c->tab, st));
+    }
+    c->r_end += move;
+    c->buf = 0;
+    return PK_OK;
+}
+
+// qprep (optionally carrying the step's append), scan, rerank, fine select.
+pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, const void* k_new,
+                       const void* v_new, hipStream_t st) {
+    const bool bf16 = c->dt == PK_BF16;
+    const int64_t row = (int64_t)pk::kD * dtype_size(c->dt);
+    {
+        StageTimer tm(c, PK_STAGE_QPREP, st);
+        PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
+                                c->cfg.vote_weight, c->lut, c->ysum, c->hist, c->nbins, k_new,
+                                v_new, c->K, c->V, row, c->cap, c->n - 1, st));
+    }
+    const int64_t n_r = c->r_end - c->sink_end;
+    if (n_r <= 0) {
+        PK_HIP(pk::launch_empty_select(c->units, sel_n, c->meta, st));
+        return PK_OK;
+    }
+    const int64_t C = coarse_count(n_r, c->cfg.coarse_permille, c->cfg.top_k);
+    const int chunk = choose_chunk(c->units, n_r);
+    const int n_chunks = (int)ceil_div(n_r, chunk);
+    {
+        StageTimer tm(c, PK_STAGE_SCAN, st);
+        PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
+                               c->max_chunks, c->lut, c->scores, c->ge, c->hist, c->nbins, st));
+    }
+    {
+        StageTimer tm(c, PK_STAGE_RERANK, st);
+        PK_HIP(pk::launch_rerank(chunk, c->scores, c->rec, c->cap, c->units, c->sink_end, n_r,
+                                 n_chunks, c->max_chunks, c->hist, c->ge, c->nbins, C,
+                                 c->cfg.top_k, c->ysum, c->tab, c->cand_pos, c->cand_est, c->cmax,
+                                 c->meta, st));
+    }
+    StageTimer tm(c, PK_STAGE_FINE, st);
+    PK_HIP(pk::launch_fine(c->cand_pos, c->cand_est, c->cmax, c->units, (int)C, c->cfg.top_k, sel,
+                           sel_n, st));
+    return PK_OK;
+}
+
+pk_status run_attend(pk_ctx* c, const void* q, const int32_t* sel, const int32_t* sel_n,
+                     float* out, hipStream_t st) {
+    const int64_t hot = c->sink_end + (c->n - c->r_end);
+    const int n_splits = (int)ceil_div(hot + c->cfg.top_k, pk::attend_split());
+    if (n_splits > c->max_splits) return PK_ERR_INVALID;
+    {
+        StageTimer tm(c, PK_STAGE_ATTEND, st);
+        PK_HIP(pk::launch_attend(c->dt == PK_BF16, c->G, c->K, c->V, c->cap, c->units, q,
+                                 c->sink_end, c->r_end, c->n, sel, sel_n, c->cfg.top_k, n_splits,
+                                 c->part, st));
+    }
+    StageTimer tm(c, PK_STAGE_COMBINE, st);
+    PK_HIP(pk::launch_combine(c->part, c->units, c->G, n_splits, out, st));
     return PK_OK;
 }
 
@@ -196,9 +274,8 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return PK_ERR_NO_DEVICE;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_NO_DEVICE;
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PK_ERR_NO_DEVICE;
-    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return PK_ERR_NO_DEVICE;
+    // the kernels are built for gfx950 only: the current device must be able to load them
+    if (pk::probe_kernel_image() != hipSuccess) return PK_ERR_NO_DEVICE;
 
     pk_ctx* c = new (std::nothrow) pk_ctx();
     if (!c) return PK_ERR_OOM;
@@ -220,8 +297,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         return PK_ERR_INVALID;
     }
     c->max_chunks = (int)std::min<int64_t>(pk::kMaxChunks, ceil_div(capacity, 256));
-    c->cmax = coarse_count(capacity, cfg->coarse_permille, cfg->top_k);
-    if (c->cmax < 1) c->cmax = 1;
+    c->cmax = std::max<int64_t>(1, coarse_count(capacity, cfg->coarse_permille, cfg->top_k));
     c->max_splits = (int)ceil_div((int64_t)cfg->n_sink + cfg->n_local + cfg->buf_tokens + cfg->top_k,
                                   pk::attend_split());
 
@@ -235,12 +311,11 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         {(void**)&c->lut, (size_t)(U * pk::kSub * 256)},
         {(void**)&c->ysum, (size_t)(U * pk::kD * 4)},
         {(void**)&c->scores, (size_t)(U * capacity * 2)},
-        {(void**)&c->bhist, (size_t)(U * c->max_chunks * (int64_t)nbins * 4)},
+        {(void**)&c->hist, (size_t)(U * nbins * 4)},
+        {(void**)&c->ge, (size_t)(U * c->max_chunks * (int64_t)nbins * 2)},
         {(void**)&c->meta, (size_t)(U * 4 * 4)},
-        {(void**)&c->off, (size_t)(U * c->max_chunks * 2 * 4)},
         {(void**)&c->cand_pos, (size_t)(U * c->cmax * 4)},
         {(void**)&c->cand_est, (size_t)(U * c->cmax * 4)},
-        {(void**)&c->tickets, (size_t)(3 * U * 4)},
         {(void**)&c->part, (size_t)(U * c->max_splits * (int64_t)G * (pk::kD + 2) * 4)},
     };
     for (auto& a : allocs) {
@@ -250,8 +325,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
             return PK_ERR_OOM;
         }
     }
-    if (hipMemset(c->tickets, 0, 3 * U * 4) != hipSuccess ||
-        hipMemset(c->meta, 0, U * 16) != hipSuccess ||
+    if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
         hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_all(c);
@@ -301,16 +375,8 @@ pk_status pk_append_decode_keys(pk_ctx* c, const void* k_new, const void* v_new,
     if (c->n + 1 > c->cap) return PK_ERR_CAPACITY;
     const hipStream_t st = (hipStream_t)stream;
     if (c->buf >= c->cfg.buf_tokens) {
-        // the previous step filled the buffer: oldest local tokens -> retrieval (encoded),
-        // buffer -> local
-        const int64_t local = c->n - c->buf - c->r_end;
-        const int64_t move = std::max<int64_t>(0, local + c->buf - c->cfg.n_local);
-        StageTimer tm(c, PK_STAGE_ENCODE, st);
-        if (move > 0)
-            PK_HIP(pk::launch_encode(c->dt == PK_BF16, c->K, c->cap, c->units, c->r_end, move,
-                                     c->ids, c->rec, c->cfg.sign_bits, c->tab, st));
-        c->r_end += move;
-        c->buf = 0;
+        pk_status s = evict(c, st);
+        if (s != PK_OK) return s;
     }
     const int64_t row = (int64_t)pk::kD * dtype_size(c->dt);
     {
@@ -325,48 +391,32 @@ pk_status pk_append_decode_keys(pk_ctx* c, const void* k_new, const void* v_new,
 pk_status pk_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, void* stream) {
     if (!c || !q || !sel || !sel_n) return PK_ERR_INVALID;
     if (!c->prefilled) return PK_ERR_INVALID;
-    const hipStream_t st = (hipStream_t)stream;
-    const bool bf16 = c->dt == PK_BF16;
-    {
-        StageTimer tm(c, PK_STAGE_QPREP, st);
-        PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
-                                c->cfg.vote_weight, c->lut, c->ysum, st));
-    }
-    const int64_t n_r = c->r_end - c->sink_end;
-    if (n_r <= 0) {
-        PK_HIP(pk::launch_empty_select(c->units, sel_n, c->meta, st));
-        return PK_OK;
-    }
-    const int64_t C = coarse_count(n_r, c->cfg.coarse_permille, c->cfg.top_k);
-    const int chunk = choose_chunk(c->units, n_r);
-    const int n_chunks = (int)ceil_div(n_r, chunk);
-    uint32_t* t_scan = c->tickets;
-    uint32_t* t_rerank = c->tickets + c->units;
-    {
-        StageTimer tm(c, PK_STAGE_SCAN, st);
-        PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
-                               c->max_chunks, c->lut, c->scores, c->bhist, c->nbins, t_scan,
-                               c->meta, c->off, C, c->cfg.top_k, st));
-    }
-    StageTimer tm(c, PK_STAGE_RERANK, st);
-    PK_HIP(pk::launch_rerank(chunk, c->scores, c->rec, c->cap, c->units, c->sink_end, n_r, n_chunks,
-                             c->max_chunks, c->meta, c->off, c->ysum, c->tab, c->cand_pos,
-                             c->cand_est, c->cmax, t_rerank, c->cfg.top_k, sel, sel_n, st));
-    return PK_OK;
+    return run_retrieve(c, q, sel, sel_n, nullptr, nullptr, (hipStream_t)stream);
 }
 
 pk_status pk_sparse_attend(pk_ctx* c, const void* q, const int32_t* sel, const int32_t* sel_n,
                            float* out, void* stream) {
     if (!c || !q || !sel || !sel_n || !out) return PK_ERR_INVALID;
     if (!c->prefilled) return PK_ERR_INVALID;
-    const int64_t hot = c->sink_end + (c->n - c->r_end);
-    const int n_splits = (int)ceil_div(hot + c->cfg.top_k, pk::attend_split());
-    if (n_splits > c->max_splits) return PK_ERR_INVALID;
-    StageTimer tm(c, PK_STAGE_ATTEND, (hipStream_t)stream);
-    PK_HIP(pk::launch_attend(c->dt == PK_BF16, c->G, c->K, c->V, c->cap, c->units, q, c->sink_end,
-                             c->r_end, c->n, sel, sel_n, c->cfg.top_k, n_splits, c->part,
-                             c->tickets + 2 * c->units, out, (hipStream_t)stream));
-    return PK_OK;
+    return run_attend(c, q, sel, sel_n, out, (hipStream_t)stream);
+}
+
+pk_status pk_decode_step(pk_ctx* c, const void* k_new, const void* v_new, const void* q,
+                         int32_t* sel, int32_t* sel_n, float* out, void* stream) {
+    if (!c || !k_new || !v_new || !q || !sel || !sel_n || !out) return PK_ERR_INVALID;
+    if (!c->prefilled || c->cfg.buf_tokens == 0) return PK_ERR_INVALID;
+    if (c->n + 1 > c->cap) return PK_ERR_CAPACITY;
+    const hipStream_t st = (hipStream_t)stream;
+    if (c->buf >= c->cfg.buf_tokens) {
+        pk_status s = evict(c, st);
+        if (s != PK_OK) return s;
+    }
+    // the query-prep kernel copies the new token to position n (the old count)
+    c->n += 1;
+    c->buf += 1;
+    pk_status s = run_retrieve(c, q, sel, sel_n, k_new, v_new, st);
+    if (s != PK_OK) return s;
+    return run_attend(c, q, sel, sel_n, out, st);
 }
 
 pk_status pk_profile_enable(pk_ctx* c, int32_t on) {

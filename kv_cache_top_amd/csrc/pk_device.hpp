@@ -105,10 +105,11 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Block-wide exclusive scan of one uint32 per thread (kBlock threads).
-// `tmp` must hold kBlock / 64 entries.  Returns the exclusive prefix; the
-// block total goes to *total.  Contains __syncthreads.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+// Block-wide exclusive scan of one uint32 per thread for a block of NT
+// threads.  `tmp` must hold NT / 64 entries.  Returns the exclusive prefix;
+// the block total goes to *total.  Contains two __syncthreads.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* tmp, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t x = v;
 #pragma unroll
@@ -120,7 +121,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         const uint32_t t = tmp[w];
         if (w < wave) before += t;
         all += t;
@@ -128,6 +129,10 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
     __syncthreads();
     *total = all;
     return before + x - v;
+}
+
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+    return block_excl_scan_t<kBlock>(v, tmp, total);
 }
 
 }  // namespace pk

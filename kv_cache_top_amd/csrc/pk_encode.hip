@@ -76,49 +76,49 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(const T* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
-// query preparation: one block per unit.
+// query preparation: one 1024-thread block per unit.
 //   y_g = H D q_g (spec arithmetic), Ysum = sum_g y_g (for the rerank);
-//   per (g, b): scores of all 256 centroids, top-rho by (score desc, c asc);
+//   per (g, b): top-rho of the 256 centroid scores by (score desc, c asc);
 //   vote table L[b][c] = sum_g weight(rank of c).
-// Centroid scores are built from shared partial sums: pair sums over
-// coordinates (0,1), (2,3), (4,5), (6,7) in their 4 sign variants, then the
-// two quad sums, then score(c) = quad_lo[c & 15] + quad_hi[c >> 4] -- the same
-// fp32 operations, in the same order, as the direct pairwise tree.
+// A 16-lane group serves one (g, b): lane chi scores the 16 centroids
+// c = 16 chi + clo.  Scores come from shared partial sums -- pair sums over
+// coordinates (0,1), (2,3), (4,5), (6,7) in their 4 sign variants, then
+// quad_lo[c & 15] + quad_hi[c >> 4] -- the same fp32 operations in the same
+// order as the direct pairwise tree.  Top-rho = rho rounds of a 16-lane
+// argmax, each removing the winner.
+// The block also clears the unit's coarse-score histogram for the scan that
+// follows, and may copy the step's new K/V token into the store.
 // ---------------------------------------------------------------------------
 struct VoteWeights {
     uint32_t w[kRhoMax];
 };
 
+constexpr int kQBlock = 1024;
+
 __device__ __forceinline__ bool better(float s, int c, float ts, int tc) {
     return s > ts || (s == ts && c < tc);
 }
 
-__device__ __forceinline__ void top_insert(float s, int c, float ts[kRhoMax], int tc[kRhoMax],
-                                           int rho) {
-#pragma unroll
-    for (int i = 0; i < kRhoMax; ++i) {
-        if (i < rho && better(s, c, ts[i], tc[i])) {
-            const float fs = ts[i];
-            const int fc = tc[i];
-            ts[i] = s;
-            tc[i] = c;
-            s = fs;
-            c = fc;
-        }
-    }
-}
-
 template <typename T>
-__global__ __launch_bounds__(kBlock) void qprep_kernel(const T* __restrict__ q, int G,
-                                                        uint64_t sign_lo, uint64_t sign_hi, int rho,
-                                                        VoteWeights wts, uint8_t* __restrict__ lut,
-                                                        float* __restrict__ ysum) {
+__global__ __launch_bounds__(kQBlock) void qprep_kernel(
+    const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
+    uint8_t* __restrict__ lut, float* __restrict__ ysum, uint32_t* __restrict__ hist_tot, int nbins,
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint8_t* __restrict__ K,
+    uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos) {
     const int u = blockIdx.x;
     const int tid = threadIdx.x;
-    __shared__ float s_y[16][kD];
+    __shared__ float s_y[8][kD];
     __shared__ uint32_t s_lut[kSub * 256];
-    for (int i = tid; i < kSub * 256; i += kBlock) s_lut[i] = 0;
-
+    for (int i = tid; i < kSub * 256; i += kQBlock) s_lut[i] = 0;
+    for (int i = tid; i < nbins; i += kQBlock) hist_tot[(int64_t)u * nbins + i] = 0;
+    if (k_new != nullptr) {
+        const int per_row = (int)(row_bytes / 16);
+        if (tid < per_row) {
+            const int64_t dst = ((u * cap + new_pos) * row_bytes) / 16 + tid;
+            reinterpret_cast<uint4*>(K)[dst] = k_new[(int64_t)u * per_row + tid];
+            reinterpret_cast<uint4*>(V)[dst] = v_new[(int64_t)u * per_row + tid];
+        }
+    }
     if (tid < 16 * G) {
         const int g = tid >> 4, l16 = tid & 15;
         float v[8];
@@ -136,62 +136,52 @@ __global__ __launch_bounds__(kBlock) void qprep_kernel(const T* __restrict__ q, 
     }
 
     const int combos = G * kSub;
-    for (int base = 0; base < combos; base += kBlock / 4) {
-        const int combo = base + (tid >> 2);
-        const int part = tid & 3;
+    const int chi = tid & 15;
+    for (int base = 0; base < combos; base += kQBlock / 16) {
+        const int combo = base + (tid >> 4);
         const bool active = combo < combos;
-        float ts[kRhoMax];
-        int tc[kRhoMax];
-#pragma unroll
-        for (int i = 0; i < kRhoMax; ++i) {
-            ts[i] = -INFINITY;
-            tc[i] = 0x7fffffff;
-        }
         const int g = active ? combo / kSub : 0, b = combo % kSub;
-        if (active) {
-            const float* y = &s_y[g][8 * b];
-            float p01[4], p23[4], p45[4], p67[4];
+        const float* y = &s_y[g][8 * b];
+        float p01[4], p23[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p01[i] = ((i & 1) ? -y[0] : y[0]) + ((i & 2) ? -y[1] : y[1]);
-                p23[i] = ((i & 1) ? -y[2] : y[2]) + ((i & 2) ? -y[3] : y[3]);
-                p45[i] = ((i & 1) ? -y[4] : y[4]) + ((i & 2) ? -y[5] : y[5]);
-                p67[i] = ((i & 1) ? -y[6] : y[6]) + ((i & 2) ? -y[7] : y[7]);
-            }
-            float qlo[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) qlo[i] = p01[i & 3] + p23[i >> 2];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int chi = 4 * part + k;
-                const float qhi = p45[chi & 3] + p67[chi >> 2];
-#pragma unroll
-                for (int clo = 0; clo < 16; ++clo) top_insert(qlo[clo] + qhi, chi * 16 + clo, ts, tc, rho);
-            }
+        for (int i = 0; i < 4; ++i) {
+            p01[i] = ((i & 1) ? -y[0] : y[0]) + ((i & 2) ? -y[1] : y[1]);
+            p23[i] = ((i & 1) ? -y[2] : y[2]) + ((i & 2) ? -y[3] : y[3]);
         }
-        // merge the four partial lists of a combo (lanes 4j .. 4j+3)
+        const float y4 = (chi & 1) ? -y[4] : y[4], y5 = (chi & 2) ? -y[5] : y[5];
+        const float y6 = (chi & 4) ? -y[6] : y[6], y7 = (chi & 8) ? -y[7] : y[7];
+        const float qhi = (y4 + y5) + (y6 + y7);
+        float sc[16];
 #pragma unroll
-        for (int mask = 1; mask <= 2; mask <<= 1) {
-            float os[kRhoMax];
-            int oc[kRhoMax];
+        for (int clo = 0; clo < 16; ++clo) sc[clo] = (p01[clo & 3] + p23[clo >> 2]) + qhi;
+        uint32_t removed = 0;
+        for (int r = 0; r < rho; ++r) {
+            float bs = -INFINITY;
+            int bc = 0x7fffffff;
 #pragma unroll
-            for (int i = 0; i < kRhoMax; ++i) {
-                os[i] = __shfl_xor(ts[i], mask);
-                oc[i] = __shfl_xor(tc[i], mask);
+            for (int clo = 0; clo < 16; ++clo) {
+                const int c = chi * 16 + clo;
+                if (!((removed >> clo) & 1u) && better(sc[clo], c, bs, bc)) {
+                    bs = sc[clo];
+                    bc = c;
+                }
             }
 #pragma unroll
-            for (int i = 0; i < kRhoMax; ++i)
-                if (i < rho) top_insert(os[i], oc[i], ts, tc, rho);
-        }
-        if (active && part == 0) {
-#pragma unroll
-            for (int r = 0; r < kRhoMax; ++r)
-                if (r < rho) atomicAdd(&s_lut[b * 256 + tc[r]], wts.w[r]);
+            for (int m = 1; m < 16; m <<= 1) {
+                const float os = __shfl_xor(bs, m, 16);
+                const int oc = __shfl_xor(bc, m, 16);
+                if (better(os, oc, bs, bc)) {
+                    bs = os;
+                    bc = oc;
+                }
+            }
+            if ((bc >> 4) == chi) removed |= 1u << (bc & 15);
+            if (active && chi == 0) atomicAdd(&s_lut[b * 256 + bc], wts.w[r]);
         }
     }
     __syncthreads();
     uint32_t* out = reinterpret_cast<uint32_t*>(lut + (int64_t)u * kSub * 256);
-    for (int i = tid; i < kSub * 256 / 4; i += kBlock) {
+    for (int i = tid; i < kSub * 256 / 4; i += kQBlock) {
         out[i] = (s_lut[4 * i] & 0xffu) | ((s_lut[4 * i + 1] & 0xffu) << 8) |
                  ((s_lut[4 * i + 2] & 0xffu) << 16) | ((s_lut[4 * i + 3] & 0xffu) << 24);
     }
@@ -238,15 +228,21 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
+                        uint32_t* hist_tot, int nbins, const void* k_new, const void* v_new,
+                        void* K, void* V, int64_t row_bytes, int64_t cap, int64_t new_pos,
                         hipStream_t st) {
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     if (bf16)
-        qprep_kernel<uint16_t><<<dim3(units), dim3(kBlock), 0, st>>>(
-            (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum);
+        qprep_kernel<uint16_t><<<dim3(units), dim3(kQBlock), 0, st>>>(
+            (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, nbins,
+            (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
+            new_pos);
     else
-        qprep_kernel<float><<<dim3(units), dim3(kBlock), 0, st>>>(
-            (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum);
+        qprep_kernel<float><<<dim3(units), dim3(kQBlock), 0, st>>>(
+            (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, nbins,
+            (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
+            new_pos);
     return hipGetLastError();
 }
 

@@ -7,81 +7,75 @@
 //  * rerank (RSQ-IP): each candidate's raw score <k, q> is estimated from its
 //    4-bit codes and scales only, and the top-k are selected.
 //
-// Work split.  The retrieval zone of every unit is cut into chunks; the scan
-// and the rerank launch one 256-thread block per (chunk, unit).  Each unit's
-// last finishing block (an atomic ticket per unit, no spinning) does that
-// unit's serial tail: the coarse threshold after the scan, the fine top-k
-// after the rerank.  Tickets are reset by the block that takes the last one,
-// so nothing needs clearing between launches.
+// Three kernels, no cross-block synchronisation inside any of them (on
+// gfx950 an agent-scope release fence writes back the XCD's L2 and costs far
+// more per block than a kernel boundary):
+//  scan    one 256-thread block per (chunk, unit): coarse scores, the chunk's
+//          suffix counts ge[s] = #{score >= s} and the unit histogram (relaxed
+//          atomics, cleared by the query-prep kernel of the same step);
+//  rerank  same grid: each block derives the coarse threshold from the unit
+//          histogram and its chunk's candidate offset from the suffix counts
+//          of the chunks before it, compacts its candidates in position
+//          order and estimates them with RSQ-IP;
+//  fine    one 1024-thread block per unit: radix select of the k-th largest
+//          estimate, ties to the lower position, compaction in order.
 #include "pk_device.hpp"
 #include "pk_launch.hpp"
 
 namespace pk {
 
-// per-unit coarse-selection summary written by the scan's last block
-//   meta[u] = {threshold score T, ties at T taken, C, k_eff}
-//   off[u][chunk] = {candidates before this chunk, keys scoring T before this chunk}
-
+template <int KPT>
 __global__ __launch_bounds__(kBlock) void scan_kernel(
-    const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int chunk,
-    int n_chunks, int max_chunks, const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores,
-    uint32_t* __restrict__ bhist, int nbins, uint32_t* __restrict__ tickets,
-    int32_t* __restrict__ meta, int32_t* __restrict__ off, int64_t C, int top_k) {
+    const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
+    const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores, uint16_t* __restrict__ ge,
+    uint32_t* __restrict__ hist_tot, int nbins) {
+    constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     __shared__ uint32_t s_lut[kSub * 256 / 4];
     __shared__ uint32_t s_hist[kMaxBins];
     __shared__ uint32_t s_tmp[kBlock / 64];
-    __shared__ int s_last;
     const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_lut);
 
+    // every id row of this thread is requested before any is used
+    const int64_t start = (int64_t)ch * chunk;
+    const uint4* idrow = reinterpret_cast<const uint4*>(ids) + u * cap + sink_end;
+    uint4 v[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int64_t i = start + j * kBlock + tid;
+        v[j] = (i < n_r) ? idrow[i] : make_uint4(0, 0, 0, 0);
+    }
     reinterpret_cast<uint4*>(s_lut)[tid] =
         reinterpret_cast<const uint4*>(lut + (int64_t)u * kSub * 256)[tid];
     for (int b = tid; b < nbins; b += kBlock) s_hist[b] = 0;
     __syncthreads();
 
-    const int64_t start = (int64_t)ch * chunk;
-    const int64_t end = (start + chunk < n_r) ? start + chunk : n_r;
-    const uint4* idrow = reinterpret_cast<const uint4*>(ids) + u * cap + sink_end;
     uint16_t* srow = scores + u * cap;
-    for (int64_t i = start + tid; i < end; i += kBlock) {
-        const uint4 v = idrow[i];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t s = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < KPT; ++j) {
+        const int64_t i = start + j * kBlock + tid;
+        if (i < n_r) {
+            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            uint32_t sc = 0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) s += lut8[(4 * j + k) * 256 + ((w[j] >> (8 * k)) & 255u)];
+            for (int a = 0; a < 4; ++a) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    sc += lut8[(4 * a + k) * 256 + ((w[a] >> (8 * k)) & 255u)];
+            }
+            srow[i] = (uint16_t)sc;
+            atomicAdd(&s_hist[sc], 1u);
         }
-        srow[i] = (uint16_t)s;
-        atomicAdd(&s_hist[s], 1u);
     }
     __syncthreads();
-    uint32_t* myhist = bhist + ((int64_t)u * max_chunks + ch) * nbins;
-    for (int b = tid; b < nbins; b += kBlock) myhist[b] = s_hist[b];
 
-    // ---- ticket: the unit's last block derives the threshold and chunk offsets
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&tickets[u], 1u) == (uint32_t)(n_chunks - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
+    // unit histogram (relaxed device-scope atomics; read by the next kernel)
     for (int b = tid; b < nbins; b += kBlock) {
-        uint32_t a = 0;
-        const uint32_t* col = bhist + (int64_t)u * max_chunks * nbins + b;
-        for (int c = 0; c < n_chunks; ++c) a += col[(int64_t)c * nbins];
-        s_hist[b] = a;
+        const uint32_t h = s_hist[b];
+        if (h) atomicAdd(&hist_tot[(int64_t)u * nbins + b], h);
     }
-    __syncthreads();
-
-    // T = largest score s with #{score >= s} >= C.  Thread t owns the bins
-    // with reversed index r = nbins-1-s in [t*per, t*per+per).
-    __shared__ int s_T, s_need;
-    if (tid == 0) {
-        s_T = 0;
-        s_need = 0;
-    }
+    // chunk suffix counts: thread t owns bins [t*per, t*per+per) in descending
+    // score order (reversed index r = nbins-1-s)
     const int per = (nbins + kBlock - 1) / kBlock;
     uint32_t seg = 0;
     for (int j = 0; j < per; ++j) {
@@ -90,106 +84,106 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
     }
     uint32_t tot;
     uint32_t run = block_excl_scan(seg, s_tmp, &tot);
+    uint16_t* myge = ge + ((int64_t)u * max_chunks + ch) * nbins;
     for (int j = 0; j < per; ++j) {
         const int r = tid * per + j;
         if (r < nbins) {
-            const uint32_t h = s_hist[nbins - 1 - r];
-            if ((int64_t)run < C && (int64_t)(run + h) >= C) {
-                s_T = nbins - 1 - r;
-                s_need = (int)(C - run);
-            }
-            run += h;
+            run += s_hist[nbins - 1 - r];
+            myge[nbins - 1 - r] = (uint16_t)run;
         }
-    }
-    __syncthreads();
-    const int T = s_T, need = s_need;
-
-    // per-chunk counts above / at the threshold, then two exclusive scans
-    __shared__ uint32_t s_gt[kMaxChunks], s_eq[kMaxChunks];
-    for (int c = tid; c < n_chunks; c += kBlock) {
-        const uint32_t* h = bhist + ((int64_t)u * max_chunks + c) * nbins;
-        uint32_t gt = 0;
-        for (int b = T + 1; b < nbins; ++b) gt += h[b];
-        s_gt[c] = gt;
-        s_eq[c] = h[T];
-    }
-    __syncthreads();
-    const int cper = (n_chunks + kBlock - 1) / kBlock;
-    uint32_t eq_seg = 0;
-    for (int j = 0; j < cper; ++j) {
-        const int c = tid * cper + j;
-        if (c < n_chunks) eq_seg += s_eq[c];
-    }
-    uint32_t eq_run = block_excl_scan(eq_seg, s_tmp, &tot);
-    uint32_t take_seg = 0;
-    for (int j = 0; j < cper; ++j) {
-        const int c = tid * cper + j;
-        if (c < n_chunks) {
-            const int64_t left = (int64_t)need - eq_run;
-            const uint32_t take_eq =
-                left <= 0 ? 0u : (left >= (int64_t)s_eq[c] ? s_eq[c] : (uint32_t)left);
-            s_gt[c] += take_eq;          // now: candidates contributed by chunk c
-            off[((int64_t)u * max_chunks + c) * 2 + 1] = (int32_t)eq_run;
-            eq_run += s_eq[c];
-            take_seg += s_gt[c];
-        }
-    }
-    uint32_t cand_run = block_excl_scan(take_seg, s_tmp, &tot);
-    for (int j = 0; j < cper; ++j) {
-        const int c = tid * cper + j;
-        if (c < n_chunks) {
-            off[((int64_t)u * max_chunks + c) * 2] = (int32_t)cand_run;
-            cand_run += s_gt[c];
-        }
-    }
-    if (tid == 0) {
-        meta[u * 4 + 0] = T;
-        meta[u * 4 + 1] = need;
-        meta[u * 4 + 2] = (int32_t)C;
-        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
-        tickets[u] = 0;
     }
 }
 
 // ---------------------------------------------------------------------------
-// rerank: compact the chunk's candidates (score > T, or = T within the first
-// `need` ties in position order), estimate each with RSQ-IP, write
-// (position, estimate) at the candidate's global rank.  16 lanes per
-// candidate, lane b reading subspace b's 4 nibble bytes and its w.
-// est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g.
+// rerank
 // ---------------------------------------------------------------------------
 template <int KPT>
 __global__ __launch_bounds__(kBlock) void rerank_kernel(
     const uint16_t* __restrict__ scores, const uint8_t* __restrict__ rec, int64_t cap,
-    int64_t sink_end, int64_t n_r, int n_chunks, int max_chunks, const int32_t* __restrict__ meta,
-    const int32_t* __restrict__ off, const float* __restrict__ ysum, CodeTables tab,
-    int32_t* __restrict__ cand_pos, float* __restrict__ cand_est, int64_t cmax,
-    uint32_t* __restrict__ tickets, int top_k, int32_t* __restrict__ sel,
-    int32_t* __restrict__ sel_n) {
+    int64_t sink_end, int64_t n_r, int max_chunks, const uint32_t* __restrict__ hist_tot,
+    const uint16_t* __restrict__ ge, int nbins, int64_t C, int top_k,
+    const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
+    float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int l16 = tid & 15;
     __shared__ int32_t s_list[chunk];
     __shared__ float s_tbl[16];
     __shared__ uint32_t s_tmp[kBlock / 64];
-    __shared__ int s_last;
+    __shared__ int s_T, s_need;
     if (tid < 16) s_tbl[tid] = ((tid & 8) ? -1.0f : 1.0f) * tab.levels[tid & 7];
+    if (tid == 0) {
+        s_T = 0;
+        s_need = 0;
+    }
 
-    const int T = meta[u * 4 + 0], need = meta[u * 4 + 1];
-    const int C = meta[u * 4 + 2];
-    const int32_t cand_before = off[((int64_t)u * max_chunks + ch) * 2];
-    const int32_t eq_before = off[((int64_t)u * max_chunks + ch) * 2 + 1];
+    // loads that do not depend on the threshold go out first: this chunk's
+    // scores and the unit histogram
     const int64_t start = (int64_t)ch * chunk;
-
     uint32_t s[KPT];
-    uint32_t eqc = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int64_t i = start + (int64_t)tid * KPT + j;
         s[j] = (i < n_r) ? (uint32_t)scores[u * cap + i] : 0xffffffffu;
-        eqc += (s[j] == (uint32_t)T) ? 1u : 0u;
     }
+    const int per = (nbins + kBlock - 1) / kBlock;
+    const uint32_t* H = hist_tot + (int64_t)u * nbins;
+    uint32_t hv[kMaxBins / kBlock];
+#pragma unroll
+    for (int j = 0; j < kMaxBins / kBlock; ++j) {
+        const int r = tid * per + j;
+        hv[j] = (j < per && r < nbins) ? H[nbins - 1 - r] : 0u;
+    }
+    float y[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) y[r] = ysum[(int64_t)u * kD + 8 * l16 + r];
+
+    // coarse threshold: T = largest score with #{score >= T} >= C; `need` ties
+    // at T are taken, lowest positions first
+    uint32_t seg = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxBins / kBlock; ++j) seg += hv[j];
     uint32_t tot;
+    uint32_t run = block_excl_scan(seg, s_tmp, &tot);
+#pragma unroll
+    for (int j = 0; j < kMaxBins / kBlock; ++j) {
+        const int r = tid * per + j;
+        if (j < per && r < nbins) {
+            if ((int64_t)run < C && (int64_t)(run + hv[j]) >= C) {
+                s_T = nbins - 1 - r;
+                s_need = (int)(C - run);
+            }
+            run += hv[j];
+        }
+    }
+    __syncthreads();
+    const int T = s_T;
+    const uint32_t need = (uint32_t)s_need;
+
+    // candidates and ties at T in the chunks before this one
+    uint32_t gt_b = 0, eq_b = 0;
+    for (int c = tid; c < ch; c += kBlock) {
+        const uint16_t* g = ge + ((int64_t)u * max_chunks + c) * nbins;
+        const uint32_t at = g[T];
+        const uint32_t above = (T + 1 < nbins) ? g[T + 1] : 0u;
+        gt_b += above;
+        eq_b += at - above;
+    }
+    uint32_t eqc = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) eqc += (s[j] == (uint32_t)T) ? 1u : 0u;
+    uint32_t gt_before, eq_before;
+    (void)block_excl_scan(gt_b, s_tmp, &gt_before);
+    (void)block_excl_scan(eq_b, s_tmp, &eq_before);
+    const uint32_t cand_before = gt_before + (eq_before < need ? eq_before : need);
+    if (ch == 0 && tid == 0) {
+        meta[u * 4 + 0] = T;
+        meta[u * 4 + 1] = (int32_t)need;
+        meta[u * 4 + 2] = (int32_t)C;
+        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
+    }
+
+    // this chunk's candidates, in position order
     uint32_t rank = eq_before + block_excl_scan(eqc, s_tmp, &tot);
     uint32_t mask = 0;
 #pragma unroll
@@ -197,103 +191,178 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
         bool in = false;
         if (s[j] != 0xffffffffu) {
             if (s[j] > (uint32_t)T) in = true;
-            else if (s[j] == (uint32_t)T) in = (rank++ < (uint32_t)need);
+            else if (s[j] == (uint32_t)T) in = (rank++ < need);
         }
         mask |= (in ? 1u : 0u) << j;
     }
-    uint32_t mine = __popc(mask);
     uint32_t n_mem;
-    uint32_t at = block_excl_scan(mine, s_tmp, &n_mem);
+    uint32_t at = block_excl_scan(__popc(mask), s_tmp, &n_mem);
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
         if ((mask >> j) & 1u) s_list[at++] = (int32_t)(sink_end + start + (int64_t)tid * KPT + j);
     __syncthreads();
 
-    float y[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] = ysum[(int64_t)u * kD + 8 * l16 + r];
+    // RSQ-IP: est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g;
+    // 16 lanes per candidate, lane b reading subspace b's nibble word and w.
+    // A group fetches the records of up to kBatch candidates before using any.
+    constexpr int kBatch = 8;
     const float inv_sqrt_d = 0.08838834764831845f;
-    for (int i = tid >> 4; i < (int)n_mem; i += kBlock / 16) {
-        const int32_t pos = s_list[i];
-        const uint8_t* r = rec + ((int64_t)u * cap + pos) * kRec;
-        const uint32_t nib = reinterpret_cast<const uint32_t*>(r)[l16];
-        const float w = reinterpret_cast<const float*>(r + 64)[l16];
-        float dot = 0.0f;
+    const int grp = tid >> 4;
+    for (int i0 = grp; i0 < (int)n_mem; i0 += kBatch * (kBlock / 16)) {
+        uint32_t nib[kBatch];
+        float w[kBatch];
+        int32_t pos[kBatch];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dot = fmaf(s_tbl[(nib >> (4 * k)) & 15u], y[k], dot);
-        const float e = sum16(w * dot);
-        if (l16 == 0 && cand_before + i < cmax) {
-            cand_pos[(int64_t)u * cmax + cand_before + i] = pos;
-            cand_est[(int64_t)u * cmax + cand_before + i] = e * inv_sqrt_d;
+        for (int k = 0; k < kBatch; ++k) {
+            const int i = i0 + k * (kBlock / 16);
+            pos[k] = (i < (int)n_mem) ? s_list[i] : -1;
+            if (pos[k] >= 0) {
+                const uint8_t* r = rec + ((int64_t)u * cap + pos[k]) * kRec;
+                nib[k] = reinterpret_cast<const uint32_t*>(r)[l16];
+                w[k] = reinterpret_cast<const float*>(r + 64)[l16];
+            } else {
+                nib[k] = 0;
+                w[k] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dot = fmaf(s_tbl[(nib[k] >> (4 * j)) & 15u], y[j], dot);
+            const float e = sum16(w[k] * dot);
+            const int i = i0 + k * (kBlock / 16);
+            const int64_t o = (int64_t)cand_before + i;
+            if (l16 == 0 && pos[k] >= 0 && o < cmax) {
+                cand_pos[(int64_t)u * cmax + o] = pos[k];
+                cand_est[(int64_t)u * cmax + o] = e * inv_sqrt_d;
+            }
         }
     }
+}
 
-    // ---- ticket: the unit's last block selects the top-k among its C candidates
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&tickets[u], 1u) == (uint32_t)(n_chunks - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+// ---------------------------------------------------------------------------
+// fine top-k: one 1024-thread block per unit.  MSB-first radix select of the
+// k-th largest order key in three passes (11, 11, 10 bits), the digit search
+// of each pass done by one wave; then compaction in candidate (= position)
+// order, each thread owning a contiguous segment.
+// ---------------------------------------------------------------------------
+constexpr int kFBlock = 1024;
+constexpr int kFineLds = 16384;  // candidates held in LDS; more are read from memory
+constexpr int kRadixBins = 2048;
 
-    const int k_eff = C < top_k ? C : top_k;
+__global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict__ cand_pos,
+                                                       const float* __restrict__ cand_est,
+                                                       int64_t cmax, int C, int top_k,
+                                                       int32_t* __restrict__ sel,
+                                                       int32_t* __restrict__ sel_n) {
+    const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    __shared__ uint32_t s_key[kFineLds];
+    __shared__ uint32_t s_h[kRadixBins];
+    __shared__ uint32_t s_tmp[kFBlock / 64];
+    __shared__ uint32_t s_digit, s_above;
     const float* est = cand_est + (int64_t)u * cmax;
     const int32_t* cpos = cand_pos + (int64_t)u * cmax;
-    __shared__ uint32_t s_h[256];
-    __shared__ uint32_t s_digit, s_above;
-    uint32_t prefix = 0, pmask = 0;
-    uint32_t remaining = (uint32_t)k_eff;
-    if (k_eff < C) {
-        // MSB-first radix select of the k_eff-th largest order key, 8 bits a pass
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            s_h[tid] = 0;
+    const int k_eff = C < top_k ? C : top_k;
+    const bool in_lds = C <= kFineLds;
+    if (in_lds) {
+        constexpr int kUnroll = 4;
+        for (int i0 = tid; i0 < C; i0 += kUnroll * kFBlock) {
+            float e[kUnroll];
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+                const int i = i0 + k * kFBlock;
+                e[k] = (i < C) ? est[i] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+                const int i = i0 + k * kFBlock;
+                if (i < C) s_key[i] = f32_order_key(e[k]);
+            }
+        }
+    }
+    __syncthreads();
+    auto key_at = [&](int i) -> uint32_t { return in_lds ? s_key[i] : f32_order_key(est[i]); };
+
+    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k_eff;
+    const bool all = k_eff >= C;
+    if (!all) {
+        const int shifts[3] = {21, 10, 0};
+        const int widths[3] = {11, 11, 10};
+        for (int p = 0; p < 3; ++p) {
+            const int shift = shifts[p];
+            const uint32_t dmask = (1u << widths[p]) - 1u;
+            const int nb = 1 << widths[p];
+            for (int b = tid; b < nb; b += kFBlock) s_h[b] = 0;
             __syncthreads();
-            for (int i = tid; i < C; i += kBlock) {
-                const uint32_t key = f32_order_key(est[i]);
-                if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & 255u], 1u);
+            for (int i = tid; i < C; i += kFBlock) {
+                const uint32_t key = key_at(i);
+                if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
             }
             __syncthreads();
-            // thread t looks at digit 255 - t; inclusive count of digits >= it
-            const uint32_t hcount = s_h[255 - tid];
-            uint32_t ge_tot;
-            const uint32_t above = block_excl_scan(hcount, s_tmp, &ge_tot);  // digits > 255-t
-            if (above < remaining && above + hcount >= remaining) {
-                s_digit = 255u - tid;
-                s_above = above;
+            if (tid < 64) {
+                // lane owns digits, descending: d = nb-1 - (lane*per + j)
+                const int per = nb / 64;
+                uint32_t segsum = 0;
+                for (int j = 0; j < per; ++j) segsum += s_h[nb - 1 - (lane * per + j)];
+                uint32_t x = segsum;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t yv = __shfl_up(x, off, 64);
+                    if (lane >= off) x += yv;
+                }
+                uint32_t above = x - segsum;  // count of larger digits
+                if (above < remaining && above + segsum >= remaining) {
+                    for (int j = 0; j < per; ++j) {
+                        const int d = nb - 1 - (lane * per + j);
+                        const uint32_t h = s_h[d];
+                        if (above + h >= remaining) {
+                            s_digit = (uint32_t)d;
+                            s_above = above;
+                            break;
+                        }
+                        above += h;
+                    }
+                }
             }
             __syncthreads();
             prefix |= s_digit << shift;
-            pmask |= 255u << shift;
+            pmask |= dmask << shift;
             remaining -= s_above;
             __syncthreads();
         }
-    } else {
-        prefix = 0;           // everything qualifies
-        pmask = 0;
-        remaining = 0xffffffffu;
     }
     const uint32_t kth = prefix;
-    // compaction in candidate (= position) order
-    uint32_t eq_run = 0, out_run = 0;
-    for (int base = 0; base < C; base += kBlock) {
-        const int i = base + tid;
-        uint32_t key = 0;
-        bool valid = i < C;
-        if (valid) key = f32_order_key(est[i]);
-        const bool eq = valid && (k_eff < C) && key == kth;
-        uint32_t eq_tot;
-        const uint32_t eq_rank = eq_run + block_excl_scan(eq ? 1u : 0u, s_tmp, &eq_tot);
-        const bool in = valid && ((k_eff >= C) || key > kth || (eq && eq_rank < remaining));
-        uint32_t in_tot;
-        const uint32_t o = out_run + block_excl_scan(in ? 1u : 0u, s_tmp, &in_tot);
-        if (in && o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = cpos[i];
-        eq_run += eq_tot;
-        out_run += in_tot;
+    // compaction: thread t owns candidates [t*seg, (t+1)*seg)
+    const int seg = (C + kFBlock - 1) / kFBlock;
+    const int b0 = tid * seg;
+    uint32_t eqc = 0;
+    for (int j = 0; j < seg; ++j) {
+        const int i = b0 + j;
+        if (i < C && !all && key_at(i) == kth) ++eqc;
     }
-    if (tid == 0) {
-        sel_n[u] = k_eff;
-        tickets[u] = 0;
+    uint32_t tot;
+    const uint32_t eq_start = block_excl_scan_t<kFBlock>(eqc, s_tmp, &tot);
+    auto selected = [&](int i, uint32_t& r) -> bool {
+        if (all) return true;
+        const uint32_t key = key_at(i);
+        return key > kth || (key == kth && r++ < remaining);
+    };
+    uint32_t inc = 0, r = eq_start;
+    for (int j = 0; j < seg; ++j) {
+        const int i = b0 + j;
+        if (i < C && selected(i, r)) ++inc;
     }
+    uint32_t o = block_excl_scan_t<kFBlock>(inc, s_tmp, &tot);
+    r = eq_start;
+    for (int j = 0; j < seg; ++j) {
+        const int i = b0 + j;
+        if (i < C && selected(i, r)) {
+            if (o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = cpos[i];
+            ++o;
+        }
+    }
+    if (tid == 0) sel_n[u] = k_eff;
 }
 
 // writes an empty selection (retrieval zone empty)
@@ -308,27 +377,42 @@ __global__ void empty_select_kernel(int units, int32_t* sel_n, int32_t* meta) {
     }
 }
 
+hipError_t probe_kernel_image() {
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&empty_select_kernel));
+}
+
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, uint32_t* bhist, int nbins, uint32_t* tickets,
-                       int32_t* meta, int32_t* off, int64_t C, int top_k, hipStream_t st) {
-    scan_kernel<<<dim3(n_chunks, units), dim3(kBlock), 0, st>>>(
-        ids, cap, sink_end, n_r, chunk, n_chunks, max_chunks, lut, scores, bhist, nbins, tickets,
-        meta, off, C, top_k);
+                       uint16_t* scores, uint16_t* ge, uint32_t* hist_tot, int nbins,
+                       hipStream_t st) {
+    const dim3 grid(n_chunks, units), blk(kBlock);
+#define PK_SCAN(K)                                                                            \
+    scan_kernel<K><<<grid, blk, 0, st>>>(ids, cap, sink_end, n_r, max_chunks, lut, scores, ge, \
+                                         hist_tot, nbins)
+    switch (chunk / kBlock) {
+        case 1: PK_SCAN(1); break;
+        case 2: PK_SCAN(2); break;
+        case 4: PK_SCAN(4); break;
+        case 8: PK_SCAN(8); break;
+        case 16: PK_SCAN(16); break;
+        case 32: PK_SCAN(32); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef PK_SCAN
     return hipGetLastError();
 }
 
 hipError_t launch_rerank(int chunk, const uint16_t* scores, const uint8_t* rec, int64_t cap,
                          int units, int64_t sink_end, int64_t n_r, int n_chunks, int max_chunks,
-                         const int32_t* meta, const int32_t* off, const float* ysum,
-                         const CodeTables& tab, int32_t* cand_pos, float* cand_est, int64_t cmax,
-                         uint32_t* tickets, int top_k, int32_t* sel, int32_t* sel_n,
-                         hipStream_t st) {
+                         const uint32_t* hist_tot, const uint16_t* ge, int nbins, int64_t C,
+                         int top_k, const float* ysum, const CodeTables& tab, int32_t* cand_pos,
+                         float* cand_est, int64_t cmax, int32_t* meta, hipStream_t st) {
     const dim3 grid(n_chunks, units), blk(kBlock);
-#define PK_RERANK(K)                                                                           \
-    rerank_kernel<K><<<grid, blk, 0, st>>>(scores, rec, cap, sink_end, n_r, n_chunks,          \
-                                           max_chunks, meta, off, ysum, tab, cand_pos,         \
-                                           cand_est, cmax, tickets, top_k, sel, sel_n)
+#define PK_RERANK(K)                                                                          \
+    rerank_kernel<K><<<grid, blk, 0, st>>>(scores, rec, cap, sink_end, n_r, max_chunks,       \
+                                           hist_tot, ge, nbins, C, top_k, ysum, tab, cand_pos, \
+                                           cand_est, cmax, meta)
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1); break;
         case 2: PK_RERANK(2); break;
@@ -339,6 +423,13 @@ hipError_t launch_rerank(int chunk, const uint16_t* scores, const uint8_t* rec, 
         default: return hipErrorInvalidValue;
     }
 #undef PK_RERANK
+    return hipGetLastError();
+}
+
+hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
+                       int C, int top_k, int32_t* sel, int32_t* sel_n, hipStream_t st) {
+    fine_kernel<<<dim3(units), dim3(kFBlock), 0, st>>>(cand_pos, cand_est, cmax, C, top_k, sel,
+                                                       sel_n);
     return hipGetLastError();
 }
 

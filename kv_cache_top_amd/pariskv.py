@@ -113,6 +113,37 @@ class ParisKV:
         sel, sel_n = self.retrieve(q, stream=stream)
         return self.sparse_attend(q, sel, sel_n, stream=stream), sel, sel_n
 
+    def decode_step(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                    sel: torch.Tensor | None = None, sel_n: torch.Tensor | None = None,
+                    out: torch.Tensor | None = None, stream=None):
+        """Append the new token, retrieve and attend in one call (pk_decode_step);
+        returns (out, sel, sel_n)."""
+        self._check_rows(k_new, (self.batch, self.n_kv, 128))
+        self._check_rows(v_new, (self.batch, self.n_kv, 128))
+        self._check_rows(q, (self.batch, self.n_q, 128))
+        dev = q.device
+        if sel is None:
+            sel = torch.empty((self.batch, self.n_kv, self.cfg.top_k), dtype=torch.int32, device=dev)
+        if sel_n is None:
+            sel_n = torch.empty((self.batch, self.n_kv), dtype=torch.int32, device=dev)
+        if out is None:
+            out = torch.empty((self.batch, self.n_q, 128), dtype=torch.float32, device=dev)
+        nat.check(nat.lib.pk_decode_step(self._ctx, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(sel),
+                                         _ptr(sel_n), _ptr(out), _stream(stream)), "pk_decode_step")
+        return out, sel, sel_n
+
+    def profile(self, on: bool = True) -> None:
+        """Start (or stop) per-stage kernel timing with HIP events."""
+        nat.check(nat.lib.pk_profile_enable(self._ctx, 1 if on else 0), "pk_profile_enable")
+
+    def profile_read(self) -> dict:
+        """{stage: (total_ms, launches)} since profiling was enabled."""
+        n = len(nat.STAGES)
+        ms = (ctypes.c_double * n)()
+        ln = (ctypes.c_int64 * n)()
+        nat.check(nat.lib.pk_profile_read(self._ctx, ms, ln), "pk_profile_read")
+        return {name: (ms[i], ln[i]) for i, name in enumerate(nat.STAGES)}
+
     # -- introspection -------------------------------------------------------
     def window(self):
         vals = [ctypes.c_int64() for _ in range(4)]

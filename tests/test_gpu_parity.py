@@ -144,6 +144,50 @@ def test_decode_window_append_evict():
         win.end_step()
 
 
+def test_decode_step_matches_separate_calls():
+    """pk_decode_step (append fused into the first retrieval kernel) gives the same
+    window, selection and output as append + retrieve + attend, across an eviction."""
+    T, N0 = 80, 3000
+    wl = W.gqa_bf16(N=N0, top_k=256, n_local=64, buf_tokens=32)
+    Kn, Vn, Qn = W.decode_stream(wl, T)
+    a = gc.make_ctx(wl, capacity=N0 + T)
+    b = gc.make_ctx(wl, capacity=N0 + T)
+    a.encode_keys(N0)
+    b.encode_keys(N0)
+    dt = gc.torch_dtype(wl)
+    for t in range(T):
+        k = torch.from_numpy(Kn[t]).to(dt).cuda()
+        v = torch.from_numpy(Vn[t]).to(dt).cuda()
+        q = torch.from_numpy(Qn[t]).to(dt).cuda()
+        out_a, sel_a, n_a = a.decode_step(k, v, q)
+        b.append(k, v)
+        sel_b, n_b = b.retrieve(q)
+        out_b = b.sparse_attend(q, sel_b, n_b)
+        assert a.window() == b.window()
+        if t % 10 == 0 or t in (31, 32, 33):
+            torch.cuda.synchronize()
+            assert torch.equal(n_a, n_b) and torch.equal(sel_a, sel_b)
+            assert torch.equal(out_a, out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.K, b.K) and torch.equal(a.V, b.V)
+
+
+def test_profiling_counts_launches():
+    wl = W.gqa_bf16(N=5000, top_k=256)
+    pkv = gc.make_ctx(wl)
+    pkv.profile(True)
+    pkv.encode_keys(wl.n_tokens)
+    q = gc.queries(wl)
+    for _ in range(3):
+        pkv.step(q)
+    prof = pkv.profile_read()
+    pkv.profile(False)
+    for stage, n in (("encode", 1), ("qprep", 3), ("scan", 3), ("rerank", 3), ("fine", 3),
+                     ("attend", 3), ("combine", 3)):
+        assert prof[stage][1] == n, (stage, prof[stage])
+        assert prof[stage][0] > 0
+
+
 def test_deterministic():
     wl = W.gqa_bf16(N=20011, top_k=512)
     pkv = gc.make_ctx(wl)
