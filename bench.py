@@ -49,7 +49,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=4)
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of a known size, 8 times; under
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE its per-dispatch readings give the
+    counters' scale (expected: 1 GiB read and 1 GiB written per dispatch)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 8}), flush=True)
 
 
 class Layer:
@@ -172,6 +189,9 @@ def main():
     import kv_cache_top_amd._native as nat
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.init()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     layers = [Layer(args, l) for l in range(args.layers)]
     # prefill encode of every layer (timed per layer, reported separately)
@@ -225,7 +245,7 @@ def main():
     for name in nat.STAGES:
         if stage_n[name]:
             stages[name] = {"launches": stage_n[name], "avg_us": 1e3 * stage_ms[name] / stage_n[name]}
-    n_prof = args.profile_steps
+    n_prof = max(1, args.profile_steps)
 
     def gbs(name):
         if name not in stages:
@@ -234,13 +254,14 @@ def main():
 
     scan_gbs = gbs("scan")
     comb_bytes = sum(sums.values()) / n_prof
-    comb_us = sum(stages[k]["avg_us"] for k in ("scan", "rerank", "attend"))
-    comb_gbs = comb_bytes / (comb_us * 1e-6) / 1e9
+    comb_us = sum(stages[k]["avg_us"] for k in ("scan", "rerank", "attend") if k in stages)
+    comb_gbs = comb_bytes / (comb_us * 1e-6) / 1e9 if comb_us else None
     for k in ("scan", "rerank", "attend"):
-        stages[k]["alg_bytes"] = int(sums[k] / n_prof)
-        stages[k]["GBps"] = gbs(k)
+        if k in stages:
+            stages[k]["alg_bytes"] = int(sums[k] / n_prof)
+            stages[k]["GBps"] = gbs(k)
 
-    rec, planted = recall(layers[(base + n_prof - 1) % nl])
+    rec, planted = recall(layers[(base + args.profile_steps - 1) % nl])
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -278,7 +299,8 @@ def main():
             "frac": (scan_gbs / HBM_PEAK_GBS) if scan_gbs else None,
             "traffic": None,
         },
-        "retrieval_hbm": {"scan_rerank_gather_GBps": comb_gbs, "frac": comb_gbs / HBM_PEAK_GBS,
+        "retrieval_hbm": {"scan_rerank_gather_GBps": comb_gbs,
+                          "frac": comb_gbs / HBM_PEAK_GBS if comb_gbs else None,
                           "bytes_per_step": int(comb_bytes), "kernel_us_per_step": comb_us},
         "stages": stages,
         "keys_scanned_per_s": keys_per_step * 1e3 / ms_step,

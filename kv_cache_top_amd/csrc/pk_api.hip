@@ -28,15 +28,15 @@ struct pk_ctx {
     bool prefilled = false;
     int64_t n = 0, sink_end = 0, r_end = 0, buf = 0;
     // sizes
-    int nbins = 0, max_chunks = 0, max_splits = 0;
-    int64_t cmax = 0;
+    int nbins = 0, hstride = 0, max_chunks = 0, max_splits = 0;
+    int64_t cmax = 0, sstride = 0;
     // device buffers
     uint8_t* ids = nullptr;       // [units][cap][16]   bucket ids
     uint8_t* rec = nullptr;       // [units][cap][128]  nibbles + w
     uint8_t* lut = nullptr;       // [units][16][256]   vote table
     float* ysum = nullptr;        // [units][128]       sum of rotated queries
-    uint16_t* scores = nullptr;   // [units][cap]       coarse scores (retrieval offset)
-    uint32_t* hist = nullptr;     // [units][nbins]     coarse-score histogram
+    uint16_t* scores = nullptr;   // [units][sstride] + pad   coarse scores (retrieval offset)
+    uint32_t* hist = nullptr;     // [units][hstride]   coarse-score histogram
     uint16_t* ge = nullptr;       // [units][max_chunks][nbins] per-chunk #{score >= s}
     int32_t* meta = nullptr;      // [units][4]
     int32_t* cand_pos = nullptr;  // [units][cmax]
@@ -194,7 +194,7 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     {
         StageTimer tm(c, PK_STAGE_QPREP, st);
         PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
-                                c->cfg.vote_weight, c->lut, c->ysum, c->hist, c->nbins, k_new,
+                                c->cfg.vote_weight, c->lut, c->ysum, c->hist, c->hstride, k_new,
                                 v_new, c->K, c->V, row, c->cap, c->n - 1, st));
     }
     const int64_t n_r = c->r_end - c->sink_end;
@@ -208,14 +208,15 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     {
         StageTimer tm(c, PK_STAGE_SCAN, st);
         PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
-                               c->max_chunks, c->lut, c->scores, c->ge, c->hist, c->nbins, st));
+                               c->max_chunks, c->lut, c->scores, c->sstride, c->ge, c->hist,
+                               c->hstride, c->nbins, st));
     }
     {
         StageTimer tm(c, PK_STAGE_RERANK, st);
-        PK_HIP(pk::launch_rerank(chunk, c->scores, c->rec, c->cap, c->units, c->sink_end, n_r,
-                                 n_chunks, c->max_chunks, c->hist, c->ge, c->nbins, C,
-                                 c->cfg.top_k, c->ysum, c->tab, c->cand_pos, c->cand_est, c->cmax,
-                                 c->meta, st));
+        PK_HIP(pk::launch_rerank(chunk, c->scores, c->sstride, c->rec, c->cap, c->units,
+                                 c->sink_end, n_r, n_chunks, c->max_chunks, c->hist, c->hstride,
+                                 c->ge, c->nbins, C, c->cfg.top_k, c->ysum, c->tab, c->cand_pos,
+                                 c->cand_est, c->cmax, c->meta, st));
     }
     StageTimer tm(c, PK_STAGE_FINE, st);
     PK_HIP(pk::launch_fine(c->cand_pos, c->cand_est, c->cmax, c->units, (int)C, c->cfg.top_k, sel,
@@ -292,6 +293,8 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     c->mem = store_mem;
     c->device = dev;
     c->nbins = nbins;
+    c->hstride = (nbins + 3) / 4 * 4;
+    c->sstride = (capacity + 7) / 8 * 8;
     if (pk_codebook(cfg->sub_dim, 8, c->tab.levels, c->tab.sq_thr) != PK_OK) {
         delete c;
         return PK_ERR_INVALID;
@@ -310,8 +313,9 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         {(void**)&c->rec, (size_t)(U * capacity * pk::kRec)},
         {(void**)&c->lut, (size_t)(U * pk::kSub * 256)},
         {(void**)&c->ysum, (size_t)(U * pk::kD * 4)},
-        {(void**)&c->scores, (size_t)(U * capacity * 2)},
-        {(void**)&c->hist, (size_t)(U * nbins * 4)},
+        // score rows padded to 16 B; the tail pad covers vector reads past the last row
+        {(void**)&c->scores, (size_t)((U * c->sstride + 8192) * 2)},
+        {(void**)&c->hist, (size_t)(U * c->hstride * 4)},
         {(void**)&c->ge, (size_t)(U * c->max_chunks * (int64_t)nbins * 2)},
         {(void**)&c->meta, (size_t)(U * 4 * 4)},
         {(void**)&c->cand_pos, (size_t)(U * c->cmax * 4)},
@@ -326,6 +330,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         }
     }
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
+        hipMemset(c->scores, 0, (U * c->sstride + 8192) * 2) != hipSuccess ||
         hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_all(c);
@@ -473,7 +478,12 @@ pk_status pk_debug_copy(pk_ctx* c, int32_t what, void* host_dst, size_t bytes, v
         case PK_DBG_NCAND: src = c->meta; break;
     }
     const hipStream_t st = (hipStream_t)stream;
-    PK_HIP(hipMemcpyAsync(host_dst, src, bytes, hipMemcpyDeviceToHost, st));
+    if (what == PK_DBG_SCORES) {
+        PK_HIP(hipMemcpy2DAsync(host_dst, c->cap * 2, src, c->sstride * 2, c->cap * 2, c->units,
+                                hipMemcpyDeviceToHost, st));
+    } else {
+        PK_HIP(hipMemcpyAsync(host_dst, src, bytes, hipMemcpyDeviceToHost, st));
+    }
     PK_HIP(hipStreamSynchronize(st));
     return PK_OK;
 }

@@ -31,12 +31,19 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     __shared__ float s_red[kBlock / 64][G][kD];
     __shared__ float s_m[G], s_l[G];
 
+    // the key slots of this 16-lane group: kk = wave*4 + grp + 16*j, j < kPer.
+    // Selected positions are read together with their count (entries past the
+    // count are masked afterwards).
+    constexpr int kPer = kSplit / (kBlock / 16);
     const int64_t n_hot = sink_end + (n_tok - r_end);
-    int nsel = sel_n[u];
-    nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
-    const int64_t total = n_hot + nsel;
     const int64_t i0 = (int64_t)sp * kSplit;
-    const int nk = (int)((total - i0) < kSplit ? (total - i0 > 0 ? total - i0 : 0) : kSplit);
+    int32_t cand[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int64_t i = i0 + wave * 4 + grp + j * (kBlock / 16) - n_hot;
+        cand[j] = sel[(int64_t)u * top_k + (i < 0 ? 0 : (i < top_k ? i : top_k - 1))];
+    }
+    int nsel = sel_n[u];
 
     // this lane's 8 coordinates of every query head of the group, pre-scaled by 1/sqrt(d)
     float qv[G][8];
@@ -47,17 +54,16 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
         for (int r = 0; r < 8; ++r) qv[g][r] *= 0.08838834764831845f;
     }
 
-    // key slots of this 16-lane group: kk = wave*4 + grp + 16*j, j < 4
-    constexpr int kPer = kSplit / (kBlock / 16);
+    nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
+    const int64_t total = n_hot + nsel;
+    const int nk = (int)((total - i0) < kSplit ? (total - i0 > 0 ? total - i0 : 0) : kSplit);
     int64_t pos[kPer];
     bool ok[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int kk = wave * 4 + grp + j * (kBlock / 16);
         const int64_t i = i0 + kk;
-        int64_t p = 0;
-        if (kk < nk) p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end))
-                                     : (int64_t)sel[(int64_t)u * top_k + (i - n_hot)];
+        const int64_t p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end)) : (int64_t)cand[j];
         ok[j] = kk < nk && p >= 0 && p < n_tok;
         pos[j] = ok[j] ? p : 0;
     }
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
             if (l16 == 0 && kk < nk) s_p[g][kk] = ok[j] ? d : -INFINITY;
         }
     }
-    __syncthreads();
+    lds_sync();
     // softmax statistics of the split, one wave per head (strided)
     for (int g = wave; g < G; g += kBlock / 64) {
         const float a = (lane < nk) ? s_p[g][lane] : -INFINITY;
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
             s_l[g] = l;
         }
     }
-    __syncthreads();
+    lds_sync();
     // weighted values
     float acc[G][8];
 #pragma unroll
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
 #pragma unroll
             for (int r = 0; r < 8; ++r) s_red[wave][g][8 * l16 + r] = acc[g][r];
     }
-    __syncthreads();
+    lds_sync();
     // partial record per (unit, split, head): [m, l, o[128]]
     float* myp = part + ((int64_t)u * n_splits + sp) * G * (kD + 2);
     for (int i = tid; i < G * kD; i += kBlock) {
@@ -148,22 +154,24 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     }
 }
 
-// merge of the split partials: one block per unit.  All (m, l) pairs are read
-// at once; wave g folds head g's; each thread then sums its outputs over the
-// splits with the loads of 16 splits in flight.
-__global__ __launch_bounds__(kBlock) void combine_kernel(const float* __restrict__ part, int G,
-                                                          int n_splits, float* __restrict__ out) {
+// merge of the split partials: one 1024-thread block per unit.  All (m, l)
+// pairs are read at once; wave g folds head g's; each thread then sums one
+// output over the splits with the loads of 32 splits in flight.
+constexpr int kCBlock = 1024;
+
+__global__ __launch_bounds__(kCBlock) void combine_kernel(const float* __restrict__ part, int G,
+                                                           int n_splits, float* __restrict__ out) {
     const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ float s_m[8][kMaxSplits];
     __shared__ float s_f[8][kMaxSplits];
     const float* up = part + (int64_t)u * n_splits * G * (kD + 2);
-    for (int i = tid; i < G * n_splits; i += kBlock) {
+    for (int i = tid; i < G * n_splits; i += kCBlock) {
         const int s = i / G, g = i - s * G;
         s_m[g][s] = up[(s * G + g) * (kD + 2)];
         s_f[g][s] = up[(s * G + g) * (kD + 2) + 1];
     }
-    __syncthreads();
-    for (int g = wave; g < G; g += kBlock / 64) {
+    lds_sync();
+    for (int g = wave; g < G; g += kCBlock / 64) {
         float M = -INFINITY;
         for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, s_m[g][s]);
 #pragma unroll
@@ -180,17 +188,17 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const float* __restrict
         const float invL = 1.0f / L;
         for (int s = lane; s < n_splits; s += 64) s_f[g][s] = s_m[g][s] * invL;
     }
-    __syncthreads();
-    constexpr int kUnroll = 16;
-    for (int i = tid; i < G * kD; i += kBlock) {
+    lds_sync();
+    constexpr int kUnroll = 32;
+    for (int i = tid; i < G * kD; i += kCBlock) {
         const int g = i / kD, d = i - g * kD;
         float o = 0.0f;
         for (int s0 = 0; s0 < n_splits; s0 += kUnroll) {
             float v[kUnroll];
 #pragma unroll
             for (int k = 0; k < kUnroll; ++k) {
-                const int s = s0 + k;
-                v[k] = (s < n_splits) ? up[(s * G + g) * (kD + 2) + 2 + d] : 0.0f;
+                const int s = s0 + k < n_splits ? s0 + k : n_splits - 1;
+                v[k] = up[(s * G + g) * (kD + 2) + 2 + d];
             }
 #pragma unroll
             for (int k = 0; k < kUnroll; ++k)
@@ -224,7 +232,7 @@ int attend_split() { return kSplit; }
 
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st) {
-    combine_kernel<<<dim3(units), dim3(kBlock), 0, st>>>(part, G, n_splits, out);
+    combine_kernel<<<dim3(units), dim3(kCBlock), 0, st>>>(part, G, n_splits, out);
     return hipGetLastError();
 }
 int attend_max_splits() { return kMaxSplits; }

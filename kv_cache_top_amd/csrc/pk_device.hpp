@@ -85,6 +85,16 @@ __device__ __forceinline__ void fwht128_g16(float v[8], int l16) {
     }
 }
 
+// Workgroup barrier that orders LDS accesses only.  Every barrier in these
+// kernels exchanges data through LDS; none hands global memory between the
+// threads of a block.  Unlike __syncthreads(), it does not wait for the
+// wave's outstanding global loads, so loads issued before it stay in flight.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ((t0+t1)+(t2+t3)) + ((t4+t5)+(t6+t7)), fp32
 __device__ __forceinline__ float tree8(const float t[8]) {
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
@@ -107,7 +117,7 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
 
 // Block-wide exclusive scan of one uint32 per thread for a block of NT
 // threads.  `tmp` must hold NT / 64 entries.  Returns the exclusive prefix;
-// the block total goes to *total.  Contains two __syncthreads.
+// the block total goes to *total.  Contains two LDS barriers.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* tmp, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -118,7 +128,7 @@ __device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* tmp,
         if (lane >= off) x += y;
     }
     if (lane == 63) tmp[wave] = x;
-    __syncthreads();
+    lds_sync();
     uint32_t before = 0, all = 0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
@@ -126,7 +136,7 @@ __device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* tmp,
         if (w < wave) before += t;
         all += t;
     }
-    __syncthreads();
+    lds_sync();
     *total = all;
     return before + x - v;
 }

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(const T* __restrict__ K,
                                                          uint64_t sign_hi, CodeTables tab) {
     __shared__ float s_lev[8];
     if (threadIdx.x < 8) s_lev[threadIdx.x] = tab.levels[threadIdx.x];
-    __syncthreads();
+    lds_sync();
 
     const int l16 = threadIdx.x & 15;
     const uint32_t sbits = lane_sign_byte(sign_lo, sign_hi, l16);
@@ -102,7 +102,7 @@ __device__ __forceinline__ bool better(float s, int c, float ts, int tc) {
 template <typename T>
 __global__ __launch_bounds__(kQBlock) void qprep_kernel(
     const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
-    uint8_t* __restrict__ lut, float* __restrict__ ysum, uint32_t* __restrict__ hist_tot, int nbins,
+    uint8_t* __restrict__ lut, float* __restrict__ ysum, uint32_t* __restrict__ hist_tot, int hstride,
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint8_t* __restrict__ K,
     uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos) {
     const int u = blockIdx.x;
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kQBlock) void qprep_kernel(
     __shared__ float s_y[8][kD];
     __shared__ uint32_t s_lut[kSub * 256];
     for (int i = tid; i < kSub * 256; i += kQBlock) s_lut[i] = 0;
-    for (int i = tid; i < nbins; i += kQBlock) hist_tot[(int64_t)u * nbins + i] = 0;
+    for (int i = tid; i < hstride; i += kQBlock) hist_tot[(int64_t)u * hstride + i] = 0;
     if (k_new != nullptr) {
         const int per_row = (int)(row_bytes / 16);
         if (tid < per_row) {
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kQBlock) void qprep_kernel(
 #pragma unroll
         for (int r = 0; r < 8; ++r) s_y[g][8 * l16 + r] = v[r];
     }
-    __syncthreads();
+    lds_sync();
     if (tid < kD) {
         float a = s_y[0][tid];
         for (int g = 1; g < G; ++g) a += s_y[g][tid];
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kQBlock) void qprep_kernel(
             if (active && chi == 0) atomicAdd(&s_lut[b * 256 + bc], wts.w[r]);
         }
     }
-    __syncthreads();
+    lds_sync();
     uint32_t* out = reinterpret_cast<uint32_t*>(lut + (int64_t)u * kSub * 256);
     for (int i = tid; i < kSub * 256 / 4; i += kQBlock) {
         out[i] = (s_lut[4 * i] & 0xffu) | ((s_lut[4 * i + 1] & 0xffu) << 8) |
@@ -228,19 +228,19 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
-                        uint32_t* hist_tot, int nbins, const void* k_new, const void* v_new,
+                        uint32_t* hist_tot, int hstride, const void* k_new, const void* v_new,
                         void* K, void* V, int64_t row_bytes, int64_t cap, int64_t new_pos,
                         hipStream_t st) {
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     if (bf16)
         qprep_kernel<uint16_t><<<dim3(units), dim3(kQBlock), 0, st>>>(
-            (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, nbins,
+            (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, hstride,
             (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
             new_pos);
     else
         qprep_kernel<float><<<dim3(units), dim3(kQBlock), 0, st>>>(
-            (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, nbins,
+            (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, hstride,
             (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
             new_pos);
     return hipGetLastError();

@@ -27,8 +27,8 @@ namespace pk {
 template <int KPT>
 __global__ __launch_bounds__(kBlock) void scan_kernel(
     const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
-    const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores, uint16_t* __restrict__ ge,
-    uint32_t* __restrict__ hist_tot, int nbins) {
+    const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores, int64_t sstride,
+    uint16_t* __restrict__ ge, uint32_t* __restrict__ hist_tot, int hstride, int nbins) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     __shared__ uint32_t s_lut[kSub * 256 / 4];
@@ -36,43 +36,56 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
     __shared__ uint32_t s_tmp[kBlock / 64];
     const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_lut);
 
-    // every id row of this thread is requested before any is used
+    // The vote table is requested first and the key id rows right after, all
+    // before any is used: scoring key j then waits only for its own row.
+    const uint4 lut_part = reinterpret_cast<const uint4*>(lut + (int64_t)u * kSub * 256)[tid];
     const int64_t start = (int64_t)ch * chunk;
     const uint4* idrow = reinterpret_cast<const uint4*>(ids) + u * cap + sink_end;
+    // loads are unconditional (index clamped to the last key, n_r >= 1) so the
+    // compiler can count them and wait for each row individually
     uint4 v[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int64_t i = start + j * kBlock + tid;
-        v[j] = (i < n_r) ? idrow[i] : make_uint4(0, 0, 0, 0);
+        v[j] = idrow[i < n_r ? i : n_r - 1];
     }
-    reinterpret_cast<uint4*>(s_lut)[tid] =
-        reinterpret_cast<const uint4*>(lut + (int64_t)u * kSub * 256)[tid];
+    reinterpret_cast<uint4*>(s_lut)[tid] = lut_part;
     for (int b = tid; b < nbins; b += kBlock) s_hist[b] = 0;
-    __syncthreads();
+    lds_sync();
 
-    uint16_t* srow = scores + u * cap;
+    // histogram: the small scores that most keys have are counted per wave
+    // with ballots (no same-address LDS atomics), the rest with atomics
+    constexpr int kSmall = 8;
+    uint32_t small[kSmall];
+#pragma unroll
+    for (int k = 0; k < kSmall; ++k) small[k] = 0;
+    uint16_t* srow = scores + u * sstride;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int64_t i = start + j * kBlock + tid;
-        if (i < n_r) {
-            const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-            uint32_t sc = 0;
+        const bool valid = i < n_r;
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t sc = 0;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < 4; ++a) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    sc += lut8[(4 * a + k) * 256 + ((w[a] >> (8 * k)) & 255u)];
-            }
-            srow[i] = (uint16_t)sc;
-            atomicAdd(&s_hist[sc], 1u);
+            for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((w[a] >> (8 * k)) & 255u)];
         }
+        if (valid) srow[i] = (uint16_t)sc;
+#pragma unroll
+        for (int k = 0; k < kSmall; ++k) small[k] += (uint32_t)__popcll(__ballot(valid && sc == (uint32_t)k));
+        if (valid && sc >= (uint32_t)kSmall) atomicAdd(&s_hist[sc], 1u);
     }
-    __syncthreads();
+    const int lane = tid & 63;
+#pragma unroll
+    for (int k = 0; k < kSmall; ++k)
+        if (lane == k && small[k] && k < nbins) atomicAdd(&s_hist[k], small[k]);
+    lds_sync();
 
     // unit histogram (relaxed device-scope atomics; read by the next kernel)
     for (int b = tid; b < nbins; b += kBlock) {
         const uint32_t h = s_hist[b];
-        if (h) atomicAdd(&hist_tot[(int64_t)u * nbins + b], h);
+        if (h) atomicAdd(&hist_tot[(int64_t)u * hstride + b], h);
     }
     // chunk suffix counts: thread t owns bins [t*per, t*per+per) in descending
     // score order (reversed index r = nbins-1-s)
@@ -99,8 +112,9 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
 // ---------------------------------------------------------------------------
 template <int KPT>
 __global__ __launch_bounds__(kBlock) void rerank_kernel(
-    const uint16_t* __restrict__ scores, const uint8_t* __restrict__ rec, int64_t cap,
-    int64_t sink_end, int64_t n_r, int max_chunks, const uint32_t* __restrict__ hist_tot,
+    const uint16_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
+    int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
+    const uint32_t* __restrict__ hist_tot, int hstride,
     const uint16_t* __restrict__ ge, int nbins, int64_t C, int top_k,
     const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
     float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
@@ -108,6 +122,7 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int l16 = tid & 15;
     __shared__ int32_t s_list[chunk];
+    __shared__ __align__(16) uint32_t s_hist[kMaxBins];
     __shared__ float s_tbl[16];
     __shared__ uint32_t s_tmp[kBlock / 64];
     __shared__ int s_T, s_need;
@@ -118,25 +133,54 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
     }
 
     // loads that do not depend on the threshold go out first: this chunk's
-    // scores and the unit histogram
+    // scores (contiguous per thread, vector loads; rows are padded so these
+    // never leave the buffer), the unit histogram and the summed query
     const int64_t start = (int64_t)ch * chunk;
     uint32_t s[KPT];
+    {
+        const uint16_t* sp = scores + u * sstride + start + (int64_t)tid * KPT;
+        if constexpr (KPT >= 8) {
+            uint4 raw[KPT / 8];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int64_t i = start + (int64_t)tid * KPT + j;
-        s[j] = (i < n_r) ? (uint32_t)scores[u * cap + i] : 0xffffffffu;
+            for (int q = 0; q < KPT / 8; ++q) raw[q] = reinterpret_cast<const uint4*>(sp)[q];
+#pragma unroll
+            for (int q = 0; q < KPT / 8; ++q) {
+                const uint32_t w4[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    s[8 * q + 2 * k] = w4[k] & 0xffffu;
+                    s[8 * q + 2 * k + 1] = w4[k] >> 16;
+                }
+            }
+        } else if constexpr (KPT == 4) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(sp);
+            s[0] = raw.x & 0xffffu; s[1] = raw.x >> 16; s[2] = raw.y & 0xffffu; s[3] = raw.y >> 16;
+        } else if constexpr (KPT == 2) {
+            const uint32_t raw = *reinterpret_cast<const uint32_t*>(sp);
+            s[0] = raw & 0xffffu; s[1] = raw >> 16;
+        } else {
+            s[0] = sp[0];
+        }
     }
+    const int nq = (nbins + 3) / 4;
+    const uint4 hq = reinterpret_cast<const uint4*>(hist_tot + (int64_t)u * hstride)[tid < nq ? tid : 0];
+    float y[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) y[r] = ysum[(int64_t)u * kD + 8 * l16 + r];
+    for (int i = tid; i < nq; i += kBlock)
+        reinterpret_cast<uint4*>(s_hist)[i] =
+            (i == tid) ? hq : reinterpret_cast<const uint4*>(hist_tot + (int64_t)u * hstride)[i];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (start + (int64_t)tid * KPT + j >= n_r) s[j] = 0xffffffffu;
+    lds_sync();
     const int per = (nbins + kBlock - 1) / kBlock;
-    const uint32_t* H = hist_tot + (int64_t)u * nbins;
     uint32_t hv[kMaxBins / kBlock];
 #pragma unroll
     for (int j = 0; j < kMaxBins / kBlock; ++j) {
         const int r = tid * per + j;
-        hv[j] = (j < per && r < nbins) ? H[nbins - 1 - r] : 0u;
+        hv[j] = (j < per && r < nbins) ? s_hist[nbins - 1 - r] : 0u;
     }
-    float y[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] = ysum[(int64_t)u * kD + 8 * l16 + r];
 
     // coarse threshold: T = largest score with #{score >= T} >= C; `need` ties
     // at T are taken, lowest positions first
@@ -156,7 +200,7 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
             run += hv[j];
         }
     }
-    __syncthreads();
+    lds_sync();
     const int T = s_T;
     const uint32_t need = (uint32_t)s_need;
 
@@ -200,7 +244,7 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
         if ((mask >> j) & 1u) s_list[at++] = (int32_t)(sink_end + start + (int64_t)tid * KPT + j);
-    __syncthreads();
+    lds_sync();
 
     // RSQ-IP: est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g;
     // 16 lanes per candidate, lane b reading subspace b's nibble word and w.
@@ -215,15 +259,11 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int i = i0 + k * (kBlock / 16);
-            pos[k] = (i < (int)n_mem) ? s_list[i] : -1;
-            if (pos[k] >= 0) {
-                const uint8_t* r = rec + ((int64_t)u * cap + pos[k]) * kRec;
-                nib[k] = reinterpret_cast<const uint32_t*>(r)[l16];
-                w[k] = reinterpret_cast<const float*>(r + 64)[l16];
-            } else {
-                nib[k] = 0;
-                w[k] = 0.0f;
-            }
+            const int32_t p = s_list[i < (int)n_mem ? i : i0];
+            pos[k] = (i < (int)n_mem) ? p : -1;
+            const uint8_t* r = rec + ((int64_t)u * cap + p) * kRec;
+            nib[k] = reinterpret_cast<const uint32_t*>(r)[l16];
+            w[k] = reinterpret_cast<const float*>(r + 64)[l16];
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -258,7 +298,7 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ sel_n) {
     const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     __shared__ uint32_t s_key[kFineLds];
-    __shared__ uint32_t s_h[kRadixBins];
+    __shared__ __align__(16) uint32_t s_h[kRadixBins];
     __shared__ uint32_t s_tmp[kFBlock / 64];
     __shared__ uint32_t s_digit, s_above;
     const float* est = cand_est + (int64_t)u * cmax;
@@ -272,7 +312,7 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
 #pragma unroll
             for (int k = 0; k < kUnroll; ++k) {
                 const int i = i0 + k * kFBlock;
-                e[k] = (i < C) ? est[i] : 0.0f;
+                e[k] = est[i < C ? i : C - 1];
             }
 #pragma unroll
             for (int k = 0; k < kUnroll; ++k) {
@@ -281,8 +321,21 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
             }
         }
     }
-    __syncthreads();
+    lds_sync();
     auto key_at = [&](int i) -> uint32_t { return in_lds ? s_key[i] : f32_order_key(est[i]); };
+
+    // this thread's compaction segment: positions requested now, used at the end
+    constexpr int kSegMax = kFineLds / kFBlock;
+    const int seg = (C + kFBlock - 1) / kFBlock;
+    const int b0 = tid * seg;
+    int32_t mypos[kSegMax];
+    if (in_lds) {
+#pragma unroll
+        for (int j = 0; j < kSegMax; ++j) {
+            const int i = b0 + j;
+            mypos[j] = cpos[(j < seg && i < C) ? i : 0];
+        }
+    }
 
     uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k_eff;
     const bool all = k_eff >= C;
@@ -294,71 +347,97 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
             const uint32_t dmask = (1u << widths[p]) - 1u;
             const int nb = 1 << widths[p];
             for (int b = tid; b < nb; b += kFBlock) s_h[b] = 0;
-            __syncthreads();
+            lds_sync();
             for (int i = tid; i < C; i += kFBlock) {
                 const uint32_t key = key_at(i);
                 if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
             }
-            __syncthreads();
+            lds_sync();
             if (tid < 64) {
-                // lane owns digits, descending: d = nb-1 - (lane*per + j)
+                // lane owns the per = nb/64 digits [lane*per, lane*per+per), read as
+                // 16-byte vectors; larger digits belong to higher lanes
                 const int per = nb / 64;
+                uint32_t h[32];
+#pragma unroll
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    if (4 * q4 < per) {
+                        const uint4 x = reinterpret_cast<const uint4*>(s_h + lane * per)[q4];
+                        h[4 * q4] = x.x;
+                        h[4 * q4 + 1] = x.y;
+                        h[4 * q4 + 2] = x.z;
+                        h[4 * q4 + 3] = x.w;
+                    } else {
+                        h[4 * q4] = h[4 * q4 + 1] = h[4 * q4 + 2] = h[4 * q4 + 3] = 0;
+                    }
+                }
                 uint32_t segsum = 0;
-                for (int j = 0; j < per; ++j) segsum += s_h[nb - 1 - (lane * per + j)];
+#pragma unroll
+                for (int j = 0; j < 32; ++j) segsum += h[j];
+                // suffix sum over lanes: counts in digits above this lane's block
                 uint32_t x = segsum;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t yv = __shfl_up(x, off, 64);
-                    if (lane >= off) x += yv;
+                    const uint32_t yv = __shfl_down(x, off, 64);
+                    if (lane + off < 64) x += yv;
                 }
-                uint32_t above = x - segsum;  // count of larger digits
+                uint32_t above = x - segsum;
                 if (above < remaining && above + segsum >= remaining) {
-                    for (int j = 0; j < per; ++j) {
-                        const int d = nb - 1 - (lane * per + j);
-                        const uint32_t h = s_h[d];
-                        if (above + h >= remaining) {
-                            s_digit = (uint32_t)d;
-                            s_above = above;
-                            break;
+#pragma unroll
+                    for (int j = 31; j >= 0; --j) {
+                        if (j < per) {
+                            if (above < remaining && above + h[j] >= remaining) {
+                                s_digit = (uint32_t)(lane * per + j);
+                                s_above = above;
+                            }
+                            above += h[j];
                         }
-                        above += h;
                     }
                 }
             }
-            __syncthreads();
+            lds_sync();
             prefix |= s_digit << shift;
             pmask |= dmask << shift;
             remaining -= s_above;
-            __syncthreads();
+            lds_sync();
         }
     }
     const uint32_t kth = prefix;
-    // compaction: thread t owns candidates [t*seg, (t+1)*seg)
-    const int seg = (C + kFBlock - 1) / kFBlock;
-    const int b0 = tid * seg;
-    uint32_t eqc = 0;
+    // compaction: thread t owns candidates [t*seg, (t+1)*seg); one block scan of
+    // (ties at kth, keys above kth) gives both offsets
+    uint32_t eqc = 0, gtc = 0;
     for (int j = 0; j < seg; ++j) {
         const int i = b0 + j;
-        if (i < C && !all && key_at(i) == kth) ++eqc;
+        if (i < C) {
+            const uint32_t key = key_at(i);
+            if (all || key > kth) ++gtc;
+            else if (key == kth) ++eqc;
+        }
     }
-    uint32_t tot;
-    const uint32_t eq_start = block_excl_scan_t<kFBlock>(eqc, s_tmp, &tot);
-    auto selected = [&](int i, uint32_t& r) -> bool {
-        if (all) return true;
+    uint32_t tot, r, gt_before;
+    if (C < 65536) {
+        const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, s_tmp, &tot);
+        r = packed >> 16;                       // ties at kth before this segment
+        gt_before = packed & 0xffffu;
+    } else {
+        r = block_excl_scan_t<kFBlock>(eqc, s_tmp, &tot);
+        gt_before = block_excl_scan_t<kFBlock>(gtc, s_tmp, &tot);
+    }
+    uint32_t o = gt_before + (r < remaining ? r : remaining);
+    for (int j = 0; j < seg; ++j) {
+        const int i = b0 + j;
+        if (i >= C) break;
         const uint32_t key = key_at(i);
-        return key > kth || (key == kth && r++ < remaining);
-    };
-    uint32_t inc = 0, r = eq_start;
-    for (int j = 0; j < seg; ++j) {
-        const int i = b0 + j;
-        if (i < C && selected(i, r)) ++inc;
-    }
-    uint32_t o = block_excl_scan_t<kFBlock>(inc, s_tmp, &tot);
-    r = eq_start;
-    for (int j = 0; j < seg; ++j) {
-        const int i = b0 + j;
-        if (i < C && selected(i, r)) {
-            if (o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = cpos[i];
+        const bool in = all || key > kth || (key == kth && r++ < remaining);
+        if (in) {
+            int32_t pj = 0;
+            if (in_lds) {
+#pragma unroll
+                for (int jj = 0; jj < kSegMax; ++jj)
+                    if (jj == j) pj = mypos[jj];
+            } else {
+                pj = cpos[i];
+            }
+            if (o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = pj;
             ++o;
         }
     }
@@ -384,12 +463,12 @@ hipError_t probe_kernel_image() {
 
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, uint16_t* ge, uint32_t* hist_tot, int nbins,
-                       hipStream_t st) {
+                       uint16_t* scores, int64_t sstride, uint16_t* ge, uint32_t* hist_tot,
+                       int hstride, int nbins, hipStream_t st) {
     const dim3 grid(n_chunks, units), blk(kBlock);
 #define PK_SCAN(K)                                                                            \
-    scan_kernel<K><<<grid, blk, 0, st>>>(ids, cap, sink_end, n_r, max_chunks, lut, scores, ge, \
-                                         hist_tot, nbins)
+    scan_kernel<K><<<grid, blk, 0, st>>>(ids, cap, sink_end, n_r, max_chunks, lut, scores,    \
+                                         sstride, ge, hist_tot, hstride, nbins)
     switch (chunk / kBlock) {
         case 1: PK_SCAN(1); break;
         case 2: PK_SCAN(2); break;
@@ -403,16 +482,17 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
     return hipGetLastError();
 }
 
-hipError_t launch_rerank(int chunk, const uint16_t* scores, const uint8_t* rec, int64_t cap,
-                         int units, int64_t sink_end, int64_t n_r, int n_chunks, int max_chunks,
-                         const uint32_t* hist_tot, const uint16_t* ge, int nbins, int64_t C,
-                         int top_k, const float* ysum, const CodeTables& tab, int32_t* cand_pos,
-                         float* cand_est, int64_t cmax, int32_t* meta, hipStream_t st) {
+hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, const uint8_t* rec,
+                         int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
+                         int max_chunks, const uint32_t* hist_tot, int hstride, const uint16_t* ge,
+                         int nbins, int64_t C, int top_k, const float* ysum, const CodeTables& tab,
+                         int32_t* cand_pos, float* cand_est, int64_t cmax, int32_t* meta,
+                         hipStream_t st) {
     const dim3 grid(n_chunks, units), blk(kBlock);
 #define PK_RERANK(K)                                                                          \
-    rerank_kernel<K><<<grid, blk, 0, st>>>(scores, rec, cap, sink_end, n_r, max_chunks,       \
-                                           hist_tot, ge, nbins, C, top_k, ysum, tab, cand_pos, \
-                                           cand_est, cmax, meta)
+    rerank_kernel<K><<<grid, blk, 0, st>>>(scores, sstride, rec, cap, sink_end, n_r,          \
+                                           max_chunks, hist_tot, hstride, ge, nbins, C, top_k, \
+                                           ysum, tab, cand_pos, cand_est, cmax, meta)
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1); break;
         case 2: PK_RERANK(2); break;
