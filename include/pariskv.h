@@ -154,8 +154,8 @@ pk_status pk_get_window(const pk_ctx* ctx, int64_t* n_tokens, int64_t* sink_end,
  * summed duration in milliseconds and the number of launches since the last
  * enable (arrays of PK_STAGE_COUNT entries).  Errors: PK_ERR_INVALID. */
 enum { PK_STAGE_ENCODE = 0, PK_STAGE_APPEND = 1, PK_STAGE_QPREP = 2, PK_STAGE_SCAN = 3,
-       PK_STAGE_RERANK = 4, PK_STAGE_FINE = 5, PK_STAGE_ATTEND = 6, PK_STAGE_COMBINE = 7,
-       PK_STAGE_COUNT = 8 };
+       PK_STAGE_SELECT = 4, PK_STAGE_RERANK = 5, PK_STAGE_FINE = 6, PK_STAGE_ATTEND = 7,
+       PK_STAGE_COMBINE = 8, PK_STAGE_COUNT = 9 };
 pk_status pk_profile_enable(pk_ctx* ctx, int32_t on);
 pk_status pk_profile_read(pk_ctx* ctx, double* ms, int64_t* launches);
 

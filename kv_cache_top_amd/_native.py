@@ -17,7 +17,7 @@ PK_OK, PK_ERR_INVALID, PK_ERR_NO_DEVICE, PK_ERR_OOM, PK_ERR_CAPACITY, PK_ERR_HIP
     PK_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
 PK_F32, PK_BF16 = 0, 1
 PK_MEM_DEVICE, PK_MEM_HOST_MAPPED = 0, 1
-STAGES = ("encode", "append", "qprep", "scan", "rerank", "fine", "attend", "combine")
+STAGES = ("encode", "append", "qprep", "scan", "select", "rerank", "fine", "attend", "combine")
 (PK_DBG_IDS, PK_DBG_REC, PK_DBG_LUT, PK_DBG_SCORES, PK_DBG_CAND, PK_DBG_EST,
  PK_DBG_NCAND) = range(7)
 

@@ -86,8 +86,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(const T* __restrict__ K,
 // quad_lo[c & 15] + quad_hi[c >> 4] -- the same fp32 operations in the same
 // order as the direct pairwise tree.  Top-rho = rho rounds of a 16-lane
 // argmax, each removing the winner.
-// The block also clears the unit's coarse-score histogram for the scan that
-// follows, and may copy the step's new K/V token into the store.
+// The block may also copy the step's new K/V token into the store.
 // ---------------------------------------------------------------------------
 struct VoteWeights {
     uint32_t w[kRhoMax];
@@ -102,7 +101,7 @@ __device__ __forceinline__ bool better(float s, int c, float ts, int tc) {
 template <typename T>
 __global__ __launch_bounds__(kQBlock) void qprep_kernel(
     const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
-    uint8_t* __restrict__ lut, float* __restrict__ ysum, uint32_t* __restrict__ hist_tot, int hstride,
+    uint8_t* __restrict__ lut, float* __restrict__ ysum,
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint8_t* __restrict__ K,
     uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos) {
     const int u = blockIdx.x;
@@ -110,7 +109,6 @@ __global__ __launch_bounds__(kQBlock) void qprep_kernel(
     __shared__ float s_y[8][kD];
     __shared__ uint32_t s_lut[kSub * 256];
     for (int i = tid; i < kSub * 256; i += kQBlock) s_lut[i] = 0;
-    for (int i = tid; i < hstride; i += kQBlock) hist_tot[(int64_t)u * hstride + i] = 0;
     if (k_new != nullptr) {
         const int per_row = (int)(row_bytes / 16);
         if (tid < per_row) {
@@ -228,19 +226,18 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
-                        uint32_t* hist_tot, int hstride, const void* k_new, const void* v_new,
-                        void* K, void* V, int64_t row_bytes, int64_t cap, int64_t new_pos,
-                        hipStream_t st) {
+                        const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
+                        int64_t cap, int64_t new_pos, hipStream_t st) {
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     if (bf16)
         qprep_kernel<uint16_t><<<dim3(units), dim3(kQBlock), 0, st>>>(
-            (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, hstride,
+            (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum,
             (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
             new_pos);
     else
         qprep_kernel<float><<<dim3(units), dim3(kQBlock), 0, st>>>(
-            (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum, hist_tot, hstride,
+            (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum,
             (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
             new_pos);
     return hipGetLastError();

@@ -7,16 +7,16 @@
 //  * rerank (RSQ-IP): each candidate's raw score <k, q> is estimated from its
 //    4-bit codes and scales only, and the top-k are selected.
 //
-// Three kernels, no cross-block synchronisation inside any of them (on
-// gfx950 an agent-scope release fence writes back the XCD's L2 and costs far
-// more per block than a kernel boundary):
-//  scan    one 256-thread block per (chunk, unit): coarse scores, the chunk's
-//          suffix counts ge[s] = #{score >= s} and the unit histogram (relaxed
-//          atomics, cleared by the query-prep kernel of the same step);
-//  rerank  same grid: each block derives the coarse threshold from the unit
-//          histogram and its chunk's candidate offset from the suffix counts
-//          of the chunks before it, compacts its candidates in position
-//          order and estimates them with RSQ-IP;
+// Four kernels, no cross-block synchronisation inside any of them (on gfx950
+// an agent-scope release fence writes back the XCD's L2 and costs far more
+// per block than a kernel boundary):
+//  scan    one 256-thread block per (chunk, unit): coarse scores and the
+//          chunk's suffix counts ge[s] = #{score >= s};
+//  select  one 1024-thread block per unit: the coarse threshold T (largest
+//          score with #{score >= T} >= C), the ties at T to take, and for
+//          every chunk the candidates and ties at T in the chunks before it;
+//  rerank  one 256-thread block per (chunk, unit): compacts the chunk's
+//          candidates in position order and estimates them with RSQ-IP;
 //  fine    one 1024-thread block per unit: radix select of the k-th largest
 //          estimate, ties to the lower position, compaction in order.
 #include "pk_device.hpp"
@@ -28,7 +28,7 @@ template <int KPT>
 __global__ __launch_bounds__(kBlock) void scan_kernel(
     const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
     const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores, int64_t sstride,
-    uint16_t* __restrict__ ge, uint32_t* __restrict__ hist_tot, int hstride, int nbins) {
+    uint16_t* __restrict__ ge, int gstride, int nbins) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     __shared__ uint32_t s_lut[kSub * 256 / 4];
@@ -82,11 +82,6 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
         if (lane == k && small[k] && k < nbins) atomicAdd(&s_hist[k], small[k]);
     lds_sync();
 
-    // unit histogram (relaxed device-scope atomics; read by the next kernel)
-    for (int b = tid; b < nbins; b += kBlock) {
-        const uint32_t h = s_hist[b];
-        if (h) atomicAdd(&hist_tot[(int64_t)u * hstride + b], h);
-    }
     // chunk suffix counts: thread t owns bins [t*per, t*per+per) in descending
     // score order (reversed index r = nbins-1-s)
     const int per = (nbins + kBlock - 1) / kBlock;
@@ -97,7 +92,7 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
     }
     uint32_t tot;
     uint32_t run = block_excl_scan(seg, s_tmp, &tot);
-    uint16_t* myge = ge + ((int64_t)u * max_chunks + ch) * nbins;
+    uint16_t* myge = ge + ((int64_t)u * max_chunks + ch) * gstride;
     for (int j = 0; j < per; ++j) {
         const int r = tid * per + j;
         if (r < nbins) {
@@ -108,33 +103,105 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// select: per unit, from the chunks' suffix counts
+//   tot[s] = sum_c ge_c[s] = #{score >= s};  T = max s with tot[s] >= C;
+//   need = C - tot[T+1] ties at T are taken (lowest positions first);
+//   off[c] = {sum_{c'<c} ge_c'[T+1], sum_{c'<c} (ge_c'[T] - ge_c'[T+1])}.
+// Chunk rows are staged through LDS in tiles of kSelTile.
+// ---------------------------------------------------------------------------
+constexpr int kSBlock = 1024;
+constexpr int kSelTile = 64;        // chunk rows per LDS tile (at most)
+constexpr int kSelLds = 16384;      // uint16 entries of staged rows (32 KB)
+
+__global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restrict__ ge,
+                                                         int gstride, int max_chunks, int n_chunks,
+                                                         int nbins, int64_t C, int top_k,
+                                                         int32_t* __restrict__ off,
+                                                         int32_t* __restrict__ meta) {
+    const int u = blockIdx.x, tid = threadIdx.x;
+    __shared__ __align__(16) uint16_t s_rows[kSelLds];
+    __shared__ uint32_t s_tot[kMaxBins + 1];
+    __shared__ uint32_t s_tmp[kSBlock / 64];
+    __shared__ int s_T;
+    const uint16_t* G0 = ge + (int64_t)u * max_chunks * gstride;
+    const int row_vec = gstride / 8;          // uint4 per row
+    const int tile = kSelLds / gstride < kSelTile ? kSelLds / gstride : kSelTile;
+    for (int b = tid; b <= nbins; b += kSBlock) s_tot[b] = 0;
+    if (tid == 0) s_T = 0;
+    lds_sync();
+    for (int c0 = 0; c0 < n_chunks; c0 += tile) {
+        const int rows = (n_chunks - c0) < tile ? (n_chunks - c0) : tile;
+        for (int i = tid; i < rows * row_vec; i += kSBlock)
+            reinterpret_cast<uint4*>(s_rows)[i] =
+                reinterpret_cast<const uint4*>(G0 + (int64_t)c0 * gstride)[i];
+        lds_sync();
+        for (int b = tid; b < nbins; b += kSBlock) {
+            uint32_t a = 0;
+            for (int r = 0; r < rows; ++r) a += s_rows[r * gstride + b];
+            s_tot[b] += a;
+        }
+        lds_sync();
+    }
+    for (int b = tid; b < nbins; b += kSBlock)
+        if ((int64_t)s_tot[b] >= C && (b + 1 == nbins || (int64_t)s_tot[b + 1] < C)) s_T = b;
+    lds_sync();
+    const int T = s_T;
+    const uint32_t above_T = (T + 1 < nbins) ? s_tot[T + 1] : 0u;
+    const uint32_t need = (uint32_t)(C - (int64_t)above_T);
+    // per-chunk counts at T, exclusive scans over chunks (thread-contiguous segments)
+    const int per = (n_chunks + kSBlock - 1) / kSBlock;
+    uint32_t gts = 0, eqs = 0;
+    for (int j = 0; j < per; ++j) {
+        const int c = tid * per + j;
+        if (c < n_chunks) {
+            const uint16_t* g = G0 + (int64_t)c * gstride;
+            const uint32_t at = g[T], ab = (T + 1 < nbins) ? g[T + 1] : 0u;
+            gts += ab;
+            eqs += at - ab;
+        }
+    }
+    uint32_t tot;
+    uint32_t gt_run = block_excl_scan_t<kSBlock>(gts, s_tmp, &tot);
+    uint32_t eq_run = block_excl_scan_t<kSBlock>(eqs, s_tmp, &tot);
+    for (int j = 0; j < per; ++j) {
+        const int c = tid * per + j;
+        if (c < n_chunks) {
+            const uint16_t* g = G0 + (int64_t)c * gstride;
+            const uint32_t at = g[T], ab = (T + 1 < nbins) ? g[T + 1] : 0u;
+            off[((int64_t)u * max_chunks + c) * 2] = (int32_t)gt_run;
+            off[((int64_t)u * max_chunks + c) * 2 + 1] = (int32_t)eq_run;
+            gt_run += ab;
+            eq_run += at - ab;
+        }
+    }
+    if (tid == 0) {
+        meta[u * 4 + 0] = T;
+        meta[u * 4 + 1] = (int32_t)need;
+        meta[u * 4 + 2] = (int32_t)C;
+        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // rerank
 // ---------------------------------------------------------------------------
 template <int KPT>
 __global__ __launch_bounds__(kBlock) void rerank_kernel(
     const uint16_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
-    int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
-    const uint32_t* __restrict__ hist_tot, int hstride,
-    const uint16_t* __restrict__ ge, int nbins, int64_t C, int top_k,
-    const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
-    float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
+    int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks, const int32_t* __restrict__ off,
+    const int32_t* __restrict__ meta, const float* __restrict__ ysum, CodeTables tab,
+    int32_t* __restrict__ cand_pos, float* __restrict__ cand_est, int64_t cmax) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int l16 = tid & 15;
     __shared__ int32_t s_list[chunk];
-    __shared__ __align__(16) uint32_t s_hist[kMaxBins];
     __shared__ float s_tbl[16];
     __shared__ uint32_t s_tmp[kBlock / 64];
-    __shared__ int s_T, s_need;
     if (tid < 16) s_tbl[tid] = ((tid & 8) ? -1.0f : 1.0f) * tab.levels[tid & 7];
-    if (tid == 0) {
-        s_T = 0;
-        s_need = 0;
-    }
 
-    // loads that do not depend on the threshold go out first: this chunk's
-    // scores (contiguous per thread, vector loads; rows are padded so these
-    // never leave the buffer), the unit histogram and the summed query
+    // one round of loads: this chunk's scores (contiguous per thread, vector
+    // loads; rows are padded so these never leave the buffer), the threshold
+    // and this chunk's offsets, the summed rotated query
     const int64_t start = (int64_t)ch * chunk;
     uint32_t s[KPT];
     {
@@ -162,74 +229,32 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
             s[0] = sp[0];
         }
     }
-    const int nq = (nbins + 3) / 4;
-    const uint4 hq = reinterpret_cast<const uint4*>(hist_tot + (int64_t)u * hstride)[tid < nq ? tid : 0];
+    const int T = meta[u * 4 + 0];
+    const uint32_t need = (uint32_t)meta[u * 4 + 1];
+    const uint32_t gt_chunk = (uint32_t)off[((int64_t)u * max_chunks + ch) * 2];
+    const uint32_t eq_chunk = (uint32_t)off[((int64_t)u * max_chunks + ch) * 2 + 1];
     float y[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) y[r] = ysum[(int64_t)u * kD + 8 * l16 + r];
-    for (int i = tid; i < nq; i += kBlock)
-        reinterpret_cast<uint4*>(s_hist)[i] =
-            (i == tid) ? hq : reinterpret_cast<const uint4*>(hist_tot + (int64_t)u * hstride)[i];
+
+    // this chunk's candidates, in position order: keys above T, and ties at T
+    // while the unit's tie budget lasts.  One packed scan of (ties, above).
+    uint32_t eqc = 0, gtc = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
+    for (int j = 0; j < KPT; ++j) {
         if (start + (int64_t)tid * KPT + j >= n_r) s[j] = 0xffffffffu;
-    lds_sync();
-    const int per = (nbins + kBlock - 1) / kBlock;
-    uint32_t hv[kMaxBins / kBlock];
-#pragma unroll
-    for (int j = 0; j < kMaxBins / kBlock; ++j) {
-        const int r = tid * per + j;
-        hv[j] = (j < per && r < nbins) ? s_hist[nbins - 1 - r] : 0u;
+        gtc += (s[j] != 0xffffffffu && s[j] > (uint32_t)T) ? 1u : 0u;
+        eqc += (s[j] == (uint32_t)T) ? 1u : 0u;
     }
-
-    // coarse threshold: T = largest score with #{score >= T} >= C; `need` ties
-    // at T are taken, lowest positions first
-    uint32_t seg = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxBins / kBlock; ++j) seg += hv[j];
     uint32_t tot;
-    uint32_t run = block_excl_scan(seg, s_tmp, &tot);
-#pragma unroll
-    for (int j = 0; j < kMaxBins / kBlock; ++j) {
-        const int r = tid * per + j;
-        if (j < per && r < nbins) {
-            if ((int64_t)run < C && (int64_t)(run + hv[j]) >= C) {
-                s_T = nbins - 1 - r;
-                s_need = (int)(C - run);
-            }
-            run += hv[j];
-        }
-    }
-    lds_sync();
-    const int T = s_T;
-    const uint32_t need = (uint32_t)s_need;
-
-    // candidates and ties at T in the chunks before this one
-    uint32_t gt_b = 0, eq_b = 0;
-    for (int c = tid; c < ch; c += kBlock) {
-        const uint16_t* g = ge + ((int64_t)u * max_chunks + c) * nbins;
-        const uint32_t at = g[T];
-        const uint32_t above = (T + 1 < nbins) ? g[T + 1] : 0u;
-        gt_b += above;
-        eq_b += at - above;
-    }
-    uint32_t eqc = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) eqc += (s[j] == (uint32_t)T) ? 1u : 0u;
-    uint32_t gt_before, eq_before;
-    (void)block_excl_scan(gt_b, s_tmp, &gt_before);
-    (void)block_excl_scan(eq_b, s_tmp, &eq_before);
-    const uint32_t cand_before = gt_before + (eq_before < need ? eq_before : need);
-    if (ch == 0 && tid == 0) {
-        meta[u * 4 + 0] = T;
-        meta[u * 4 + 1] = (int32_t)need;
-        meta[u * 4 + 2] = (int32_t)C;
-        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
-    }
-
-    // this chunk's candidates, in position order
-    uint32_t rank = eq_before + block_excl_scan(eqc, s_tmp, &tot);
-    uint32_t mask = 0;
+    const uint32_t packed = block_excl_scan((eqc << 16) | gtc, s_tmp, &tot);
+    const uint32_t eq_t = packed >> 16, gt_t = packed & 0xffffu;
+    const uint32_t taken_before_chunk = eq_chunk < need ? eq_chunk : need;
+    auto taken = [&](uint32_t e) { return (e < need ? e : need) - taken_before_chunk; };
+    uint32_t at = gt_t + taken(eq_chunk + eq_t);
+    const uint32_t n_mem = (tot & 0xffffu) + taken(eq_chunk + (tot >> 16));
+    const uint32_t cand_before = gt_chunk + taken_before_chunk;
+    uint32_t rank = eq_chunk + eq_t;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         bool in = false;
@@ -237,13 +262,8 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
             if (s[j] > (uint32_t)T) in = true;
             else if (s[j] == (uint32_t)T) in = (rank++ < need);
         }
-        mask |= (in ? 1u : 0u) << j;
+        if (in) s_list[at++] = (int32_t)(sink_end + start + (int64_t)tid * KPT + j);
     }
-    uint32_t n_mem;
-    uint32_t at = block_excl_scan(__popc(mask), s_tmp, &n_mem);
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-        if ((mask >> j) & 1u) s_list[at++] = (int32_t)(sink_end + start + (int64_t)tid * KPT + j);
     lds_sync();
 
     // RSQ-IP: est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g;
@@ -463,12 +483,12 @@ hipError_t probe_kernel_image() {
 
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, int64_t sstride, uint16_t* ge, uint32_t* hist_tot,
-                       int hstride, int nbins, hipStream_t st) {
+                       uint16_t* scores, int64_t sstride, uint16_t* ge, int gstride, int nbins,
+                       hipStream_t st) {
     const dim3 grid(n_chunks, units), blk(kBlock);
 #define PK_SCAN(K)                                                                            \
     scan_kernel<K><<<grid, blk, 0, st>>>(ids, cap, sink_end, n_r, max_chunks, lut, scores,    \
-                                         sstride, ge, hist_tot, hstride, nbins)
+                                         sstride, ge, gstride, nbins)
     switch (chunk / kBlock) {
         case 1: PK_SCAN(1); break;
         case 2: PK_SCAN(2); break;
@@ -482,17 +502,24 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
     return hipGetLastError();
 }
 
+hipError_t launch_select(const uint16_t* ge, int gstride, int max_chunks, int n_chunks, int units,
+                         int nbins, int64_t C, int top_k, int32_t* off, int32_t* meta,
+                         hipStream_t st) {
+    select_kernel<<<dim3(units), dim3(kSBlock), 0, st>>>(ge, gstride, max_chunks, n_chunks, nbins,
+                                                          C, top_k, off, meta);
+    return hipGetLastError();
+}
+
 hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, const uint8_t* rec,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
-                         int max_chunks, const uint32_t* hist_tot, int hstride, const uint16_t* ge,
-                         int nbins, int64_t C, int top_k, const float* ysum, const CodeTables& tab,
-                         int32_t* cand_pos, float* cand_est, int64_t cmax, int32_t* meta,
-                         hipStream_t st) {
+                         int max_chunks, const int32_t* off, const int32_t* meta,
+                         const float* ysum, const CodeTables& tab, int32_t* cand_pos,
+                         float* cand_est, int64_t cmax, hipStream_t st) {
     const dim3 grid(n_chunks, units), blk(kBlock);
-#define PK_RERANK(K)                                                                          \
-    rerank_kernel<K><<<grid, blk, 0, st>>>(scores, sstride, rec, cap, sink_end, n_r,          \
-                                           max_chunks, hist_tot, hstride, ge, nbins, C, top_k, \
-                                           ysum, tab, cand_pos, cand_est, cmax, meta)
+#define PK_RERANK(K)                                                                        \
+    rerank_kernel<K><<<grid, blk, 0, st>>>(scores, sstride, rec, cap, sink_end, n_r,        \
+                                           max_chunks, off, meta, ysum, tab, cand_pos,     \
+                                           cand_est, cmax)
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1); break;
         case 2: PK_RERANK(2); break;
