@@ -28,7 +28,7 @@ struct pk_ctx {
     bool prefilled = false;
     int64_t n = 0, sink_end = 0, r_end = 0, buf = 0;
     // sizes
-    int nbins = 0, gstride = 0, max_chunks = 0, max_splits = 0;
+    int nbins = 0, hstride = 0, max_chunks = 0, max_splits = 0;
     int64_t cmax = 0, sstride = 0;
     // device buffers
     uint8_t* ids = nullptr;       // [units][cap][16]   bucket ids
@@ -36,7 +36,7 @@ struct pk_ctx {
     uint8_t* lut = nullptr;       // [units][16][256]   vote table
     float* ysum = nullptr;        // [units][128]       sum of rotated queries
     uint16_t* scores = nullptr;   // [units][sstride] + pad   coarse scores (retrieval offset)
-    uint16_t* ge = nullptr;       // [units][max_chunks][gstride] per-chunk #{score >= s}
+    uint16_t* hist = nullptr;     // [units][max_chunks][hstride] per-chunk score histograms
     int32_t* off = nullptr;       // [units][max_chunks][2] candidates / ties before a chunk
     int32_t* meta = nullptr;      // [units][4]          {T, ties taken, C, k_eff}
     int32_t* cand_pos = nullptr;  // [units][cmax]
@@ -129,7 +129,7 @@ void free_all(pk_ctx* c) {
     release_events(c);
     for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
     c->event_pool.clear();
-    void* bufs[] = {c->ids, c->rec,  c->lut,      c->ysum,     c->scores, c->ge,
+    void* bufs[] = {c->ids, c->rec,  c->lut,      c->ysum,     c->scores, c->hist,
                     c->off, c->meta, c->cand_pos, c->cand_est, c->part};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
@@ -208,12 +208,12 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     {
         StageTimer tm(c, PK_STAGE_SCAN, st);
         PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
-                               c->max_chunks, c->lut, c->scores, c->sstride, c->ge, c->gstride,
+                               c->max_chunks, c->lut, c->scores, c->sstride, c->hist, c->hstride,
                                c->nbins, st));
     }
     {
         StageTimer tm(c, PK_STAGE_SELECT, st);
-        PK_HIP(pk::launch_select(c->ge, c->gstride, c->max_chunks, n_chunks, c->units, c->nbins, C,
+        PK_HIP(pk::launch_select(c->hist, c->hstride, c->max_chunks, n_chunks, c->units, c->nbins, C,
                                  c->cfg.top_k, c->off, c->meta, st));
     }
     {
@@ -297,7 +297,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     c->mem = store_mem;
     c->device = dev;
     c->nbins = nbins;
-    c->gstride = (nbins + 7) / 8 * 8;
+    c->hstride = (nbins + 7) / 8 * 8;
     c->sstride = (capacity + 7) / 8 * 8;
     if (pk_codebook(cfg->sub_dim, 8, c->tab.levels, c->tab.sq_thr) != PK_OK) {
         delete c;
@@ -319,7 +319,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         {(void**)&c->ysum, (size_t)(U * pk::kD * 4)},
         // score rows padded to 16 B; the tail pad covers vector reads past the last row
         {(void**)&c->scores, (size_t)((U * c->sstride + 8192) * 2)},
-        {(void**)&c->ge, (size_t)(U * c->max_chunks * (int64_t)c->gstride * 2)},
+        {(void**)&c->hist, (size_t)(U * c->max_chunks * (int64_t)c->hstride * 2)},
         {(void**)&c->off, (size_t)(U * c->max_chunks * 2 * 4)},
         {(void**)&c->meta, (size_t)(U * 4 * 4)},
         {(void**)&c->cand_pos, (size_t)(U * c->cmax * 4)},

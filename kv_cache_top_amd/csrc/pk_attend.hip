@@ -45,14 +45,10 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     }
     int nsel = sel_n[u];
 
-    // this lane's 8 coordinates of every query head of the group, pre-scaled by 1/sqrt(d)
-    float qv[G][8];
+    // this lane's 8 coordinates of every query head of the group
+    Raw8<T> qv[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        load8(q + ((int64_t)u * G + g) * kD + 8 * l16, qv[g]);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) qv[g][r] *= 0.08838834764831845f;
-    }
+    for (int g = 0; g < G; ++g) qv[g].load(q + ((int64_t)u * G + g) * kD + 8 * l16);
 
     nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
     const int64_t total = n_hot + nsel;
@@ -68,11 +64,11 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
         pos[j] = ok[j] ? p : 0;
     }
     // every K and V row of the group is requested before any is used
-    float kv[kPer][8], vv[kPer][8];
+    Raw8<T> kv[kPer], vv[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        load8(K + ((int64_t)u * cap + pos[j]) * kD + 8 * l16, kv[j]);
-        load8(V + ((int64_t)u * cap + pos[j]) * kD + 8 * l16, vv[j]);
+        kv[j].load(K + ((int64_t)u * cap + pos[j]) * kD + 8 * l16);
+        vv[j].load(V + ((int64_t)u * cap + pos[j]) * kD + 8 * l16);
     }
     // scores
 #pragma unroll
@@ -83,7 +79,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
             float d = 0.0f;
 #pragma unroll
             for (int r = 0; r < 8; ++r) d = fmaf(qv[g][r], kv[j][r], d);
-            d = sum16(d);
+            d = sum16(d) * 0.08838834764831845f;  // 1/sqrt(d)
             if (l16 == 0 && kk < nk) s_p[g][kk] = ok[j] ? d : -INFINITY;
         }
     }
@@ -154,58 +150,49 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     }
 }
 
-// merge of the split partials: one 1024-thread block per unit.  All (m, l)
-// pairs are read at once; wave g folds head g's; each thread then sums one
-// output over the splits with the loads of 32 splits in flight.
-constexpr int kCBlock = 1024;
+// merge of the split partials: one 128-thread block per (query head, unit),
+// thread d owning output coordinate d.  Splits are folded in groups of 64,
+// everything of a group requested before any is used: lane k of each wave
+// reads (m, l) of split s0 + k, the group maximum M' rescales the running
+// sums, lane k's weight e^(m - M') is broadcast to the wave, and
+// acc += o_s e^(m_s - M'), L += l_s e^(m_s - M').  out = acc / L.
+constexpr int kCGroup = 64;
 
-__global__ __launch_bounds__(kCBlock) void combine_kernel(const float* __restrict__ part, int G,
-                                                           int n_splits, float* __restrict__ out) {
-    const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __shared__ float s_m[8][kMaxSplits];
-    __shared__ float s_f[8][kMaxSplits];
-    const float* up = part + (int64_t)u * n_splits * G * (kD + 2);
-    for (int i = tid; i < G * n_splits; i += kCBlock) {
-        const int s = i / G, g = i - s * G;
-        s_m[g][s] = up[(s * G + g) * (kD + 2)];
-        s_f[g][s] = up[(s * G + g) * (kD + 2) + 1];
-    }
-    lds_sync();
-    for (int g = wave; g < G; g += kCBlock / 64) {
-        float M = -INFINITY;
-        for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, s_m[g][s]);
+__global__ __launch_bounds__(kD) void combine_kernel(const float* __restrict__ part, int G,
+                                                     int n_splits, float* __restrict__ out) {
+    const int g = blockIdx.x, u = blockIdx.y, d = threadIdx.x, lane = d & 63;
+    const int64_t stride = (int64_t)G * (kD + 2);      // between splits
+    const float* hp = part + (int64_t)u * n_splits * stride + (int64_t)g * (kD + 2);
+    float M = -INFINITY, L = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < n_splits; s0 += kCGroup) {
+        const int nk = n_splits - s0 < kCGroup ? n_splits - s0 : kCGroup;
+        const int sl = s0 + (lane < nk ? lane : nk - 1);
+        float ml = hp[sl * stride];
+        float ll = hp[sl * stride + 1];
+        float ov[kCGroup];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        float L = 0.0f;
-        for (int s = lane; s < n_splits; s += 64) {
-            const float ms = s_m[g][s];
-            const float f = (ms == -INFINITY) ? 0.0f : __expf(ms - M);
-            s_m[g][s] = f;                 // reuse: weight before normalisation
-            L = fmaf(s_f[g][s], f, L);
+        for (int k = 0; k < kCGroup; ++k) {
+            const int s = s0 + (k < nk ? k : nk - 1);
+            ov[k] = hp[s * stride + 2 + d];
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-        const float invL = 1.0f / L;
-        for (int s = lane; s < n_splits; s += 64) s_f[g][s] = s_m[g][s] * invL;
-    }
-    lds_sync();
-    constexpr int kUnroll = 32;
-    for (int i = tid; i < G * kD; i += kCBlock) {
-        const int g = i / kD, d = i - g * kD;
-        float o = 0.0f;
-        for (int s0 = 0; s0 < n_splits; s0 += kUnroll) {
-            float v[kUnroll];
-#pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
-                const int s = s0 + k < n_splits ? s0 + k : n_splits - 1;
-                v[k] = up[(s * G + g) * (kD + 2) + 2 + d];
-            }
-#pragma unroll
-            for (int k = 0; k < kUnroll; ++k)
-                if (s0 + k < n_splits) o = fmaf(v[k], s_f[g][s0 + k], o);
+        if (lane >= nk) {
+            ml = -INFINITY;
+            ll = 0.0f;
         }
-        out[((int64_t)u * G + g) * kD + d] = o;
+        const float Mg = fmaxf(M, wave_max_f(ml));
+        if (Mg == -INFINITY) continue;                  // nothing attended yet
+        const float r = (M == -INFINITY) ? 0.0f : __expf(M - Mg);
+        const float f = (ml == -INFINITY) ? 0.0f : __expf(ml - Mg);
+        L = fmaf(L, r, wave_sum_f(ll * f));
+        float a = acc * r;
+#pragma unroll
+        for (int k = 0; k < kCGroup; ++k) {
+            if (k < nk) a = fmaf(ov[k], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k)), a);
+        }
+        acc = a;
+        M = Mg;
     }
+    out[((int64_t)u * G + g) * kD + d] = acc / L;
 }
 
 template <typename T>
@@ -232,7 +219,7 @@ int attend_split() { return kSplit; }
 
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st) {
-    combine_kernel<<<dim3(units), dim3(kCBlock), 0, st>>>(part, G, n_splits, out);
+    combine_kernel<<<dim3(G, units), dim3(kD), 0, st>>>(part, G, n_splits, out);
     return hipGetLastError();
 }
 int attend_max_splits() { return kMaxSplits; }

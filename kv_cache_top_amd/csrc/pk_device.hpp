@@ -45,6 +45,29 @@ __device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
     }
 }
 
+// 8 consecutive elements kept in their storage type until used (bf16 rows
+// take 4 VGPRs instead of 8).
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+    uint4 a;
+    __device__ __forceinline__ void load(const uint16_t* p) { a = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ float operator[](int i) const {
+        const uint32_t w = (i >> 1) == 0 ? a.x : (i >> 1) == 1 ? a.y : (i >> 1) == 2 ? a.z : a.w;
+        return bf16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ float operator[](int i) const {
+        return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : i == 3 ? a.w
+             : i == 4 ? b.x : i == 5 ? b.y : i == 6 ? b.z : b.w;
+    }
+};
+
 // The 8 sign bits of the SRHT diagonal that fall on lane l16's coordinates.
 __device__ __forceinline__ uint32_t lane_sign_byte(uint64_t lo, uint64_t hi, int l16) {
     const uint64_t w = (l16 < 8) ? lo : hi;
@@ -57,11 +80,44 @@ __device__ __forceinline__ void apply_signs(float v[8], uint32_t bits) {
         if ((bits >> r) & 1u) v[r] = -v[r];
 }
 
+// Lane exchanges inside each row of 16 lanes by DPP (data-parallel
+// primitives: the permutation is a modifier of one VALU move, no LDS
+// traffic).  xor16<M>(x) returns x of lane (l16 ^ M).  Every lane of the row
+// must be active.
+//   M = 1, 2: quad permutations [1,0,3,2], [2,3,0,1]
+//   M = 4:    half-row mirror (l ^ 7), then quad permutation [3,2,1,0] (l ^ 3)
+//   M = 8:    row rotation by 8
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+template <int M>
+__device__ __forceinline__ int xor16(int x) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8, "lane mask");
+    if constexpr (M == 1) return dpp_mov<0xB1>(x);
+    if constexpr (M == 2) return dpp_mov<0x4E>(x);
+    if constexpr (M == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(x));
+    return dpp_mov<0x128>(x);
+}
+template <int M>
+__device__ __forceinline__ float xor16(float x) {
+    return __int_as_float(xor16<M>(__float_as_int(x)));
+}
+
 // Unnormalised 128-point Walsh-Hadamard transform across a 16-lane group.
 // Stages h = 1, 2, 4 are inside the lane; h = 8, 16, 32, 64 pair lane l16
 // with lane l16 ^ (h / 8).  Every butterfly is (a + b, a - b) with a the lower
 // index, one IEEE fp32 add/sub, and the stages run in ascending order, so the
 // result is bit-identical to any other implementation of that order.
+template <int LM>
+__device__ __forceinline__ void fwht_lane_stage(float v[8], int l16) {
+    const bool upper = (l16 & LM) != 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float o = xor16<LM>(v[r]);
+        v[r] = upper ? (o - v[r]) : (v[r] + o);
+    }
+}
 __device__ __forceinline__ void fwht128_g16(float v[8], int l16) {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
@@ -74,15 +130,10 @@ __device__ __forceinline__ void fwht128_g16(float v[8], int l16) {
             }
         }
     }
-#pragma unroll
-    for (int lm = 1; lm < 16; lm <<= 1) {
-        const bool upper = (l16 & lm) != 0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float o = __shfl_xor(v[r], lm, 16);
-            v[r] = upper ? (o - v[r]) : (v[r] + o);
-        }
-    }
+    fwht_lane_stage<1>(v, l16);
+    fwht_lane_stage<2>(v, l16);
+    fwht_lane_stage<4>(v, l16);
+    fwht_lane_stage<8>(v, l16);
 }
 
 // Workgroup barrier that orders LDS accesses only.  Every barrier in these
@@ -100,12 +151,55 @@ __device__ __forceinline__ float tree8(const float t[8]) {
     return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
 }
 
+// Sum over a row of 16 lanes: pairs, quads, half rows (mirror), rows
+// (mirror).  Each step adds the same two operands in every lane of the
+// group it joins, so all 16 lanes end with the same value.
 __device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 8, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 1, 16);
+    x += xor16<1>(x);
+    x += xor16<2>(x);
+    x += __int_as_float(dpp_mov<0x141>(__float_as_int(x)));
+    x += __int_as_float(dpp_mov<0x140>(__float_as_int(x)));
     return x;
+}
+
+// Maximum over a row of 16 lanes (every lane gets it).
+__device__ __forceinline__ uint32_t max16(uint32_t x) {
+    x = max(x, (uint32_t)xor16<1>((int)x));
+    x = max(x, (uint32_t)xor16<2>((int)x));
+    x = max(x, (uint32_t)dpp_mov<0x141>((int)x));
+    x = max(x, (uint32_t)dpp_mov<0x140>((int)x));
+    return x;
+}
+
+// Maximum over the wave, returned in every lane (wave-uniform).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    x = max16(x);
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// Wave-uniform maximum / sum of a float over the 64 lanes.
+__device__ __forceinline__ float wave_max_f(float x) {
+    x = fmaxf(x, xor16<1>(x));
+    x = fmaxf(x, xor16<2>(x));
+    x = fmaxf(x, __int_as_float(dpp_mov<0x141>(__float_as_int(x))));
+    x = fmaxf(x, __int_as_float(dpp_mov<0x140>(__float_as_int(x))));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+    x = sum16(x);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (a + b) + (c + d);
 }
 
 // order-preserving map of fp32 to uint32 (larger float -> larger key)

@@ -76,40 +76,39 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(const T* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
-// query preparation: one 1024-thread block per unit.
-//   y_g = H D q_g (spec arithmetic), Ysum = sum_g y_g (for the rerank);
-//   per (g, b): top-rho of the 256 centroid scores by (score desc, c asc);
-//   vote table L[b][c] = sum_g weight(rank of c).
-// A 16-lane group serves one (g, b): lane chi scores the 16 centroids
-// c = 16 chi + clo.  Scores come from shared partial sums -- pair sums over
-// coordinates (0,1), (2,3), (4,5), (6,7) in their 4 sign variants, then
-// quad_lo[c & 15] + quad_hi[c >> 4] -- the same fp32 operations in the same
-// order as the direct pairwise tree.  Top-rho = rho rounds of a 16-lane
-// argmax, each removing the winner.
-// The block may also copy the step's new K/V token into the store.
+// query preparation: one block of G waves per (subspace b, unit).
+//   y_g = H D q_g (spec arithmetic); wave g rotates query head g (the four
+//   16-lane groups of the wave compute the same transform) and reads the 8
+//   coordinates of subspace b from lane b, so y_{g,b} is wave-uniform;
+//   the 256 centroid scores of (g, b): lane l scores c = l + 64 t, t < 4, as
+//   the pairwise fp32 tree ((t0+t1)+(t2+t3)) + ((t4+t5)+(t6+t7)) of the
+//   signed coordinates;
+//   top-rho by (score desc, c asc): rho rounds of a wave maximum of the
+//   order keys, the lowest index among the lanes holding it, and removal;
+//   vote table row L[b][c] = sum_g weight(rank of c in head g's picks).
+// Block (0, u) also writes Ysum = sum_g y_g (for the rerank) and may copy the
+// step's new K/V token into the store.
 // ---------------------------------------------------------------------------
 struct VoteWeights {
     uint32_t w[kRhoMax];
 };
 
-constexpr int kQBlock = 1024;
-
-__device__ __forceinline__ bool better(float s, int c, float ts, int tc) {
-    return s > ts || (s == ts && c < tc);
-}
+constexpr int kQMaxBlock = 512;  // G <= 8 waves
 
 template <typename T>
-__global__ __launch_bounds__(kQBlock) void qprep_kernel(
+__global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
     const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
     uint8_t* __restrict__ lut, float* __restrict__ ysum,
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint8_t* __restrict__ K,
     uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos) {
-    const int u = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int b = blockIdx.x, u = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6, l16 = lane & 15;
+    __shared__ uint32_t s_row[256];
     __shared__ float s_y[8][kD];
-    __shared__ uint32_t s_lut[kSub * 256];
-    for (int i = tid; i < kSub * 256; i += kQBlock) s_lut[i] = 0;
-    if (k_new != nullptr) {
+
+    float v[8];
+    load8(q + ((int64_t)u * G + g) * kD + 8 * l16, v);
+    if (b == 0 && k_new != nullptr) {
         const int per_row = (int)(row_bytes / 16);
         if (tid < per_row) {
             const int64_t dst = ((u * cap + new_pos) * row_bytes) / 16 + tid;
@@ -117,71 +116,56 @@ __global__ __launch_bounds__(kQBlock) void qprep_kernel(
             reinterpret_cast<uint4*>(V)[dst] = v_new[(int64_t)u * per_row + tid];
         }
     }
-    if (tid < 16 * G) {
-        const int g = tid >> 4, l16 = tid & 15;
-        float v[8];
-        load8(q + ((int64_t)u * G + g) * kD + 8 * l16, v);
-        apply_signs(v, lane_sign_byte(sign_lo, sign_hi, l16));
-        fwht128_g16(v, l16);
+    for (int i = tid; i < 256; i += 64 * G) s_row[i] = 0;
+    apply_signs(v, lane_sign_byte(sign_lo, sign_hi, l16));
+    fwht128_g16(v, l16);
+    if (b == 0 && lane < 16) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) s_y[g][8 * l16 + r] = v[r];
     }
-    lds_sync();
-    if (tid < kD) {
-        float a = s_y[0][tid];
-        for (int g = 1; g < G; ++g) a += s_y[g][tid];
-        ysum[(int64_t)u * kD + tid] = a;
-    }
 
-    const int combos = G * kSub;
-    const int chi = tid & 15;
-    for (int base = 0; base < combos; base += kQBlock / 16) {
-        const int combo = base + (tid >> 4);
-        const bool active = combo < combos;
-        const int g = active ? combo / kSub : 0, b = combo % kSub;
-        const float* y = &s_y[g][8 * b];
-        float p01[4], p23[4];
+    // subspace b of head g, wave-uniform
+    float y[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p01[i] = ((i & 1) ? -y[0] : y[0]) + ((i & 2) ? -y[1] : y[1]);
-            p23[i] = ((i & 1) ? -y[2] : y[2]) + ((i & 2) ? -y[3] : y[3]);
-        }
-        const float y4 = (chi & 1) ? -y[4] : y[4], y5 = (chi & 2) ? -y[5] : y[5];
-        const float y6 = (chi & 4) ? -y[6] : y[6], y7 = (chi & 8) ? -y[7] : y[7];
-        const float qhi = (y4 + y5) + (y6 + y7);
-        float sc[16];
+    for (int r = 0; r < 8; ++r) y[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[r]), b));
+    const float t0 = (lane & 1) ? -y[0] : y[0], t1 = (lane & 2) ? -y[1] : y[1];
+    const float t2 = (lane & 4) ? -y[2] : y[2], t3 = (lane & 8) ? -y[3] : y[3];
+    const float t4 = (lane & 16) ? -y[4] : y[4], t5 = (lane & 32) ? -y[5] : y[5];
+    const float lo = (t0 + t1) + (t2 + t3);
+    const float p45 = t4 + t5;
+    uint32_t key[4];
 #pragma unroll
-        for (int clo = 0; clo < 16; ++clo) sc[clo] = (p01[clo & 3] + p23[clo >> 2]) + qhi;
-        uint32_t removed = 0;
-        for (int r = 0; r < rho; ++r) {
-            float bs = -INFINITY;
-            int bc = 0x7fffffff;
-#pragma unroll
-            for (int clo = 0; clo < 16; ++clo) {
-                const int c = chi * 16 + clo;
-                if (!((removed >> clo) & 1u) && better(sc[clo], c, bs, bc)) {
-                    bs = sc[clo];
-                    bc = c;
-                }
-            }
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
-                const float os = __shfl_xor(bs, m, 16);
-                const int oc = __shfl_xor(bc, m, 16);
-                if (better(os, oc, bs, bc)) {
-                    bs = os;
-                    bc = oc;
-                }
-            }
-            if ((bc >> 4) == chi) removed |= 1u << (bc & 15);
-            if (active && chi == 0) atomicAdd(&s_lut[b * 256 + bc], wts.w[r]);
-        }
+    for (int t = 0; t < 4; ++t) {
+        const float t6 = (t & 1) ? -y[6] : y[6], t7 = (t & 2) ? -y[7] : y[7];
+        key[t] = f32_order_key(lo + (p45 + (t6 + t7)));  // > 0 for every finite score
     }
     lds_sync();
-    uint32_t* out = reinterpret_cast<uint32_t*>(lut + (int64_t)u * kSub * 256);
-    for (int i = tid; i < kSub * 256 / 4; i += kQBlock) {
-        out[i] = (s_lut[4 * i] & 0xffu) | ((s_lut[4 * i + 1] & 0xffu) << 8) |
-                 ((s_lut[4 * i + 2] & 0xffu) << 16) | ((s_lut[4 * i + 3] & 0xffu) << 24);
+
+    for (int r = 0; r < rho; ++r) {
+        const uint32_t m = wave_max(max(max(key[0], key[1]), max(key[2], key[3])));
+        int c = 256;
+#pragma unroll
+        for (int t = 3; t >= 0; --t) {
+            const uint64_t bal = __ballot(key[t] == m);
+            if (bal != 0) c = 64 * t + (__ffsll((unsigned long long)bal) - 1);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (c == 64 * t + lane) key[t] = 0;  // removed
+        if (lane == 0) atomicAdd(&s_row[c], wts.w[r]);
+    }
+    lds_sync();
+    if (tid < 64) {
+        uint32_t* out = reinterpret_cast<uint32_t*>(lut + ((int64_t)u * kSub + b) * 256);
+        out[tid] = (s_row[4 * tid] & 0xffu) | ((s_row[4 * tid + 1] & 0xffu) << 8) |
+                   ((s_row[4 * tid + 2] & 0xffu) << 16) | ((s_row[4 * tid + 3] & 0xffu) << 24);
+    }
+    if (b == 0) {
+        for (int i = tid; i < kD; i += 64 * G) {
+            float a = s_y[0][i];
+            for (int h = 1; h < G; ++h) a += s_y[h][i];
+            ysum[(int64_t)u * kD + i] = a;
+        }
     }
 }
 
@@ -230,13 +214,14 @@ hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64
                         int64_t cap, int64_t new_pos, hipStream_t st) {
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
+    const dim3 grid(kSub, units), blk(64 * G);
     if (bf16)
-        qprep_kernel<uint16_t><<<dim3(units), dim3(kQBlock), 0, st>>>(
+        qprep_kernel<uint16_t><<<grid, blk, 0, st>>>(
             (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum,
             (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
             new_pos);
     else
-        qprep_kernel<float><<<dim3(units), dim3(kQBlock), 0, st>>>(
+        qprep_kernel<float><<<grid, blk, 0, st>>>(
             (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum,
             (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
             new_pos);

@@ -19,10 +19,10 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
                          int64_t row_bytes, int64_t cap, int64_t pos, int units, hipStream_t st);
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, int64_t sstride, uint16_t* ge, int gstride, int nbins,
+                       uint16_t* scores, int64_t sstride, uint16_t* hist, int hstride, int nbins,
                        hipStream_t st);
-hipError_t launch_select(const uint16_t* ge, int gstride, int max_chunks, int n_chunks, int units,
-                         int nbins, int64_t C, int top_k, int32_t* off, int32_t* meta,
+hipError_t launch_select(const uint16_t* hist, int hstride, int max_chunks, int n_chunks,
+                         int units, int nbins, int64_t C, int top_k, int32_t* off, int32_t* meta,
                          hipStream_t st);
 hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, const uint8_t* rec,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,

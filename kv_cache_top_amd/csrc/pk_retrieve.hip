@@ -11,29 +11,29 @@
 // an agent-scope release fence writes back the XCD's L2 and costs far more
 // per block than a kernel boundary):
 //  scan    one 256-thread block per (chunk, unit): coarse scores and the
-//          chunk's suffix counts ge[s] = #{score >= s};
+//          chunk's score histogram;
 //  select  one 1024-thread block per unit: the coarse threshold T (largest
 //          score with #{score >= T} >= C), the ties at T to take, and for
 //          every chunk the candidates and ties at T in the chunks before it;
 //  rerank  one 256-thread block per (chunk, unit): compacts the chunk's
 //          candidates in position order and estimates them with RSQ-IP;
-//  fine    one 1024-thread block per unit: radix select of the k-th largest
-//          estimate, ties to the lower position, compaction in order.
+//  fine    one 1024-thread block per unit: the k-th largest estimate by
+//          value bucketing (radix select as the fallback), ties to the lower
+//          position, compaction in order.
 #include "pk_device.hpp"
 #include "pk_launch.hpp"
 
 namespace pk {
 
 template <int KPT>
-__global__ __launch_bounds__(kBlock) void scan_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void scan_kernel(
     const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
     const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores, int64_t sstride,
-    uint16_t* __restrict__ ge, int gstride, int nbins) {
+    uint16_t* __restrict__ hist, int hstride, int nbins) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     __shared__ uint32_t s_lut[kSub * 256 / 4];
-    __shared__ uint32_t s_hist[kMaxBins];
-    __shared__ uint32_t s_tmp[kBlock / 64];
+    extern __shared__ uint32_t s_hist[];  // nbins entries (sized at launch)
     const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_lut);
 
     // The vote table is requested first and the key id rows right after, all
@@ -82,63 +82,112 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
         if (lane == k && small[k] && k < nbins) atomicAdd(&s_hist[k], small[k]);
     lds_sync();
 
-    // chunk suffix counts: thread t owns bins [t*per, t*per+per) in descending
-    // score order (reversed index r = nbins-1-s)
-    const int per = (nbins + kBlock - 1) / kBlock;
-    uint32_t seg = 0;
-    for (int j = 0; j < per; ++j) {
-        const int r = tid * per + j;
-        if (r < nbins) seg += s_hist[nbins - 1 - r];
-    }
-    uint32_t tot;
-    uint32_t run = block_excl_scan(seg, s_tmp, &tot);
-    uint16_t* myge = ge + ((int64_t)u * max_chunks + ch) * gstride;
-    for (int j = 0; j < per; ++j) {
-        const int r = tid * per + j;
-        if (r < nbins) {
-            run += s_hist[nbins - 1 - r];
-            myge[nbins - 1 - r] = (uint16_t)run;
-        }
-    }
+    // the chunk's histogram row (a chunk holds at most 8192 keys: uint16)
+    uint16_t* myh = hist + ((int64_t)u * max_chunks + ch) * hstride;
+    for (int b = tid; b < nbins; b += kBlock) myh[b] = (uint16_t)s_hist[b];
 }
 
 // ---------------------------------------------------------------------------
-// select: per unit, from the chunks' suffix counts
-//   tot[s] = sum_c ge_c[s] = #{score >= s};  T = max s with tot[s] >= C;
-//   need = C - tot[T+1] ties at T are taken (lowest positions first);
-//   off[c] = {sum_{c'<c} ge_c'[T+1], sum_{c'<c} (ge_c'[T] - ge_c'[T+1])}.
-// Chunk rows are staged through LDS in tiles of kSelTile.
+// select: per unit, from the chunks' histogram rows h_c
+//   tot[s] = sum_c h_c[s];  ge[s] = sum_{s' >= s} tot[s'] = #{score >= s};
+//   T = max s with ge[s] >= C;  need = C - ge[T+1] ties at T are taken
+//   (lowest positions first);  per chunk: gt_c = sum_{s > T} h_c[s],
+//   eq_c = h_c[T];  off[c] = {sum_{c'<c} gt_c', sum_{c'<c} eq_c'}.
+// Chunk rows are staged through LDS (all at once for up to 64 KB of rows).
 // ---------------------------------------------------------------------------
 constexpr int kSBlock = 1024;
-constexpr int kSelTile = 64;        // chunk rows per LDS tile (at most)
-constexpr int kSelLds = 16384;      // uint16 entries of staged rows (32 KB)
+constexpr int kSelLds = 32768;      // uint16 entries of staged rows (64 KB)
 
-__global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restrict__ ge,
-                                                         int gstride, int max_chunks, int n_chunks,
+// Exclusive scans of two uint32 per thread over a block of NT threads, sharing
+// the barriers.  `tmp` must hold 2 * NT / 64 entries.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(uint32_t& a, uint32_t& b, uint32_t* tmp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = a, y = b;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t xs = __shfl_up(x, off, 64), ys = __shfl_up(y, off, 64);
+        if (lane >= off) {
+            x += xs;
+            y += ys;
+        }
+    }
+    if (lane == 63) {
+        tmp[wave] = x;
+        tmp[NT / 64 + wave] = y;
+    }
+    lds_sync();
+    uint32_t bx = 0, by = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        if (w < wave) {
+            bx += tmp[w];
+            by += tmp[NT / 64 + w];
+        }
+    }
+    a = bx + x - a;
+    b = by + y - b;
+}
+
+__global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restrict__ hist,
+                                                         int hstride, int max_chunks, int n_chunks,
                                                          int nbins, int64_t C, int top_k,
                                                          int32_t* __restrict__ off,
                                                          int32_t* __restrict__ meta) {
     const int u = blockIdx.x, tid = threadIdx.x;
     __shared__ __align__(16) uint16_t s_rows[kSelLds];
     __shared__ uint32_t s_tot[kMaxBins + 1];
-    __shared__ uint32_t s_tmp[kSBlock / 64];
+    __shared__ uint32_t s_gt[kMaxChunks], s_eq[kMaxChunks];
+    __shared__ uint32_t s_tmp[2 * kSBlock / 64];
     __shared__ int s_T;
-    const uint16_t* G0 = ge + (int64_t)u * max_chunks * gstride;
-    const int row_vec = gstride / 8;          // uint4 per row
-    const int tile = kSelLds / gstride < kSelTile ? kSelLds / gstride : kSelTile;
+    const uint16_t* H0 = hist + (int64_t)u * max_chunks * hstride;
+    const int row_vec = hstride / 8;          // uint4 per row
+    const int tile = kSelLds / hstride;       // rows staged at once
+    const bool one_tile = n_chunks <= tile;
     for (int b = tid; b <= nbins; b += kSBlock) s_tot[b] = 0;
     if (tid == 0) s_T = 0;
-    lds_sync();
     for (int c0 = 0; c0 < n_chunks; c0 += tile) {
         const int rows = (n_chunks - c0) < tile ? (n_chunks - c0) : tile;
         for (int i = tid; i < rows * row_vec; i += kSBlock)
             reinterpret_cast<uint4*>(s_rows)[i] =
-                reinterpret_cast<const uint4*>(G0 + (int64_t)c0 * gstride)[i];
+                reinterpret_cast<const uint4*>(H0 + (int64_t)c0 * hstride)[i];
         lds_sync();
-        for (int b = tid; b < nbins; b += kSBlock) {
+        // tot[b] += sum over the tile's rows; work item (b, quarter of the rows)
+        const int qrows = (rows + 3) / 4;
+        for (int w = tid; w < 4 * nbins; w += kSBlock) {
+            const int b = w % nbins, r0 = (w / nbins) * qrows;
+            const int r1 = r0 + qrows < rows ? r0 + qrows : rows;
             uint32_t a = 0;
-            for (int r = 0; r < rows; ++r) a += s_rows[r * gstride + b];
-            s_tot[b] += a;
+            for (int r = r0; r < r1; ++r) a += s_rows[r * hstride + b];
+            if (a) atomicAdd(&s_tot[b], a);
+        }
+        lds_sync();
+    }
+    // suffix counts in place: thread t owns bins [t*per, t*per+per) of the
+    // descending order (reversed index r = nbins-1-s)
+    {
+        const int per = (nbins + kSBlock - 1) / kSBlock;
+        uint32_t seg = 0;
+        for (int j = 0; j < per; ++j) {
+            const int r = tid * per + j;
+            if (r < nbins) seg += s_tot[nbins - 1 - r];
+        }
+        uint32_t tot;
+        uint32_t run = block_excl_scan_t<kSBlock>(seg, s_tmp, &tot);
+        uint32_t h[4];                         // per <= 4: nbins <= 4096
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = tid * per + j;
+            h[j] = (j < per && r < nbins) ? s_tot[nbins - 1 - r] : 0u;
+        }
+        lds_sync();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = tid * per + j;
+            if (j < per && r < nbins) {
+                run += h[j];
+                s_tot[nbins - 1 - r] = run;    // now #{score >= s}
+            }
         }
         lds_sync();
     }
@@ -148,30 +197,42 @@ __global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restr
     const int T = s_T;
     const uint32_t above_T = (T + 1 < nbins) ? s_tot[T + 1] : 0u;
     const uint32_t need = (uint32_t)(C - (int64_t)above_T);
-    // per-chunk counts at T, exclusive scans over chunks (thread-contiguous segments)
-    const int per = (n_chunks + kSBlock - 1) / kSBlock;
-    uint32_t gts = 0, eqs = 0;
-    for (int j = 0; j < per; ++j) {
-        const int c = tid * per + j;
-        if (c < n_chunks) {
-            const uint16_t* g = G0 + (int64_t)c * gstride;
-            const uint32_t at = g[T], ab = (T + 1 < nbins) ? g[T + 1] : 0u;
-            gts += ab;
-            eqs += at - ab;
+    // per-chunk counts: a 16-lane group per chunk sums h_c[s] over s > T
+    for (int w0 = 0; w0 < n_chunks * 16; w0 += kSBlock) {
+        const int w = w0 + tid;
+        const int c = w >> 4, l16 = w & 15;
+        const uint16_t* row = one_tile ? s_rows + c * hstride : H0 + (int64_t)c * hstride;
+        uint32_t a = 0;
+        if (c < n_chunks)
+            for (int b = T + 1 + l16; b < nbins; b += 16) a += row[b];
+        a += (uint32_t)xor16<1>((int)a);        // 16-lane sum (every lane active)
+        a += (uint32_t)xor16<2>((int)a);
+        a += (uint32_t)dpp_mov<0x141>((int)a);
+        a += (uint32_t)dpp_mov<0x140>((int)a);
+        if (c < n_chunks && l16 == 0) {
+            s_gt[c] = a;
+            s_eq[c] = row[T];
         }
     }
-    uint32_t tot;
-    uint32_t gt_run = block_excl_scan_t<kSBlock>(gts, s_tmp, &tot);
-    uint32_t eq_run = block_excl_scan_t<kSBlock>(eqs, s_tmp, &tot);
+    lds_sync();
+    // exclusive scans over chunks, thread t owning chunks [t*per, t*per+per)
+    const int per = (n_chunks + kSBlock - 1) / kSBlock;
+    uint32_t gt_run = 0, eq_run = 0;
     for (int j = 0; j < per; ++j) {
         const int c = tid * per + j;
         if (c < n_chunks) {
-            const uint16_t* g = G0 + (int64_t)c * gstride;
-            const uint32_t at = g[T], ab = (T + 1 < nbins) ? g[T + 1] : 0u;
+            gt_run += s_gt[c];
+            eq_run += s_eq[c];
+        }
+    }
+    block_excl_scan2<kSBlock>(gt_run, eq_run, s_tmp);
+    for (int j = 0; j < per; ++j) {
+        const int c = tid * per + j;
+        if (c < n_chunks) {
             off[((int64_t)u * max_chunks + c) * 2] = (int32_t)gt_run;
             off[((int64_t)u * max_chunks + c) * 2 + 1] = (int32_t)eq_run;
-            gt_run += ab;
-            eq_run += at - ab;
+            gt_run += s_gt[c];
+            eq_run += s_eq[c];
         }
     }
     if (tid == 0) {
@@ -302,64 +363,188 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// fine top-k: one 1024-thread block per unit.  MSB-first radix select of the
-// k-th largest order key in three passes (11, 11, 10 bits), the digit search
-// of each pass done by one wave; then compaction in candidate (= position)
-// order, each thread owning a contiguous segment.
+// fine top-k: one 1024-thread block per unit.  The k-th largest estimate is
+// found by value bucketing: 2048 equal-width buckets over [min, max] (the
+// bucket index (v - min) * 2048 / (max - min), truncated, is non-decreasing
+// in v, so higher buckets hold only larger values), a digit search for the
+// bucket holding the k-th, and an exact rank count among that bucket's
+// members.  If the bucket is too full (or the range degenerate), an
+// MSB-first radix select over the order keys in three passes (11, 11, 10
+// bits) decides instead.  Then compaction in candidate (= position) order,
+// each thread owning a contiguous segment; ties at the k-th go to the lower
+// positions.
 // ---------------------------------------------------------------------------
 constexpr int kFBlock = 1024;
 constexpr int kFineLds = 16384;  // candidates held in LDS; more are read from memory
 constexpr int kRadixBins = 2048;
+constexpr int kRankMax = 1024;   // bucket members ranked directly
 
+__device__ __forceinline__ float order_key_to_f32(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// one wave finds the digit d of the histogram h[0..nb) holding the
+// `remaining`-th largest element: above(d) < remaining <= above(d) + h[d],
+// above(d) = sum of h over digits > d.  Writes d and above(d).
+__device__ __forceinline__ void digit_search(const uint32_t* s_h, int nb, uint32_t remaining,
+                                             int lane, uint32_t* s_digit, uint32_t* s_above) {
+    // lane owns the per = nb/64 digits [lane*per, lane*per+per), read as
+    // 16-byte vectors; larger digits belong to higher lanes
+    const int per = nb / 64;
+    uint32_t h[32];
+#pragma unroll
+    for (int q4 = 0; q4 < 8; ++q4) {
+        if (4 * q4 < per) {
+            const uint4 x = reinterpret_cast<const uint4*>(s_h + lane * per)[q4];
+            h[4 * q4] = x.x;
+            h[4 * q4 + 1] = x.y;
+            h[4 * q4 + 2] = x.z;
+            h[4 * q4 + 3] = x.w;
+        } else {
+            h[4 * q4] = h[4 * q4 + 1] = h[4 * q4 + 2] = h[4 * q4 + 3] = 0;
+        }
+    }
+    uint32_t segsum = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) segsum += h[j];
+    // suffix sum over lanes: counts in digits above this lane's block
+    uint32_t x = segsum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t yv = __shfl_down(x, off, 64);
+        if (lane + off < 64) x += yv;
+    }
+    uint32_t above = x - segsum;
+    if (above < remaining && above + segsum >= remaining) {
+#pragma unroll
+        for (int j = 31; j >= 0; --j) {
+            if (j < per) {
+                if (above < remaining && above + h[j] >= remaining) {
+                    *s_digit = (uint32_t)(lane * per + j);
+                    *s_above = above;
+                }
+                above += h[j];
+            }
+        }
+    }
+}
+
+template <int SEG>
 __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict__ cand_pos,
                                                        const float* __restrict__ cand_est,
                                                        int64_t cmax, int C, int top_k,
                                                        int32_t* __restrict__ sel,
                                                        int32_t* __restrict__ sel_n) {
-    const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-    __shared__ uint32_t s_key[kFineLds];
+    const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ uint32_t s_key[SEG * kFBlock];
     __shared__ __align__(16) uint32_t s_h[kRadixBins];
+    __shared__ uint32_t s_mem[kRankMax];
     __shared__ uint32_t s_tmp[kFBlock / 64];
-    __shared__ uint32_t s_digit, s_above;
+    __shared__ uint32_t s_wmax[kFBlock / 64], s_wmin[kFBlock / 64];
+    __shared__ uint32_t s_digit, s_above, s_cnt, s_kth, s_gt;
     const float* est = cand_est + (int64_t)u * cmax;
     const int32_t* cpos = cand_pos + (int64_t)u * cmax;
     const int k_eff = C < top_k ? C : top_k;
-    const bool in_lds = C <= kFineLds;
-    if (in_lds) {
-        constexpr int kUnroll = 4;
-        for (int i0 = tid; i0 < C; i0 += kUnroll * kFBlock) {
-            float e[kUnroll];
-#pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
-                const int i = i0 + k * kFBlock;
-                e[k] = est[i < C ? i : C - 1];
-            }
-#pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
-                const int i = i0 + k * kFBlock;
-                if (i < C) s_key[i] = f32_order_key(e[k]);
-            }
-        }
-    }
-    lds_sync();
-    auto key_at = [&](int i) -> uint32_t { return in_lds ? s_key[i] : f32_order_key(est[i]); };
-
-    // this thread's compaction segment: positions requested now, used at the end
-    constexpr int kSegMax = kFineLds / kFBlock;
+    const bool in_lds = C <= SEG * kFBlock;
+    // thread t owns candidates [t*seg, (t+1)*seg) for loading and for the final
+    // compaction: their estimates and positions are requested together, once
+    constexpr int kSegMax = SEG;
     const int seg = (C + kFBlock - 1) / kFBlock;
     const int b0 = tid * seg;
+    uint32_t kmax = 0, kmin_inv = 0;  // running max of keys and of ~keys
     int32_t mypos[kSegMax];
     if (in_lds) {
+        float e[kSegMax];
 #pragma unroll
         for (int j = 0; j < kSegMax; ++j) {
             const int i = b0 + j;
-            mypos[j] = cpos[(j < seg && i < C) ? i : 0];
+            const int ic = (j < seg && i < C) ? i : C - 1;  // clamped: a real element
+            e[j] = est[ic];
+            mypos[j] = cpos[ic];
+        }
+#pragma unroll
+        for (int j = 0; j < kSegMax; ++j) {
+            const int i = b0 + j;
+            const uint32_t key = f32_order_key(e[j]);
+            if (j < seg && i < C) s_key[i] = key;
+            kmax = max(kmax, key);
+            kmin_inv = max(kmin_inv, ~key);
+        }
+    } else {
+        for (int i = tid; i < C; i += kFBlock) {
+            const uint32_t key = f32_order_key(est[i]);
+            kmax = max(kmax, key);
+            kmin_inv = max(kmin_inv, ~key);
         }
     }
+    kmax = wave_max(kmax);
+    kmin_inv = wave_max(kmin_inv);
+    if (lane == 0) {
+        s_wmax[wave] = kmax;
+        s_wmin[wave] = kmin_inv;
+    }
+    if (tid == 0) s_cnt = 0;
+    lds_sync();
+    auto key_at = [&](int i) -> uint32_t { return in_lds ? s_key[i] : f32_order_key(est[i]); };
 
-    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k_eff;
+    uint32_t kth = 0, remaining = (uint32_t)k_eff;
     const bool all = k_eff >= C;
+    bool found = all;
     if (!all) {
+        kmax = 0;
+        kmin_inv = 0;
+#pragma unroll
+        for (int w = 0; w < kFBlock / 64; ++w) {
+            kmax = max(kmax, s_wmax[w]);
+            kmin_inv = max(kmin_inv, s_wmin[w]);
+        }
+        const float vmax = order_key_to_f32(kmax), vmin = order_key_to_f32(~kmin_inv);
+        const float span = vmax - vmin;
+        const float scale = (float)kRadixBins / span;
+        // finite, positive span and scale: (v - vmin) * scale is then finite and in [0, ~2048]
+        if (span > 0.0f && span <= 3.0e38f && scale <= 3.0e38f) {
+            const float top = (float)(kRadixBins - 1);
+            auto bucket = [&](uint32_t key) -> uint32_t {
+                return (uint32_t)fminf((order_key_to_f32(key) - vmin) * scale, top);
+            };
+            for (int b = tid; b < kRadixBins; b += kFBlock) s_h[b] = 0;
+            lds_sync();
+            for (int i = tid; i < C; i += kFBlock) atomicAdd(&s_h[bucket(key_at(i))], 1u);
+            lds_sync();
+            if (tid < 64) digit_search(s_h, kRadixBins, remaining, lane, &s_digit, &s_above);
+            lds_sync();
+            const uint32_t bstar = s_digit;
+            const uint32_t rem = remaining - s_above;   // 1 <= rem <= members of bstar
+            const uint32_t n_b = s_h[bstar];
+            if (n_b <= (uint32_t)kRankMax) {
+                for (int i = tid; i < C; i += kFBlock) {
+                    const uint32_t key = key_at(i);
+                    if (bucket(key) == bstar) s_mem[atomicAdd(&s_cnt, 1u)] = key;
+                }
+                lds_sync();
+                // exact rank of every member: the k-th value has gt < rem <= ge
+                for (int m = tid; m < (int)n_b; m += kFBlock) {
+                    const uint32_t km = s_mem[m];
+                    uint32_t gt = 0, ge = 0;
+                    for (int j = 0; j < (int)n_b; ++j) {
+                        const uint32_t kj = s_mem[j];
+                        gt += kj > km ? 1u : 0u;
+                        ge += kj >= km ? 1u : 0u;
+                    }
+                    if (gt < rem && rem <= ge) {  // every writer writes the same values
+                        s_kth = km;
+                        s_gt = gt;
+                    }
+                }
+                lds_sync();
+                kth = s_kth;
+                remaining = rem - s_gt;
+                found = true;
+            }
+        }
+    }
+    if (!found) {
+        uint32_t prefix = 0, pmask = 0;
         const int shifts[3] = {21, 10, 0};
         const int widths[3] = {11, 11, 10};
         for (int p = 0; p < 3; ++p) {
@@ -373,55 +558,15 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
                 if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
             }
             lds_sync();
-            if (tid < 64) {
-                // lane owns the per = nb/64 digits [lane*per, lane*per+per), read as
-                // 16-byte vectors; larger digits belong to higher lanes
-                const int per = nb / 64;
-                uint32_t h[32];
-#pragma unroll
-                for (int q4 = 0; q4 < 8; ++q4) {
-                    if (4 * q4 < per) {
-                        const uint4 x = reinterpret_cast<const uint4*>(s_h + lane * per)[q4];
-                        h[4 * q4] = x.x;
-                        h[4 * q4 + 1] = x.y;
-                        h[4 * q4 + 2] = x.z;
-                        h[4 * q4 + 3] = x.w;
-                    } else {
-                        h[4 * q4] = h[4 * q4 + 1] = h[4 * q4 + 2] = h[4 * q4 + 3] = 0;
-                    }
-                }
-                uint32_t segsum = 0;
-#pragma unroll
-                for (int j = 0; j < 32; ++j) segsum += h[j];
-                // suffix sum over lanes: counts in digits above this lane's block
-                uint32_t x = segsum;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t yv = __shfl_down(x, off, 64);
-                    if (lane + off < 64) x += yv;
-                }
-                uint32_t above = x - segsum;
-                if (above < remaining && above + segsum >= remaining) {
-#pragma unroll
-                    for (int j = 31; j >= 0; --j) {
-                        if (j < per) {
-                            if (above < remaining && above + h[j] >= remaining) {
-                                s_digit = (uint32_t)(lane * per + j);
-                                s_above = above;
-                            }
-                            above += h[j];
-                        }
-                    }
-                }
-            }
+            if (tid < 64) digit_search(s_h, nb, remaining, lane, &s_digit, &s_above);
             lds_sync();
             prefix |= s_digit << shift;
             pmask |= dmask << shift;
             remaining -= s_above;
             lds_sync();
         }
+        kth = prefix;
     }
-    const uint32_t kth = prefix;
     // compaction: thread t owns candidates [t*seg, (t+1)*seg); one block scan of
     // (ties at kth, keys above kth) gives both offsets
     uint32_t eqc = 0, gtc = 0;
@@ -483,12 +628,16 @@ hipError_t probe_kernel_image() {
 
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, int64_t sstride, uint16_t* ge, int gstride, int nbins,
+                       uint16_t* scores, int64_t sstride, uint16_t* hist, int hstride, int nbins,
                        hipStream_t st) {
+    if (nbins < 1 || nbins > kMaxBins) return hipErrorInvalidValue;
     const dim3 grid(n_chunks, units), blk(kBlock);
+    // the histogram is the only dynamic LDS: small vote tables keep the
+    // block small enough for eight resident blocks per CU
+    const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
 #define PK_SCAN(K)                                                                            \
-    scan_kernel<K><<<grid, blk, 0, st>>>(ids, cap, sink_end, n_r, max_chunks, lut, scores,    \
-                                         sstride, ge, gstride, nbins)
+    scan_kernel<K><<<grid, blk, hist_bytes, st>>>(ids, cap, sink_end, n_r, max_chunks, lut,   \
+                                                  scores, sstride, hist, hstride, nbins)
     switch (chunk / kBlock) {
         case 1: PK_SCAN(1); break;
         case 2: PK_SCAN(2); break;
@@ -502,11 +651,12 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
     return hipGetLastError();
 }
 
-hipError_t launch_select(const uint16_t* ge, int gstride, int max_chunks, int n_chunks, int units,
-                         int nbins, int64_t C, int top_k, int32_t* off, int32_t* meta,
+hipError_t launch_select(const uint16_t* hist, int hstride, int max_chunks, int n_chunks,
+                         int units, int nbins, int64_t C, int top_k, int32_t* off, int32_t* meta,
                          hipStream_t st) {
-    select_kernel<<<dim3(units), dim3(kSBlock), 0, st>>>(ge, gstride, max_chunks, n_chunks, nbins,
-                                                          C, top_k, off, meta);
+    if (n_chunks < 1 || n_chunks > kMaxChunks || hstride > kSelLds) return hipErrorInvalidValue;
+    select_kernel<<<dim3(units), dim3(kSBlock), 0, st>>>(hist, hstride, max_chunks, n_chunks,
+                                                          nbins, C, top_k, off, meta);
     return hipGetLastError();
 }
 
@@ -535,8 +685,16 @@ hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, con
 
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
                        int C, int top_k, int32_t* sel, int32_t* sel_n, hipStream_t st) {
-    fine_kernel<<<dim3(units), dim3(kFBlock), 0, st>>>(cand_pos, cand_est, cmax, C, top_k, sel,
-                                                       sel_n);
+    // the segment length covers C in LDS up to kFineLds candidates; beyond that
+    // the keys are read from memory
+    const dim3 grid(units), blk(kFBlock);
+    if (C <= 4 * kFBlock)
+        fine_kernel<4><<<grid, blk, 0, st>>>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n);
+    else if (C <= 8 * kFBlock)
+        fine_kernel<8><<<grid, blk, 0, st>>>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n);
+    else
+        fine_kernel<kFineLds / kFBlock><<<grid, blk, 0, st>>>(cand_pos, cand_est, cmax, C, top_k,
+                                                               sel, sel_n);
     return hipGetLastError();
 }
 

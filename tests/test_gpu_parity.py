@@ -111,6 +111,35 @@ def test_single_token_context():
     assert np.max(np.abs(out[0, 0] - wl.V[0, 0, 0])) <= 1e-6
 
 
+def test_fine_ties_identical_keys():
+    """Every retrieval-zone key identical: all coarse scores and estimates tie, so
+    candidates and the top-k are the lowest positions (degenerate value range)."""
+    wl = W.gqa_bf16(N=20000, top_k=512, permille=100)
+    wl.K[:, :, 4:] = wl.K[:, :, 4:5]
+    pkv, sel, sel_n, _ = _full_check(wl, units=[0, 7], tag="identical")
+    _, sink_end, _, _ = pkv.window()
+    s = sel.cpu().numpy().reshape(wl.n_units, -1)
+    assert np.array_equal(s[0], np.arange(sink_end, sink_end + 512))
+
+
+def test_fine_ties_periodic_keys():
+    """64 distinct keys repeated along the context: large groups of exactly tied
+    estimates around the k-th (the bucket of the k-th holds a whole group)."""
+    wl = W.gqa_bf16(N=20000, top_k=512, permille=100)
+    src = 4 + (np.arange(4, 20000) - 4) % 64
+    wl.K[:, :, 4:] = wl.K[:, :, src]
+    _full_check(wl, units=[0, 7], tag="periodic")
+
+
+def test_fine_two_key_groups():
+    """Two distinct keys only (one every 40 positions, the other elsewhere): more
+    than a thousand exact ties at the k-th estimate."""
+    wl = W.gqa_bf16(N=65536, top_k=1024, permille=50)
+    pos = np.arange(4, 65536)
+    wl.K[:, :, pos] = np.where((pos % 40 == 0)[None, None, :, None], wl.K[:, :, 4:5], wl.K[:, :, 5:6])
+    _full_check(wl, units=[0], tag="two-groups")
+
+
 def test_decode_window_append_evict():
     """Appends through several buffer fills: the window mirror follows the oracle's,
     evicted keys are encoded exactly like a prefill encode, and sampled steps match."""
