@@ -53,17 +53,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     for (int b = tid; b < nbins; b += kBlock) s_hist[b] = 0;
     lds_sync();
 
-    // histogram: the small scores that most keys have are counted per wave
-    // with ballots (no same-address LDS atomics), the rest with atomics
-    constexpr int kSmall = 8;
-    uint32_t small[kSmall];
-#pragma unroll
-    for (int k = 0; k < kSmall; ++k) small[k] = 0;
+    // histogram: scores 0..7, which most keys have, go to eight byte counters
+    // per thread (at most KPT <= 32 keys each, no overflow), summed over the
+    // wave at the end; larger scores go to LDS atomics
+    uint64_t c8 = 0;
     uint16_t* srow = scores + u * sstride;
+    const bool full = start + chunk <= n_r;   // no tail in this chunk
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int64_t i = start + j * kBlock + tid;
-        const bool valid = i < n_r;
+        const bool valid = full || i < n_r;
         const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint32_t sc = 0;
 #pragma unroll
@@ -72,14 +71,35 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
             for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((w[a] >> (8 * k)) & 255u)];
         }
         if (valid) srow[i] = (uint16_t)sc;
-#pragma unroll
-        for (int k = 0; k < kSmall; ++k) small[k] += (uint32_t)__popcll(__ballot(valid && sc == (uint32_t)k));
-        if (valid && sc >= (uint32_t)kSmall) atomicAdd(&s_hist[sc], 1u);
+        c8 += (valid && sc < 8u) ? (1ull << (sc << 3)) : 0ull;
+        if (valid && sc >= 8u) atomicAdd(&s_hist[sc], 1u);
     }
-    const int lane = tid & 63;
+    {
+        // bytes 0..7 of c8 = counts of scores 0..7; widen to 16-bit fields
+        // (a wave holds at most 64 * 32 per score) and sum over the wave
+        const uint32_t lo = (uint32_t)c8, hi = (uint32_t)(c8 >> 32);
+        uint32_t f[4] = {lo & 0x00ff00ffu, (lo >> 8) & 0x00ff00ffu,     // scores {0,2}, {1,3}
+                         hi & 0x00ff00ffu, (hi >> 8) & 0x00ff00ffu};    // scores {4,6}, {5,7}
 #pragma unroll
-    for (int k = 0; k < kSmall; ++k)
-        if (lane == k && small[k] && k < nbins) atomicAdd(&s_hist[k], small[k]);
+        for (int q = 0; q < 4; ++q) {
+            uint32_t x = f[q];
+            x += (uint32_t)xor16<1>((int)x);
+            x += (uint32_t)xor16<2>((int)x);
+            x += (uint32_t)dpp_mov<0x141>((int)x);
+            x += (uint32_t)dpp_mov<0x140>((int)x);
+            f[q] = (uint32_t)__builtin_amdgcn_readlane((int)x, 0) +
+                   (uint32_t)__builtin_amdgcn_readlane((int)x, 16) +
+                   (uint32_t)__builtin_amdgcn_readlane((int)x, 32) +
+                   (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+        }
+        const int lane = tid & 63;
+        if (lane < 8 && lane < nbins) {
+            const uint32_t fq = f[0] * (lane == 0 || lane == 2) + f[1] * (lane == 1 || lane == 3) +
+                                f[2] * (lane == 4 || lane == 6) + f[3] * (lane == 5 || lane == 7);
+            const uint32_t cnt = (lane & 2) ? (fq >> 16) : (fq & 0xffffu);
+            if (cnt) atomicAdd(&s_hist[lane], cnt);
+        }
+    }
     lds_sync();
 
     // the chunk's histogram row (a chunk holds at most 8192 keys: uint16)
