@@ -87,13 +87,9 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     // softmax statistics of the split, one wave per head (strided)
     for (int g = wave; g < G; g += kBlock / 64) {
         const float a = (lane < nk) ? s_p[g][lane] : -INFINITY;
-        float m = a;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float m = wave_max_f(a);
         const float e = (lane < nk && m != -INFINITY) ? __expf(a - m) : 0.0f;
-        float l = e;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+        const float l = wave_sum_f(e);
         if (lane < nk) s_p[g][lane] = e;
         if (lane == 0) {
             s_m[g] = m;

@@ -181,6 +181,25 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
     return max(max(a, b), max(c, d));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each
+// row of 16 lanes with zero-filling row shifts (DPP), then the totals of the
+// rows below are added.  Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_zfill(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += dpp_zfill<0x111>(x);   // row_shr:1
+    x += dpp_zfill<0x112>(x);   // row_shr:2
+    x += dpp_zfill<0x114>(x);   // row_shr:4
+    x += dpp_zfill<0x118>(x);   // row_shr:8
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+
 // Wave-uniform maximum / sum of a float over the 64 lanes.
 __device__ __forceinline__ float wave_max_f(float x) {
     x = fmaxf(x, xor16<1>(x));
@@ -215,12 +234,7 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* tmp, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) tmp[wave] = x;
     lds_sync();
     uint32_t before = 0, all = 0;

@@ -123,15 +123,7 @@ constexpr int kSelLds = 32768;      // uint16 entries of staged rows (64 KB)
 template <int NT>
 __device__ __forceinline__ void block_excl_scan2(uint32_t& a, uint32_t& b, uint32_t* tmp) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = a, y = b;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t xs = __shfl_up(x, off, 64), ys = __shfl_up(y, off, 64);
-        if (lane >= off) {
-            x += xs;
-            y += ys;
-        }
-    }
+    const uint32_t x = wave_incl_scan(a), y = wave_incl_scan(b);
     if (lane == 63) {
         tmp[wave] = x;
         tmp[NT / 64 + wave] = y;
@@ -427,14 +419,10 @@ __device__ __forceinline__ void digit_search(const uint32_t* s_h, int nb, uint32
     uint32_t segsum = 0;
 #pragma unroll
     for (int j = 0; j < 32; ++j) segsum += h[j];
-    // suffix sum over lanes: counts in digits above this lane's block
-    uint32_t x = segsum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t yv = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += yv;
-    }
-    uint32_t above = x - segsum;
+    // counts in the digits of the lanes above this one
+    const uint32_t incl = wave_incl_scan(segsum);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    uint32_t above = total - incl;
     if (above < remaining && above + segsum >= remaining) {
 #pragma unroll
         for (int j = 31; j >= 0; --j) {
@@ -457,6 +445,7 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ sel_n) {
     const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ uint32_t s_key[SEG * kFBlock];
+    __shared__ int32_t s_pos[SEG * kFBlock];
     __shared__ __align__(16) uint32_t s_h[kRadixBins];
     __shared__ uint32_t s_mem[kRankMax];
     __shared__ uint32_t s_tmp[kFBlock / 64];
@@ -466,27 +455,29 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     const int32_t* cpos = cand_pos + (int64_t)u * cmax;
     const int k_eff = C < top_k ? C : top_k;
     const bool in_lds = C <= SEG * kFBlock;
-    // thread t owns candidates [t*seg, (t+1)*seg) for loading and for the final
-    // compaction: their estimates and positions are requested together, once
-    constexpr int kSegMax = SEG;
+    // estimates and positions are read once, coalesced, into LDS; thread t
+    // later compacts the contiguous segment [t*seg, (t+1)*seg)
     const int seg = (C + kFBlock - 1) / kFBlock;
     const int b0 = tid * seg;
     uint32_t kmax = 0, kmin_inv = 0;  // running max of keys and of ~keys
-    int32_t mypos[kSegMax];
     if (in_lds) {
-        float e[kSegMax];
+        float e[SEG];
+        int32_t p[SEG];
 #pragma unroll
-        for (int j = 0; j < kSegMax; ++j) {
-            const int i = b0 + j;
-            const int ic = (j < seg && i < C) ? i : C - 1;  // clamped: a real element
+        for (int j = 0; j < SEG; ++j) {
+            const int i = j * kFBlock + tid;
+            const int ic = i < C ? i : C - 1;   // clamped: a real element
             e[j] = est[ic];
-            mypos[j] = cpos[ic];
+            p[j] = cpos[ic];
         }
 #pragma unroll
-        for (int j = 0; j < kSegMax; ++j) {
-            const int i = b0 + j;
+        for (int j = 0; j < SEG; ++j) {
+            const int i = j * kFBlock + tid;
             const uint32_t key = f32_order_key(e[j]);
-            if (j < seg && i < C) s_key[i] = key;
+            if (i < C) {
+                s_key[i] = key;
+                s_pos[i] = p[j];
+            }
             kmax = max(kmax, key);
             kmin_inv = max(kmin_inv, ~key);
         }
@@ -614,14 +605,7 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
         const uint32_t key = key_at(i);
         const bool in = all || key > kth || (key == kth && r++ < remaining);
         if (in) {
-            int32_t pj = 0;
-            if (in_lds) {
-#pragma unroll
-                for (int jj = 0; jj < kSegMax; ++jj)
-                    if (jj == j) pj = mypos[jj];
-            } else {
-                pj = cpos[i];
-            }
+            const int32_t pj = in_lds ? s_pos[i] : cpos[i];
             if (o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = pj;
             ++o;
         }
