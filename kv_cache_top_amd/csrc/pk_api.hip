@@ -52,6 +52,13 @@ struct pk_ctx {
     std::vector<hipEvent_t> event_pool;
 };
 
+namespace pk {
+LaunchTiming& launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+}  // namespace pk
+
 namespace {
 
 bool g_verbose = std::getenv("PK_VERBOSE") != nullptr;
@@ -80,23 +87,32 @@ hipEvent_t take_event(pk_ctx* c) {
     return e;
 }
 
-// Brackets one launch with events when profiling is on.
+// Times the next launch when profiling is on: the event pair is recorded by
+// the kernel dispatch itself (begin and end of the kernel), so the duration
+// excludes launch overheads between kernels.
 struct StageTimer {
     pk_ctx* c;
     int stage;
-    hipStream_t st;
-    hipEvent_t a = nullptr;
-    StageTimer(pk_ctx* c_, int stage_, hipStream_t st_) : c(c_), stage(stage_), st(st_) {
-        if (c->profiling && (a = take_event(c)) != nullptr) (void)hipEventRecord(a, st);
+    hipEvent_t a = nullptr, b = nullptr;
+    StageTimer(pk_ctx* c_, int stage_, hipStream_t) : c(c_), stage(stage_) {
+        if (!c->profiling) return;
+        a = take_event(c);
+        b = a ? take_event(c) : nullptr;
+        if (!b) {
+            if (a) c->event_pool.push_back(a);
+            a = nullptr;
+            return;
+        }
+        pk::launch_timing() = {a, b};
     }
     ~StageTimer() {
         if (!a) return;
-        hipEvent_t b = take_event(c);
-        if (!b) {
+        if (pk::launch_timing().start == a) {  // nothing was launched
+            pk::launch_timing() = {};
             c->event_pool.push_back(a);
+            c->event_pool.push_back(b);
             return;
         }
-        (void)hipEventRecord(b, st);
         c->marks.push_back({stage, a, b});
     }
 };

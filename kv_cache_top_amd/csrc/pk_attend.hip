@@ -7,7 +7,7 @@
 // directly from host memory by the kernel.
 //
 // Split-K: the attended list of a unit (hot tokens first, then the selected
-// positions) is cut into splits of kSplit keys, one 256-thread block each.
+// positions) is cut into splits of kSplit = 128 keys, one 256-thread block each.
 // A 16-lane group handles one key row at a time (8 coordinates per lane);
 // the G query heads of the group share every K and V row read.  Each block
 // writes its partial (max, sum, unnormalised output) per query head; a second
@@ -17,8 +17,9 @@
 
 namespace pk {
 
-constexpr int kSplit = 64;
+constexpr int kSplit = 128;
 constexpr int kMaxSplits = 1024;
+static_assert(kSplit % 64 == 0, "softmax statistics take 64 keys per wave pass");
 
 template <typename T, int G>
 __global__ __launch_bounds__(kBlock) void attend_kernel(
@@ -85,12 +86,26 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     }
     lds_sync();
     // softmax statistics of the split, one wave per head (strided)
+    constexpr int kSlots = kSplit / 64;   // scores per lane
     for (int g = wave; g < G; g += kBlock / 64) {
-        const float a = (lane < nk) ? s_p[g][lane] : -INFINITY;
-        const float m = wave_max_f(a);
-        const float e = (lane < nk && m != -INFINITY) ? __expf(a - m) : 0.0f;
-        const float l = wave_sum_f(e);
-        if (lane < nk) s_p[g][lane] = e;
+        float a[kSlots];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            const int kk = lane + 64 * k;
+            a[k] = (kk < nk) ? s_p[g][kk] : -INFINITY;
+            mx = fmaxf(mx, a[k]);
+        }
+        const float m = wave_max_f(mx);
+        float es = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            const int kk = lane + 64 * k;
+            const float e = (kk < nk && m != -INFINITY) ? __expf(a[k] - m) : 0.0f;
+            if (kk < nk) s_p[g][kk] = e;
+            es += e;
+        }
+        const float l = wave_sum_f(es);
         if (lane == 0) {
             s_m[g] = m;
             s_l[g] = l;
@@ -152,7 +167,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
 // reads (m, l) of split s0 + k, the group maximum M' rescales the running
 // sums, lane k's weight e^(m - M') is broadcast to the wave, and
 // acc += o_s e^(m_s - M'), L += l_s e^(m_s - M').  out = acc / L.
-constexpr int kCGroup = 64;
+constexpr int kCGroup = 32;
 
 __global__ __launch_bounds__(kD) void combine_kernel(const float* __restrict__ part, int G,
                                                      int n_splits, float* __restrict__ out) {
@@ -197,26 +212,24 @@ static hipError_t launch_attend_t(int G, const T* K, const T* V, int64_t cap, in
                                   const int32_t* sel, const int32_t* sel_n, int top_k,
                                   int n_splits, float* part, hipStream_t st) {
     const dim3 grid(n_splits, units), blk(kBlock);
-#define PK_ATT(GG)                                                                              \
-    attend_kernel<T, GG><<<grid, blk, 0, st>>>(K, V, cap, q, sink_end, r_end, n_tok, sel, sel_n, \
-                                               top_k, n_splits, part)
+#define PK_ATT(GG)                                                                            \
+    return launch(attend_kernel<T, GG>, grid, blk, 0, st, K, V, cap, q, sink_end, r_end, n_tok, \
+                  sel, sel_n, top_k, n_splits, part)
     switch (G) {
-        case 1: PK_ATT(1); break;
-        case 2: PK_ATT(2); break;
-        case 4: PK_ATT(4); break;
-        case 8: PK_ATT(8); break;
+        case 1: PK_ATT(1);
+        case 2: PK_ATT(2);
+        case 4: PK_ATT(4);
+        case 8: PK_ATT(8);
         default: return hipErrorInvalidValue;
     }
 #undef PK_ATT
-    return hipGetLastError();
 }
 
 int attend_split() { return kSplit; }
 
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st) {
-    combine_kernel<<<dim3(G, units), dim3(kD), 0, st>>>(part, G, n_splits, out);
-    return hipGetLastError();
+    return launch(combine_kernel, dim3(G, units), dim3(kD), 0, st, part, G, n_splits, out);
 }
 int attend_max_splits() { return kMaxSplits; }
 

@@ -199,13 +199,12 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
     const int64_t groups_needed = total;
     int64_t blocks = (groups_needed + (kBlock / 16) - 1) / (kBlock / 16);
     if (blocks > 65536) blocks = 65536;
+    const dim3 grid((unsigned)blocks), blk(kBlock);
     if (bf16)
-        encode_kernel<uint16_t><<<dim3((unsigned)blocks), dim3(kBlock), 0, st>>>(
-            (const uint16_t*)K, cap, p0, count, total, ids, rec, sign[0], sign[1], tab);
-    else
-        encode_kernel<float><<<dim3((unsigned)blocks), dim3(kBlock), 0, st>>>(
-            (const float*)K, cap, p0, count, total, ids, rec, sign[0], sign[1], tab);
-    return hipGetLastError();
+        return launch(encode_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)K, cap, p0,
+                      count, total, ids, rec, sign[0], sign[1], tab);
+    return launch(encode_kernel<float>, grid, blk, 0, st, (const float*)K, cap, p0, count, total,
+                  ids, rec, sign[0], sign[1], tab);
 }
 
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
@@ -216,26 +215,20 @@ hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     const dim3 grid(kSub, units), blk(64 * G);
     if (bf16)
-        qprep_kernel<uint16_t><<<grid, blk, 0, st>>>(
-            (const uint16_t*)q, G, sign[0], sign[1], rho, w, lut, ysum,
-            (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
-            new_pos);
-    else
-        qprep_kernel<float><<<grid, blk, 0, st>>>(
-            (const float*)q, G, sign[0], sign[1], rho, w, lut, ysum,
-            (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
-            new_pos);
-    return hipGetLastError();
+        return launch(qprep_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)q, G, sign[0],
+                      sign[1], rho, w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new,
+                      (uint8_t*)K, (uint8_t*)V, row_bytes, cap, new_pos);
+    return launch(qprep_kernel<float>, grid, blk, 0, st, (const float*)q, G, sign[0], sign[1], rho,
+                  w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V,
+                  row_bytes, cap, new_pos);
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
                          int64_t row_bytes, int64_t cap, int64_t pos, int units, hipStream_t st) {
     const int64_t n = (int64_t)units * (row_bytes / 16);
     const int blocks = (int)((n + kBlock - 1) / kBlock);
-    append_kernel<<<dim3(blocks), dim3(kBlock), 0, st>>>((const uint4*)k_new, (const uint4*)v_new,
-                                                          (uint8_t*)K, (uint8_t*)V, row_bytes, cap,
-                                                          pos, units);
-    return hipGetLastError();
+    return launch(append_kernel, dim3(blocks), dim3(kBlock), 0, st, (const uint4*)k_new,
+                  (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap, pos, units);
 }
 
 }  // namespace pk

@@ -1,10 +1,46 @@
 // Kernel launchers (host side), one per kernel family.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace pk {
+
+// Kernel timing attached to the dispatch itself: when `start` is set, the next
+// launch() records start/stop with the kernel's own begin and end
+// (hipExtLaunchKernel) and clears them.  Host-thread local.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+template <typename Tuple, size_t... I>
+inline void arg_addresses(Tuple& t, void** out, std::index_sequence<I...>) {
+    ((out[I] = static_cast<void*>(&std::get<I>(t))), ...);
+}
+
+// kernel<<<grid, block, shm, st>>>(args...), or the timed form of it.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shm,
+                         hipStream_t st, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    LaunchTiming& t = launch_timing();
+    if (t.start != nullptr) {
+        std::tuple<KArgs...> tup{static_cast<KArgs>(args)...};
+        void* addr[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+        arg_addresses(tup, addr, std::index_sequence_for<KArgs...>{});
+        const hipEvent_t a = t.start, b = t.stop;
+        t.start = t.stop = nullptr;
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, addr, shm, st,
+                                  a, b, 0);
+    }
+    kernel<<<grid, block, shm, st>>>(static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
 
 struct CodeTables;
 

@@ -146,69 +146,72 @@ __global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restr
                                                          int nbins, int64_t C, int top_k,
                                                          int32_t* __restrict__ off,
                                                          int32_t* __restrict__ meta) {
-    const int u = blockIdx.x, tid = threadIdx.x;
+    const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ __align__(16) uint16_t s_rows[kSelLds];
-    __shared__ uint32_t s_tot[kMaxBins + 1];
+    __shared__ uint32_t s_tot[kMaxBins];
     __shared__ uint32_t s_gt[kMaxChunks], s_eq[kMaxChunks];
     __shared__ uint32_t s_tmp[2 * kSBlock / 64];
-    __shared__ int s_T;
+    __shared__ uint32_t s_T, s_need;
     const uint16_t* H0 = hist + (int64_t)u * max_chunks * hstride;
     const int row_vec = hstride / 8;          // uint4 per row
     const int tile = kSelLds / hstride;       // rows staged at once
     const bool one_tile = n_chunks <= tile;
-    for (int b = tid; b <= nbins; b += kSBlock) s_tot[b] = 0;
-    if (tid == 0) s_T = 0;
+
+    // bin totals: the four lanes of a quad sum every fourth row of one bin
     for (int c0 = 0; c0 < n_chunks; c0 += tile) {
         const int rows = (n_chunks - c0) < tile ? (n_chunks - c0) : tile;
+        if (c0 > 0) lds_sync();               // previous tile fully read
         for (int i = tid; i < rows * row_vec; i += kSBlock)
             reinterpret_cast<uint4*>(s_rows)[i] =
                 reinterpret_cast<const uint4*>(H0 + (int64_t)c0 * hstride)[i];
         lds_sync();
-        // tot[b] += sum over the tile's rows; work item (b, quarter of the rows)
-        const int qrows = (rows + 3) / 4;
-        for (int w = tid; w < 4 * nbins; w += kSBlock) {
-            const int b = w % nbins, r0 = (w / nbins) * qrows;
-            const int r1 = r0 + qrows < rows ? r0 + qrows : rows;
+        const int q = tid & 3;
+        for (int b0 = 0; b0 < nbins; b0 += kSBlock / 4) {
+            const int b = b0 + (tid >> 2);
             uint32_t a = 0;
-            for (int r = r0; r < r1; ++r) a += s_rows[r * hstride + b];
-            if (a) atomicAdd(&s_tot[b], a);
+            if (b < nbins)
+                for (int r = q; r < rows; r += 4) a += s_rows[r * hstride + b];
+            a += (uint32_t)xor16<1>((int)a);
+            a += (uint32_t)xor16<2>((int)a);
+            if (q == 0 && b < nbins) s_tot[b] = (c0 == 0 ? 0u : s_tot[b]) + a;
         }
-        lds_sync();
     }
-    // suffix counts in place: thread t owns bins [t*per, t*per+per) of the
-    // descending order (reversed index r = nbins-1-s)
-    {
-        const int per = (nbins + kSBlock - 1) / kSBlock;
+    lds_sync();
+
+    // wave 0: suffix counts ge[s] = #{score >= s} (lane l owns the per bins
+    // [l*per, l*per+per) of the descending order), T = max s with ge[s] >= C
+    // (ge is non-increasing: T + 1 = number of bins with ge >= C), need = C -
+    // ge[T+1] ties at T
+    if (wave == 0) {
+        const int per = (nbins + 63) / 64;
         uint32_t seg = 0;
         for (int j = 0; j < per; ++j) {
-            const int r = tid * per + j;
+            const int r = lane * per + j;
             if (r < nbins) seg += s_tot[nbins - 1 - r];
         }
-        uint32_t tot;
-        uint32_t run = block_excl_scan_t<kSBlock>(seg, s_tmp, &tot);
-        uint32_t h[4];                         // per <= 4: nbins <= 4096
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = tid * per + j;
-            h[j] = (j < per && r < nbins) ? s_tot[nbins - 1 - r] : 0u;
-        }
-        lds_sync();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = tid * per + j;
-            if (j < per && r < nbins) {
-                run += h[j];
-                s_tot[nbins - 1 - r] = run;    // now #{score >= s}
+        uint32_t run = wave_incl_scan(seg) - seg;
+        uint32_t n_ge = 0, ge_next = 0;       // ge of the bin just above the highest counted
+        for (int j = 0; j < per; ++j) {
+            const int r = lane * per + j;
+            if (r < nbins) {
+                const uint32_t before = run;  // ge[s + 1]
+                run += s_tot[nbins - 1 - r];  // ge[s]
+                if ((int64_t)run >= C) {
+                    ++n_ge;
+                    if ((int64_t)before < C) ge_next = before;   // s = T: ge[T+1]
+                }
             }
         }
-        lds_sync();
+        const uint32_t T1 = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(n_ge), 63);
+        const uint32_t above = (uint32_t)wave_max((uint32_t)ge_next);
+        if (lane == 0) {
+            s_T = T1 - 1;
+            s_need = (uint32_t)(C - (int64_t)above);
+        }
     }
-    for (int b = tid; b < nbins; b += kSBlock)
-        if ((int64_t)s_tot[b] >= C && (b + 1 == nbins || (int64_t)s_tot[b + 1] < C)) s_T = b;
     lds_sync();
-    const int T = s_T;
-    const uint32_t above_T = (T + 1 < nbins) ? s_tot[T + 1] : 0u;
-    const uint32_t need = (uint32_t)(C - (int64_t)above_T);
+    const int T = (int)s_T;
+
     // per-chunk counts: a 16-lane group per chunk sums h_c[s] over s > T
     for (int w0 = 0; w0 < n_chunks * 16; w0 += kSBlock) {
         const int w = w0 + tid;
@@ -227,29 +230,41 @@ __global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restr
         }
     }
     lds_sync();
-    // exclusive scans over chunks, thread t owning chunks [t*per, t*per+per)
-    const int per = (n_chunks + kSBlock - 1) / kSBlock;
-    uint32_t gt_run = 0, eq_run = 0;
-    for (int j = 0; j < per; ++j) {
-        const int c = tid * per + j;
-        if (c < n_chunks) {
-            gt_run += s_gt[c];
-            eq_run += s_eq[c];
+    // exclusive scans over chunks
+    if (n_chunks <= 64) {
+        if (wave == 0) {
+            const uint32_t g = lane < n_chunks ? s_gt[lane] : 0u;
+            const uint32_t e = lane < n_chunks ? s_eq[lane] : 0u;
+            const uint32_t gb = wave_incl_scan(g) - g, eb = wave_incl_scan(e) - e;
+            if (lane < n_chunks) {
+                off[((int64_t)u * max_chunks + lane) * 2] = (int32_t)gb;
+                off[((int64_t)u * max_chunks + lane) * 2 + 1] = (int32_t)eb;
+            }
         }
-    }
-    block_excl_scan2<kSBlock>(gt_run, eq_run, s_tmp);
-    for (int j = 0; j < per; ++j) {
-        const int c = tid * per + j;
-        if (c < n_chunks) {
-            off[((int64_t)u * max_chunks + c) * 2] = (int32_t)gt_run;
-            off[((int64_t)u * max_chunks + c) * 2 + 1] = (int32_t)eq_run;
-            gt_run += s_gt[c];
-            eq_run += s_eq[c];
+    } else {
+        const int per = (n_chunks + kSBlock - 1) / kSBlock;
+        uint32_t gt_run = 0, eq_run = 0;
+        for (int j = 0; j < per; ++j) {
+            const int c = tid * per + j;
+            if (c < n_chunks) {
+                gt_run += s_gt[c];
+                eq_run += s_eq[c];
+            }
+        }
+        block_excl_scan2<kSBlock>(gt_run, eq_run, s_tmp);
+        for (int j = 0; j < per; ++j) {
+            const int c = tid * per + j;
+            if (c < n_chunks) {
+                off[((int64_t)u * max_chunks + c) * 2] = (int32_t)gt_run;
+                off[((int64_t)u * max_chunks + c) * 2 + 1] = (int32_t)eq_run;
+                gt_run += s_gt[c];
+                eq_run += s_eq[c];
+            }
         }
     }
     if (tid == 0) {
         meta[u * 4 + 0] = T;
-        meta[u * 4 + 1] = (int32_t)need;
+        meta[u * 4 + 1] = (int32_t)s_need;
         meta[u * 4 + 2] = (int32_t)C;
         meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
     }
@@ -639,29 +654,27 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
     // the histogram is the only dynamic LDS: small vote tables keep the
     // block small enough for eight resident blocks per CU
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
-#define PK_SCAN(K)                                                                            \
-    scan_kernel<K><<<grid, blk, hist_bytes, st>>>(ids, cap, sink_end, n_r, max_chunks, lut,   \
-                                                  scores, sstride, hist, hstride, nbins)
+#define PK_SCAN(K)                                                                         \
+    return launch(scan_kernel<K>, grid, blk, hist_bytes, st, ids, cap, sink_end, n_r,        \
+                  max_chunks, lut, scores, sstride, hist, hstride, nbins)
     switch (chunk / kBlock) {
-        case 1: PK_SCAN(1); break;
-        case 2: PK_SCAN(2); break;
-        case 4: PK_SCAN(4); break;
-        case 8: PK_SCAN(8); break;
-        case 16: PK_SCAN(16); break;
-        case 32: PK_SCAN(32); break;
+        case 1: PK_SCAN(1);
+        case 2: PK_SCAN(2);
+        case 4: PK_SCAN(4);
+        case 8: PK_SCAN(8);
+        case 16: PK_SCAN(16);
+        case 32: PK_SCAN(32);
         default: return hipErrorInvalidValue;
     }
 #undef PK_SCAN
-    return hipGetLastError();
 }
 
 hipError_t launch_select(const uint16_t* hist, int hstride, int max_chunks, int n_chunks,
                          int units, int nbins, int64_t C, int top_k, int32_t* off, int32_t* meta,
                          hipStream_t st) {
     if (n_chunks < 1 || n_chunks > kMaxChunks || hstride > kSelLds) return hipErrorInvalidValue;
-    select_kernel<<<dim3(units), dim3(kSBlock), 0, st>>>(hist, hstride, max_chunks, n_chunks,
-                                                          nbins, C, top_k, off, meta);
-    return hipGetLastError();
+    return launch(select_kernel, dim3(units), dim3(kSBlock), 0, st, hist, hstride, max_chunks,
+                  n_chunks, nbins, C, top_k, off, meta);
 }
 
 hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, const uint8_t* rec,
@@ -671,20 +684,18 @@ hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, con
                          float* cand_est, int64_t cmax, hipStream_t st) {
     const dim3 grid(n_chunks, units), blk(kBlock);
 #define PK_RERANK(K)                                                                        \
-    rerank_kernel<K><<<grid, blk, 0, st>>>(scores, sstride, rec, cap, sink_end, n_r,        \
-                                           max_chunks, off, meta, ysum, tab, cand_pos,     \
-                                           cand_est, cmax)
+    return launch(rerank_kernel<K>, grid, blk, 0, st, scores, sstride, rec, cap, sink_end, n_r, \
+                  max_chunks, off, meta, ysum, tab, cand_pos, cand_est, cmax)
     switch (chunk / kBlock) {
-        case 1: PK_RERANK(1); break;
-        case 2: PK_RERANK(2); break;
-        case 4: PK_RERANK(4); break;
-        case 8: PK_RERANK(8); break;
-        case 16: PK_RERANK(16); break;
-        case 32: PK_RERANK(32); break;
+        case 1: PK_RERANK(1);
+        case 2: PK_RERANK(2);
+        case 4: PK_RERANK(4);
+        case 8: PK_RERANK(8);
+        case 16: PK_RERANK(16);
+        case 32: PK_RERANK(32);
         default: return hipErrorInvalidValue;
     }
 #undef PK_RERANK
-    return hipGetLastError();
 }
 
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
@@ -693,18 +704,18 @@ hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t c
     // the keys are read from memory
     const dim3 grid(units), blk(kFBlock);
     if (C <= 4 * kFBlock)
-        fine_kernel<4><<<grid, blk, 0, st>>>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n);
-    else if (C <= 8 * kFBlock)
-        fine_kernel<8><<<grid, blk, 0, st>>>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n);
-    else
-        fine_kernel<kFineLds / kFBlock><<<grid, blk, 0, st>>>(cand_pos, cand_est, cmax, C, top_k,
-                                                               sel, sel_n);
-    return hipGetLastError();
+        return launch(fine_kernel<4>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
+                      sel_n);
+    if (C <= 8 * kFBlock)
+        return launch(fine_kernel<8>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
+                      sel_n);
+    return launch(fine_kernel<kFineLds / kFBlock>, grid, blk, 0, st, cand_pos, cand_est, cmax, C,
+                  top_k, sel, sel_n);
 }
 
 hipError_t launch_empty_select(int units, int32_t* sel_n, int32_t* meta, hipStream_t st) {
-    empty_select_kernel<<<dim3((units + 63) / 64), dim3(64), 0, st>>>(units, sel_n, meta);
-    return hipGetLastError();
+    return launch(empty_select_kernel, dim3((units + 63) / 64), dim3(64), 0, st, units, sel_n,
+                  meta);
 }
 
 }  // namespace pk

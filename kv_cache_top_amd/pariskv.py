@@ -61,6 +61,7 @@ class ParisKV:
                                     _ptr(k_store), _ptr(v_store),
                                     nat.PK_MEM_HOST_MAPPED if host_mapped else nat.PK_MEM_DEVICE,
                                     ctypes.byref(self._ctx)), "pk_create")
+        self._decode_fn = nat.lib.pk_decode_step
 
     # -- lifecycle ---------------------------------------------------------
     def close(self) -> None:
@@ -131,6 +132,14 @@ class ParisKV:
         nat.check(nat.lib.pk_decode_step(self._ctx, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(sel),
                                          _ptr(sel_n), _ptr(out), _stream(stream)), "pk_decode_step")
         return out, sel, sel_n
+
+    def decode_step_raw(self, k_new: int, v_new: int, q: int, sel: int, sel_n: int, out: int,
+                        stream: int) -> None:
+        """pk_decode_step on raw device addresses and a raw hipStream_t (no
+        checks): for callers that validated their buffers once and issue many
+        steps, where per-call tensor handling would cost more than the launch."""
+        nat.check(self._decode_fn(self._ctx, k_new, v_new, q, sel, sel_n, out, stream),
+                  "pk_decode_step")
 
     def profile(self, on: bool = True) -> None:
         """Start (or stop) per-stage kernel timing with HIP events."""

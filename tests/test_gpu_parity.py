@@ -201,6 +201,32 @@ def test_decode_step_matches_separate_calls():
     assert torch.equal(a.K, b.K) and torch.equal(a.V, b.V)
 
 
+def test_decode_step_raw_matches_decode_step():
+    """The raw-address entry of the binding issues the same pk_decode_step."""
+    T, N0 = 12, 3000
+    wl = W.gqa_bf16(N=N0, top_k=256, n_local=64, buf_tokens=8)
+    Kn, Vn, Qn = W.decode_stream(wl, T)
+    a = gc.make_ctx(wl, capacity=N0 + T)
+    b = gc.make_ctx(wl, capacity=N0 + T)
+    a.encode_keys(N0)
+    b.encode_keys(N0)
+    dt = gc.torch_dtype(wl)
+    sel = torch.empty((wl.batch, wl.n_kv, 256), dtype=torch.int32, device="cuda")
+    sel_n = torch.empty((wl.batch, wl.n_kv), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.batch, wl.n_kv * wl.group, 128), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(T):
+        k = torch.from_numpy(Kn[t]).to(dt).cuda()
+        v = torch.from_numpy(Vn[t]).to(dt).cuda()
+        q = torch.from_numpy(Qn[t]).to(dt).cuda()
+        out_a, sel_a, n_a = a.decode_step(k, v, q)
+        b.decode_step_raw(k.data_ptr(), v.data_ptr(), q.data_ptr(), sel.data_ptr(),
+                          sel_n.data_ptr(), out.data_ptr(), stream)
+        torch.cuda.synchronize()
+        assert a.window() == b.window()
+        assert torch.equal(n_a, sel_n) and torch.equal(sel_a, sel) and torch.equal(out_a, out)
+
+
 def test_profiling_counts_launches():
     wl = W.gqa_bf16(N=5000, top_k=256)
     pkv = gc.make_ctx(wl)
