@@ -21,6 +21,9 @@ constexpr int kSplit = 128;
 constexpr int kMaxSplits = 1024;
 static_assert(kSplit % 64 == 0, "softmax statistics take 64 keys per wave pass");
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 template <typename T, int G>
 __global__ __launch_bounds__(kBlock) void attend_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int64_t cap, const T* __restrict__ q,
@@ -28,60 +31,112 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     const int32_t* __restrict__ sel_n, int top_k, int n_splits, float* __restrict__ part) {
     const int u = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, l16 = lane & 15;
+    constexpr bool kMfma = sizeof(T) == 2;   // bf16: q k^T on the matrix cores
+    constexpr int kPer = kSplit / (kBlock / 16);   // keys per 16-lane group
+    static_assert(kSplit == 32 * (kBlock / 64), "a wave owns 32 keys of the split");
+    static_assert(!kMfma || G <= 8, "query heads fill MFMA rows 0..G-1 of 16");
     __shared__ float s_p[G][kSplit];
     __shared__ float s_red[kBlock / 64][G][kD];
     __shared__ float s_m[G], s_l[G];
+    constexpr float kInvSqrtD = 0.08838834764831845f;
 
-    // the key slots of this 16-lane group: kk = wave*4 + grp + 16*j, j < kPer.
-    // Selected positions are read together with their count (entries past the
-    // count are masked afterwards).
-    constexpr int kPer = kSplit / (kBlock / 16);
+    // Wave w owns keys [32w, 32w + 32) of the split.  Values: the 16-lane
+    // group grp handles keys 32w + grp + 4j (j < 8), 8 coordinates per lane.
+    // Keys (bf16): MFMA tiles of 16 keys, lane l16 loading key 32w + 16h + l16.
     const int64_t n_hot = sink_end + (n_tok - r_end);
     const int64_t i0 = (int64_t)sp * kSplit;
-    int32_t cand[kPer];
+    auto sel_at = [&](int kk) -> int32_t {
+        const int64_t i = i0 + kk - n_hot;
+        return sel[(int64_t)u * top_k + (i < 0 ? 0 : (i < top_k ? i : top_k - 1))];
+    };
+    int32_t cand_v[kPer], cand_k[2];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int64_t i = i0 + wave * 4 + grp + j * (kBlock / 16) - n_hot;
-        cand[j] = sel[(int64_t)u * top_k + (i < 0 ? 0 : (i < top_k ? i : top_k - 1))];
+    for (int j = 0; j < kPer; ++j) cand_v[j] = sel_at(32 * wave + grp + 4 * j);
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) cand_k[h] = sel_at(32 * wave + 16 * h + l16);
     }
     int nsel = sel_n[u];
 
-    // this lane's 8 coordinates of every query head of the group
-    Raw8<T> qv[G];
+    // query operand.  bf16: A rows = heads (rows >= G zero), lane l holds head
+    // l16's dims 32s + 8 grp .. +8 of step s.  fp32: this lane's 8 dims of every head.
+    uint4 qa[4];
+    Raw8<T> qv[kMfma ? 1 : G];
+    if constexpr (kMfma) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) qv[g].load(q + ((int64_t)u * G + g) * kD + 8 * l16);
+        for (int st = 0; st < 4; ++st)
+            qa[st] = (l16 < G) ? *reinterpret_cast<const uint4*>(
+                                     q + ((int64_t)u * G + l16) * kD + 32 * st + 8 * grp)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) qv[g].load(q + ((int64_t)u * G + g) * kD + 8 * l16);
+    }
 
     nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
     const int64_t total = n_hot + nsel;
     const int nk = (int)((total - i0) < kSplit ? (total - i0 > 0 ? total - i0 : 0) : kSplit);
-    int64_t pos[kPer];
-    bool ok[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int kk = wave * 4 + grp + j * (kBlock / 16);
+    auto place = [&](int kk, int32_t c, bool& ok) -> int64_t {
         const int64_t i = i0 + kk;
-        const int64_t p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end)) : (int64_t)cand[j];
-        ok[j] = kk < nk && p >= 0 && p < n_tok;
-        pos[j] = ok[j] ? p : 0;
+        const int64_t p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end)) : (int64_t)c;
+        ok = kk < nk && p >= 0 && p < n_tok;
+        return ok ? p : 0;
+    };
+    bool ok_v[kPer], ok_k[2];
+    int64_t pos_v[kPer], pos_k[2];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) pos_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], ok_v[j]);
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pos_k[h] = place(32 * wave + 16 * h + l16, cand_k[h], ok_k[h]);
     }
-    // every K and V row of the group is requested before any is used
-    Raw8<T> kv[kPer], vv[kPer];
+    // every K and V row is requested before any is used
+    uint4 kb[2][4];
+    Raw8<T> kv[kMfma ? 1 : kPer], vv[kPer];
+    if constexpr (kMfma) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        kv[j].load(K + ((int64_t)u * cap + pos[j]) * kD + 8 * l16);
-        vv[j].load(V + ((int64_t)u * cap + pos[j]) * kD + 8 * l16);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                kb[h][st] = *reinterpret_cast<const uint4*>(
+                    K + ((int64_t)u * cap + pos_k[h]) * kD + 32 * st + 8 * grp);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) kv[j].load(K + ((int64_t)u * cap + pos_v[j]) * kD + 8 * l16);
     }
-    // scores
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int kk = wave * 4 + grp + j * (kBlock / 16);
+    for (int j = 0; j < kPer; ++j) vv[j].load(V + ((int64_t)u * cap + pos_v[j]) * kD + 8 * l16);
+
+    // scores / sqrt(d) into s_p[head][key]
+    if constexpr (kMfma) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float d = 0.0f;
+        for (int h = 0; h < 2; ++h) {
+            f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < 8; ++r) d = fmaf(qv[g][r], kv[j][r], d);
-            d = sum16(d) * 0.08838834764831845f;  // 1/sqrt(d)
-            if (l16 == 0 && kk < nk) s_p[g][kk] = ok[j] ? d : -INFINITY;
+            for (int st = 0; st < 4; ++st)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                            __builtin_bit_cast(bf16x8_t, kb[h][st]),
+                                                            c, 0, 0, 0);
+            // lane holds rows (heads) 4 grp + i of column (key) l16
+            const int kk = 32 * wave + 16 * h + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int g = 4 * grp + i;
+                if (g < G) s_p[g][kk] = ok_k[h] ? c[i] * kInvSqrtD : -INFINITY;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int kk = 32 * wave + grp + 4 * j;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float d = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) d = fmaf(qv[g][r], kv[j][r], d);
+                d = sum16(d) * kInvSqrtD;
+                if (l16 == 0) s_p[g][kk] = ok_v[j] ? d : -INFINITY;
+            }
         }
     }
     lds_sync();
@@ -120,7 +175,7 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
         for (int r = 0; r < 8; ++r) acc[g][r] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        const int kk = wave * 4 + grp + j * (kBlock / 16);
+        const int kk = 32 * wave + grp + 4 * j;
         if (kk < nk) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -130,15 +185,11 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
             }
         }
     }
+    // sum over the four 16-lane groups of the wave (lane exchanges across rows)
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            float a = acc[g][r];
-            a += __shfl_xor(a, 16);
-            a += __shfl_xor(a, 32);
-            acc[g][r] = a;
-        }
+        for (int r = 0; r < 8; ++r) acc[g][r] = sum_rows4(acc[g][r]);
     if (grp == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)

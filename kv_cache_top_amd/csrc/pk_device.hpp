@@ -200,6 +200,16 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
 }
 
+// Sum of x over lanes {l, l^16, l^32, l^48}: the four rows of the wave
+// (v_permlane16_swap / v_permlane32_swap exchange rows without LDS).  Both
+// lanes of each exchange add the same two operands in the same order.
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Wave-uniform maximum / sum of a float over the 64 lanes.
 __device__ __forceinline__ float wave_max_f(float x) {
     x = fmaxf(x, xor16<1>(x));
