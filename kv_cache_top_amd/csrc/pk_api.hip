@@ -42,6 +42,7 @@ struct pk_ctx {
     int32_t* cand_pos = nullptr;  // [units][cmax]
     float* cand_est = nullptr;    // [units][cmax]
     float* part = nullptr;        // [units][max_splits][G][130]
+    pk::HotRing ring;             // device rows of the hot zone (host-memory stores only)
     // optional per-stage timing
     bool profiling = false;
     struct Mark {
@@ -145,8 +146,8 @@ void free_all(pk_ctx* c) {
     release_events(c);
     for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
     c->event_pool.clear();
-    void* bufs[] = {c->ids, c->rec,  c->lut,      c->ysum,     c->scores, c->hist,
-                    c->off, c->meta, c->cand_pos, c->cand_est, c->part};
+    void* bufs[] = {c->ids,  c->rec,      c->lut,      c->ysum, c->scores, c->hist,   c->off,
+                    c->meta, c->cand_pos, c->cand_est, c->part, c->ring.k, c->ring.v};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
 }
@@ -211,7 +212,7 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
         StageTimer tm(c, PK_STAGE_QPREP, st);
         PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
                                 c->cfg.vote_weight, c->lut, c->ysum, k_new, v_new, c->K, c->V,
-                                row, c->cap, c->n - 1, st));
+                                row, c->cap, c->n - 1, c->ring, st));
     }
     const int64_t n_r = c->r_end - c->sink_end;
     if (n_r <= 0) {
@@ -253,7 +254,7 @@ pk_status run_attend(pk_ctx* c, const void* q, const int32_t* sel, const int32_t
         StageTimer tm(c, PK_STAGE_ATTEND, st);
         PK_HIP(pk::launch_attend(c->dt == PK_BF16, c->G, c->K, c->V, c->cap, c->units, q,
                                  c->sink_end, c->r_end, c->n, sel, sel_n, c->cfg.top_k, n_splits,
-                                 c->part, st));
+                                 c->part, c->ring, st));
     }
     StageTimer tm(c, PK_STAGE_COMBINE, st);
     PK_HIP(pk::launch_combine(c->part, c->units, c->G, n_splits, out, st));
@@ -349,6 +350,17 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
             return PK_ERR_OOM;
         }
     }
+    c->ring.n_sink = cfg->n_sink;
+    c->ring.span = std::max<int64_t>(1, (int64_t)cfg->n_local + cfg->buf_tokens);
+    c->ring.rows = c->ring.n_sink + c->ring.span;
+    if (store_mem == PK_MEM_HOST_MAPPED) {
+        const size_t rb = (size_t)(U * c->ring.rows * pk::kD * dtype_size(kv_dtype));
+        if (hipMalloc(&c->ring.k, rb) != hipSuccess || hipMalloc(&c->ring.v, rb) != hipSuccess) {
+            free_all(c);
+            delete c;
+            return PK_ERR_OOM;
+        }
+    }
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
         hipMemset(c->scores, 0, (U * c->sstride + 8192) * 2) != hipSuccess ||
         hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
@@ -386,6 +398,8 @@ pk_status pk_encode_keys(pk_ctx* c, int64_t n_tokens, void* stream) {
     StageTimer tm(c, PK_STAGE_ENCODE, (hipStream_t)stream);
     PK_HIP(pk::launch_encode(c->dt == PK_BF16, c->K, c->cap, c->units, sink_end, r_end - sink_end,
                              c->ids, c->rec, c->cfg.sign_bits, c->tab, (hipStream_t)stream));
+    PK_HIP(pk::launch_ring_fill(c->K, c->V, (int64_t)pk::kD * dtype_size(c->dt), c->cap, c->units,
+                                sink_end, r_end, n_tokens, c->ring, (hipStream_t)stream));
     c->n = n_tokens;
     c->sink_end = sink_end;
     c->r_end = r_end;
@@ -406,7 +420,8 @@ pk_status pk_append_decode_keys(pk_ctx* c, const void* k_new, const void* v_new,
     const int64_t row = (int64_t)pk::kD * dtype_size(c->dt);
     {
         StageTimer tm(c, PK_STAGE_APPEND, st);
-        PK_HIP(pk::launch_append(k_new, v_new, c->K, c->V, row, c->cap, c->n, c->units, st));
+        PK_HIP(pk::launch_append(k_new, v_new, c->K, c->V, row, c->cap, c->n, c->units, c->ring,
+                                 st));
     }
     c->n += 1;
     c->buf += 1;

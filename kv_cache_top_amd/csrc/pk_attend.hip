@@ -28,7 +28,9 @@ template <typename T, int G>
 __global__ __launch_bounds__(kBlock) void attend_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int64_t cap, const T* __restrict__ q,
     int64_t sink_end, int64_t r_end, int64_t n_tok, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_n, int top_k, int n_splits, float* __restrict__ part) {
+    const int32_t* __restrict__ sel_n, int top_k, int n_splits, float* __restrict__ part,
+    const T* __restrict__ rk, const T* __restrict__ rv, int64_t ring_rows, int64_t ring_sink,
+    int64_t ring_span, int64_t ring_base) {
     const int u = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, grp = lane >> 4, l16 = lane & 15;
     constexpr bool kMfma = sizeof(T) == 2;   // bf16: q k^T on the matrix cores
@@ -76,36 +78,51 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
     const int64_t total = n_hot + nsel;
     const int nk = (int)((total - i0) < kSplit ? (total - i0 > 0 ? total - i0 : 0) : kSplit);
-    auto place = [&](int kk, int32_t c, bool& ok) -> int64_t {
+    // row of attended key kk: from the device ring for the hot zone when the
+    // store is host memory, else from the store
+    auto place = [&](int kk, int32_t c, bool& ok, bool& hot) -> int64_t {
         const int64_t i = i0 + kk;
         const int64_t p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end)) : (int64_t)c;
         ok = kk < nk && p >= 0 && p < n_tok;
-        return ok ? p : 0;
+        if (!ok) {                          // masked: any valid row, on the device if possible
+            hot = rk != nullptr;
+            return hot ? (int64_t)u * ring_rows : (int64_t)u * cap;
+        }
+        hot = rk != nullptr && i < n_hot;
+        if (hot) {
+            if (i < sink_end) return (int64_t)u * ring_rows + i;
+            int64_t s = ring_base + (i - sink_end);
+            s = s >= ring_span ? s - ring_span : s;
+            return (int64_t)u * ring_rows + ring_sink + s;
+        }
+        return (int64_t)u * cap + p;
     };
-    bool ok_v[kPer], ok_k[2];
-    int64_t pos_v[kPer], pos_k[2];
+    bool ok_v[kPer], ok_k[2], hot_v[kPer], hot_k[2];
+    int64_t row_v[kPer], row_k[2];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) pos_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], ok_v[j]);
+    for (int j = 0; j < kPer; ++j)
+        row_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], ok_v[j], hot_v[j]);
     if constexpr (kMfma) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) pos_k[h] = place(32 * wave + 16 * h + l16, cand_k[h], ok_k[h]);
+        for (int h = 0; h < 2; ++h)
+            row_k[h] = place(32 * wave + 16 * h + l16, cand_k[h], ok_k[h], hot_k[h]);
     }
     // every K and V row is requested before any is used
     uint4 kb[2][4];
     Raw8<T> kv[kMfma ? 1 : kPer], vv[kPer];
     if constexpr (kMfma) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+            const T* kr = (hot_k[h] ? rk : K) + row_k[h] * kD + 8 * grp;
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
-                kb[h][st] = *reinterpret_cast<const uint4*>(
-                    K + ((int64_t)u * cap + pos_k[h]) * kD + 32 * st + 8 * grp);
+            for (int st = 0; st < 4; ++st) kb[h][st] = *reinterpret_cast<const uint4*>(kr + 32 * st);
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) kv[j].load(K + ((int64_t)u * cap + pos_v[j]) * kD + 8 * l16);
+        for (int j = 0; j < kPer; ++j) kv[j].load((hot_v[j] ? rk : K) + row_v[j] * kD + 8 * l16);
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) vv[j].load(V + ((int64_t)u * cap + pos_v[j]) * kD + 8 * l16);
+    for (int j = 0; j < kPer; ++j) vv[j].load((hot_v[j] ? rv : V) + row_v[j] * kD + 8 * l16);
 
     // scores / sqrt(d) into s_p[head][key]
     if constexpr (kMfma) {
@@ -261,11 +278,14 @@ template <typename T>
 static hipError_t launch_attend_t(int G, const T* K, const T* V, int64_t cap, int units,
                                   const T* q, int64_t sink_end, int64_t r_end, int64_t n_tok,
                                   const int32_t* sel, const int32_t* sel_n, int top_k,
-                                  int n_splits, float* part, hipStream_t st) {
+                                  int n_splits, float* part, const HotRing& ring,
+                                  hipStream_t st) {
     const dim3 grid(n_splits, units), blk(kBlock);
+    const int64_t base = r_end % ring.span;
 #define PK_ATT(GG)                                                                            \
     return launch(attend_kernel<T, GG>, grid, blk, 0, st, K, V, cap, q, sink_end, r_end, n_tok, \
-                  sel, sel_n, top_k, n_splits, part)
+                  sel, sel_n, top_k, n_splits, part, (const T*)ring.k, (const T*)ring.v,       \
+                  ring.rows, ring.n_sink, ring.span, base)
     switch (G) {
         case 1: PK_ATT(1);
         case 2: PK_ATT(2);
@@ -287,13 +307,15 @@ int attend_max_splits() { return kMaxSplits; }
 hipError_t launch_attend(bool bf16, int G, const void* K, const void* V, int64_t cap, int units,
                          const void* q, int64_t sink_end, int64_t r_end, int64_t n_tok,
                          const int32_t* sel, const int32_t* sel_n, int top_k, int n_splits,
-                         float* part, hipStream_t st) {
+                         float* part, const HotRing& ring, hipStream_t st) {
+    if (ring.span < 1) return hipErrorInvalidValue;
     if (bf16)
         return launch_attend_t<uint16_t>(G, (const uint16_t*)K, (const uint16_t*)V, cap, units,
                                          (const uint16_t*)q, sink_end, r_end, n_tok, sel, sel_n,
-                                         top_k, n_splits, part, st);
+                                         top_k, n_splits, part, ring, st);
     return launch_attend_t<float>(G, (const float*)K, (const float*)V, cap, units, (const float*)q,
-                                  sink_end, r_end, n_tok, sel, sel_n, top_k, n_splits, part, st);
+                                  sink_end, r_end, n_tok, sel, sel_n, top_k, n_splits, part, ring,
+                                  st);
 }
 
 }  // namespace pk

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
     const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
     uint8_t* __restrict__ lut, float* __restrict__ ysum,
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint8_t* __restrict__ K,
-    uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos) {
+    uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos, uint4* __restrict__ rk,
+    uint4* __restrict__ rv, int64_t ring_rows, int64_t ring_slot) {
     const int b = blockIdx.x, u = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6, l16 = lane & 15;
     __shared__ uint32_t s_row[256];
@@ -112,8 +113,14 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
         const int per_row = (int)(row_bytes / 16);
         if (tid < per_row) {
             const int64_t dst = ((u * cap + new_pos) * row_bytes) / 16 + tid;
-            reinterpret_cast<uint4*>(K)[dst] = k_new[(int64_t)u * per_row + tid];
-            reinterpret_cast<uint4*>(V)[dst] = v_new[(int64_t)u * per_row + tid];
+            const uint4 kx = k_new[(int64_t)u * per_row + tid], vx = v_new[(int64_t)u * per_row + tid];
+            reinterpret_cast<uint4*>(K)[dst] = kx;
+            reinterpret_cast<uint4*>(V)[dst] = vx;
+            if (rk != nullptr) {
+                const int64_t rd = ((int64_t)u * ring_rows + ring_slot) * per_row + tid;
+                rk[rd] = kx;
+                rv[rd] = vx;
+            }
         }
     }
     for (int i = tid; i < 256; i += 64 * G) s_row[i] = 0;
@@ -176,7 +183,10 @@ __global__ __launch_bounds__(kBlock) void append_kernel(const uint4* __restrict_
                                                          const uint4* __restrict__ v_new,
                                                          uint8_t* __restrict__ K,
                                                          uint8_t* __restrict__ V, int64_t row_bytes,
-                                                         int64_t cap, int64_t pos, int units) {
+                                                         int64_t cap, int64_t pos, int units,
+                                                         uint4* __restrict__ rk,
+                                                         uint4* __restrict__ rv, int64_t ring_rows,
+                                                         int64_t ring_slot) {
     const int per_row = (int)(row_bytes / 16);
     const int64_t n = (int64_t)units * per_row;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n;
@@ -185,6 +195,37 @@ __global__ __launch_bounds__(kBlock) void append_kernel(const uint4* __restrict_
         const int64_t dst = ((u * cap + pos) * row_bytes) / 16 + j;
         reinterpret_cast<uint4*>(K)[dst] = k_new[i];
         reinterpret_cast<uint4*>(V)[dst] = v_new[i];
+        if (rk != nullptr) {
+            const int64_t rd = (u * ring_rows + ring_slot) * per_row + j;
+            rk[rd] = k_new[i];
+            rv[rd] = v_new[i];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// ring fill (prefill of a host-memory store): the sink rows [0, sink_end) and
+// the local rows [r_end, n) of every unit, read over the host link once
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void ring_fill_kernel(const uint4* __restrict__ K,
+                                                            const uint4* __restrict__ V,
+                                                            uint4* __restrict__ rk,
+                                                            uint4* __restrict__ rv, int per_row,
+                                                            int64_t cap, int units,
+                                                            int64_t sink_end, int64_t r_end,
+                                                            int64_t n, int64_t ring_rows,
+                                                            int64_t n_sink, int64_t span) {
+    const int64_t hot = sink_end + (n - r_end);
+    const int64_t total = (int64_t)units * hot * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * kBlock) {
+        const int64_t j = i % per_row, t = i / per_row;
+        const int64_t u = t / hot, h = t - u * hot;
+        const int64_t p = h < sink_end ? h : r_end + (h - sink_end);
+        const int64_t slot = p < n_sink ? p : n_sink + p % span;
+        const int64_t src = (u * cap + p) * per_row + j, dst = (u * ring_rows + slot) * per_row + j;
+        rk[dst] = K[src];
+        rv[dst] = V[src];
     }
 }
 
@@ -210,25 +251,44 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
-                        int64_t cap, int64_t new_pos, hipStream_t st) {
+                        int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st) {
+    const int64_t slot = new_pos < ring.n_sink ? new_pos : ring.n_sink + new_pos % ring.span;
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     const dim3 grid(kSub, units), blk(64 * G);
     if (bf16)
         return launch(qprep_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)q, G, sign[0],
                       sign[1], rho, w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new,
-                      (uint8_t*)K, (uint8_t*)V, row_bytes, cap, new_pos);
+                      (uint8_t*)K, (uint8_t*)V, row_bytes, cap, new_pos, (uint4*)ring.k,
+                      (uint4*)ring.v, ring.rows, slot);
     return launch(qprep_kernel<float>, grid, blk, 0, st, (const float*)q, G, sign[0], sign[1], rho,
                   w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V,
-                  row_bytes, cap, new_pos);
+                  row_bytes, cap, new_pos, (uint4*)ring.k, (uint4*)ring.v, ring.rows, slot);
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
-                         int64_t row_bytes, int64_t cap, int64_t pos, int units, hipStream_t st) {
+                         int64_t row_bytes, int64_t cap, int64_t pos, int units,
+                         const HotRing& ring, hipStream_t st) {
     const int64_t n = (int64_t)units * (row_bytes / 16);
     const int blocks = (int)((n + kBlock - 1) / kBlock);
+    const int64_t slot = pos < ring.n_sink ? pos : ring.n_sink + pos % ring.span;
     return launch(append_kernel, dim3(blocks), dim3(kBlock), 0, st, (const uint4*)k_new,
-                  (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap, pos, units);
+                  (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap, pos, units,
+                  (uint4*)ring.k, (uint4*)ring.v, ring.rows, slot);
+}
+
+hipError_t launch_ring_fill(const void* K, const void* V, int64_t row_bytes, int64_t cap,
+                            int units, int64_t sink_end, int64_t r_end, int64_t n,
+                            const HotRing& ring, hipStream_t st) {
+    if (ring.k == nullptr) return hipSuccess;
+    const int per_row = (int)(row_bytes / 16);
+    const int64_t total = (int64_t)units * (sink_end + (n - r_end)) * per_row;
+    if (total <= 0) return hipSuccess;
+    int64_t blocks = (total + kBlock - 1) / kBlock;
+    if (blocks > 8192) blocks = 8192;
+    return launch(ring_fill_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, (const uint4*)K,
+                  (const uint4*)V, (uint4*)ring.k, (uint4*)ring.v, per_row, cap, units, sink_end,
+                  r_end, n, ring.rows, ring.n_sink, ring.span);
 }
 
 }  // namespace pk

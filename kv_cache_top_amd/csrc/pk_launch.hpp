@@ -44,15 +44,32 @@ inline hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
 
 struct CodeTables;
 
+// Device copy of the always-attended rows (sink, local, update buffer) kept
+// when the caller's K/V store is host memory: attention then reads only the
+// retrieved rows over the host link.  Row of position p: p for sink tokens,
+// n_sink + (p mod span) for the local/buffer zone (span = n_local + U rows).
+struct HotRing {
+    void* k = nullptr;        // [units][rows][d], nullptr: no ring (device store)
+    void* v = nullptr;
+    int64_t rows = 0;         // n_sink + span
+    int64_t n_sink = 0;
+    int64_t span = 1;
+};
+
 hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64_t p0,
                          int64_t count, uint8_t* ids, uint8_t* rec, const uint64_t sign[2],
                          const CodeTables& tab, hipStream_t st);
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
-                        int64_t cap, int64_t new_pos, hipStream_t st);
+                        int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st);
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
-                         int64_t row_bytes, int64_t cap, int64_t pos, int units, hipStream_t st);
+                         int64_t row_bytes, int64_t cap, int64_t pos, int units,
+                         const HotRing& ring, hipStream_t st);
+// copy rows [0, sink_end) and [r_end, n) of every unit from the store into the ring
+hipError_t launch_ring_fill(const void* K, const void* V, int64_t row_bytes, int64_t cap,
+                            int units, int64_t sink_end, int64_t r_end, int64_t n,
+                            const HotRing& ring, hipStream_t st);
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
                        uint16_t* scores, int64_t sstride, uint16_t* hist, int hstride, int nbins,
@@ -76,7 +93,7 @@ int attend_max_splits();
 hipError_t launch_attend(bool bf16, int G, const void* K, const void* V, int64_t cap, int units,
                          const void* q, int64_t sink_end, int64_t r_end, int64_t n_tok,
                          const int32_t* sel, const int32_t* sel_n, int top_k, int n_splits,
-                         float* part, hipStream_t st);
+                         float* part, const HotRing& ring, hipStream_t st);
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st);
 

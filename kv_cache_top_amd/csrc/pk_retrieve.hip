@@ -283,9 +283,18 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int l16 = tid & 15;
     __shared__ int32_t s_list[chunk];
-    __shared__ float s_tbl[16];
+    __shared__ float2 s_pair[256];     // nibble byte (code of coord 2i+1 << 4 | code of 2i)
     __shared__ uint32_t s_tmp[kBlock / 64];
-    if (tid < 16) s_tbl[tid] = ((tid & 8) ? -1.0f : 1.0f) * tab.levels[tid & 7];
+    {
+        // signed level of a 4-bit code: sign bit 3, magnitude index bits 0..2
+        auto level = [&](uint32_t c) {
+            float m = tab.levels[0];
+#pragma unroll
+            for (int l = 1; l < 8; ++l) m = ((c & 7u) == (uint32_t)l) ? tab.levels[l] : m;
+            return (c & 8u) ? -m : m;
+        };
+        for (int b = tid; b < 256; b += kBlock) s_pair[b] = make_float2(level(b & 15u), level(b >> 4));
+    }
 
     // one round of loads: this chunk's scores (contiguous per thread, vector
     // loads; rows are padded so these never leave the buffer), the threshold
@@ -357,9 +366,14 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
     // RSQ-IP: est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g;
     // 16 lanes per candidate, lane b reading subspace b's nibble word and w.
     // A group fetches the records of up to kBatch candidates before using any.
+    // Codes are dequantised two at a time from the byte-indexed level pairs.
+    // Record offsets within the unit fit 32 bits (capacity <= 2^24 keys).
     constexpr int kBatch = 8;
     const float inv_sqrt_d = 0.08838834764831845f;
     const int grp = tid >> 4;
+    const uint8_t* urec = rec + (int64_t)u * cap * kRec;
+    int32_t* upos = cand_pos + (int64_t)u * cmax;
+    float* uest = cand_est + (int64_t)u * cmax;
     for (int i0 = grp; i0 < (int)n_mem; i0 += kBatch * (kBlock / 16)) {
         uint32_t nib[kBatch];
         float w[kBatch];
@@ -369,21 +383,24 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
             const int i = i0 + k * (kBlock / 16);
             const int32_t p = s_list[i < (int)n_mem ? i : i0];
             pos[k] = (i < (int)n_mem) ? p : -1;
-            const uint8_t* r = rec + ((int64_t)u * cap + p) * kRec;
-            nib[k] = reinterpret_cast<const uint32_t*>(r)[l16];
-            w[k] = reinterpret_cast<const float*>(r + 64)[l16];
+            const uint32_t ro = (uint32_t)p * (uint32_t)kRec + 4u * (uint32_t)l16;
+            nib[k] = *reinterpret_cast<const uint32_t*>(urec + ro);
+            w[k] = *reinterpret_cast<const float*>(urec + ro + 64u);
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             float dot = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dot = fmaf(s_tbl[(nib[k] >> (4 * j)) & 15u], y[j], dot);
+            for (int b = 0; b < 4; ++b) {
+                const float2 lv = s_pair[(nib[k] >> (8 * b)) & 255u];
+                dot = fmaf(lv.x, y[2 * b], dot);
+                dot = fmaf(lv.y, y[2 * b + 1], dot);
+            }
             const float e = sum16(w[k] * dot);
-            const int i = i0 + k * (kBlock / 16);
-            const int64_t o = (int64_t)cand_before + i;
-            if (l16 == 0 && pos[k] >= 0 && o < cmax) {
-                cand_pos[(int64_t)u * cmax + o] = pos[k];
-                cand_est[(int64_t)u * cmax + o] = e * inv_sqrt_d;
+            const uint32_t o = cand_before + (uint32_t)(i0 + k * (kBlock / 16));
+            if (l16 == 0 && pos[k] >= 0 && (int64_t)o < cmax) {
+                upos[o] = pos[k];
+                uest[o] = e * inv_sqrt_d;
             }
         }
     }

@@ -47,13 +47,22 @@ class ParisKV:
         self.batch, self.n_kv, self.n_q, self.capacity, self.dtype = batch, n_kv, n_q, capacity, dtype
         self.group = n_q // n_kv
         shape = (batch, n_kv, capacity, 128)
+
+        def alloc():
+            if host_mapped:   # pinned host memory, addressable by the device
+                return torch.empty(shape, dtype=dtype, pin_memory=True)
+            return torch.empty(shape, dtype=dtype, device=device)
         if k_store is None:
-            k_store = torch.empty(shape, dtype=dtype, device=device)
+            k_store = alloc()
         if v_store is None:
-            v_store = torch.empty(shape, dtype=dtype, device=device)
+            v_store = alloc()
         for t in (k_store, v_store):
             if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
                 raise ValueError(f"store must be a contiguous {dtype} tensor of shape {shape}")
+            if host_mapped and (t.device.type != "cpu" or not t.is_pinned()):
+                raise ValueError("host_mapped stores must be pinned host tensors")
+            if not host_mapped and t.device.type != "cuda":
+                raise ValueError("device stores must be GPU tensors")
         self.K, self.V = k_store, v_store
         self.device = torch.device(device)
         self._ctx = ctypes.c_void_p()

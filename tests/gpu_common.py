@@ -28,7 +28,7 @@ def torch_dtype(wl):
     return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
 
-def make_ctx(wl, capacity=None, **override):
+def make_ctx(wl, capacity=None, host_mapped=False, **override):
     from kv_cache_top_amd import ParisKV
     p = wl.params
     kw = dict(rho=p.rho, vote_weights=p.vote_weights, coarse_permille=p.coarse_permille,
@@ -37,7 +37,8 @@ def make_ctx(wl, capacity=None, **override):
     kw.update(override)
     cap = capacity or wl.n_tokens
     dt = torch_dtype(wl)
-    pkv = ParisKV(batch=wl.batch, n_kv=wl.n_kv, n_q=wl.n_kv * wl.group, capacity=cap, dtype=dt, **kw)
+    pkv = ParisKV(batch=wl.batch, n_kv=wl.n_kv, n_q=wl.n_kv * wl.group, capacity=cap, dtype=dt,
+                  host_mapped=host_mapped, **kw)
     N = wl.n_tokens
     pkv.K[:, :, :N].copy_(torch.from_numpy(wl.K).to(dt))
     pkv.V[:, :, :N].copy_(torch.from_numpy(wl.V).to(dt))
