@@ -190,6 +190,41 @@ def test_1m_context_host_mapped_store():
     gc.log(f"[1M] ok: C = {C}, tie swaps {res[3]['n_diff']}, attention max-abs {err:.3g}")
 
 
+def test_drift_decode_16k_steps():
+    """32768-token prefill, then 16384 decode steps whose key and query mean drifts by two
+    standard deviations along a random direction (update buffer U = 256, k = 1024).
+    Parity with the oracle at five steps spread over the run; recall@k against the exact
+    top-k of the retrieval zone every 1024 steps (reported)."""
+    T, N0 = 16384, 32768
+    wl = W.gqa_bf16(N=N0, top_k=1024, buf_tokens=256)
+    Kn, Vn, Qn = W.decode_stream(wl, T)
+    pkv = gc.make_ctx(wl, capacity=N0 + T)
+    pkv.encode_keys(N0)
+    dt = gc.torch_dtype(wl)
+    Kd = torch.from_numpy(Kn).to(dt).cuda()
+    Vd = torch.from_numpy(Vn).to(dt).cuda()
+    Qd = torch.from_numpy(Qn).to(dt).cuda()
+    full = W.Workload(wl.name, wl.batch, wl.n_kv, wl.group, N0 + T, wl.dtype, wl.params,
+                      wl.sign_bits, np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2),
+                      np.concatenate([wl.V, np.moveaxis(Vn, 0, 2)], axis=2), wl.Q)
+    check_at = {0, 4095, 8191, 12287, T - 1}
+    curve = []
+    for t in range(T):
+        out, sel, sel_n = pkv.decode_step(Kd[t], Vd[t], Qd[t])
+        if t in check_at or (t + 1) % 1024 == 0:
+            torch.cuda.synchronize()
+            full.Q = Qn[t]
+            if t in check_at:
+                enc = gc.check_encode(full, pkv, [0])
+                gc.check_retrieval(full, pkv, [0], sel, sel_n, enc)
+                gc.check_attention(full, pkv, [0], sel, sel_n, out)
+            if (t + 1) % 1024 == 0:
+                rec, _ = gc.recall_report(full, pkv, list(range(wl.n_units)), sel, sel_n)
+                curve.append(rec)
+                gc.log(f"[drift] step {t + 1}: window {pkv.window()}, recall@k {rec:.3f}")
+    assert len(curve) == T // 1024 and all(0.0 <= r <= 1.0 for r in curve)
+
+
 def test_decode_window_append_evict():
     """Appends through several buffer fills: the window mirror follows the oracle's,
     evicted keys are encoded exactly like a prefill encode, and sampled steps match."""
