@@ -51,7 +51,194 @@ def parse():
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
+                    help="3: 128K context, batch 4 (default); 4: 1M context, K/V store in pinned "
+                         "host memory; 5: 16384 drifting decode steps after a 32K prefill")
     return ap.parse_args()
+
+
+def stream_reference(torch):
+    """Plain streaming kernels on this GPU over 1 GiB: the library's streaming-read
+    reference kernel (pk_stream_read) and a torch device copy (read + write bytes)."""
+    import ctypes
+    import kv_cache_top_amd._native as nat
+    x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
+    y = torch.empty_like(x)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def read():
+        nat.check(nat.lib.pk_stream_read(ctypes.c_void_p(x.data_ptr()), 1 << 30,
+                                         ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)),
+                  "pk_stream_read")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for name, fn, nbytes in (("read_GBps", read, 1 << 30), ("copy_GBps", lambda: y.copy_(x), 2 << 30)):
+        for _ in range(3):
+            fn()
+        a.record()
+        for _ in range(10):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = nbytes * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def stage_times(ctx_list, steps_fn, n_steps, torch, nat):
+    """Per-stage kernel durations (dispatch-attached HIP events) over n_steps."""
+    for c in ctx_list:
+        c.profile(True)
+    steps_fn(n_steps)
+    torch.cuda.synchronize()
+    ms = {k: 0.0 for k in nat.STAGES}
+    cnt = {k: 0 for k in nat.STAGES}
+    for c in ctx_list:
+        for k, (m, n) in c.profile_read().items():
+            ms[k] += m
+            cnt[k] += n
+        c.profile(False)
+    return {k: {"launches": cnt[k], "avg_us": 1e3 * ms[k] / cnt[k]} for k in nat.STAGES if cnt[k]}
+
+
+def run_config4(args):
+    """1M-token context, batch 1 x 8 kv heads (G = 4), bf16, the K/V store in pinned host
+    memory: ids and records in HBM, sink/local/buffer rows in a device ring, the
+    retrieved rows read by the attention kernel over the host link."""
+    import torch
+    import kv_cache_top_amd._native as nat
+    from kv_cache_top_amd import ParisKV
+    from synth import workloads as W
+    N = 1 << 20
+    t0 = time.time()
+    wl = W.gqa_bf16(N=N, batch=1, n_local=1024, buf_tokens=args.buf_tokens, threads=args.threads,
+                    name="gqa_1m_b1_host_store_bf16")
+    p = wl.params
+    dt = torch.bfloat16
+    ctx = ParisKV(batch=1, n_kv=8, n_q=32, capacity=N + args.steps + args.warmup + 64, dtype=dt,
+                  host_mapped=True, rho=p.rho, vote_weights=p.vote_weights,
+                  coarse_permille=p.coarse_permille, top_k=p.top_k, n_sink=p.n_sink,
+                  n_local=p.n_local, buf_tokens=p.buf_tokens,
+                  sign_bits=tuple(int(x) for x in wl.sign_bits))
+    ctx.K[:, :, :N].copy_(torch.from_numpy(wl.K).to(dt))
+    ctx.V[:, :, :N].copy_(torch.from_numpy(wl.V).to(dt))
+    log(f"1M context generated and stored in host memory in {time.time() - t0:.1f}s")
+    ctx.profile(True)
+    ctx.encode_keys(N)
+    enc_ms = ctx.profile_read()["encode"][0]
+    ctx.profile(False)
+    pool = 16
+    q = torch.from_numpy(W.query_pool(wl, pool)).to(dt).cuda()
+    kn, vn, _ = W.decode_stream(wl, pool, drift_sigma=0.0)
+    kn, vn = torch.from_numpy(kn).to(dt).cuda(), torch.from_numpy(vn).to(dt).cuda()
+    sel = torch.empty((1, 8, p.top_k), dtype=torch.int32, device="cuda")
+    sel_n = torch.empty((1, 8), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    state = {"t": 0}
+
+    def steps(n):
+        for _ in range(n):
+            i = state["t"] % pool
+            state["t"] += 1
+            ctx.decode_step_raw(kn[i].data_ptr(), vn[i].data_ptr(), q[i].data_ptr(), sel.data_ptr(),
+                                sel_n.data_ptr(), out.data_ptr(), stream)
+
+    steps(args.warmup)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    steps(args.steps)
+    b.record()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / args.steps
+    stages = stage_times([ctx], steps, min(args.profile_steps, 32), torch, nat)
+    n, sink_end, r_end, _ = ctx.window()
+    n_r = r_end - sink_end
+    C = min(n_r, max(p.top_k, (p.coarse_permille * n_r + 999) // 1000))
+    scan_b, rerank_b = 16 * n_r * 8, 128 * C * 8
+    host_b = 512 * min(p.top_k, C) * 8              # retrieved K and V rows over the host link
+    ring_b = 512 * (sink_end + n - r_end) * 8       # hot rows from the device ring
+    st = lambda k: stages[k]["avg_us"] * 1e-6
+    result = {
+        "metric": "decode retrieval+sparse-attn steps/s at 1M ctx, K/V store in host memory",
+        "value": 1e3 / ms_step, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": 1, "kv_heads": 8, "q_heads": 32, "head_dim": 128,
+                   "context": N, "kv_store": "pinned host memory", "top_k": p.top_k,
+                   "coarse_permille": p.coarse_permille, "sink": p.n_sink, "local": p.n_local,
+                   "update_buffer": p.buf_tokens},
+        "hbm": {"scan_GBps": scan_b / st("scan") / 1e9, "rerank_GBps": rerank_b / st("rerank") / 1e9,
+                "scan_bytes": scan_b, "rerank_bytes": rerank_b},
+        "host_link": {"retrieved_bytes_per_step": host_b, "ring_bytes_per_step": ring_b,
+                      "attend_us": stages["attend"]["avg_us"],
+                      "retrieved_GBps": host_b / st("attend") / 1e9},
+        "stages": stages,
+        "encode": {"keys": 8 * n_r, "ms": enc_ms, "host_read_GBps": 8 * n_r * 256 / (enc_ms * 1e-3) / 1e9},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def run_config5(args):
+    """Drifting decode: 32768-token prefill (batch 1 x 8 kv heads, G = 4, bf16), then
+    16384 decode steps whose key/query mean drifts by two standard deviations; U = 256,
+    k = 1024.  Timed in 16 segments of 1024 steps; recall@k of every unit against the
+    exact top-k of its retrieval zone after each segment (untimed)."""
+    import torch
+    from kv_cache_top_amd import ParisKV
+    from synth import workloads as W
+    N0, T, seg = 32768, 16384, 1024
+    wl = W.gqa_bf16(N=N0, top_k=1024, buf_tokens=256, threads=args.threads,
+                    name="gqa_32k_drift16k_bf16")
+    p = wl.params
+    Kn, Vn, Qn = W.decode_stream(wl, T)
+    dt = torch.bfloat16
+    ctx = ParisKV(batch=1, n_kv=8, n_q=32, capacity=N0 + T, dtype=dt, rho=p.rho,
+                  vote_weights=p.vote_weights, coarse_permille=p.coarse_permille, top_k=p.top_k,
+                  n_sink=p.n_sink, n_local=p.n_local, buf_tokens=p.buf_tokens,
+                  sign_bits=tuple(int(x) for x in wl.sign_bits))
+    ctx.K[:, :, :N0].copy_(torch.from_numpy(wl.K).to(dt))
+    ctx.V[:, :, :N0].copy_(torch.from_numpy(wl.V).to(dt))
+    ctx.encode_keys(N0)
+    Kd, Vd, Qd = (torch.from_numpy(x).to(dt).cuda() for x in (Kn, Vn, Qn))
+    Kall = np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2)
+    sel = torch.empty((1, 8, p.top_k), dtype=torch.int32, device="cuda")
+    sel_n = torch.empty((1, 8), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_ms, curve = 0.0, []
+    for s0 in range(0, T, seg):
+        a.record()
+        for t in range(s0, s0 + seg):
+            ctx.decode_step_raw(Kd[t].data_ptr(), Vd[t].data_ptr(), Qd[t].data_ptr(), sel.data_ptr(),
+                                sel_n.data_ptr(), out.data_ptr(), stream)
+        b.record()
+        torch.cuda.synchronize()
+        total_ms += a.elapsed_time(b)
+        n, sink_end, r_end, _ = ctx.window()
+        s_h, n_h = sel.cpu().numpy().reshape(8, -1), sel_n.cpu().numpy()[0]
+        pos = np.arange(sink_end, r_end)
+        rec = [recall_at_k(s_h[u][:n_h[u]], exact_topk(Kall[0, u], Qn[s0 + seg - 1, 0, 4 * u:4 * u + 4],
+                                                       pos, p.top_k)) for u in range(8)]
+        curve.append(round(float(np.mean(rec)), 4))
+        log(f"steps {s0 + seg}: window {ctx.window()}, recall@k {curve[-1]:.3f}")
+    result = {
+        "metric": "drifting decode steps/s over 16384 steps after a 32K prefill, recall@k per 1K steps",
+        "value": T / (total_ms * 1e-3), "unit": "steps/s", "n_gpus": 1, "steps": T, "warmup": 0,
+        "ms_per_step": total_ms / T, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": 1, "kv_heads": 8, "q_heads": 32, "head_dim": 128,
+                   "prefill": N0, "decode_steps": T, "drift_sigma": 2.0, "top_k": p.top_k,
+                   "coarse_permille": p.coarse_permille, "sink": p.n_sink, "local": p.n_local,
+                   "update_buffer": p.buf_tokens},
+        "recall_at_k_per_1k_steps": curve,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def calibrate_copy():
@@ -208,8 +395,19 @@ def cpu_baseline(args, layer, budget_s=10.0):
                       f"whole-batch step"}
 
 
+def exact_topk(K, Qg, positions, k):
+    """Quality reference for recall@k (not part of the method): the k positions with the
+    largest summed raw score sum_g <q_g, k_i> in float64, ties to the lower position."""
+    s = np.asarray(K, np.float64)[positions] @ np.atleast_2d(np.asarray(Qg, np.float64)).sum(0)
+    order = np.lexsort((positions, -s))
+    return positions[order[:min(k, positions.size)]]
+
+
+def recall_at_k(selected, reference):
+    return len(np.intersect1d(selected, reference)) / len(reference) if len(reference) else 1.0
+
+
 def recall(layer):
-    from oracle import pariskv as ok
     wl = layer.wl
     n, sink_end, r_end, _ = layer.ctx.window()
     sel = layer.sel.cpu().numpy().reshape(wl.n_units, -1)
@@ -220,9 +418,9 @@ def recall(layer):
         b, h = divmod(u, wl.n_kv)
         K = wl.K[b, h]
         pos = np.arange(sink_end, min(r_end, wl.n_tokens))
-        ref = ok.exact_topk(K, q[b, 4 * h:4 * h + 4], pos, wl.params.top_k)
+        ref = exact_topk(K, q[b, 4 * h:4 * h + 4], pos, wl.params.top_k)
         got = sel[u][:sel_n[u]]
-        rec.append(ok.recall(got, ref))
+        rec.append(recall_at_k(got, ref))
         pl.append(float(np.isin(wl.planted[b, h], got).mean()))
     return float(np.mean(rec)), float(np.mean(pl))
 
@@ -242,6 +440,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.config == 4:
+        return run_config4(args)
+    if args.config == 5:
+        return run_config5(args)
 
     layers = [Layer(args, l) for l in range(args.layers)]
     # prefill encode of every layer (timed per layer, reported separately)
@@ -312,6 +514,7 @@ def main():
             stages[k]["GBps"] = gbs(k)
 
     rec, planted = recall(layers[(base + args.profile_steps - 1) % nl])
+    sref = stream_reference(torch)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -351,7 +554,9 @@ def main():
         },
         "retrieval_hbm": {"scan_rerank_gather_GBps": comb_gbs,
                           "frac": comb_gbs / HBM_PEAK_GBS if comb_gbs else None,
+                          "frac_of_stream_read": comb_gbs / sref["read_GBps"] if comb_gbs else None,
                           "bytes_per_step": int(comb_bytes), "kernel_us_per_step": comb_us},
+        "stream_reference": sref,
         "stages": stages,
         "keys_scanned_per_s": keys_per_step * 1e3 / ms_step,
         "host_submit_ms_per_step": 1e3 * host_s / args.steps,

@@ -148,6 +148,14 @@ const char* pk_status_string(pk_status s);
 pk_status pk_get_window(const pk_ctx* ctx, int64_t* n_tokens, int64_t* sink_end, int64_t* r_end,
                         int64_t* buf);
 
+/* Measurement reference, not part of the method: reads `bytes` bytes at `src`
+ * (device memory, 16-byte aligned, a multiple of 16 bytes) with a plain
+ * streaming kernel, so that the path's bandwidth can be set against this
+ * device's streaming-read rate.  *sink (device, 4 bytes) is written only in the
+ * unlikely case that the checksum of the data equals a fixed constant.
+ * Errors: PK_ERR_INVALID (NULL, misaligned or zero size). */
+pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Per-stage kernel timing.  While enabled, every kernel the context launches
  * is bracketed by HIP events recorded on the stream it runs on.
  * pk_profile_read synchronises those events and returns, per stage, the

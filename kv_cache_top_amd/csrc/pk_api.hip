@@ -380,6 +380,14 @@ void pk_destroy(pk_ctx* ctx) {
     delete ctx;
 }
 
+pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink || bytes == 0 || (bytes & 15) ||
+        (reinterpret_cast<uintptr_t>(src) & 15))
+        return PK_ERR_INVALID;
+    PK_HIP(pk::launch_stream_read(src, (int64_t)(bytes / 16), sink, (hipStream_t)stream));
+    return PK_OK;
+}
+
 pk_status pk_get_window(const pk_ctx* c, int64_t* n_tokens, int64_t* sink_end, int64_t* r_end,
                         int64_t* buf) {
     if (!c) return PK_ERR_INVALID;

@@ -113,10 +113,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
 //   T = max s with ge[s] >= C;  need = C - ge[T+1] ties at T are taken
 //   (lowest positions first);  per chunk: gt_c = sum_{s > T} h_c[s],
 //   eq_c = h_c[T];  off[c] = {sum_{c'<c} gt_c', sum_{c'<c} eq_c'}.
-// Chunk rows are staged through LDS (all at once for up to 64 KB of rows).
+// Chunk rows are staged through LDS (all at once for up to 80 KB of rows).
 // ---------------------------------------------------------------------------
 constexpr int kSBlock = 1024;
-constexpr int kSelLds = 32768;      // uint16 entries of staged rows (64 KB)
+constexpr int kSelLds = 40960;      // uint16 entries of staged rows (80 KB)
 
 // Exclusive scans of two uint32 per thread over a block of NT threads, sharing
 // the barriers.  `tmp` must hold 2 * NT / 64 entries.
@@ -514,10 +514,19 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
             kmin_inv = max(kmin_inv, ~key);
         }
     } else {
-        for (int i = tid; i < C; i += kFBlock) {
-            const uint32_t key = f32_order_key(est[i]);
-            kmax = max(kmax, key);
-            kmin_inv = max(kmin_inv, ~key);
+        for (int i0 = tid; i0 < C; i0 += 8 * kFBlock) {
+            float e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * kFBlock;
+                e[k] = est[i < C ? i : C - 1];        // clamped: a real element
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t key = f32_order_key(e[k]);
+                kmax = max(kmax, key);
+                kmin_inv = max(kmin_inv, ~key);
+            }
         }
     }
     kmax = wave_max(kmax);
@@ -528,7 +537,48 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     }
     if (tid == 0) s_cnt = 0;
     lds_sync();
-    auto key_at = [&](int i) -> uint32_t { return in_lds ? s_key[i] : f32_order_key(est[i]); };
+    // f(i, key) for every candidate i = tid + j * kFBlock; from memory (too many
+    // candidates for LDS) eight loads are in flight at a time
+    auto for_all = [&](auto&& f) {
+        if (in_lds) {
+            for (int i = tid; i < C; i += kFBlock) f(i, s_key[i]);
+            return;
+        }
+        for (int i0 = tid; i0 < C; i0 += 8 * kFBlock) {
+            float e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * kFBlock;
+                e[k] = est[i < C ? i : C - 1];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * kFBlock;
+                if (i < C) f(i, f32_order_key(e[k]));
+            }
+        }
+    };
+    // f(i, key) for this thread's segment [b0, b0 + seg), in order
+    auto for_segment = [&](auto&& f) {
+        if (in_lds) {
+            for (int j = 0; j < seg; ++j)
+                if (b0 + j < C) f(b0 + j, s_key[b0 + j]);
+            return;
+        }
+        for (int j0 = 0; j0 < seg; j0 += 8) {
+            float e[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = b0 + j0 + k;
+                e[k] = est[(j0 + k < seg && i < C) ? i : C - 1];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = b0 + j0 + k;
+                if (j0 + k < seg && i < C) f(i, f32_order_key(e[k]));
+            }
+        }
+    };
 
     uint32_t kth = 0, remaining = (uint32_t)k_eff;
     const bool all = k_eff >= C;
@@ -552,7 +602,7 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
             };
             for (int b = tid; b < kRadixBins; b += kFBlock) s_h[b] = 0;
             lds_sync();
-            for (int i = tid; i < C; i += kFBlock) atomicAdd(&s_h[bucket(key_at(i))], 1u);
+            for_all([&](int, uint32_t key) { atomicAdd(&s_h[bucket(key)], 1u); });
             lds_sync();
             if (tid < 64) digit_search(s_h, kRadixBins, remaining, lane, &s_digit, &s_above);
             lds_sync();
@@ -560,10 +610,9 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
             const uint32_t rem = remaining - s_above;   // 1 <= rem <= members of bstar
             const uint32_t n_b = s_h[bstar];
             if (n_b <= (uint32_t)kRankMax) {
-                for (int i = tid; i < C; i += kFBlock) {
-                    const uint32_t key = key_at(i);
+                for_all([&](int, uint32_t key) {
                     if (bucket(key) == bstar) s_mem[atomicAdd(&s_cnt, 1u)] = key;
-                }
+                });
                 lds_sync();
                 // exact rank of every member: the k-th value has gt < rem <= ge
                 for (int m = tid; m < (int)n_b; m += kFBlock) {
@@ -596,10 +645,9 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
             const int nb = 1 << widths[p];
             for (int b = tid; b < nb; b += kFBlock) s_h[b] = 0;
             lds_sync();
-            for (int i = tid; i < C; i += kFBlock) {
-                const uint32_t key = key_at(i);
+            for_all([&](int, uint32_t key) {
                 if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
-            }
+            });
             lds_sync();
             if (tid < 64) digit_search(s_h, nb, remaining, lane, &s_digit, &s_above);
             lds_sync();
@@ -613,14 +661,10 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     // compaction: thread t owns candidates [t*seg, (t+1)*seg); one block scan of
     // (ties at kth, keys above kth) gives both offsets
     uint32_t eqc = 0, gtc = 0;
-    for (int j = 0; j < seg; ++j) {
-        const int i = b0 + j;
-        if (i < C) {
-            const uint32_t key = key_at(i);
-            if (all || key > kth) ++gtc;
-            else if (key == kth) ++eqc;
-        }
-    }
+    for_segment([&](int, uint32_t key) {
+        if (all || key > kth) ++gtc;
+        else if (key == kth) ++eqc;
+    });
     uint32_t tot, r, gt_before;
     if (C < 65536) {
         const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, s_tmp, &tot);
@@ -631,17 +675,14 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
         gt_before = block_excl_scan_t<kFBlock>(gtc, s_tmp, &tot);
     }
     uint32_t o = gt_before + (r < remaining ? r : remaining);
-    for (int j = 0; j < seg; ++j) {
-        const int i = b0 + j;
-        if (i >= C) break;
-        const uint32_t key = key_at(i);
+    for_segment([&](int i, uint32_t key) {
         const bool in = all || key > kth || (key == kth && r++ < remaining);
         if (in) {
             const int32_t pj = in_lds ? s_pos[i] : cpos[i];
             if (o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = pj;
             ++o;
         }
-    }
+    });
     if (tid == 0) sel_n[u] = k_eff;
 }
 
