@@ -37,19 +37,38 @@ def _run(cmd):
     return r
 
 
+def _check_no_scratch(src: str, remarks: str) -> None:
+    """Every kernel must keep its state in registers and LDS: a private (scratch)
+    segment means per-lane memory round trips inside the hot loops."""
+    name = None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+            if size != 0:
+                raise RuntimeError(f"{src}: kernel {name} uses {size} B/lane of scratch")
+
+
 def build(verbose: bool = False) -> str:
     from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append((obj, [HIPCC, "-x", "hip", *COMMON, *HIP_FLAGS, "-c", os.path.join(CSRC, src),
-                           "-o", obj]))
+        jobs.append((obj, [HIPCC, "-x", "hip", *COMMON, *HIP_FLAGS,
+                           "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+                           "-o", obj], src))
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append((obj, ["g++", *COMMON, "-Wall", "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, ["g++", *COMMON, "-Wall", "-c", os.path.join(CSRC, src), "-o", obj], None))
+
+    def one(job):
+        r = _run(job[1])
+        if job[2] is not None:
+            _check_no_scratch(job[2], r.stdout + r.stderr)
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 16)) as ex:
-        list(ex.map(lambda j: _run(j[1]), jobs))
+        list(ex.map(one, jobs))
     objs = [j[0] for j in jobs]
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])

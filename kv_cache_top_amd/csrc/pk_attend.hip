@@ -24,7 +24,7 @@ static_assert(kSplit % 64 == 0, "softmax statistics take 64 keys per wave pass")
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <typename T, int G>
+template <typename T, int G, bool RING>
 __global__ __launch_bounds__(kBlock) void attend_kernel(
     const T* __restrict__ K, const T* __restrict__ V, int64_t cap, const T* __restrict__ q,
     int64_t sink_end, int64_t r_end, int64_t n_tok, const int32_t* __restrict__ sel,
@@ -84,11 +84,15 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
         const int64_t i = i0 + kk;
         const int64_t p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end)) : (int64_t)c;
         ok = kk < nk && p >= 0 && p < n_tok;
-        if (!ok) {                          // masked: any valid row, on the device if possible
-            hot = rk != nullptr;
-            return hot ? (int64_t)u * ring_rows : (int64_t)u * cap;
+        if constexpr (!RING) {
+            hot = false;
+            return (int64_t)u * cap + (ok ? p : 0);
         }
-        hot = rk != nullptr && i < n_hot;
+        if (!ok) {                          // masked: any valid row, on the device
+            hot = true;
+            return (int64_t)u * ring_rows;
+        }
+        hot = i < n_hot;
         if (hot) {
             if (i < sink_end) return (int64_t)u * ring_rows + i;
             int64_t s = ring_base + (i - sink_end);
@@ -113,16 +117,16 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
     if constexpr (kMfma) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const T* kr = (hot_k[h] ? rk : K) + row_k[h] * kD + 8 * grp;
+            const T* kr = (RING && hot_k[h] ? rk : K) + row_k[h] * kD + 8 * grp;
 #pragma unroll
             for (int st = 0; st < 4; ++st) kb[h][st] = *reinterpret_cast<const uint4*>(kr + 32 * st);
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) kv[j].load((hot_v[j] ? rk : K) + row_v[j] * kD + 8 * l16);
+        for (int j = 0; j < kPer; ++j) kv[j].load((RING && hot_v[j] ? rk : K) + row_v[j] * kD + 8 * l16);
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) vv[j].load((hot_v[j] ? rv : V) + row_v[j] * kD + 8 * l16);
+    for (int j = 0; j < kPer; ++j) vv[j].load((RING && hot_v[j] ? rv : V) + row_v[j] * kD + 8 * l16);
 
     // scores / sqrt(d) into s_p[head][key]
     if constexpr (kMfma) {
@@ -283,9 +287,13 @@ static hipError_t launch_attend_t(int G, const T* K, const T* V, int64_t cap, in
     const dim3 grid(n_splits, units), blk(kBlock);
     const int64_t base = r_end % ring.span;
 #define PK_ATT(GG)                                                                            \
-    return launch(attend_kernel<T, GG>, grid, blk, 0, st, K, V, cap, q, sink_end, r_end, n_tok, \
-                  sel, sel_n, top_k, n_splits, part, (const T*)ring.k, (const T*)ring.v,       \
-                  ring.rows, ring.n_sink, ring.span, base)
+    return ring.k != nullptr                                                                  \
+               ? launch(attend_kernel<T, GG, true>, grid, blk, 0, st, K, V, cap, q, sink_end,  \
+                        r_end, n_tok, sel, sel_n, top_k, n_splits, part, (const T*)ring.k,     \
+                        (const T*)ring.v, ring.rows, ring.n_sink, ring.span, base)             \
+               : launch(attend_kernel<T, GG, false>, grid, blk, 0, st, K, V, cap, q, sink_end, \
+                        r_end, n_tok, sel, sel_n, top_k, n_splits, part, (const T*)nullptr,    \
+                        (const T*)nullptr, ring.rows, ring.n_sink, ring.span, base)
     switch (G) {
         case 1: PK_ATT(1);
         case 2: PK_ATT(2);

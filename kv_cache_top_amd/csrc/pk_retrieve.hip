@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restr
 // rerank
 // ---------------------------------------------------------------------------
 template <int KPT>
-__global__ __launch_bounds__(kBlock) void rerank_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void rerank_kernel(
     const uint16_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
     int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks, const int32_t* __restrict__ off,
     const int32_t* __restrict__ meta, const float* __restrict__ ysum, CodeTables tab,
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
     // A group fetches the records of up to kBatch candidates before using any.
     // Codes are dequantised two at a time from the byte-indexed level pairs.
     // Record offsets within the unit fit 32 bits (capacity <= 2^24 keys).
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 16;
     const float inv_sqrt_d = 0.08838834764831845f;
     const int grp = tid >> 4;
     const uint8_t* urec = rec + (int64_t)u * cap * kRec;
@@ -377,12 +377,10 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
     for (int i0 = grp; i0 < (int)n_mem; i0 += kBatch * (kBlock / 16)) {
         uint32_t nib[kBatch];
         float w[kBatch];
-        int32_t pos[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int i = i0 + k * (kBlock / 16);
             const int32_t p = s_list[i < (int)n_mem ? i : i0];
-            pos[k] = (i < (int)n_mem) ? p : -1;
             const uint32_t ro = (uint32_t)p * (uint32_t)kRec + 4u * (uint32_t)l16;
             nib[k] = *reinterpret_cast<const uint32_t*>(urec + ro);
             w[k] = *reinterpret_cast<const float*>(urec + ro + 64u);
@@ -397,9 +395,10 @@ __global__ __launch_bounds__(kBlock) void rerank_kernel(
                 dot = fmaf(lv.y, y[2 * b + 1], dot);
             }
             const float e = sum16(w[k] * dot);
-            const uint32_t o = cand_before + (uint32_t)(i0 + k * (kBlock / 16));
-            if (l16 == 0 && pos[k] >= 0 && (int64_t)o < cmax) {
-                upos[o] = pos[k];
+            const int i = i0 + k * (kBlock / 16);
+            const uint32_t o = cand_before + (uint32_t)i;
+            if (l16 == 0 && i < (int)n_mem && (int64_t)o < cmax) {
+                upos[o] = s_list[i];
                 uest[o] = e * inv_sqrt_d;
             }
         }
@@ -469,7 +468,7 @@ __device__ __forceinline__ void digit_search(const uint32_t* s_h, int nb, uint32
     }
 }
 
-template <int SEG>
+template <int SEG, bool IN_LDS>
 __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict__ cand_pos,
                                                        const float* __restrict__ cand_est,
                                                        int64_t cmax, int C, int top_k,
@@ -486,13 +485,13 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     const float* est = cand_est + (int64_t)u * cmax;
     const int32_t* cpos = cand_pos + (int64_t)u * cmax;
     const int k_eff = C < top_k ? C : top_k;
-    const bool in_lds = C <= SEG * kFBlock;
+    constexpr bool in_lds = IN_LDS;   // all candidates held in LDS (C <= SEG * kFBlock)
     // estimates and positions are read once, coalesced, into LDS; thread t
     // later compacts the contiguous segment [t*seg, (t+1)*seg)
     const int seg = (C + kFBlock - 1) / kFBlock;
     const int b0 = tid * seg;
     uint32_t kmax = 0, kmin_inv = 0;  // running max of keys and of ~keys
-    if (in_lds) {
+    if constexpr (in_lds) {
         float e[SEG];
         int32_t p[SEG];
 #pragma unroll
@@ -540,7 +539,7 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     // f(i, key) for every candidate i = tid + j * kFBlock; from memory (too many
     // candidates for LDS) eight loads are in flight at a time
     auto for_all = [&](auto&& f) {
-        if (in_lds) {
+        if constexpr (in_lds) {
             for (int i = tid; i < C; i += kFBlock) f(i, s_key[i]);
             return;
         }
@@ -560,7 +559,7 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     };
     // f(i, key) for this thread's segment [b0, b0 + seg), in order
     auto for_segment = [&](auto&& f) {
-        if (in_lds) {
+        if constexpr (in_lds) {
             for (int j = 0; j < seg; ++j)
                 if (b0 + j < C) f(b0 + j, s_key[b0 + j]);
             return;
@@ -637,12 +636,11 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     }
     if (!found) {
         uint32_t prefix = 0, pmask = 0;
-        const int shifts[3] = {21, 10, 0};
-        const int widths[3] = {11, 11, 10};
         for (int p = 0; p < 3; ++p) {
-            const int shift = shifts[p];
-            const uint32_t dmask = (1u << widths[p]) - 1u;
-            const int nb = 1 << widths[p];
+            const int width = p == 2 ? 10 : 11;               // digits of 11, 11, 10 bits
+            const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
+            const uint32_t dmask = (1u << width) - 1u;
+            const int nb = 1 << width;
             for (int b = tid; b < nb; b += kFBlock) s_h[b] = 0;
             lds_sync();
             for_all([&](int, uint32_t key) {
@@ -662,8 +660,8 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     // (ties at kth, keys above kth) gives both offsets
     uint32_t eqc = 0, gtc = 0;
     for_segment([&](int, uint32_t key) {
-        if (all || key > kth) ++gtc;
-        else if (key == kth) ++eqc;
+        gtc += (all || key > kth) ? 1u : 0u;
+        eqc += (!all && key == kth) ? 1u : 0u;
     });
     uint32_t tot, r, gt_before;
     if (C < 65536) {
@@ -676,12 +674,16 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     }
     uint32_t o = gt_before + (r < remaining ? r : remaining);
     for_segment([&](int i, uint32_t key) {
-        const bool in = all || key > kth || (key == kth && r++ < remaining);
-        if (in) {
-            const int32_t pj = in_lds ? s_pos[i] : cpos[i];
-            if (o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = pj;
-            ++o;
+        const bool eq = !all && key == kth;
+        const bool in = all || key > kth || (eq && r < remaining);
+        r += eq ? 1u : 0u;
+        if (in && o < (uint32_t)k_eff) {
+            int32_t pj;
+            if constexpr (in_lds) pj = s_pos[i];
+            else pj = cpos[i];
+            sel[(int64_t)u * top_k + o] = pj;
         }
+        o += in ? 1u : 0u;
     });
     if (tid == 0) sel_n[u] = k_eff;
 }
@@ -762,13 +764,16 @@ hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t c
     // the keys are read from memory
     const dim3 grid(units), blk(kFBlock);
     if (C <= 4 * kFBlock)
-        return launch(fine_kernel<4>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
-                      sel_n);
+        return launch(fine_kernel<4, true>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
+                      sel, sel_n);
     if (C <= 8 * kFBlock)
-        return launch(fine_kernel<8>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
-                      sel_n);
-    return launch(fine_kernel<kFineLds / kFBlock>, grid, blk, 0, st, cand_pos, cand_est, cmax, C,
-                  top_k, sel, sel_n);
+        return launch(fine_kernel<8, true>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
+                      sel, sel_n);
+    if (C <= kFineLds)
+        return launch(fine_kernel<kFineLds / kFBlock, true>, grid, blk, 0, st, cand_pos, cand_est,
+                      cmax, C, top_k, sel, sel_n);
+    return launch(fine_kernel<1, false>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
+                  sel_n);
 }
 
 hipError_t launch_empty_select(int units, int32_t* sel_n, int32_t* meta, hipStream_t st) {
