@@ -337,9 +337,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     // this chunk's candidates, in position order: keys above T, and ties at T
     // while the unit's tie budget lasts.  One packed scan of (ties, above).
     uint32_t eqc = 0, gtc = 0;
+    const int kbase = (int)start + tid * KPT;   // retrieval zone < 2^24 keys
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        if (start + (int64_t)tid * KPT + j >= n_r) s[j] = 0xffffffffu;
+        if (kbase + j >= (int)n_r) s[j] = 0xffffffffu;
         gtc += (s[j] != 0xffffffffu && s[j] > (uint32_t)T) ? 1u : 0u;
         eqc += (s[j] == (uint32_t)T) ? 1u : 0u;
     }
@@ -387,6 +388,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
+            const int i = i0 + k * (kBlock / 16);
+            if (i >= (int)n_mem) break;          // uniform in the 16-lane group
             float dot = 0.0f;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -395,9 +398,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
                 dot = fmaf(lv.y, y[2 * b + 1], dot);
             }
             const float e = sum16(w[k] * dot);
-            const int i = i0 + k * (kBlock / 16);
             const uint32_t o = cand_before + (uint32_t)i;
-            if (l16 == 0 && i < (int)n_mem && (int64_t)o < cmax) {
+            if (l16 == 0 && (int64_t)o < cmax) {
                 upos[o] = s_list[i];
                 uest[o] = e * inv_sqrt_d;
             }
