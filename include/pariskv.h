@@ -160,7 +160,9 @@ pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* st
  * is bracketed by HIP events recorded on the stream it runs on.
  * pk_profile_read synchronises those events and returns, per stage, the
  * summed duration in milliseconds and the number of launches since the last
- * enable (arrays of PK_STAGE_COUNT entries).  Errors: PK_ERR_INVALID. */
+ * enable (arrays of PK_STAGE_COUNT entries).  The coarse threshold is found
+ * inside the rerank launch, so PK_STAGE_SELECT records no launches.
+ * Errors: PK_ERR_INVALID. */
 enum { PK_STAGE_ENCODE = 0, PK_STAGE_APPEND = 1, PK_STAGE_QPREP = 2, PK_STAGE_SCAN = 3,
        PK_STAGE_SELECT = 4, PK_STAGE_RERANK = 5, PK_STAGE_FINE = 6, PK_STAGE_ATTEND = 7,
        PK_STAGE_COMBINE = 8, PK_STAGE_COUNT = 9 };

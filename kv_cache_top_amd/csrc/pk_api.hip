@@ -36,8 +36,8 @@ struct pk_ctx {
     uint8_t* lut = nullptr;       // [units][16][256]   vote table
     float* ysum = nullptr;        // [units][128]       sum of rotated queries
     uint16_t* scores = nullptr;   // [units][sstride] + pad   coarse scores (retrieval offset)
-    uint16_t* hist = nullptr;     // [units][max_chunks][hstride] per-chunk score histograms
-    int32_t* off = nullptr;       // [units][max_chunks][2] candidates / ties before a chunk
+    uint16_t* hist = nullptr;     // [units][max_chunks][hstride] per-chunk #{score >= s}
+    uint32_t* tot = nullptr;      // [units][nbins rounded up to even]  unit score histogram
     int32_t* meta = nullptr;      // [units][4]          {T, ties taken, C, k_eff}
     int32_t* cand_pos = nullptr;  // [units][cmax]
     float* cand_est = nullptr;    // [units][cmax]
@@ -146,7 +146,7 @@ void free_all(pk_ctx* c) {
     release_events(c);
     for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
     c->event_pool.clear();
-    void* bufs[] = {c->ids,  c->rec,      c->lut,      c->ysum, c->scores, c->hist,   c->off,
+    void* bufs[] = {c->ids,  c->rec,      c->lut,      c->ysum, c->scores, c->hist,   c->tot,
                     c->meta, c->cand_pos, c->cand_est, c->part, c->ring.k, c->ring.v};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
@@ -211,8 +211,8 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     {
         StageTimer tm(c, PK_STAGE_QPREP, st);
         PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
-                                c->cfg.vote_weight, c->lut, c->ysum, k_new, v_new, c->K, c->V,
-                                row, c->cap, c->n - 1, c->ring, st));
+                                c->cfg.vote_weight, c->lut, c->ysum, c->tot, c->nbins, k_new,
+                                v_new, c->K, c->V, row, c->cap, c->n - 1, c->ring, st));
     }
     const int64_t n_r = c->r_end - c->sink_end;
     if (n_r <= 0) {
@@ -226,18 +226,14 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
         StageTimer tm(c, PK_STAGE_SCAN, st);
         PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
                                c->max_chunks, c->lut, c->scores, c->sstride, c->hist, c->hstride,
-                               c->nbins, st));
-    }
-    {
-        StageTimer tm(c, PK_STAGE_SELECT, st);
-        PK_HIP(pk::launch_select(c->hist, c->hstride, c->max_chunks, n_chunks, c->units, c->nbins, C,
-                                 c->cfg.top_k, c->off, c->meta, st));
+                               c->tot, c->nbins, st));
     }
     {
         StageTimer tm(c, PK_STAGE_RERANK, st);
         PK_HIP(pk::launch_rerank(chunk, c->scores, c->sstride, c->rec, c->cap, c->units,
-                                 c->sink_end, n_r, n_chunks, c->max_chunks, c->off, c->meta,
-                                 c->ysum, c->tab, c->cand_pos, c->cand_est, c->cmax, st));
+                                 c->sink_end, n_r, n_chunks, c->max_chunks, c->hist, c->hstride,
+                                 c->tot, c->nbins, C, c->cfg.top_k, c->ysum, c->tab, c->cand_pos,
+                                 c->cand_est, c->cmax, c->meta, st));
     }
     StageTimer tm(c, PK_STAGE_FINE, st);
     PK_HIP(pk::launch_fine(c->cand_pos, c->cand_est, c->cmax, c->units, (int)C, c->cfg.top_k, sel,
@@ -321,7 +317,10 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         return PK_ERR_INVALID;
     }
     c->max_chunks = (int)std::min<int64_t>(pk::kMaxChunks, ceil_div(capacity, 256));
-    c->cmax = std::max<int64_t>(1, coarse_count(capacity, cfg->coarse_permille, cfg->top_k));
+    // candidate rows hold a multiple of 16 entries: the fine selection reads
+    // them in 16-byte vectors
+    c->cmax = (std::max<int64_t>(1, coarse_count(capacity, cfg->coarse_permille, cfg->top_k)) + 15) /
+              16 * 16;
     c->max_splits = (int)ceil_div((int64_t)cfg->n_sink + cfg->n_local + cfg->buf_tokens + cfg->top_k,
                                   pk::attend_split());
 
@@ -337,7 +336,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         // score rows padded to 16 B; the tail pad covers vector reads past the last row
         {(void**)&c->scores, (size_t)((U * c->sstride + 8192) * 2)},
         {(void**)&c->hist, (size_t)(U * c->max_chunks * (int64_t)c->hstride * 2)},
-        {(void**)&c->off, (size_t)(U * c->max_chunks * 2 * 4)},
+        {(void**)&c->tot, (size_t)(U * ((c->nbins + 1) & ~1) * 4)},
         {(void**)&c->meta, (size_t)(U * 4 * 4)},
         {(void**)&c->cand_pos, (size_t)(U * c->cmax * 4)},
         {(void**)&c->cand_est, (size_t)(U * c->cmax * 4)},
@@ -362,6 +361,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         }
     }
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
+        hipMemset(c->tot, 0, U * ((c->nbins + 1) & ~1) * 4) != hipSuccess ||
         hipMemset(c->scores, 0, (U * c->sstride + 8192) * 2) != hipSuccess ||
         hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {

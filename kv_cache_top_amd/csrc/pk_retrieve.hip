@@ -7,16 +7,17 @@
 //  * rerank (RSQ-IP): each candidate's raw score <k, q> is estimated from its
 //    4-bit codes and scales only, and the top-k are selected.
 //
-// Four kernels, no cross-block synchronisation inside any of them (on gfx950
+// Three kernels, no cross-block synchronisation inside any of them (on gfx950
 // an agent-scope release fence writes back the XCD's L2 and costs far more
 // per block than a kernel boundary):
-//  scan    one 256-thread block per (chunk, unit): coarse scores and the
-//          chunk's score histogram;
-//  select  one 1024-thread block per unit: the coarse threshold T (largest
-//          score with #{score >= T} >= C), the ties at T to take, and for
-//          every chunk the candidates and ties at T in the chunks before it;
-//  rerank  one 256-thread block per (chunk, unit): compacts the chunk's
-//          candidates in position order and estimates them with RSQ-IP;
+//  scan    one 256-thread block per (chunk, unit): coarse scores, the chunk's
+//          suffix counts sfx_c[s] = #{score >= s}, and the unit's histogram
+//          (device atomics into a table the query preparation zeroed);
+//  rerank  one 256-thread block per (chunk, unit): from the unit histogram
+//          the coarse threshold T (largest score with #{score >= T} >= C) and
+//          the ties at T to take, from the earlier chunks' suffix counts the
+//          candidates before this chunk; then compacts the chunk's candidates
+//          in position order and estimates them with RSQ-IP;
 //  fine    one 1024-thread block per unit: the k-th largest estimate by
 //          value bucketing (radix select as the fallback), ties to the lower
 //          position, compaction in order.
@@ -29,7 +30,7 @@ template <int KPT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void scan_kernel(
     const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
     const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores, int64_t sstride,
-    uint16_t* __restrict__ hist, int hstride, int nbins) {
+    uint16_t* __restrict__ hist, int hstride, uint32_t* __restrict__ tot, int nbins) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     __shared__ uint32_t s_lut[kSub * 256 / 4];
@@ -102,189 +103,57 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     }
     lds_sync();
 
-    // the chunk's histogram row (a chunk holds at most 8192 keys: uint16)
-    uint16_t* myh = hist + ((int64_t)u * max_chunks + ch) * hstride;
-    for (int b = tid; b < nbins; b += kBlock) myh[b] = (uint16_t)s_hist[b];
-}
-
-// ---------------------------------------------------------------------------
-// select: per unit, from the chunks' histogram rows h_c
-//   tot[s] = sum_c h_c[s];  ge[s] = sum_{s' >= s} tot[s'] = #{score >= s};
-//   T = max s with ge[s] >= C;  need = C - ge[T+1] ties at T are taken
-//   (lowest positions first);  per chunk: gt_c = sum_{s > T} h_c[s],
-//   eq_c = h_c[T];  off[c] = {sum_{c'<c} gt_c', sum_{c'<c} eq_c'}.
-// Chunk rows are staged through LDS (all at once for up to 80 KB of rows).
-// ---------------------------------------------------------------------------
-constexpr int kSBlock = 1024;
-constexpr int kSelLds = 40960;      // uint16 entries of staged rows (80 KB)
-
-// Exclusive scans of two uint32 per thread over a block of NT threads, sharing
-// the barriers.  `tmp` must hold 2 * NT / 64 entries.
-template <int NT>
-__device__ __forceinline__ void block_excl_scan2(uint32_t& a, uint32_t& b, uint32_t* tmp) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t x = wave_incl_scan(a), y = wave_incl_scan(b);
-    if (lane == 63) {
-        tmp[wave] = x;
-        tmp[NT / 64 + wave] = y;
-    }
-    lds_sync();
-    uint32_t bx = 0, by = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        if (w < wave) {
-            bx += tmp[w];
-            by += tmp[NT / 64 + w];
+    // waves 1..: add the chunk's counts to the unit's score histogram (zeroed
+    // by the query preparation of this step).  wave 0: the chunk's suffix
+    // counts sfx[b] = #{keys with score >= b} (a chunk holds at most 8192
+    // keys: uint16); lane l sums the bins ranked l*per .. l*per+per-1 in
+    // descending score order.
+    const int wave = tid >> 6;
+    if (wave > 0) {
+        // two bins per 64-bit atomic (a count stays below 2^24: no carry
+        // between the halves); rows of (nbins + 1) & ~1 entries
+        uint64_t* ut = reinterpret_cast<uint64_t*>(tot + (int64_t)u * ((nbins + 1) & ~1));
+        for (int i = tid - 64; 2 * i < nbins; i += kBlock - 64) {
+            const uint64_t h = (uint64_t)s_hist[2 * i] |
+                               ((uint64_t)(2 * i + 1 < nbins ? s_hist[2 * i + 1] : 0u) << 32);
+            if (h != 0u) __hip_atomic_fetch_add(ut + i, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    }
-    a = bx + x - a;
-    b = by + y - b;
-}
-
-__global__ __launch_bounds__(kSBlock) void select_kernel(const uint16_t* __restrict__ hist,
-                                                         int hstride, int max_chunks, int n_chunks,
-                                                         int nbins, int64_t C, int top_k,
-                                                         int32_t* __restrict__ off,
-                                                         int32_t* __restrict__ meta) {
-    const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __shared__ __align__(16) uint16_t s_rows[kSelLds];
-    __shared__ uint32_t s_tot[kMaxBins];
-    __shared__ uint32_t s_gt[kMaxChunks], s_eq[kMaxChunks];
-    __shared__ uint32_t s_tmp[2 * kSBlock / 64];
-    __shared__ uint32_t s_T, s_need;
-    const uint16_t* H0 = hist + (int64_t)u * max_chunks * hstride;
-    const int row_vec = hstride / 8;          // uint4 per row
-    const int tile = kSelLds / hstride;       // rows staged at once
-    const bool one_tile = n_chunks <= tile;
-
-    // bin totals: the four lanes of a quad sum every fourth row of one bin
-    for (int c0 = 0; c0 < n_chunks; c0 += tile) {
-        const int rows = (n_chunks - c0) < tile ? (n_chunks - c0) : tile;
-        if (c0 > 0) lds_sync();               // previous tile fully read
-        for (int i = tid; i < rows * row_vec; i += kSBlock)
-            reinterpret_cast<uint4*>(s_rows)[i] =
-                reinterpret_cast<const uint4*>(H0 + (int64_t)c0 * hstride)[i];
-        lds_sync();
-        const int q = tid & 3;
-        for (int b0 = 0; b0 < nbins; b0 += kSBlock / 4) {
-            const int b = b0 + (tid >> 2);
-            uint32_t a = 0;
-            if (b < nbins)
-                for (int r = q; r < rows; r += 4) a += s_rows[r * hstride + b];
-            a += (uint32_t)xor16<1>((int)a);
-            a += (uint32_t)xor16<2>((int)a);
-            if (q == 0 && b < nbins) s_tot[b] = (c0 == 0 ? 0u : s_tot[b]) + a;
-        }
-    }
-    lds_sync();
-
-    // wave 0: suffix counts ge[s] = #{score >= s} (lane l owns the per bins
-    // [l*per, l*per+per) of the descending order), T = max s with ge[s] >= C
-    // (ge is non-increasing: T + 1 = number of bins with ge >= C), need = C -
-    // ge[T+1] ties at T
-    if (wave == 0) {
-        const int per = (nbins + 63) / 64;
+    } else {
+        const int lane = tid, per = (nbins + 63) / 64;
         uint32_t seg = 0;
         for (int j = 0; j < per; ++j) {
             const int r = lane * per + j;
-            if (r < nbins) seg += s_tot[nbins - 1 - r];
+            if (r < nbins) seg += s_hist[nbins - 1 - r];
         }
         uint32_t run = wave_incl_scan(seg) - seg;
-        uint32_t n_ge = 0, ge_next = 0;       // ge of the bin just above the highest counted
+        uint16_t* myh = hist + ((int64_t)u * max_chunks + ch) * hstride;
         for (int j = 0; j < per; ++j) {
             const int r = lane * per + j;
             if (r < nbins) {
-                const uint32_t before = run;  // ge[s + 1]
-                run += s_tot[nbins - 1 - r];  // ge[s]
-                if ((int64_t)run >= C) {
-                    ++n_ge;
-                    if ((int64_t)before < C) ge_next = before;   // s = T: ge[T+1]
-                }
+                run += s_hist[nbins - 1 - r];
+                myh[nbins - 1 - r] = (uint16_t)run;
             }
         }
-        const uint32_t T1 = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(n_ge), 63);
-        const uint32_t above = (uint32_t)wave_max((uint32_t)ge_next);
-        if (lane == 0) {
-            s_T = T1 - 1;
-            s_need = (uint32_t)(C - (int64_t)above);
-        }
-    }
-    lds_sync();
-    const int T = (int)s_T;
-
-    // per-chunk counts: a 16-lane group per chunk sums h_c[s] over s > T
-    for (int w0 = 0; w0 < n_chunks * 16; w0 += kSBlock) {
-        const int w = w0 + tid;
-        const int c = w >> 4, l16 = w & 15;
-        const uint16_t* row = one_tile ? s_rows + c * hstride : H0 + (int64_t)c * hstride;
-        uint32_t a = 0;
-        if (c < n_chunks)
-            for (int b = T + 1 + l16; b < nbins; b += 16) a += row[b];
-        a += (uint32_t)xor16<1>((int)a);        // 16-lane sum (every lane active)
-        a += (uint32_t)xor16<2>((int)a);
-        a += (uint32_t)dpp_mov<0x141>((int)a);
-        a += (uint32_t)dpp_mov<0x140>((int)a);
-        if (c < n_chunks && l16 == 0) {
-            s_gt[c] = a;
-            s_eq[c] = row[T];
-        }
-    }
-    lds_sync();
-    // exclusive scans over chunks
-    if (n_chunks <= 64) {
-        if (wave == 0) {
-            const uint32_t g = lane < n_chunks ? s_gt[lane] : 0u;
-            const uint32_t e = lane < n_chunks ? s_eq[lane] : 0u;
-            const uint32_t gb = wave_incl_scan(g) - g, eb = wave_incl_scan(e) - e;
-            if (lane < n_chunks) {
-                off[((int64_t)u * max_chunks + lane) * 2] = (int32_t)gb;
-                off[((int64_t)u * max_chunks + lane) * 2 + 1] = (int32_t)eb;
-            }
-        }
-    } else {
-        const int per = (n_chunks + kSBlock - 1) / kSBlock;
-        uint32_t gt_run = 0, eq_run = 0;
-        for (int j = 0; j < per; ++j) {
-            const int c = tid * per + j;
-            if (c < n_chunks) {
-                gt_run += s_gt[c];
-                eq_run += s_eq[c];
-            }
-        }
-        block_excl_scan2<kSBlock>(gt_run, eq_run, s_tmp);
-        for (int j = 0; j < per; ++j) {
-            const int c = tid * per + j;
-            if (c < n_chunks) {
-                off[((int64_t)u * max_chunks + c) * 2] = (int32_t)gt_run;
-                off[((int64_t)u * max_chunks + c) * 2 + 1] = (int32_t)eq_run;
-                gt_run += s_gt[c];
-                eq_run += s_eq[c];
-            }
-        }
-    }
-    if (tid == 0) {
-        meta[u * 4 + 0] = T;
-        meta[u * 4 + 1] = (int32_t)s_need;
-        meta[u * 4 + 2] = (int32_t)C;
-        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
     }
 }
 
-// ---------------------------------------------------------------------------
-// rerank
-// ---------------------------------------------------------------------------
+// rerank.  Coarse selection, per unit: ge[s] = #{score >= s} from the unit
+// histogram; T = max s with ge[s] >= C; the ties at T taken are the first
+// need = C - ge[T+1] in position order.  Chunk c holds gt_c = sfx_c[T+1]
+// keys above T and eq_c = sfx_c[T] - gt_c ties; this chunk's candidates start
+// after the earlier chunks' keys above T and the ties taken among theirs.
 template <int KPT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void rerank_kernel(
     const uint16_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
-    int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks, const int32_t* __restrict__ off,
-    const int32_t* __restrict__ meta, const float* __restrict__ ysum, CodeTables tab,
-    int32_t* __restrict__ cand_pos, float* __restrict__ cand_est, int64_t cmax) {
+    int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks, const uint16_t* __restrict__ hist,
+    int hstride, const uint32_t* __restrict__ tot, int nbins, int64_t C, int top_k,
+    const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
+    float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int l16 = tid & 15;
     __shared__ int32_t s_list[chunk];
     __shared__ float2 s_pair[256];     // nibble byte (code of coord 2i+1 << 4 | code of 2i)
-    __shared__ uint32_t s_tmp[kBlock / 64];
     {
         // signed level of a 4-bit code: sign bit 3, magnitude index bits 0..2
         auto level = [&](uint32_t c) {
@@ -297,8 +166,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     }
 
     // one round of loads: this chunk's scores (contiguous per thread, vector
-    // loads; rows are padded so these never leave the buffer), the threshold
-    // and this chunk's offsets, the summed rotated query
+    // loads; rows are padded so these never leave the buffer), the summed
+    // rotated query, the unit histogram
+    // the unit histogram's first 512 bins are requested before anything else
+    const uint32_t* ut = tot + (int64_t)u * ((nbins + 1) & ~1);
+    const uint32_t t0 = tid < nbins ? ut[tid] : 0u;
+    const uint32_t t1 = tid + kBlock < nbins ? ut[tid + kBlock] : 0u;
     const int64_t start = (int64_t)ch * chunk;
     uint32_t s[KPT];
     {
@@ -326,16 +199,68 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
             s[0] = sp[0];
         }
     }
-    const int T = meta[u * 4 + 0];
-    const uint32_t need = (uint32_t)meta[u * 4 + 1];
-    const uint32_t gt_chunk = (uint32_t)off[((int64_t)u * max_chunks + ch) * 2];
-    const uint32_t eq_chunk = (uint32_t)off[((int64_t)u * max_chunks + ch) * 2 + 1];
     float y[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) y[r] = ysum[(int64_t)u * kD + 8 * l16 + r];
+    extern __shared__ uint32_t s_ut[];   // the unit histogram (nbins entries, sized at launch)
+    if (tid < nbins) s_ut[tid] = t0;
+    if (tid + kBlock < nbins) s_ut[tid + kBlock] = t1;
+    for (int b = tid + 2 * kBlock; b < nbins; b += kBlock) s_ut[b] = ut[b];
+    lds_sync();
+
+    // wave 0: T and need from the unit histogram; lane l owns the bins ranked
+    // l*per .. l*per+per-1 in descending score order (ge is non-increasing, so
+    // T + 1 = number of scores s with ge[s] >= C)
+    const int lane = tid & 63, wave = tid >> 6;
+    __shared__ uint32_t s_T, s_need;
+    __shared__ uint32_t s_red[3 * kBlock / 64];
+    if (wave == 0) {
+        const int per = (nbins + 63) / 64;
+        uint32_t seg = 0;
+        for (int j = 0; j < per; ++j) {
+            const int r = lane * per + j;
+            if (r < nbins) seg += s_ut[nbins - 1 - r];
+        }
+        uint32_t run = wave_incl_scan(seg) - seg;
+        uint32_t n_ge = 0, ge_next = 0;      // ge[T+1], seen by the lane that reaches C
+        for (int j = 0; j < per; ++j) {
+            const int r = lane * per + j;
+            if (r < nbins) {
+                const uint32_t before = run;
+                run += s_ut[nbins - 1 - r];
+                if ((int64_t)run >= C) {
+                    ++n_ge;
+                    if ((int64_t)before < C) ge_next = before;
+                }
+            }
+        }
+        const uint32_t T1 = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(n_ge), 63);
+        const uint32_t above = wave_max(ge_next);
+        if (lane == 0) {
+            s_T = T1 - 1;                    // C <= n_r: bin 0 always counts, T >= 0
+            s_need = (uint32_t)(C - (int64_t)above);
+        }
+    }
+    lds_sync();
+    const int T = (int)s_T;
+    const uint32_t need = s_need;
+    if (ch == 0 && tid == 0) {
+        meta[u * 4 + 0] = T;
+        meta[u * 4 + 1] = (int32_t)need;
+        meta[u * 4 + 2] = (int32_t)C;
+        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
+    }
+    // keys above T and ties at T in the chunks before this one
+    uint32_t gtb = 0, eqb = 0;
+    for (int c = tid; c < ch; c += kBlock) {
+        const uint16_t* row = hist + ((int64_t)u * max_chunks + c) * hstride;
+        const uint32_t g = (T >= 0 && T + 1 < nbins) ? row[T + 1] : 0u;
+        gtb += g;
+        eqb += T >= 0 ? (uint32_t)row[T] - g : 0u;
+    }
 
     // this chunk's candidates, in position order: keys above T, and ties at T
-    // while the unit's tie budget lasts.  One packed scan of (ties, above).
+    // while the unit's tie budget lasts
     uint32_t eqc = 0, gtc = 0;
     const int kbase = (int)start + tid * KPT;   // retrieval zone < 2^24 keys
 #pragma unroll
@@ -344,13 +269,39 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         gtc += (s[j] != 0xffffffffu && s[j] > (uint32_t)T) ? 1u : 0u;
         eqc += (s[j] == (uint32_t)T) ? 1u : 0u;
     }
-    uint32_t tot;
-    const uint32_t packed = block_excl_scan((eqc << 16) | gtc, s_tmp, &tot);
+    // one barrier for three block-wide sums: the packed (ties, above) scan of
+    // this chunk and the earlier chunks' totals
+    uint32_t packed, tot_c, gt_chunk, eq_chunk;
+    {
+        const uint32_t v = (eqc << 16) | gtc;
+        const uint32_t x = wave_incl_scan(v);
+        const uint32_t gw = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(gtb), 63);
+        const uint32_t ew = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(eqb), 63);
+        if (lane == 63) s_red[wave] = x;
+        if (lane == 0) {
+            s_red[kBlock / 64 + wave] = gw;
+            s_red[2 * kBlock / 64 + wave] = ew;
+        }
+        lds_sync();
+        uint32_t before = 0, all = 0, ga = 0, ea = 0;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) {
+            const uint32_t t = s_red[w];
+            if (w < wave) before += t;
+            all += t;
+            ga += s_red[kBlock / 64 + w];
+            ea += s_red[2 * kBlock / 64 + w];
+        }
+        packed = before + x - v;
+        tot_c = all;
+        gt_chunk = ga;
+        eq_chunk = ea;
+    }
     const uint32_t eq_t = packed >> 16, gt_t = packed & 0xffffu;
     const uint32_t taken_before_chunk = eq_chunk < need ? eq_chunk : need;
     auto taken = [&](uint32_t e) { return (e < need ? e : need) - taken_before_chunk; };
     uint32_t at = gt_t + taken(eq_chunk + eq_t);
-    const uint32_t n_mem = (tot & 0xffffu) + taken(eq_chunk + (tot >> 16));
+    const uint32_t n_mem = (tot_c & 0xffffu) + taken(eq_chunk + (tot_c >> 16));
     const uint32_t cand_before = gt_chunk + taken_before_chunk;
     uint32_t rank = eq_chunk + eq_t;
 #pragma unroll
@@ -418,9 +369,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
 // bits) decides instead.  Then compaction in candidate (= position) order,
 // each thread owning a contiguous segment; ties at the k-th go to the lower
 // positions.
+// Up to kFineReg candidates, thread t keeps its segment [t*SEG, t*SEG+SEG)
+// in registers for every pass; beyond that the passes stream the estimates
+// from memory.
 // ---------------------------------------------------------------------------
 constexpr int kFBlock = 1024;
-constexpr int kFineLds = 16384;  // candidates held in LDS; more are read from memory
+constexpr int kFineReg = 16 * kFBlock;  // candidates held in registers
 constexpr int kRadixBins = 2048;
 constexpr int kRankMax = 1024;   // bucket members ranked directly
 
@@ -428,93 +382,237 @@ __device__ __forceinline__ float order_key_to_f32(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// one wave finds the digit d of the histogram h[0..nb) holding the
-// `remaining`-th largest element: above(d) < remaining <= above(d) + h[d],
-// above(d) = sum of h over digits > d.  Writes d and above(d).
+// one wave finds the digit d of the histogram h[0..nb) (nb = 64 * per, per <=
+// 32) holding the `remaining`-th largest element: above(d) < remaining <=
+// above(d) + h[d], above(d) = sum of h over digits > d, for 1 <= remaining <=
+// sum of h.  Writes d and above(d).  Two levels: lane l first sums the digits
+// [l*per, l*per+per) (higher digits belong to higher lanes) to find the lane
+// holding d, then lanes 0..per-1 take that lane's digits in descending order.
 __device__ __forceinline__ void digit_search(const uint32_t* s_h, int nb, uint32_t remaining,
                                              int lane, uint32_t* s_digit, uint32_t* s_above) {
-    // lane owns the per = nb/64 digits [lane*per, lane*per+per), read as
-    // 16-byte vectors; larger digits belong to higher lanes
     const int per = nb / 64;
-    uint32_t h[32];
+    uint32_t segsum = 0;
 #pragma unroll
     for (int q4 = 0; q4 < 8; ++q4) {
         if (4 * q4 < per) {
             const uint4 x = reinterpret_cast<const uint4*>(s_h + lane * per)[q4];
-            h[4 * q4] = x.x;
-            h[4 * q4 + 1] = x.y;
-            h[4 * q4 + 2] = x.z;
-            h[4 * q4 + 3] = x.w;
-        } else {
-            h[4 * q4] = h[4 * q4 + 1] = h[4 * q4 + 2] = h[4 * q4 + 3] = 0;
+            segsum += (x.x + x.y) + (x.z + x.w);
         }
     }
-    uint32_t segsum = 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) segsum += h[j];
-    // counts in the digits of the lanes above this one
     const uint32_t incl = wave_incl_scan(segsum);
     const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    uint32_t above = total - incl;
-    if (above < remaining && above + segsum >= remaining) {
-#pragma unroll
-        for (int j = 31; j >= 0; --j) {
-            if (j < per) {
-                if (above < remaining && above + h[j] >= remaining) {
-                    *s_digit = (uint32_t)(lane * per + j);
-                    *s_above = above;
-                }
-                above += h[j];
-            }
-        }
+    const uint32_t above = total - incl;       // digits of the higher lanes
+    const uint64_t hit = __ballot(above < remaining && above + segsum >= remaining);
+    const int L = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+    const uint32_t aL = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+    const int top = L * per + per - 1;
+    const uint32_t h = lane < per ? s_h[top - lane] : 0u;
+    const uint32_t ab = aL + wave_incl_scan(h) - h;
+    const uint64_t hit2 = __ballot(lane < per && ab < remaining && ab + h >= remaining);
+    if (hit2 != 0 && lane == __ffsll((unsigned long long)hit2) - 1) {
+        *s_digit = (uint32_t)(top - lane);
+        *s_above = ab;
     }
 }
 
-template <int SEG, bool IN_LDS>
-__global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict__ cand_pos,
-                                                       const float* __restrict__ cand_est,
-                                                       int64_t cmax, int C, int top_k,
-                                                       int32_t* __restrict__ sel,
-                                                       int32_t* __restrict__ sel_n) {
-    const int u = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __shared__ uint32_t s_key[SEG * kFBlock];
-    __shared__ int32_t s_pos[SEG * kFBlock];
-    __shared__ __align__(16) uint32_t s_h[kRadixBins];
-    __shared__ uint32_t s_mem[kRankMax];
-    __shared__ uint32_t s_tmp[kFBlock / 64];
-    __shared__ uint32_t s_wmax[kFBlock / 64], s_wmin[kFBlock / 64];
-    __shared__ uint32_t s_digit, s_above, s_cnt, s_kth, s_gt;
+// Shared steps of both variants.  Keys are f32 order keys (larger key =
+// larger estimate).  ForAll(f) calls f(key) for every candidate of this
+// thread; the result is kth and `remaining` = ties at kth to take.
+struct FineShared {
+    uint32_t h[kRadixBins];
+    uint32_t mem[kRankMax];
+    uint32_t tmp[kFBlock / 64];
+    uint32_t wmax[kFBlock / 64], wmin[kFBlock / 64];
+    uint32_t digit, above, cnt, kth, gt;
+};
+
+template <typename ForAll>
+__device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, uint32_t kmin_inv,
+                                               int k_eff, ForAll&& for_all, uint32_t& kth,
+                                               uint32_t& remaining) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    kmax = wave_max(kmax);
+    kmin_inv = wave_max(kmin_inv);
+    if (lane == 0) {
+        sh.wmax[wave] = kmax;
+        sh.wmin[wave] = kmin_inv;
+    }
+    if (tid == 0) {
+        sh.cnt = 0;
+        sh.digit = 0;
+        sh.above = 0;
+    }
+    lds_sync();
+    kth = 0;
+    remaining = (uint32_t)k_eff;
+    kmax = 0;
+    kmin_inv = 0;
+#pragma unroll
+    for (int w = 0; w < kFBlock / 64; ++w) {
+        kmax = max(kmax, sh.wmax[w]);
+        kmin_inv = max(kmin_inv, sh.wmin[w]);
+    }
+    const float vmax = order_key_to_f32(kmax), vmin = order_key_to_f32(~kmin_inv);
+    const float span = vmax - vmin;
+    const float scale = (float)kRadixBins / span;
+    // finite, positive span and scale: (v - vmin) * scale is then finite and in [0, ~2048]
+    if (span > 0.0f && span <= 3.0e38f && scale <= 3.0e38f) {
+        const float topb = (float)(kRadixBins - 1);
+        auto bucket = [&](uint32_t key) -> uint32_t {
+            return (uint32_t)fminf((order_key_to_f32(key) - vmin) * scale, topb);
+        };
+        for (int b = tid; b < kRadixBins; b += kFBlock) sh.h[b] = 0;
+        lds_sync();
+        for_all([&](uint32_t key) { atomicAdd(&sh.h[bucket(key)], 1u); });
+        lds_sync();
+        if (wave == 0) digit_search(sh.h, kRadixBins, remaining, lane, &sh.digit, &sh.above);
+        lds_sync();
+        const uint32_t bstar = sh.digit;
+        const uint32_t rem = remaining - sh.above;   // 1 <= rem <= members of bstar
+        const uint32_t n_b = sh.h[bstar];
+        if (n_b <= (uint32_t)kRankMax) {
+            for_all([&](uint32_t key) {
+                if (bucket(key) == bstar) sh.mem[atomicAdd(&sh.cnt, 1u)] = key;
+            });
+            lds_sync();
+            // exact rank of every member: the k-th value has gt < rem <= ge
+            for (int m = tid; m < (int)n_b; m += kFBlock) {
+                const uint32_t km = sh.mem[m];
+                uint32_t gt = 0, ge = 0;
+                for (int j = 0; j < (int)n_b; ++j) {
+                    const uint32_t kj = sh.mem[j];
+                    gt += kj > km ? 1u : 0u;
+                    ge += kj >= km ? 1u : 0u;
+                }
+                if (gt < rem && rem <= ge) {  // every writer writes the same values
+                    sh.kth = km;
+                    sh.gt = gt;
+                }
+            }
+            lds_sync();
+            kth = sh.kth;
+            remaining = rem - sh.gt;
+            return;
+        }
+    }
+    // radix select over the order keys
+    uint32_t prefix = 0, pmask = 0;
+    for (int p = 0; p < 3; ++p) {
+        const int width = p == 2 ? 10 : 11;               // digits of 11, 11, 10 bits
+        const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
+        const uint32_t dmask = (1u << width) - 1u;
+        const int nb = 1 << width;
+        for (int b = tid; b < nb; b += kFBlock) sh.h[b] = 0;
+        lds_sync();
+        for_all([&](uint32_t key) {
+            if ((key & pmask) == prefix) atomicAdd(&sh.h[(key >> shift) & dmask], 1u);
+        });
+        lds_sync();
+        if (wave == 0) digit_search(sh.h, nb, remaining, lane, &sh.digit, &sh.above);
+        lds_sync();
+        prefix |= sh.digit << shift;
+        pmask |= dmask << shift;
+        remaining -= sh.above;
+        lds_sync();
+    }
+    kth = prefix;
+}
+
+// candidates held in registers: C <= SEG * kFBlock, SEG in {4, 8, 16}; the
+// candidate rows hold a multiple of 16 entries, so the 16-byte vector loads of
+// a segment that starts below C stay inside the unit's row
+template <int SEG>
+__global__ __launch_bounds__(kFBlock) void fine_reg_kernel(const int32_t* __restrict__ cand_pos,
+                                                           const float* __restrict__ cand_est,
+                                                           int64_t cmax, int C, int top_k,
+                                                           int32_t* __restrict__ sel,
+                                                           int32_t* __restrict__ sel_n) {
+    const int u = blockIdx.x, tid = threadIdx.x;
+    __shared__ FineShared sh;
+    const int k_eff = C < top_k ? C : top_k;
+    const int b0 = tid * SEG;
+    const int bl = b0 < C ? b0 : 0;          // a segment past C loads the row's start
+    uint32_t key[SEG];
+    int32_t pos[SEG];
+    {
+        const float4* e4 = reinterpret_cast<const float4*>(cand_est + (int64_t)u * cmax + bl);
+        const int4* p4 = reinterpret_cast<const int4*>(cand_pos + (int64_t)u * cmax + bl);
+        float4 e[SEG / 4];
+        int4 pv[SEG / 4];
+#pragma unroll
+        for (int q = 0; q < SEG / 4; ++q) {
+            e[q] = e4[q];
+            pv[q] = p4[q];
+        }
+#pragma unroll
+        for (int q = 0; q < SEG / 4; ++q) {
+            key[4 * q] = f32_order_key(e[q].x);
+            key[4 * q + 1] = f32_order_key(e[q].y);
+            key[4 * q + 2] = f32_order_key(e[q].z);
+            key[4 * q + 3] = f32_order_key(e[q].w);
+            pos[4 * q] = pv[q].x;
+            pos[4 * q + 1] = pv[q].y;
+            pos[4 * q + 2] = pv[q].z;
+            pos[4 * q + 3] = pv[q].w;
+        }
+    }
+    const int nv = C - b0 < 0 ? 0 : (C - b0 < SEG ? C - b0 : SEG);   // valid entries
+    const bool all = k_eff >= C;
+    uint32_t kth = 0, remaining = (uint32_t)k_eff;
+    if (!all) {
+        uint32_t kmax = 0, kmin_inv = 0;
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) {
+            kmax = max(kmax, j < nv ? key[j] : 0u);
+            kmin_inv = max(kmin_inv, j < nv ? ~key[j] : 0u);
+        }
+        fine_threshold(sh, kmax, kmin_inv, k_eff,
+                       [&](auto&& f) {
+#pragma unroll
+                           for (int j = 0; j < SEG; ++j)
+                               if (j < nv) f(key[j]);
+                       },
+                       kth, remaining);
+    }
+    // compaction: one block scan of (ties at kth, keys above kth) gives both
+    // offsets (C <= 16384: the halves never carry)
+    uint32_t eqc = 0, gtc = 0;
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        gtc += (j < nv && (all || key[j] > kth)) ? 1u : 0u;
+        eqc += (j < nv && !all && key[j] == kth) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, sh.tmp, &tot);
+    uint32_t r = packed >> 16;                 // ties at kth before this segment
+    uint32_t o = (packed & 0xffffu) + (r < remaining ? r : remaining);
+    int32_t* usel = sel + (int64_t)u * top_k;
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        const bool eq = j < nv && !all && key[j] == kth;
+        const bool in = j < nv && (all || key[j] > kth || (eq && r < remaining));
+        r += eq ? 1u : 0u;
+        if (in && o < (uint32_t)k_eff) usel[o] = pos[j];
+        o += in ? 1u : 0u;
+    }
+    if (tid == 0) sel_n[u] = k_eff;
+}
+
+// more candidates than registers hold: every pass streams the estimates from
+// memory, eight loads in flight per thread; thread t compacts [t*seg, t*seg+seg)
+__global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __restrict__ cand_pos,
+                                                           const float* __restrict__ cand_est,
+                                                           int64_t cmax, int C, int top_k,
+                                                           int32_t* __restrict__ sel,
+                                                           int32_t* __restrict__ sel_n) {
+    const int u = blockIdx.x, tid = threadIdx.x;
+    __shared__ FineShared sh;
     const float* est = cand_est + (int64_t)u * cmax;
     const int32_t* cpos = cand_pos + (int64_t)u * cmax;
     const int k_eff = C < top_k ? C : top_k;
-    constexpr bool in_lds = IN_LDS;   // all candidates held in LDS (C <= SEG * kFBlock)
-    // estimates and positions are read once, coalesced, into LDS; thread t
-    // later compacts the contiguous segment [t*seg, (t+1)*seg)
     const int seg = (C + kFBlock - 1) / kFBlock;
     const int b0 = tid * seg;
-    uint32_t kmax = 0, kmin_inv = 0;  // running max of keys and of ~keys
-    if constexpr (in_lds) {
-        float e[SEG];
-        int32_t p[SEG];
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) {
-            const int i = j * kFBlock + tid;
-            const int ic = i < C ? i : C - 1;   // clamped: a real element
-            e[j] = est[ic];
-            p[j] = cpos[ic];
-        }
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) {
-            const int i = j * kFBlock + tid;
-            const uint32_t key = f32_order_key(e[j]);
-            if (i < C) {
-                s_key[i] = key;
-                s_pos[i] = p[j];
-            }
-            kmax = max(kmax, key);
-            kmin_inv = max(kmin_inv, ~key);
-        }
-    } else {
+    auto for_all = [&](auto&& f) {
         for (int i0 = tid; i0 < C; i0 += 8 * kFBlock) {
             float e[8];
 #pragma unroll
@@ -523,49 +621,12 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
                 e[k] = est[i < C ? i : C - 1];        // clamped: a real element
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t key = f32_order_key(e[k]);
-                kmax = max(kmax, key);
-                kmin_inv = max(kmin_inv, ~key);
-            }
-        }
-    }
-    kmax = wave_max(kmax);
-    kmin_inv = wave_max(kmin_inv);
-    if (lane == 0) {
-        s_wmax[wave] = kmax;
-        s_wmin[wave] = kmin_inv;
-    }
-    if (tid == 0) s_cnt = 0;
-    lds_sync();
-    // f(i, key) for every candidate i = tid + j * kFBlock; from memory (too many
-    // candidates for LDS) eight loads are in flight at a time
-    auto for_all = [&](auto&& f) {
-        if constexpr (in_lds) {
-            for (int i = tid; i < C; i += kFBlock) f(i, s_key[i]);
-            return;
-        }
-        for (int i0 = tid; i0 < C; i0 += 8 * kFBlock) {
-            float e[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int i = i0 + k * kFBlock;
-                e[k] = est[i < C ? i : C - 1];
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int i = i0 + k * kFBlock;
-                if (i < C) f(i, f32_order_key(e[k]));
-            }
+            for (int k = 0; k < 8; ++k)
+                if (i0 + k * kFBlock < C) f(f32_order_key(e[k]));
         }
     };
     // f(i, key) for this thread's segment [b0, b0 + seg), in order
     auto for_segment = [&](auto&& f) {
-        if constexpr (in_lds) {
-            for (int j = 0; j < seg; ++j)
-                if (b0 + j < C) f(b0 + j, s_key[b0 + j]);
-            return;
-        }
         for (int j0 = 0; j0 < seg; j0 += 8) {
             float e[8];
 #pragma unroll
@@ -580,86 +641,16 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
             }
         }
     };
-
-    uint32_t kth = 0, remaining = (uint32_t)k_eff;
     const bool all = k_eff >= C;
-    bool found = all;
+    uint32_t kth = 0, remaining = (uint32_t)k_eff;
     if (!all) {
-        kmax = 0;
-        kmin_inv = 0;
-#pragma unroll
-        for (int w = 0; w < kFBlock / 64; ++w) {
-            kmax = max(kmax, s_wmax[w]);
-            kmin_inv = max(kmin_inv, s_wmin[w]);
-        }
-        const float vmax = order_key_to_f32(kmax), vmin = order_key_to_f32(~kmin_inv);
-        const float span = vmax - vmin;
-        const float scale = (float)kRadixBins / span;
-        // finite, positive span and scale: (v - vmin) * scale is then finite and in [0, ~2048]
-        if (span > 0.0f && span <= 3.0e38f && scale <= 3.0e38f) {
-            const float top = (float)(kRadixBins - 1);
-            auto bucket = [&](uint32_t key) -> uint32_t {
-                return (uint32_t)fminf((order_key_to_f32(key) - vmin) * scale, top);
-            };
-            for (int b = tid; b < kRadixBins; b += kFBlock) s_h[b] = 0;
-            lds_sync();
-            for_all([&](int, uint32_t key) { atomicAdd(&s_h[bucket(key)], 1u); });
-            lds_sync();
-            if (tid < 64) digit_search(s_h, kRadixBins, remaining, lane, &s_digit, &s_above);
-            lds_sync();
-            const uint32_t bstar = s_digit;
-            const uint32_t rem = remaining - s_above;   // 1 <= rem <= members of bstar
-            const uint32_t n_b = s_h[bstar];
-            if (n_b <= (uint32_t)kRankMax) {
-                for_all([&](int, uint32_t key) {
-                    if (bucket(key) == bstar) s_mem[atomicAdd(&s_cnt, 1u)] = key;
-                });
-                lds_sync();
-                // exact rank of every member: the k-th value has gt < rem <= ge
-                for (int m = tid; m < (int)n_b; m += kFBlock) {
-                    const uint32_t km = s_mem[m];
-                    uint32_t gt = 0, ge = 0;
-                    for (int j = 0; j < (int)n_b; ++j) {
-                        const uint32_t kj = s_mem[j];
-                        gt += kj > km ? 1u : 0u;
-                        ge += kj >= km ? 1u : 0u;
-                    }
-                    if (gt < rem && rem <= ge) {  // every writer writes the same values
-                        s_kth = km;
-                        s_gt = gt;
-                    }
-                }
-                lds_sync();
-                kth = s_kth;
-                remaining = rem - s_gt;
-                found = true;
-            }
-        }
+        uint32_t kmax = 0, kmin_inv = 0;
+        for_all([&](uint32_t key) {
+            kmax = max(kmax, key);
+            kmin_inv = max(kmin_inv, ~key);
+        });
+        fine_threshold(sh, kmax, kmin_inv, k_eff, for_all, kth, remaining);
     }
-    if (!found) {
-        uint32_t prefix = 0, pmask = 0;
-        for (int p = 0; p < 3; ++p) {
-            const int width = p == 2 ? 10 : 11;               // digits of 11, 11, 10 bits
-            const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
-            const uint32_t dmask = (1u << width) - 1u;
-            const int nb = 1 << width;
-            for (int b = tid; b < nb; b += kFBlock) s_h[b] = 0;
-            lds_sync();
-            for_all([&](int, uint32_t key) {
-                if ((key & pmask) == prefix) atomicAdd(&s_h[(key >> shift) & dmask], 1u);
-            });
-            lds_sync();
-            if (tid < 64) digit_search(s_h, nb, remaining, lane, &s_digit, &s_above);
-            lds_sync();
-            prefix |= s_digit << shift;
-            pmask |= dmask << shift;
-            remaining -= s_above;
-            lds_sync();
-        }
-        kth = prefix;
-    }
-    // compaction: thread t owns candidates [t*seg, (t+1)*seg); one block scan of
-    // (ties at kth, keys above kth) gives both offsets
     uint32_t eqc = 0, gtc = 0;
     for_segment([&](int, uint32_t key) {
         gtc += (all || key > kth) ? 1u : 0u;
@@ -667,30 +658,24 @@ __global__ __launch_bounds__(kFBlock) void fine_kernel(const int32_t* __restrict
     });
     uint32_t tot, r, gt_before;
     if (C < 65536) {
-        const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, s_tmp, &tot);
-        r = packed >> 16;                       // ties at kth before this segment
+        const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, sh.tmp, &tot);
+        r = packed >> 16;
         gt_before = packed & 0xffffu;
     } else {
-        r = block_excl_scan_t<kFBlock>(eqc, s_tmp, &tot);
-        gt_before = block_excl_scan_t<kFBlock>(gtc, s_tmp, &tot);
+        r = block_excl_scan_t<kFBlock>(eqc, sh.tmp, &tot);
+        gt_before = block_excl_scan_t<kFBlock>(gtc, sh.tmp, &tot);
     }
     uint32_t o = gt_before + (r < remaining ? r : remaining);
     for_segment([&](int i, uint32_t key) {
         const bool eq = !all && key == kth;
         const bool in = all || key > kth || (eq && r < remaining);
         r += eq ? 1u : 0u;
-        if (in && o < (uint32_t)k_eff) {
-            int32_t pj;
-            if constexpr (in_lds) pj = s_pos[i];
-            else pj = cpos[i];
-            sel[(int64_t)u * top_k + o] = pj;
-        }
+        if (in && o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = cpos[i];
         o += in ? 1u : 0u;
     });
     if (tid == 0) sel_n[u] = k_eff;
 }
 
-// writes an empty selection (retrieval zone empty)
 __global__ void empty_select_kernel(int units, int32_t* sel_n, int32_t* meta) {
     const int u = blockIdx.x * blockDim.x + threadIdx.x;
     if (u < units) {
@@ -709,16 +694,17 @@ hipError_t probe_kernel_image() {
 
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, int64_t sstride, uint16_t* hist, int hstride, int nbins,
-                       hipStream_t st) {
-    if (nbins < 1 || nbins > kMaxBins) return hipErrorInvalidValue;
+                       uint16_t* scores, int64_t sstride, uint16_t* hist, int hstride,
+                       uint32_t* tot, int nbins, hipStream_t st) {
+    if (nbins < 1 || nbins > kMaxBins || hstride < nbins || n_chunks > max_chunks)
+        return hipErrorInvalidValue;
     const dim3 grid(n_chunks, units), blk(kBlock);
     // the histogram is the only dynamic LDS: small vote tables keep the
     // block small enough for eight resident blocks per CU
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
 #define PK_SCAN(K)                                                                         \
     return launch(scan_kernel<K>, grid, blk, hist_bytes, st, ids, cap, sink_end, n_r,        \
-                  max_chunks, lut, scores, sstride, hist, hstride, nbins)
+                  max_chunks, lut, scores, sstride, hist, hstride, tot, nbins)
     switch (chunk / kBlock) {
         case 1: PK_SCAN(1);
         case 2: PK_SCAN(2);
@@ -731,23 +717,21 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
 #undef PK_SCAN
 }
 
-hipError_t launch_select(const uint16_t* hist, int hstride, int max_chunks, int n_chunks,
-                         int units, int nbins, int64_t C, int top_k, int32_t* off, int32_t* meta,
-                         hipStream_t st) {
-    if (n_chunks < 1 || n_chunks > kMaxChunks || hstride > kSelLds) return hipErrorInvalidValue;
-    return launch(select_kernel, dim3(units), dim3(kSBlock), 0, st, hist, hstride, max_chunks,
-                  n_chunks, nbins, C, top_k, off, meta);
-}
-
 hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, const uint8_t* rec,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
-                         int max_chunks, const int32_t* off, const int32_t* meta,
-                         const float* ysum, const CodeTables& tab, int32_t* cand_pos,
-                         float* cand_est, int64_t cmax, hipStream_t st) {
+                         int max_chunks, const uint16_t* hist, int hstride, const uint32_t* tot,
+                         int nbins, int64_t C, int top_k, const float* ysum,
+                         const CodeTables& tab, int32_t* cand_pos, float* cand_est, int64_t cmax,
+                         int32_t* meta, hipStream_t st) {
+    if (nbins < 1 || nbins > kMaxBins || hstride < nbins || n_chunks > max_chunks || C < 1 ||
+        C > n_r)
+        return hipErrorInvalidValue;
     const dim3 grid(n_chunks, units), blk(kBlock);
-#define PK_RERANK(K)                                                                        \
-    return launch(rerank_kernel<K>, grid, blk, 0, st, scores, sstride, rec, cap, sink_end, n_r, \
-                  max_chunks, off, meta, ysum, tab, cand_pos, cand_est, cmax)
+    const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
+#define PK_RERANK(K)                                                                          \
+    return launch(rerank_kernel<K>, grid, blk, hist_bytes, st, scores, sstride, rec, cap,       \
+                  sink_end, n_r, max_chunks, hist, hstride, tot, nbins, C, top_k, ysum, tab,    \
+                  cand_pos, cand_est, cmax, meta)
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1);
         case 2: PK_RERANK(2);
@@ -762,19 +746,22 @@ hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, con
 
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
                        int C, int top_k, int32_t* sel, int32_t* sel_n, hipStream_t st) {
-    // the segment length covers C in LDS up to kFineLds candidates; beyond that
-    // the keys are read from memory
+    // registers hold up to 16 candidates per thread; rows must be padded to
+    // 16 entries for the register variants' vector loads
+    if (C < 1 || C > cmax) return hipErrorInvalidValue;
     const dim3 grid(units), blk(kFBlock);
-    if (C <= 4 * kFBlock)
-        return launch(fine_kernel<4, true>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
-                      sel, sel_n);
-    if (C <= 8 * kFBlock)
-        return launch(fine_kernel<8, true>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
-                      sel, sel_n);
-    if (C <= kFineLds)
-        return launch(fine_kernel<kFineLds / kFBlock, true>, grid, blk, 0, st, cand_pos, cand_est,
-                      cmax, C, top_k, sel, sel_n);
-    return launch(fine_kernel<1, false>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
+    if (cmax % 16 == 0) {
+        if (C <= 4 * kFBlock)
+            return launch(fine_reg_kernel<4>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
+                          sel, sel_n);
+        if (C <= 8 * kFBlock)
+            return launch(fine_reg_kernel<8>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
+                          sel, sel_n);
+        if (C <= kFineReg)
+            return launch(fine_reg_kernel<16>, grid, blk, 0, st, cand_pos, cand_est, cmax, C,
+                          top_k, sel, sel_n);
+    }
+    return launch(fine_mem_kernel, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
                   sel_n);
 }
 

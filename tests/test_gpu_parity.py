@@ -322,10 +322,11 @@ def test_profiling_counts_launches():
         pkv.step(q)
     prof = pkv.profile_read()
     pkv.profile(False)
-    for stage, n in (("encode", 1), ("qprep", 3), ("scan", 3), ("select", 3), ("rerank", 3),
+    for stage, n in (("encode", 1), ("qprep", 3), ("scan", 3), ("rerank", 3),
                      ("fine", 3), ("attend", 3), ("combine", 3)):
         assert prof[stage][1] == n, (stage, prof[stage])
         assert prof[stage][0] > 0
+    assert prof["select"][1] == 0    # the coarse threshold is found inside the rerank launch
 
 
 def test_deterministic():
