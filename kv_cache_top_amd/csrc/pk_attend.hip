@@ -119,14 +119,17 @@ __global__ __launch_bounds__(kBlock) void attend_kernel(
         for (int h = 0; h < 2; ++h) {
             const T* kr = (RING && hot_k[h] ? rk : K) + row_k[h] * kD + 8 * grp;
 #pragma unroll
-            for (int st = 0; st < 4; ++st) kb[h][st] = *reinterpret_cast<const uint4*>(kr + 32 * st);
+            for (int st = 0; st < 4; ++st)
+                kb[h][st] = load_nt(reinterpret_cast<const uint4*>(kr + 32 * st));
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) kv[j].load((RING && hot_v[j] ? rk : K) + row_v[j] * kD + 8 * l16);
+        for (int j = 0; j < kPer; ++j)
+            kv[j].load_stream((RING && hot_v[j] ? rk : K) + row_v[j] * kD + 8 * l16);
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) vv[j].load((RING && hot_v[j] ? rv : V) + row_v[j] * kD + 8 * l16);
+    for (int j = 0; j < kPer; ++j)
+        vv[j].load_stream((RING && hot_v[j] ? rv : V) + row_v[j] * kD + 8 * l16);
 
     // scores / sqrt(d) into s_p[head][key]
     if constexpr (kMfma) {

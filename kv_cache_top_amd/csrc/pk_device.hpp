@@ -47,10 +47,21 @@ __device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
 
 // 8 consecutive elements kept in their storage type until used (bf16 rows
 // take 4 VGPRs instead of 8).
+// 16-byte load marked nontemporal (streamed once: keeps the cache for data
+// that is read again)
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 template <typename T> struct Raw8;
 template <> struct Raw8<uint16_t> {
     uint4 a;
     __device__ __forceinline__ void load(const uint16_t* p) { a = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void load_stream(const uint16_t* p) {
+        a = load_nt(reinterpret_cast<const uint4*>(p));
+    }
     __device__ __forceinline__ float operator[](int i) const {
         const uint32_t w = (i >> 1) == 0 ? a.x : (i >> 1) == 1 ? a.y : (i >> 1) == 2 ? a.z : a.w;
         return bf16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xffffu));
@@ -61,6 +72,12 @@ template <> struct Raw8<float> {
     __device__ __forceinline__ void load(const float* p) {
         a = *reinterpret_cast<const float4*>(p);
         b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void load_stream(const float* p) {
+        const uint4 x = load_nt(reinterpret_cast<const uint4*>(p));
+        const uint4 y = load_nt(reinterpret_cast<const uint4*>(p + 4));
+        a = make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+        b = make_float4(__uint_as_float(y.x), __uint_as_float(y.y), __uint_as_float(y.z), __uint_as_float(y.w));
     }
     __device__ __forceinline__ float operator[](int i) const {
         return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : i == 3 ? a.w

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int64_t i = start + j * kBlock + tid;
-        v[j] = idrow[i < n_r ? i : n_r - 1];
+        v[j] = load_nt(idrow + (i < n_r ? i : n_r - 1));
     }
     reinterpret_cast<uint4*>(s_lut)[tid] = lut_part;
     for (int b = tid; b < nbins; b += kBlock) s_hist[b] = 0;
