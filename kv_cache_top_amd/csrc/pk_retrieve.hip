@@ -57,13 +57,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     // histogram: scores 0..7, which most keys have, go to eight byte counters
     // per thread (at most KPT <= 32 keys each, no overflow), summed over the
     // wave at the end; larger scores go to LDS atomics
+    // The scores are stored only after every key is scored: vector memory
+    // counters cover loads and stores alike, so a store issued before the
+    // wait for a later key's row would make that wait cover the store too.
     uint64_t c8 = 0;
-    uint16_t* srow = scores + u * sstride;
-    const bool full = start + chunk <= n_r;   // no tail in this chunk
+    const int nval = (int)(n_r - start < chunk ? n_r - start : chunk);   // valid keys of the chunk
+    uint32_t scv[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        const int64_t i = start + j * kBlock + tid;
-        const bool valid = full || i < n_r;
+        const bool valid = j * kBlock + tid < nval;
         const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint32_t sc = 0;
 #pragma unroll
@@ -71,9 +73,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
 #pragma unroll
             for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((w[a] >> (8 * k)) & 255u)];
         }
-        if (valid) srow[i] = (uint16_t)sc;
+        scv[j] = sc;
         c8 += (valid && sc < 8u) ? (1ull << (sc << 3)) : 0ull;
         if (valid && sc >= 8u) atomicAdd(&s_hist[sc], 1u);
+    }
+    uint16_t* srow = scores + u * sstride + start + tid;
+    if (nval == chunk) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) srow[j * kBlock] = (uint16_t)scv[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (j * kBlock + tid < nval) srow[j * kBlock] = (uint16_t)scv[j];
     }
     {
         // bytes 0..7 of c8 = counts of scores 0..7; widen to 16-bit fields
@@ -244,12 +255,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     lds_sync();
     const int T = (int)s_T;
     const uint32_t need = s_need;
-    if (ch == 0 && tid == 0) {
-        meta[u * 4 + 0] = T;
-        meta[u * 4 + 1] = (int32_t)need;
-        meta[u * 4 + 2] = (int32_t)C;
-        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
-    }
     // keys above T and ties at T in the chunks before this one
     uint32_t gtb = 0, eqb = 0;
     for (int c = tid; c < ch; c += kBlock) {
@@ -355,6 +360,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
                 uest[o] = e * inv_sqrt_d;
             }
         }
+    }
+    // (stored last: a store ahead of a load's wait would be waited for too)
+    if (ch == 0 && tid == 0) {
+        meta[u * 4 + 0] = T;
+        meta[u * 4 + 1] = (int32_t)need;
+        meta[u * 4 + 2] = (int32_t)C;
+        meta[u * 4 + 3] = (int32_t)(C < top_k ? C : top_k);
     }
 }
 
