@@ -183,6 +183,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     const uint32_t* ut = tot + (int64_t)u * ((nbins + 1) & ~1);
     const uint32_t t0 = tid < nbins ? ut[tid] : 0u;
     const uint32_t t1 = tid + kBlock < nbins ? ut[tid + kBlock] : 0u;
+    // the first W suffix counts of the earlier chunks (up to 64 of them) come
+    // with the first loads: thread 4c + q holds entries 8q .. 8q+7 of chunk c.
+    // Rows are hstride (a multiple of 8) entries long.
+    const int W = hstride < 32 ? hstride : 32;
+    const int pc = tid >> 2, pq = tid & 3;
+    const bool pre_ok = pc < ch && 8 * pq < W;
+    uint4 pre = make_uint4(0u, 0u, 0u, 0u);
+    if (pre_ok)
+        pre = *reinterpret_cast<const uint4*>(hist + ((int64_t)u * max_chunks + pc) * hstride + 8 * pq);
     const int64_t start = (int64_t)ch * chunk;
     uint32_t s[KPT];
     {
@@ -219,49 +228,68 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     for (int b = tid + 2 * kBlock; b < nbins; b += kBlock) s_ut[b] = ut[b];
     lds_sync();
 
-    // wave 0: T and need from the unit histogram; lane l owns the bins ranked
-    // l*per .. l*per+per-1 in descending score order (ge is non-increasing, so
-    // T + 1 = number of scores s with ge[s] >= C)
+    // T and need from the unit histogram: thread t owns the bins ranked
+    // t*per .. t*per+per-1 in descending score order; ge[s] = #{score >= s} is
+    // non-increasing in s, and the one bin where it reaches C is T
     const int lane = tid & 63, wave = tid >> 6;
     __shared__ uint32_t s_T, s_need;
     __shared__ uint32_t s_red[3 * kBlock / 64];
-    if (wave == 0) {
-        const int per = (nbins + 63) / 64;
+    if (tid == 0) {
+        s_T = 0;
+        s_need = 0;
+    }
+    {
+        const int per = (nbins + kBlock - 1) / kBlock;
         uint32_t seg = 0;
         for (int j = 0; j < per; ++j) {
-            const int r = lane * per + j;
+            const int r = tid * per + j;
             if (r < nbins) seg += s_ut[nbins - 1 - r];
         }
-        uint32_t run = wave_incl_scan(seg) - seg;
-        uint32_t n_ge = 0, ge_next = 0;      // ge[T+1], seen by the lane that reaches C
+        const uint32_t x = wave_incl_scan(seg);
+        if (lane == 63) s_red[wave] = x;
+        lds_sync();
+        uint32_t run = x - seg;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; ++w) run += w < wave ? s_red[w] : 0u;
         for (int j = 0; j < per; ++j) {
-            const int r = lane * per + j;
+            const int r = tid * per + j;
             if (r < nbins) {
-                const uint32_t before = run;
+                const uint32_t before = run;   // ge of the next higher score
                 run += s_ut[nbins - 1 - r];
-                if ((int64_t)run >= C) {
-                    ++n_ge;
-                    if ((int64_t)before < C) ge_next = before;
+                if ((int64_t)before < C && (int64_t)run >= C) {   // C <= n_r: exactly one bin
+                    s_T = (uint32_t)(nbins - 1 - r);
+                    s_need = (uint32_t)(C - (int64_t)before);
                 }
             }
         }
-        const uint32_t T1 = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(n_ge), 63);
-        const uint32_t above = wave_max(ge_next);
-        if (lane == 0) {
-            s_T = T1 - 1;                    // C <= n_r: bin 0 always counts, T >= 0
-            s_need = (uint32_t)(C - (int64_t)above);
-        }
+        lds_sync();
     }
-    lds_sync();
-    const int T = (int)s_T;
+    const int T = (int)(s_T < (uint32_t)nbins ? s_T : (uint32_t)nbins - 1u);
     const uint32_t need = s_need;
-    // keys above T and ties at T in the chunks before this one
+    // keys above T (sfx_c[T+1]) and ties at T (sfx_c[T] - sfx_c[T+1]) in the
+    // chunks before this one: from the early entries when T + 1 is among
+    // them, else loaded now
     uint32_t gtb = 0, eqb = 0;
-    for (int c = tid; c < ch; c += kBlock) {
-        const uint16_t* row = hist + ((int64_t)u * max_chunks + c) * hstride;
-        const uint32_t g = (T >= 0 && T + 1 < nbins) ? row[T + 1] : 0u;
-        gtb += g;
-        eqb += T >= 0 ? (uint32_t)row[T] - g : 0u;
+    const int Wv = W < nbins ? W : nbins;
+    if (T + 1 < Wv && ch <= kBlock / 4) {
+        auto entry = [&](int e) -> uint32_t {   // entry e (0..7) of this thread's eight
+            const int w = e >> 1;
+            const uint32_t x = w == 0 ? pre.x : (w == 1 ? pre.y : (w == 2 ? pre.z : pre.w));
+            return (e & 1) ? (x >> 16) : (x & 0xffffu);
+        };
+        if (pre_ok && (T >> 3) == pq) eqb += entry(T & 7);
+        if (pre_ok && ((T + 1) >> 3) == pq) {
+            const uint32_t g = entry((T + 1) & 7);
+            gtb += g;
+            eqb -= g;                          // block sums wrap back to sfx[T] - sfx[T+1]
+        }
+    } else {
+        for (int c = tid; c < ch; c += kBlock) {
+            const uint16_t* row = hist + ((int64_t)u * max_chunks + c) * hstride;
+            const uint32_t g = (T >= 0 && T + 1 < nbins) ? row[T + 1] : 0u;
+            gtb += g;
+            eqb += T >= 0 ? (uint32_t)row[T] - g : 0u;
+        }
     }
 
     // this chunk's candidates, in position order: keys above T, and ties at T
