@@ -152,6 +152,13 @@ void free_all(pk_ctx* c) {
         if (p) (void)hipFree(p);
 }
 
+// attention splits: the hot tokens (at most sink + local + buffer) and the
+// selection are split separately
+int64_t max_attend_splits(const pk_config& cfg) {
+    const int64_t hot = (int64_t)cfg.n_sink + cfg.n_local + cfg.buf_tokens;
+    return ceil_div(hot, pk::attend_split_keys()) + ceil_div(cfg.top_k, pk::attend_split_keys());
+}
+
 pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capacity, int* G_out,
                           int* nbins_out) {
     if (!cfg || n_kv < 1 || n_q < 1 || capacity < 1) return PK_ERR_INVALID;
@@ -174,8 +181,7 @@ pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capac
     const int nbins = cfg->n_sub * G * wmax + 1;
     if (nbins > pk::kMaxBins) return PK_ERR_UNSUPPORTED;
     if (capacity > (int64_t)1 << 24) return PK_ERR_UNSUPPORTED;
-    const int64_t attended = (int64_t)cfg->n_sink + cfg->n_local + cfg->buf_tokens + cfg->top_k;
-    if (ceil_div(attended, pk::attend_split()) > pk::attend_max_splits()) return PK_ERR_UNSUPPORTED;
+    if (max_attend_splits(*cfg) > pk::attend_max_splits()) return PK_ERR_UNSUPPORTED;
     *G_out = G;
     *nbins_out = nbins;
     return PK_OK;
@@ -203,9 +209,21 @@ pk_status evict(pk_ctx* c, hipStream_t st) {
     return PK_OK;
 }
 
+// splits of this step's attention: n_hot_splits over the hot tokens, then
+// the selection
+void split_plan(const pk_ctx* c, int* n_splits, int* n_hot_splits) {
+    const int64_t hot = c->sink_end + (c->n - c->r_end);
+    *n_hot_splits = (int)ceil_div(hot, pk::attend_split_keys());
+    *n_splits = *n_hot_splits + (int)ceil_div(c->cfg.top_k, pk::attend_split_keys());
+}
+
 // qprep (optionally carrying the step's append), scan, rerank, fine select.
+// With fuse_hot the fine launch also computes the hot-zone attention splits
+// when it can (*hot_done tells whether it did).
 pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, const void* k_new,
-                       const void* v_new, hipStream_t st) {
+                       const void* v_new, hipStream_t st, bool fuse_hot = false,
+                       bool* hot_done = nullptr) {
+    if (hot_done) *hot_done = false;
     const bool bf16 = c->dt == PK_BF16;
     const int64_t row = (int64_t)pk::kD * dtype_size(c->dt);
     {
@@ -236,21 +254,32 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
                                  c->cand_est, c->cmax, c->meta, st));
     }
     StageTimer tm(c, PK_STAGE_FINE, st);
+    int n_splits = 0, n_hs = 0;
+    split_plan(c, &n_splits, &n_hs);
+    if (fuse_hot && n_hs > 0 && n_splits <= c->max_splits &&
+        pk::fine_hot_supported(bf16, c->G, c->ring.k != nullptr, (int)C, c->cmax)) {
+        PK_HIP(pk::launch_fine_hot(c->cand_pos, c->cand_est, c->cmax, c->units, (int)C,
+                                   c->cfg.top_k, sel, sel_n, c->G, c->K, c->V, c->cap, q,
+                                   c->sink_end, c->r_end, c->n, n_splits, n_hs, c->part, st));
+        if (hot_done) *hot_done = true;
+        return PK_OK;
+    }
     PK_HIP(pk::launch_fine(c->cand_pos, c->cand_est, c->cmax, c->units, (int)C, c->cfg.top_k, sel,
                            sel_n, st));
     return PK_OK;
 }
 
+// attention splits (those after the hot ones when hot_done), then the merge
 pk_status run_attend(pk_ctx* c, const void* q, const int32_t* sel, const int32_t* sel_n,
-                     float* out, hipStream_t st) {
-    const int64_t hot = c->sink_end + (c->n - c->r_end);
-    const int n_splits = (int)ceil_div(hot + c->cfg.top_k, pk::attend_split());
+                     float* out, hipStream_t st, bool hot_done = false) {
+    int n_splits = 0, n_hs = 0;
+    split_plan(c, &n_splits, &n_hs);
     if (n_splits > c->max_splits) return PK_ERR_INVALID;
     {
         StageTimer tm(c, PK_STAGE_ATTEND, st);
         PK_HIP(pk::launch_attend(c->dt == PK_BF16, c->G, c->K, c->V, c->cap, c->units, q,
                                  c->sink_end, c->r_end, c->n, sel, sel_n, c->cfg.top_k, n_splits,
-                                 c->part, c->ring, st));
+                                 n_hs, hot_done ? n_hs : 0, c->part, c->ring, st));
     }
     StageTimer tm(c, PK_STAGE_COMBINE, st);
     PK_HIP(pk::launch_combine(c->part, c->units, c->G, n_splits, out, st));
@@ -321,8 +350,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     // them in 16-byte vectors
     c->cmax = (std::max<int64_t>(1, coarse_count(capacity, cfg->coarse_permille, cfg->top_k)) + 15) /
               16 * 16;
-    c->max_splits = (int)ceil_div((int64_t)cfg->n_sink + cfg->n_local + cfg->buf_tokens + cfg->top_k,
-                                  pk::attend_split());
+    c->max_splits = (int)max_attend_splits(*cfg);
 
     const int64_t U = c->units;
     struct Alloc {
@@ -462,9 +490,10 @@ pk_status pk_decode_step(pk_ctx* c, const void* k_new, const void* v_new, const 
     // the query-prep kernel copies the new token to position n (the old count)
     c->n += 1;
     c->buf += 1;
-    pk_status s = run_retrieve(c, q, sel, sel_n, k_new, v_new, st);
+    bool hot_done = false;
+    pk_status s = run_retrieve(c, q, sel, sel_n, k_new, v_new, st, true, &hot_done);
     if (s != PK_OK) return s;
-    return run_attend(c, q, sel, sel_n, out, st);
+    return run_attend(c, q, sel, sel_n, out, st, hot_done);
 }
 
 pk_status pk_profile_enable(pk_ctx* c, int32_t on) {

@@ -1,0 +1,319 @@
+// One split of the sparse GQA decode attention (gfx950), as a device
+// function: the attention kernel runs one split per 256-thread block, and the
+// fused fine-selection kernel runs hot-zone splits on blocks of 1024 threads
+// next to its selection blocks.
+//
+// ParisKV page, "Problem definition": decoding attends only a top-k subset of
+// past tokens; "Sliding-window update mechanism": sink, local and buffer
+// tokens are always at hand; "UVA offloading": the retrieved rows may be read
+// directly from host memory by the kernel.
+//
+// Split-K over the attended list of a unit: the hot tokens (sink, then the
+// local window with the update buffer) in ceil(n_hot / kSplit) splits, then
+// the selected positions in ceil(top_k / kSplit) splits; kSplit = 128 keys.
+// A 16-lane group handles one key row at a time (8 coordinates per lane); the
+// G query heads of the group share every K and V row read.  Each split writes
+// its partial (max, sum, unnormalised output) per query head; a second kernel
+// merges the splits of each unit.
+#pragma once
+
+#include "pk_device.hpp"
+#include "pk_launch.hpp"
+
+namespace pk {
+
+constexpr int kSplit = 128;
+constexpr int kMaxSplits = 1024;
+constexpr int kAttThreads = 256;   // threads of one split
+static_assert(kSplit % 64 == 0, "softmax statistics take 64 keys per wave pass");
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct AttendArgs {
+    const T* K;                 // [units][cap][d] stores
+    const T* V;
+    int64_t cap;
+    const T* q;                 // [units][G][d]
+    int64_t sink_end, r_end, n_tok;
+    const int32_t* sel;         // [units][top_k]
+    const int32_t* sel_n;       // [units]
+    int top_k;
+    int n_splits, n_hot_splits; // splits per unit; the first n_hot_splits cover the hot tokens
+    float* part;                // [units][n_splits][G][2 + d]
+    const T* rk;                // device ring of the hot rows (host-memory stores), else null
+    const T* rv;
+    int64_t ring_rows, ring_sink, ring_span, ring_base;
+};
+
+// kernel arguments of the splits of one attention pass
+template <typename T>
+inline AttendArgs<T> attend_args(const void* K, const void* V, int64_t cap, const void* q,
+                          int64_t sink_end, int64_t r_end, int64_t n_tok, const int32_t* sel,
+                          const int32_t* sel_n, int top_k, int n_splits, int n_hot_splits,
+                          float* part, const HotRing& ring) {
+    AttendArgs<T> a;
+    a.K = (const T*)K;
+    a.V = (const T*)V;
+    a.cap = cap;
+    a.q = (const T*)q;
+    a.sink_end = sink_end;
+    a.r_end = r_end;
+    a.n_tok = n_tok;
+    a.sel = sel;
+    a.sel_n = sel_n;
+    a.top_k = top_k;
+    a.n_splits = n_splits;
+    a.n_hot_splits = n_hot_splits;
+    a.part = part;
+    a.rk = (const T*)ring.k;
+    a.rv = (const T*)ring.v;
+    a.ring_rows = ring.rows;
+    a.ring_sink = ring.n_sink;
+    a.ring_span = ring.span;
+    a.ring_base = r_end % ring.span;
+    return a;
+}
+template <int G>
+struct AttendLds {
+    float p[G][kSplit];
+    float red[kAttThreads / 64][G][kD];
+    float m[G], l[G];
+};
+
+// Split sp of unit u, computed by the 256 threads t = 0..255 of a group of four
+// waves.  It holds kSplitBarriers block-wide barriers: in a block of several
+// groups every group calls it, or attend_split_idle, which passes the same
+// barriers and does nothing else.  An inactive group runs the same steps on
+// masked keys and writes nothing.
+constexpr int kSplitBarriers = 3;
+__device__ __forceinline__ void attend_split_idle() {
+#pragma unroll
+    for (int i = 0; i < kSplitBarriers; ++i) lds_sync();
+}
+
+template <typename T, int G, bool RING>
+__device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int sp, int t,
+                                             bool active, AttendLds<G>& L) {
+    const int lane = t & 63, wave = t >> 6, grp = lane >> 4, l16 = lane & 15;
+    constexpr bool kMfma = sizeof(T) == 2;   // bf16: q k^T on the matrix cores
+    constexpr int kPer = kSplit / (kAttThreads / 16);   // keys per 16-lane group
+    static_assert(kSplit == 32 * (kAttThreads / 64), "a wave owns 32 keys of the split");
+    static_assert(!kMfma || G <= 8, "query heads fill MFMA rows 0..G-1 of 16");
+    constexpr float kInvSqrtD = 0.08838834764831845f;
+    const T* __restrict__ K = a.K;
+    const T* __restrict__ V = a.V;
+    const T* __restrict__ q = a.q;
+    const T* __restrict__ rk = a.rk;
+    const T* __restrict__ rv = a.rv;
+    const int64_t cap = a.cap, sink_end = a.sink_end, r_end = a.r_end, n_tok = a.n_tok;
+    const int64_t ring_rows = a.ring_rows, ring_sink = a.ring_sink, ring_span = a.ring_span,
+                  ring_base = a.ring_base;
+    const int top_k = a.top_k;
+
+    // Wave w owns keys [32w, 32w + 32) of the split.  Values: the 16-lane
+    // group grp handles keys 32w + grp + 4j (j < 8), 8 coordinates per lane.
+    // Keys (bf16): MFMA tiles of 16 keys, lane l16 loading key 32w + 16h + l16.
+    // Hot splits read neither sel nor sel_n (the fused kernel computes them
+    // at the same time).
+    const int64_t n_hot = sink_end + (n_tok - r_end);
+    const bool hot_split = sp < a.n_hot_splits;
+    int64_t i0, end;
+    if (hot_split) {
+        i0 = (int64_t)sp * kSplit;
+        end = n_hot;
+    } else {
+        int nsel = a.sel_n[u];
+        nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
+        i0 = n_hot + (int64_t)(sp - a.n_hot_splits) * kSplit;
+        end = n_hot + nsel;
+    }
+    const int nk = active ? (int)((end - i0) < kSplit ? (end - i0 > 0 ? end - i0 : 0) : kSplit) : 0;
+    auto sel_at = [&](int kk) -> int32_t {
+        if (hot_split) return 0;
+        const int64_t i = i0 + kk - n_hot;
+        return a.sel[(int64_t)u * top_k + (i < 0 ? 0 : (i < top_k ? i : top_k - 1))];
+    };
+    int32_t cand_v[kPer], cand_k[2];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cand_v[j] = sel_at(32 * wave + grp + 4 * j);
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) cand_k[h] = sel_at(32 * wave + 16 * h + l16);
+    }
+    // query operand.  bf16: A rows = heads (rows >= G zero), lane l holds head
+    // l16's dims 32s + 8 grp .. +8 of step s.  fp32: this lane's 8 dims of every head.
+    uint4 qa[4];
+    Raw8<T> qv[kMfma ? 1 : G];
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            qa[st] = (l16 < G) ? *reinterpret_cast<const uint4*>(
+                                     q + ((int64_t)u * G + l16) * kD + 32 * st + 8 * grp)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) qv[g].load(q + ((int64_t)u * G + g) * kD + 8 * l16);
+    }
+
+    // row of attended key kk: from the device ring for the hot zone when the
+    // store is host memory, else from the store
+    auto place = [&](int kk, int32_t c, bool& ok, bool& hot) -> int64_t {
+        const int64_t i = i0 + kk;
+        const int64_t p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end)) : (int64_t)c;
+        ok = kk < nk && p >= 0 && p < n_tok;
+        if constexpr (!RING) {
+            hot = false;
+            return (int64_t)u * cap + (ok ? p : 0);
+        }
+        if (!ok) {                          // masked: any valid row, on the device
+            hot = true;
+            return (int64_t)u * ring_rows;
+        }
+        hot = i < n_hot;
+        if (hot) {
+            if (i < sink_end) return (int64_t)u * ring_rows + i;
+            int64_t s = ring_base + (i - sink_end);
+            s = s >= ring_span ? s - ring_span : s;
+            return (int64_t)u * ring_rows + ring_sink + s;
+        }
+        return (int64_t)u * cap + p;
+    };
+    bool ok_v[kPer], ok_k[2], hot_v[kPer], hot_k[2];
+    int64_t row_v[kPer], row_k[2];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        row_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], ok_v[j], hot_v[j]);
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            row_k[h] = place(32 * wave + 16 * h + l16, cand_k[h], ok_k[h], hot_k[h]);
+    }
+    // every K and V row is requested before any is used
+    uint4 kb[2][4];
+    Raw8<T> kv[kMfma ? 1 : kPer], vv[kPer];
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const T* kr = (RING && hot_k[h] ? rk : K) + row_k[h] * kD + 8 * grp;
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                kb[h][st] = load_nt(reinterpret_cast<const uint4*>(kr + 32 * st));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            kv[j].load_stream((RING && hot_v[j] ? rk : K) + row_v[j] * kD + 8 * l16);
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+        vv[j].load_stream((RING && hot_v[j] ? rv : V) + row_v[j] * kD + 8 * l16);
+
+    // scores / sqrt(d) into L.p[head][key]
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                            __builtin_bit_cast(bf16x8_t, kb[h][st]),
+                                                            c, 0, 0, 0);
+            // lane holds rows (heads) 4 grp + i of column (key) l16
+            const int kk = 32 * wave + 16 * h + l16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int g = 4 * grp + i;
+                if (g < G) L.p[g][kk] = ok_k[h] ? c[i] * kInvSqrtD : -INFINITY;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int kk = 32 * wave + grp + 4 * j;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float d = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) d = fmaf(qv[g][r], kv[j][r], d);
+                d = sum16(d) * kInvSqrtD;
+                if (l16 == 0) L.p[g][kk] = ok_v[j] ? d : -INFINITY;
+            }
+        }
+    }
+    lds_sync();
+    // softmax statistics of the split, one wave per head (strided)
+    constexpr int kSlots = kSplit / 64;   // scores per lane
+    for (int g = wave; g < G; g += kAttThreads / 64) {
+        float sv[kSlots];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            const int kk = lane + 64 * k;
+            sv[k] = (kk < nk) ? L.p[g][kk] : -INFINITY;
+            mx = fmaxf(mx, sv[k]);
+        }
+        const float m = wave_max_f(mx);
+        float es = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kSlots; ++k) {
+            const int kk = lane + 64 * k;
+            const float e = (kk < nk && m != -INFINITY) ? __expf(sv[k] - m) : 0.0f;
+            if (kk < nk) L.p[g][kk] = e;
+            es += e;
+        }
+        const float l = wave_sum_f(es);
+        if (lane == 0) {
+            L.m[g] = m;
+            L.l[g] = l;
+        }
+    }
+    lds_sync();
+    // weighted values
+    float acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[g][r] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int kk = 32 * wave + grp + 4 * j;
+        if (kk < nk) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float pg = L.p[g][kk];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[g][r] = fmaf(pg, vv[j][r], acc[g][r]);
+            }
+        }
+    }
+    // sum over the four 16-lane groups of the wave (lane exchanges across rows)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[g][r] = sum_rows4(acc[g][r]);
+    if (grp == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int r = 0; r < 8; ++r) L.red[wave][g][8 * l16 + r] = acc[g][r];
+    }
+    lds_sync();
+    // partial record per (unit, split, head): [m, l, o[128]]
+    if (!active) return;
+    float* myp = a.part + ((int64_t)u * a.n_splits + sp) * G * (kD + 2);
+    for (int i = t; i < G * kD; i += kAttThreads) {
+        const int g = i / kD, d = i - g * kD;
+        float o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kAttThreads / 64; ++w) o += L.red[w][g][d];
+        myp[g * (kD + 2) + 2 + d] = o;
+    }
+    if (t < G) {
+        myp[t * (kD + 2)] = L.m[t];
+        myp[t * (kD + 2) + 1] = L.l[t];
+    }
+}
+
+}  // namespace pk

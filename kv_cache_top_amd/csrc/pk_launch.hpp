@@ -93,13 +93,23 @@ hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t c
 hipError_t launch_empty_select(int units, int32_t* sel_n, int32_t* meta, hipStream_t st);
 // hipSuccess when the current device can run this library's code object
 hipError_t probe_kernel_image();
-int attend_split();
+int attend_split_keys();   // keys per attention split
 int attend_max_splits();
-// split-K attention (partials per split), then the merge of the splits into out
+// split-K attention (partials per split) over splits sp0 .. n_splits-1; the
+// first n_hot_splits splits cover the hot tokens, the rest the selection
 hipError_t launch_attend(bool bf16, int G, const void* K, const void* V, int64_t cap, int units,
                          const void* q, int64_t sink_end, int64_t r_end, int64_t n_tok,
                          const int32_t* sel, const int32_t* sel_n, int top_k, int n_splits,
-                         float* part, const HotRing& ring, hipStream_t st);
+                         int n_hot_splits, int sp0, float* part, const HotRing& ring,
+                         hipStream_t st);
+// fine selection plus the hot-zone attention splits in one launch (bf16
+// device stores, G <= 4, C <= 16384 register-held candidates)
+bool fine_hot_supported(bool bf16, int G, bool ring, int C, int64_t cmax);
+hipError_t launch_fine_hot(const int32_t* cand_pos, const float* cand_est, int64_t cmax,
+                           int units, int C, int top_k, int32_t* sel, int32_t* sel_n, int G,
+                           const void* K, const void* V, int64_t cap, const void* q,
+                           int64_t sink_end, int64_t r_end, int64_t n_tok, int n_splits,
+                           int n_hot_splits, float* part, hipStream_t st);
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st);
 
