@@ -17,6 +17,8 @@
 // merges the splits of each unit.
 #pragma once
 
+#include <type_traits>
+
 #include "pk_device.hpp"
 #include "pk_launch.hpp"
 
@@ -76,7 +78,7 @@ inline AttendArgs<T> attend_args(const void* K, const void* V, int64_t cap, cons
     return a;
 }
 template <int G>
-struct AttendLds {
+struct alignas(16) AttendLds {
     float p[G][kSplit];
     float red[kAttThreads / 64][G][kD];
     float m[G], l[G];
@@ -112,9 +114,11 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
                   ring_base = a.ring_base;
     const int top_k = a.top_k;
 
-    // Wave w owns keys [32w, 32w + 32) of the split.  Values: the 16-lane
-    // group grp handles keys 32w + grp + 4j (j < 8), 8 coordinates per lane.
-    // Keys (bf16): MFMA tiles of 16 keys, lane l16 loading key 32w + 16h + l16.
+    // Wave w owns keys [32w, 32w + 32) of the split.  Values: the wave reads
+    // each of its 32 rows whole, lane l taking coordinates 2l and 2l + 1.
+    // Keys (bf16): MFMA tiles of 16 keys, lane l16 loading key 32w + 16h + l16;
+    // (fp32): the 16-lane group grp handles keys 32w + grp + 4j (j < 8), 8
+    // coordinates per lane.
     // Hot splits read neither sel nor sel_n (the fused kernel computes them
     // at the same time).
     const int64_t n_hot = sink_end + (n_tok - r_end);
@@ -135,12 +139,16 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
         const int64_t i = i0 + kk - n_hot;
         return a.sel[(int64_t)u * top_k + (i < 0 ? 0 : (i < top_k ? i : top_k - 1))];
     };
-    int32_t cand_v[kPer], cand_k[2];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) cand_v[j] = sel_at(32 * wave + grp + 4 * j);
+    constexpr int kPerK = kMfma ? 1 : kPer;
+    int32_t cand_v[kPerK], cand_k[2];
+    const int kl = lane & 31;
+    const int32_t cand_r = sel_at(32 * wave + kl);
     if constexpr (kMfma) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) cand_k[h] = sel_at(32 * wave + 16 * h + l16);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) cand_v[j] = sel_at(32 * wave + grp + 4 * j);
     }
     // query operand.  bf16: A rows = heads (rows >= G zero), lane l holds head
     // l16's dims 32s + 8 grp .. +8 of step s.  fp32: this lane's 8 dims of every head.
@@ -180,19 +188,21 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
         }
         return (int64_t)u * cap + p;
     };
-    bool ok_v[kPer], ok_k[2], hot_v[kPer], hot_k[2];
-    int64_t row_v[kPer], row_k[2];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-        row_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], ok_v[j], hot_v[j]);
+    bool ok_v[kPerK], ok_k[2], hot_v[kPerK], hot_k[2], ok_r, hot_r;
+    int64_t row_v[kPerK], row_k[2];
+    const int64_t row_r = place(32 * wave + kl, cand_r, ok_r, hot_r);
     if constexpr (kMfma) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             row_k[h] = place(32 * wave + 16 * h + l16, cand_k[h], ok_k[h], hot_k[h]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            row_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], ok_v[j], hot_v[j]);
     }
     // every K and V row is requested before any is used
     uint4 kb[2][4];
-    Raw8<T> kv[kMfma ? 1 : kPer], vv[kPer];
+    Raw8<T> kv[kPerK];
     if constexpr (kMfma) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -206,9 +216,21 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
         for (int j = 0; j < kPer; ++j)
             kv[j].load_stream((RING && hot_v[j] ? rk : K) + row_v[j] * kD + 8 * l16);
     }
+    // value rows: key 32w + k is placed by lane k; its row address is uniform
+    // across the wave
+    typedef uint32_t VPairBf16;                                   // two bf16
+    typedef float VPairF32 __attribute__((ext_vector_type(2)));   // two fp32
+    using VPair = std::conditional_t<kMfma, VPairBf16, VPairF32>;
+    VPair vw[32];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j)
-        vv[j].load_stream((RING && hot_v[j] ? rv : V) + row_v[j] * kD + 8 * l16);
+    for (int k = 0; k < 32; ++k) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)row_r, k);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(row_r >> 32), k);
+        const int64_t r = (int64_t)(((uint64_t)hi << 32) | lo);
+        const bool hk = RING && __builtin_amdgcn_readlane((int)hot_r, k) != 0;
+        const VPair* vr = reinterpret_cast<const VPair*>((hk ? rv : V) + r * kD);
+        vw[k] = __builtin_nontemporal_load(vr + lane);
+    }
 
     // scores / sqrt(d) into L.p[head][key]
     if constexpr (kMfma) {
@@ -260,7 +282,7 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
         for (int k = 0; k < kSlots; ++k) {
             const int kk = lane + 64 * k;
             const float e = (kk < nk && m != -INFINITY) ? __expf(sv[k] - m) : 0.0f;
-            if (kk < nk) L.p[g][kk] = e;
+            L.p[g][kk] = e;                    // 0 for the masked keys
             es += e;
         }
         const float l = wave_sum_f(es);
@@ -270,35 +292,38 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
         }
     }
     lds_sync();
-    // weighted values
-    float acc[G][8];
+    // weighted values: lane l accumulates coordinates 2l, 2l + 1 over the
+    // wave's 32 keys, reading the weights of four keys at a time
+    float acc[G][2];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) acc[g][r] = 0.0f;
+    for (int k4 = 0; k4 < 8; ++k4) {
+        float4 pg[G];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int kk = 32 * wave + grp + 4 * j;
-        if (kk < nk) {
+        for (int g = 0; g < G; ++g) pg[g] = *reinterpret_cast<const float4*>(&L.p[g][32 * wave + 4 * k4]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            float v0, v1;
+            if constexpr (kMfma) {
+                const uint32_t x = vw[4 * k4 + kk];
+                v0 = __uint_as_float(x << 16);
+                v1 = __uint_as_float(x & 0xffff0000u);
+            } else {
+                v0 = vw[4 * k4 + kk].x;
+                v1 = vw[4 * k4 + kk].y;
+            }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float pg = L.p[g][kk];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) acc[g][r] = fmaf(pg, vv[j][r], acc[g][r]);
+                const float p = kk == 0 ? pg[g].x : (kk == 1 ? pg[g].y : (kk == 2 ? pg[g].z : pg[g].w));
+                acc[g][0] = fmaf(p, v0, acc[g][0]);
+                acc[g][1] = fmaf(p, v1, acc[g][1]);
             }
         }
     }
-    // sum over the four 16-lane groups of the wave (lane exchanges across rows)
 #pragma unroll
     for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) acc[g][r] = sum_rows4(acc[g][r]);
-    if (grp == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int r = 0; r < 8; ++r) L.red[wave][g][8 * l16 + r] = acc[g][r];
-    }
+        *reinterpret_cast<float2*>(&L.red[wave][g][2 * lane]) = make_float2(acc[g][0], acc[g][1]);
     lds_sync();
     // partial record per (unit, split, head): [m, l, o[128]]
     if (!active) return;
