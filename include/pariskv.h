@@ -175,7 +175,7 @@ pk_status pk_profile_read(pk_ctx* ctx, double* ms, int64_t* launches);
  *   PK_DBG_IDS     uint8  [units][cap][B]           bucket ids
  *   PK_DBG_REC     uint8  [units][cap][128]         64 B nibbles (coord 2i in low half of byte i) + float32 w[B]
  *   PK_DBG_LUT     uint8  [units][B][256]           vote table of the last pk_retrieve
- *   PK_DBG_SCORES  uint16 [units][cap]              coarse score of retrieval position sink_end + i
+ *   PK_DBG_SCORES  uint8  [units][cap]              min(coarse score, 255) of retrieval position sink_end + i
  *   PK_DBG_CAND    int32  [units][cmax]             candidate positions (ascending), first n_cand valid
  *   PK_DBG_EST     float  [units][cmax]             RSQ-IP estimate of each candidate
  *   PK_DBG_NCAND   int32  [units][4]                {threshold score, ties taken, n_cand, k_eff}  */

@@ -35,7 +35,7 @@ struct pk_ctx {
     uint8_t* rec = nullptr;       // [units][cap][128]  nibbles + w
     uint8_t* lut = nullptr;       // [units][16][256]   vote table
     float* ysum = nullptr;        // [units][128]       sum of rotated queries
-    uint16_t* scores = nullptr;   // [units][sstride] + pad   coarse scores (retrieval offset)
+    uint8_t* scores = nullptr;    // [units][sstride] + pad   min(coarse score, 255) (retrieval offset)
     uint16_t* hist = nullptr;     // [units][max_chunks][hstride] per-chunk #{score >= s}
     uint32_t* tot = nullptr;      // [units][nbins rounded up to even]  unit score histogram
     int32_t* meta = nullptr;      // [units][4]          {T, ties taken, C, k_eff}
@@ -248,7 +248,8 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     }
     {
         StageTimer tm(c, PK_STAGE_RERANK, st);
-        PK_HIP(pk::launch_rerank(chunk, c->scores, c->sstride, c->rec, c->cap, c->units,
+        PK_HIP(pk::launch_rerank(chunk, c->scores, c->sstride, c->rec, c->ids, c->lut, c->cap,
+                                 c->units,
                                  c->sink_end, n_r, n_chunks, c->max_chunks, c->hist, c->hstride,
                                  c->tot, c->nbins, C, c->cfg.top_k, c->ysum, c->tab, c->cand_pos,
                                  c->cand_est, c->cmax, c->meta, st));
@@ -362,7 +363,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         {(void**)&c->lut, (size_t)(U * pk::kSub * 256)},
         {(void**)&c->ysum, (size_t)(U * pk::kD * 4)},
         // score rows padded to 16 B; the tail pad covers vector reads past the last row
-        {(void**)&c->scores, (size_t)((U * c->sstride + 8192) * 2)},
+        {(void**)&c->scores, (size_t)(U * c->sstride + 8192)},   // last chunk read whole
         {(void**)&c->hist, (size_t)(U * c->max_chunks * (int64_t)c->hstride * 2)},
         {(void**)&c->tot, (size_t)(U * ((c->nbins + 1) & ~1) * 4)},
         {(void**)&c->meta, (size_t)(U * 4 * 4)},
@@ -390,7 +391,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     }
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
         hipMemset(c->tot, 0, U * ((c->nbins + 1) & ~1) * 4) != hipSuccess ||
-        hipMemset(c->scores, 0, (U * c->sstride + 8192) * 2) != hipSuccess ||
+        hipMemset(c->scores, 0, U * c->sstride + 8192) != hipSuccess ||
         hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_all(c);
@@ -527,7 +528,7 @@ size_t pk_debug_size(const pk_ctx* c, int32_t what) {
         case PK_DBG_IDS: return U * cap * pk::kSub;
         case PK_DBG_REC: return U * cap * pk::kRec;
         case PK_DBG_LUT: return U * pk::kSub * 256;
-        case PK_DBG_SCORES: return U * cap * 2;
+        case PK_DBG_SCORES: return U * cap;
         case PK_DBG_CAND: return U * (size_t)c->cmax * 4;
         case PK_DBG_EST: return U * (size_t)c->cmax * 4;
         case PK_DBG_NCAND: return U * 16;
@@ -551,7 +552,7 @@ pk_status pk_debug_copy(pk_ctx* c, int32_t what, void* host_dst, size_t bytes, v
     }
     const hipStream_t st = (hipStream_t)stream;
     if (what == PK_DBG_SCORES) {
-        PK_HIP(hipMemcpy2DAsync(host_dst, c->cap * 2, src, c->sstride * 2, c->cap * 2, c->units,
+        PK_HIP(hipMemcpy2DAsync(host_dst, c->cap, src, c->sstride, c->cap, c->units,
                                 hipMemcpyDeviceToHost, st));
     } else {
         PK_HIP(hipMemcpyAsync(host_dst, src, bytes, hipMemcpyDeviceToHost, st));

@@ -78,11 +78,13 @@ hipError_t launch_ring_fill(const void* K, const void* V, int64_t row_bytes, int
 // tot (zeroed beforehand by launch_qprep)
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, int64_t sstride, uint16_t* hist, int hstride,
+                       uint8_t* scores, int64_t sstride, uint16_t* hist, int hstride,
                        uint32_t* tot, int nbins, hipStream_t st);
 // coarse threshold and candidates (meta = {T, ties taken, C, k_eff} per unit),
-// then the RSQ-IP estimates of the candidates
-hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, const uint8_t* rec,
+// then the RSQ-IP estimates of the candidates; ids and lut rescore the keys
+// whose stored score saturated when the threshold reaches 255
+hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, const uint8_t* rec,
+                         const uint8_t* ids, const uint8_t* lut,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
                          int max_chunks, const uint16_t* hist, int hstride, const uint32_t* tot,
                          int nbins, int64_t C, int top_k, const float* ysum,

@@ -30,7 +30,7 @@ namespace pk {
 template <int KPT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void scan_kernel(
     const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
-    const uint8_t* __restrict__ lut, uint16_t* __restrict__ scores, int64_t sstride,
+    const uint8_t* __restrict__ lut, uint8_t* __restrict__ scores, int64_t sstride,
     uint16_t* __restrict__ hist, int hstride, uint32_t* __restrict__ tot, int nbins) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
@@ -78,14 +78,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         c8 += (valid && sc < 8u) ? (1ull << (sc << 3)) : 0ull;
         if (valid && sc >= 8u) atomicAdd(&s_hist[sc], 1u);
     }
-    uint16_t* srow = scores + u * sstride + start + tid;
+    // stored as bytes, saturated at 255 (the rerank rescores saturated keys in
+    // the rare case that the threshold reaches 255)
+    uint8_t* srow = scores + u * sstride + start + tid;
     if (nval == chunk) {
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) srow[j * kBlock] = (uint16_t)scv[j];
+        for (int j = 0; j < KPT; ++j) srow[j * kBlock] = (uint8_t)min(scv[j], 255u);
     } else {
 #pragma unroll
         for (int j = 0; j < KPT; ++j)
-            if (j * kBlock + tid < nval) srow[j * kBlock] = (uint16_t)scv[j];
+            if (j * kBlock + tid < nval) srow[j * kBlock] = (uint8_t)min(scv[j], 255u);
     }
     {
         // bytes 0..7 of c8 = counts of scores 0..7; widen to 16-bit fields
@@ -156,7 +158,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
 // after the earlier chunks' keys above T and the ties taken among theirs.
 template <int KPT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void rerank_kernel(
-    const uint16_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
+    const uint8_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
+    const uint8_t* __restrict__ ids, const uint8_t* __restrict__ lut,
     int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks, const uint16_t* __restrict__ hist,
     int hstride, const uint32_t* __restrict__ tot, int nbins, int64_t C, int top_k,
     const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int l16 = tid & 15;
-    __shared__ int32_t s_list[chunk];
+    __shared__ __align__(16) int32_t s_list[chunk < 1024 ? 1024 : chunk];   // also the vote table
     __shared__ float2 s_pair[256];     // nibble byte (code of coord 2i+1 << 4 | code of 2i)
     {
         // signed level of a 4-bit code: sign bit 3, magnitude index bits 0..2
@@ -194,31 +197,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     if (pre_ok)
         pre = *reinterpret_cast<const uint4*>(hist + ((int64_t)u * max_chunks + pc) * hstride + 8 * pq);
     const int64_t start = (int64_t)ch * chunk;
+    const int kbase = (int)start + tid * KPT;   // retrieval zone < 2^24 keys
     uint32_t s[KPT];
     {
-        const uint16_t* sp = scores + u * sstride + start + (int64_t)tid * KPT;
-        if constexpr (KPT >= 8) {
-            uint4 raw[KPT / 8];
+        const uint8_t* sp = scores + u * sstride + start + (int64_t)tid * KPT;
+        uint32_t w[(KPT + 3) / 4];
+        if constexpr (KPT >= 16) {
 #pragma unroll
-            for (int q = 0; q < KPT / 8; ++q) raw[q] = reinterpret_cast<const uint4*>(sp)[q];
-#pragma unroll
-            for (int q = 0; q < KPT / 8; ++q) {
-                const uint32_t w4[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    s[8 * q + 2 * k] = w4[k] & 0xffffu;
-                    s[8 * q + 2 * k + 1] = w4[k] >> 16;
-                }
+            for (int q = 0; q < KPT / 16; ++q) {
+                const uint4 x = reinterpret_cast<const uint4*>(sp)[q];
+                w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
             }
+        } else if constexpr (KPT == 8) {
+            const uint2 x = *reinterpret_cast<const uint2*>(sp);
+            w[0] = x.x; w[1] = x.y;
         } else if constexpr (KPT == 4) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(sp);
-            s[0] = raw.x & 0xffffu; s[1] = raw.x >> 16; s[2] = raw.y & 0xffffu; s[3] = raw.y >> 16;
+            w[0] = *reinterpret_cast<const uint32_t*>(sp);
         } else if constexpr (KPT == 2) {
-            const uint32_t raw = *reinterpret_cast<const uint32_t*>(sp);
-            s[0] = raw & 0xffffu; s[1] = raw >> 16;
+            w[0] = *reinterpret_cast<const uint16_t*>(sp);
         } else {
-            s[0] = sp[0];
+            w[0] = sp[0];
         }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) s[j] = (w[j >> 2] >> (8 * (j & 3))) & 255u;
     }
     float y[8];
 #pragma unroll
@@ -293,10 +294,33 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         }
     }
 
+    // a stored 255 stands for 255 or more: when the threshold is that high the
+    // saturated keys are rescored from their bucket ids (block-uniform branch)
+    if (T >= 255) {
+        reinterpret_cast<uint4*>(s_list)[tid] =
+            reinterpret_cast<const uint4*>(lut + (int64_t)u * kSub * 256)[tid];
+        lds_sync();
+        const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_list);
+        const uint4* idrow = reinterpret_cast<const uint4*>(ids) + u * cap + sink_end;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            if (s[j] == 255u && kbase + j < (int)n_r) {
+                const uint4 v = idrow[kbase + j];
+                const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                uint32_t sc = 0;
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((wv[a] >> (8 * k)) & 255u)];
+                s[j] = sc;
+            }
+        }
+        lds_sync();                            // the table is dead before s_list is written
+    }
+
     // this chunk's candidates, in position order: keys above T, and ties at T
     // while the unit's tie budget lasts
     uint32_t eqc = 0, gtc = 0;
-    const int kbase = (int)start + tid * KPT;   // retrieval zone < 2^24 keys
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         if (kbase + j >= (int)n_r) s[j] = 0xffffffffu;
@@ -505,7 +529,7 @@ hipError_t probe_kernel_image() {
 
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
-                       uint16_t* scores, int64_t sstride, uint16_t* hist, int hstride,
+                       uint8_t* scores, int64_t sstride, uint16_t* hist, int hstride,
                        uint32_t* tot, int nbins, hipStream_t st) {
     if (nbins < 1 || nbins > kMaxBins || hstride < nbins || n_chunks > max_chunks)
         return hipErrorInvalidValue;
@@ -528,7 +552,8 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
 #undef PK_SCAN
 }
 
-hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, const uint8_t* rec,
+hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, const uint8_t* rec,
+                         const uint8_t* ids, const uint8_t* lut,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
                          int max_chunks, const uint16_t* hist, int hstride, const uint32_t* tot,
                          int nbins, int64_t C, int top_k, const float* ysum,
@@ -540,8 +565,8 @@ hipError_t launch_rerank(int chunk, const uint16_t* scores, int64_t sstride, con
     const dim3 grid(n_chunks, units), blk(kBlock);
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
 #define PK_RERANK(K)                                                                          \
-    return launch(rerank_kernel<K>, grid, blk, hist_bytes, st, scores, sstride, rec, cap,       \
-                  sink_end, n_r, max_chunks, hist, hstride, tot, nbins, C, top_k, ysum, tab,    \
+    return launch(rerank_kernel<K>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, lut,  \
+                  cap, sink_end, n_r, max_chunks, hist, hstride, tot, nbins, C, top_k, ysum, tab,    \
                   cand_pos, cand_est, cmax, meta)
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1);

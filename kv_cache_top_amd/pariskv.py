@@ -169,7 +169,7 @@ class ParisKV:
         return tuple(v.value for v in vals)   # (n_tokens, sink_end, r_end, buf)
 
     _DBG_DTYPE = {nat.PK_DBG_IDS: np.uint8, nat.PK_DBG_REC: np.uint8, nat.PK_DBG_LUT: np.uint8,
-                  nat.PK_DBG_SCORES: np.uint16, nat.PK_DBG_CAND: np.int32, nat.PK_DBG_EST: np.float32,
+                  nat.PK_DBG_SCORES: np.uint8, nat.PK_DBG_CAND: np.int32, nat.PK_DBG_EST: np.float32,
                   nat.PK_DBG_NCAND: np.int32}
 
     def debug(self, what: int, stream=None) -> np.ndarray:

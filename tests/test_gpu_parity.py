@@ -122,6 +122,24 @@ def test_fine_ties_identical_keys():
     assert np.array_equal(s[0], np.arange(sink_end, sink_end + 512))
 
 
+def test_saturated_coarse_scores():
+    """A fifth of the keys equal to the query shared by the whole GQA group: those
+    score the maximum 256 (every subspace's top centroid for every head), above
+    the 255 a stored score holds, and they are more than the coarse budget, so
+    the threshold is 256 and the saturated keys are rescored from their ids."""
+    wl = W.gqa_bf16(N=20000, top_k=512, permille=100)
+    G = wl.group
+    for h in range(wl.n_kv):
+        wl.Q[:, h * G:(h + 1) * G] = wl.Q[:, h * G:h * G + 1]
+    pos = np.arange(4, 20000)
+    hit = pos[pos % 5 == 0]
+    for h in range(wl.n_kv):
+        wl.K[:, h, hit] = wl.Q[:, h * G][:, None, :]
+    pkv, sel, sel_n, _ = _full_check(wl, units=[0, 5], tag="saturated")
+    meta = pkv.debug(6)
+    assert meta[0][0] == 256 and meta[5][0] == 256, meta[:, 0]
+
+
 def test_fine_ties_periodic_keys():
     """64 distinct keys repeated along the context: large groups of exactly tied
     estimates around the k-th (the bucket of the k-th holds a whole group)."""
