@@ -37,7 +37,10 @@ struct pk_ctx {
     float* ysum = nullptr;        // [units][128]       sum of rotated queries
     uint8_t* scores = nullptr;    // [units][sstride] + pad   min(coarse score, 255) (retrieval offset)
     uint16_t* hist = nullptr;     // [units][max_chunks][hstride] per-chunk #{score >= s}
-    uint32_t* tot = nullptr;      // [units][nbins rounded up to even]  unit score histogram
+    uint32_t* tot = nullptr;      // [2][units][nbins rounded up to even]  unit score histograms:
+                                  // the scan adds into tables[tot_cur], the rerank reads it
+                                  // and zeroes the other one for the next step
+    int tot_cur = 0;
     int32_t* meta = nullptr;      // [units][4]          {T, ties taken, C, k_eff}
     int32_t* cand_pos = nullptr;  // [units][cmax]
     float* cand_est = nullptr;    // [units][cmax]
@@ -229,8 +232,8 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     {
         StageTimer tm(c, PK_STAGE_QPREP, st);
         PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
-                                c->cfg.vote_weight, c->lut, c->ysum, c->tot, c->nbins, k_new,
-                                v_new, c->K, c->V, row, c->cap, c->n - 1, c->ring, st));
+                                c->cfg.vote_weight, c->lut, c->ysum, k_new, v_new, c->K, c->V,
+                                row, c->cap, c->n - 1, c->ring, st));
     }
     const int64_t n_r = c->r_end - c->sink_end;
     if (n_r <= 0) {
@@ -240,19 +243,23 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     const int64_t C = coarse_count(n_r, c->cfg.coarse_permille, c->cfg.top_k);
     const int chunk = choose_chunk(c->units, n_r);
     const int n_chunks = (int)ceil_div(n_r, chunk);
+    const int64_t tstride = (c->nbins + 1) & ~1;
+    uint32_t* tot_now = c->tot + (int64_t)c->tot_cur * c->units * tstride;
+    uint32_t* tot_next = c->tot + (int64_t)(1 - c->tot_cur) * c->units * tstride;
+    c->tot_cur = 1 - c->tot_cur;
     {
         StageTimer tm(c, PK_STAGE_SCAN, st);
         PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
                                c->max_chunks, c->lut, c->scores, c->sstride, c->hist, c->hstride,
-                               c->tot, c->nbins, st));
+                               tot_now, c->nbins, st));
     }
     {
         StageTimer tm(c, PK_STAGE_RERANK, st);
         PK_HIP(pk::launch_rerank(chunk, c->scores, c->sstride, c->rec, c->ids, c->lut, c->cap,
-                                 c->units,
-                                 c->sink_end, n_r, n_chunks, c->max_chunks, c->hist, c->hstride,
-                                 c->tot, c->nbins, C, c->cfg.top_k, c->ysum, c->tab, c->cand_pos,
-                                 c->cand_est, c->cmax, c->meta, st));
+                                 c->units, c->sink_end, n_r, n_chunks, c->max_chunks, c->hist,
+                                 c->hstride, tot_now, tot_next, c->nbins, C, c->cfg.top_k,
+                                 c->ysum, c->tab, c->cand_pos, c->cand_est, c->cmax, c->meta,
+                                 st));
     }
     StageTimer tm(c, PK_STAGE_FINE, st);
     int n_splits = 0, n_hs = 0;
@@ -365,7 +372,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         // score rows padded to 16 B; the tail pad covers vector reads past the last row
         {(void**)&c->scores, (size_t)(U * c->sstride + 8192)},   // last chunk read whole
         {(void**)&c->hist, (size_t)(U * c->max_chunks * (int64_t)c->hstride * 2)},
-        {(void**)&c->tot, (size_t)(U * ((c->nbins + 1) & ~1) * 4)},
+        {(void**)&c->tot, (size_t)(2 * U * ((c->nbins + 1) & ~1) * 4)},
         {(void**)&c->meta, (size_t)(U * 4 * 4)},
         {(void**)&c->cand_pos, (size_t)(U * c->cmax * 4)},
         {(void**)&c->cand_est, (size_t)(U * c->cmax * 4)},
@@ -390,7 +397,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         }
     }
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
-        hipMemset(c->tot, 0, U * ((c->nbins + 1) & ~1) * 4) != hipSuccess ||
+        hipMemset(c->tot, 0, 2 * U * ((c->nbins + 1) & ~1) * 4) != hipSuccess ||
         hipMemset(c->scores, 0, U * c->sstride + 8192) != hipSuccess ||
         hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {

@@ -98,7 +98,7 @@ constexpr int kQMaxBlock = 512;  // G <= 8 waves
 template <typename T>
 __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
     const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
-    uint8_t* __restrict__ lut, float* __restrict__ ysum, uint32_t* __restrict__ tot, int nbins,
+    uint8_t* __restrict__ lut, float* __restrict__ ysum,
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint8_t* __restrict__ K,
     uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos, uint4* __restrict__ rk,
     uint4* __restrict__ rv, int64_t ring_rows, int64_t ring_slot) {
@@ -124,9 +124,6 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
         }
     }
     for (int i = tid; i < 256; i += 64 * G) s_row[i] = 0;
-    // the unit's coarse-score histogram starts from zero for this step's scan
-    const int tstride = (nbins + 1) & ~1;
-    for (int i = b * 64 * G + tid; i < tstride; i += kSub * 64 * G) tot[(int64_t)u * tstride + i] = 0u;
     apply_signs(v, lane_sign_byte(sign_lo, sign_hi, l16));
     fwht128_g16(v, l16);
     if (b == 0 && lane < 16) {
@@ -275,20 +272,19 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
-                        uint32_t* tot, int nbins, const void* k_new, const void* v_new, void* K,
-                        void* V, int64_t row_bytes, int64_t cap, int64_t new_pos,
-                        const HotRing& ring, hipStream_t st) {
+                        const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
+                        int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st) {
     const int64_t slot = new_pos < ring.n_sink ? new_pos : ring.n_sink + new_pos % ring.span;
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     const dim3 grid(kSub, units), blk(64 * G);
     if (bf16)
         return launch(qprep_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)q, G, sign[0],
-                      sign[1], rho, w, lut, ysum, tot, nbins, (const uint4*)k_new, (const uint4*)v_new,
+                      sign[1], rho, w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new,
                       (uint8_t*)K, (uint8_t*)V, row_bytes, cap, new_pos, (uint4*)ring.k,
                       (uint4*)ring.v, ring.rows, slot);
     return launch(qprep_kernel<float>, grid, blk, 0, st, (const float*)q, G, sign[0], sign[1], rho,
-                  w, lut, ysum, tot, nbins, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V,
+                  w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V,
                   row_bytes, cap, new_pos, (uint4*)ring.k, (uint4*)ring.v, ring.rows, slot);
 }
 

@@ -59,13 +59,11 @@ struct HotRing {
 hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64_t p0,
                          int64_t count, uint8_t* ids, uint8_t* rec, const uint64_t sign[2],
                          const CodeTables& tab, hipStream_t st);
-// query rotation, vote tables and summed query; zeroes the units' score
-// histograms tot[units][(nbins + 1) & ~1] for the scan that follows
+// query rotation, vote tables and summed query (plus the step's append)
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
-                        uint32_t* tot, int nbins, const void* k_new, const void* v_new, void* K,
-                        void* V, int64_t row_bytes, int64_t cap, int64_t new_pos,
-                        const HotRing& ring, hipStream_t st);
+                        const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
+                        int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st);
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
                          int64_t row_bytes, int64_t cap, int64_t pos, int units,
                          const HotRing& ring, hipStream_t st);
@@ -75,19 +73,20 @@ hipError_t launch_ring_fill(const void* K, const void* V, int64_t row_bytes, int
                             int units, int64_t sink_end, int64_t r_end, int64_t n,
                             const HotRing& ring, hipStream_t st);
 // coarse scores, per-chunk suffix counts, and the unit histogram added into
-// tot (zeroed beforehand by launch_qprep)
+// tot[units][(nbins + 1) & ~1] (zero beforehand)
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
                        uint8_t* scores, int64_t sstride, uint16_t* hist, int hstride,
                        uint32_t* tot, int nbins, hipStream_t st);
 // coarse threshold and candidates (meta = {T, ties taken, C, k_eff} per unit),
 // then the RSQ-IP estimates of the candidates; ids and lut rescore the keys
-// whose stored score saturated when the threshold reaches 255
+// whose stored score saturated when the threshold reaches 255; tot_clear (the
+// other histogram table) is zeroed for the next step
 hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, const uint8_t* rec,
                          const uint8_t* ids, const uint8_t* lut,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
                          int max_chunks, const uint16_t* hist, int hstride, const uint32_t* tot,
-                         int nbins, int64_t C, int top_k, const float* ysum,
+                         uint32_t* tot_clear, int nbins, int64_t C, int top_k, const float* ysum,
                          const CodeTables& tab, int32_t* cand_pos, float* cand_est, int64_t cmax,
                          int32_t* meta, hipStream_t st);
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,

@@ -161,7 +161,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     const uint8_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
     const uint8_t* __restrict__ ids, const uint8_t* __restrict__ lut,
     int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks, const uint16_t* __restrict__ hist,
-    int hstride, const uint32_t* __restrict__ tot, int nbins, int64_t C, int top_k,
+    int hstride, const uint32_t* __restrict__ tot, uint32_t* __restrict__ tot_clear, int nbins,
+    int64_t C, int top_k,
     const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
     float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
     constexpr int chunk = KPT * kBlock;
@@ -415,6 +416,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         }
     }
     // (stored last: a store ahead of a load's wait would be waited for too)
+    if (ch == 0) {
+        const int tstride = (nbins + 1) & ~1;
+        for (int i = tid; i < tstride; i += kBlock) tot_clear[(int64_t)u * tstride + i] = 0u;
+    }
     if (ch == 0 && tid == 0) {
         meta[u * 4 + 0] = T;
         meta[u * 4 + 1] = (int32_t)need;
@@ -556,7 +561,7 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
                          const uint8_t* ids, const uint8_t* lut,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
                          int max_chunks, const uint16_t* hist, int hstride, const uint32_t* tot,
-                         int nbins, int64_t C, int top_k, const float* ysum,
+                         uint32_t* tot_clear, int nbins, int64_t C, int top_k, const float* ysum,
                          const CodeTables& tab, int32_t* cand_pos, float* cand_est, int64_t cmax,
                          int32_t* meta, hipStream_t st) {
     if (nbins < 1 || nbins > kMaxBins || hstride < nbins || n_chunks > max_chunks || C < 1 ||
@@ -566,8 +571,8 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
 #define PK_RERANK(K)                                                                          \
     return launch(rerank_kernel<K>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, lut,  \
-                  cap, sink_end, n_r, max_chunks, hist, hstride, tot, nbins, C, top_k, ysum, tab,    \
-                  cand_pos, cand_est, cmax, meta)
+                  cap, sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, C,      \
+                  top_k, ysum, tab, cand_pos, cand_est, cmax, meta)
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1);
         case 2: PK_RERANK(2);
