@@ -342,7 +342,10 @@ def measured_traffic():
 def counts(layer):
     """Algorithmic HBM bytes of one step's scan / rerank / attention on this layer at
     its current window: scan 16 B per retrieval-zone key, rerank 128 B per
-    candidate, attention one bf16 K row and one V row (512 B) per attended key."""
+    candidate, attention one bf16 K row and one V row (512 B) per attended key.  The
+    hot-zone rows (sink, local, buffer) are gathered by the fine-selection launch
+    (bf16 device stores, G <= 4, at most 16384 candidates), the selected rows by
+    the attention launch."""
     p = layer.wl.params
     n, sink_end, r_end, buf = layer.ctx.window()
     units = layer.wl.n_units
@@ -350,8 +353,11 @@ def counts(layer):
     C = min(n_r, max(p.top_k, (p.coarse_permille * n_r + 999) // 1000))
     k_eff = min(p.top_k, C)
     hot = sink_end + (n - r_end)
-    return dict(scan=16 * n_r * units, rerank=128 * C * units, attend=512 * (hot + k_eff) * units,
-                keys=n_r * units)
+    fused = layer.wl.dtype == "bf16" and layer.wl.group <= 4 and C <= 16384 and \
+        not getattr(layer, "host_mapped", False)
+    return dict(scan=16 * n_r * units, rerank=128 * C * units,
+                attend=512 * (k_eff + (0 if fused else hot)) * units,
+                fine=512 * hot * units if fused else 0, keys=n_r * units)
 
 
 def cpu_baseline(args, layer, budget_s=10.0):
@@ -477,7 +483,7 @@ def main():
     # profiled pass: per-stage kernel durations from HIP events on the launch stream
     for L in layers:
         L.ctx.profile(True)
-    sums = {k: 0.0 for k in ("scan", "rerank", "attend")}
+    sums = {k: 0.0 for k in ("scan", "rerank", "fine", "attend")}
     base = args.warmup + args.steps
     for i in range(args.profile_steps):
         L = layers[(base + i) % nl]
@@ -506,9 +512,12 @@ def main():
 
     scan_gbs = gbs("scan")
     comb_bytes = sum(sums.values()) / n_prof
+    # the hot rows are gathered inside the fine-selection launch: its whole time counts
     comb_us = sum(stages[k]["avg_us"] for k in ("scan", "rerank", "attend") if k in stages)
+    if sums["fine"] and "fine" in stages:
+        comb_us += stages["fine"]["avg_us"]
     comb_gbs = comb_bytes / (comb_us * 1e-6) / 1e9 if comb_us else None
-    for k in ("scan", "rerank", "attend"):
+    for k in ("scan", "rerank", "attend") + (("fine",) if sums["fine"] else ()):
         if k in stages:
             stages[k]["alg_bytes"] = int(sums[k] / n_prof)
             stages[k]["GBps"] = gbs(k)
