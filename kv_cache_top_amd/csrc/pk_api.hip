@@ -354,10 +354,10 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         return PK_ERR_INVALID;
     }
     c->max_chunks = (int)std::min<int64_t>(pk::kMaxChunks, ceil_div(capacity, 256));
-    // candidate rows hold a multiple of 16 entries: the fine selection reads
-    // them in 16-byte vectors
-    c->cmax = (std::max<int64_t>(1, coarse_count(capacity, cfg->coarse_permille, cfg->top_k)) + 15) /
-              16 * 16;
+    // candidate rows hold a multiple of 64 entries: the fine selection reads a
+    // thread's (up to 64) candidates in 16-byte vectors
+    c->cmax = (std::max<int64_t>(1, coarse_count(capacity, cfg->coarse_permille, cfg->top_k)) + 63) /
+              64 * 64;
     c->max_splits = (int)max_attend_splits(*cfg);
 
     const int64_t U = c->units;

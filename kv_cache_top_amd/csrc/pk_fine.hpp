@@ -167,9 +167,9 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
     kth = prefix;
 }
 
-// candidates held in registers: C <= SEG * kFBlock, SEG in {4, 8, 16}; the
-// candidate rows hold a multiple of 16 entries, so the 16-byte vector loads of
-// a segment that starts below C stay inside the unit's row
+// candidates held in registers: C <= SEG * kFBlock, SEG in {4, 8, 16, 32, 64}
+// (C < 65536); the candidate rows hold a multiple of SEG entries, so the
+// 16-byte vector loads of a segment that starts below C stay inside the row
 template <int SEG>
 __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_pos,
                                               const float* __restrict__ cand_est, int64_t cmax,
@@ -179,17 +179,21 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
     const int k_eff = C < top_k ? C : top_k;
     const int b0 = tid * SEG;
     const int bl = b0 < C ? b0 : 0;          // a segment past C loads the row's start
+    // up to 16 candidates per thread the positions stay in registers too; with
+    // more, only the selected ones are read back at the end
+    constexpr bool kPosReg = SEG <= 16;
+    const int32_t* upos = cand_pos + (int64_t)u * cmax;
     uint32_t key[SEG];
-    int32_t pos[SEG];
+    int32_t pos[kPosReg ? SEG : 1];
     {
         const float4* e4 = reinterpret_cast<const float4*>(cand_est + (int64_t)u * cmax + bl);
-        const int4* p4 = reinterpret_cast<const int4*>(cand_pos + (int64_t)u * cmax + bl);
+        const int4* p4 = reinterpret_cast<const int4*>(upos + bl);
         float4 e[SEG / 4];
-        int4 pv[SEG / 4];
+        int4 pv[kPosReg ? SEG / 4 : 1];
 #pragma unroll
         for (int q = 0; q < SEG / 4; ++q) {
             e[q] = e4[q];
-            pv[q] = p4[q];
+            if constexpr (kPosReg) pv[q] = p4[q];
         }
 #pragma unroll
         for (int q = 0; q < SEG / 4; ++q) {
@@ -197,10 +201,12 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
             key[4 * q + 1] = f32_order_key(e[q].y);
             key[4 * q + 2] = f32_order_key(e[q].z);
             key[4 * q + 3] = f32_order_key(e[q].w);
-            pos[4 * q] = pv[q].x;
-            pos[4 * q + 1] = pv[q].y;
-            pos[4 * q + 2] = pv[q].z;
-            pos[4 * q + 3] = pv[q].w;
+            if constexpr (kPosReg) {
+                pos[4 * q] = pv[q].x;
+                pos[4 * q + 1] = pv[q].y;
+                pos[4 * q + 2] = pv[q].z;
+                pos[4 * q + 3] = pv[q].w;
+            }
         }
     }
     const int nv = C - b0 < 0 ? 0 : (C - b0 < SEG ? C - b0 : SEG);   // valid entries
@@ -222,7 +228,7 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
                        kth, remaining);
     }
     // compaction: one block scan of (ties at kth, keys above kth) gives both
-    // offsets (C <= 16384: the halves never carry)
+    // offsets (C < 65536: the halves never carry)
     uint32_t eqc = 0, gtc = 0;
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
@@ -239,7 +245,10 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
         const bool eq = j < nv && !all && key[j] == kth;
         const bool in = j < nv && (all || key[j] > kth || (eq && r < remaining));
         r += eq ? 1u : 0u;
-        if (in && o < (uint32_t)k_eff) usel[o] = pos[j];
+        if (in && o < (uint32_t)k_eff) {
+            if constexpr (kPosReg) usel[o] = pos[j];
+            else usel[o] = upos[b0 + j];
+        }
         o += in ? 1u : 0u;
     }
     if (tid == 0) sel_n[u] = k_eff;

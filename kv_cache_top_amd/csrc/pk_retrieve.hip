@@ -439,7 +439,8 @@ __global__ __launch_bounds__(kFBlock) void fine_reg_kernel(const int32_t* __rest
 }
 
 // more candidates than registers hold: every pass streams the estimates from
-// memory, eight loads in flight per thread; thread t compacts [t*seg, t*seg+seg)
+// memory, kMemBatch loads in flight per thread; thread t compacts [t*seg, t*seg+seg)
+constexpr int kMemBatch = 8;
 __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __restrict__ cand_pos,
                                                            const float* __restrict__ cand_est,
                                                            int64_t cmax, int C, int top_k,
@@ -453,29 +454,29 @@ __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __rest
     const int seg = (C + kFBlock - 1) / kFBlock;
     const int b0 = tid * seg;
     auto for_all = [&](auto&& f) {
-        for (int i0 = tid; i0 < C; i0 += 8 * kFBlock) {
-            float e[8];
+        for (int i0 = tid; i0 < C; i0 += kMemBatch * kFBlock) {
+            float e[kMemBatch];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kMemBatch; ++k) {
                 const int i = i0 + k * kFBlock;
                 e[k] = est[i < C ? i : C - 1];        // clamped: a real element
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
+            for (int k = 0; k < kMemBatch; ++k)
                 if (i0 + k * kFBlock < C) f(f32_order_key(e[k]));
         }
     };
     // f(i, key) for this thread's segment [b0, b0 + seg), in order
     auto for_segment = [&](auto&& f) {
-        for (int j0 = 0; j0 < seg; j0 += 8) {
-            float e[8];
+        for (int j0 = 0; j0 < seg; j0 += kMemBatch) {
+            float e[kMemBatch];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kMemBatch; ++k) {
                 const int i = b0 + j0 + k;
                 e[k] = est[(j0 + k < seg && i < C) ? i : C - 1];
             }
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kMemBatch; ++k) {
                 const int i = b0 + j0 + k;
                 if (j0 + k < seg && i < C) f(i, f32_order_key(e[k]));
             }
@@ -587,21 +588,19 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
 
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
                        int C, int top_k, int32_t* sel, int32_t* sel_n, hipStream_t st) {
-    // registers hold up to 16 candidates per thread; rows must be padded to
-    // 16 entries for the register variants' vector loads
+    // registers hold up to 32 candidates per thread (SEG of them in rows padded
+    // to a multiple of SEG); beyond that the passes stream from memory
     if (C < 1 || C > cmax) return hipErrorInvalidValue;
     const dim3 grid(units), blk(kFBlock);
-    if (cmax % 16 == 0) {
-        if (C <= 4 * kFBlock)
-            return launch(fine_reg_kernel<4>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
-                          sel, sel_n);
-        if (C <= 8 * kFBlock)
-            return launch(fine_reg_kernel<8>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k,
-                          sel, sel_n);
-        if (C <= kFineReg)
-            return launch(fine_reg_kernel<16>, grid, blk, 0, st, cand_pos, cand_est, cmax, C,
-                          top_k, sel, sel_n);
-    }
+#define PK_FREG(S)                                                                              \
+    if (C <= S * kFBlock && C < 65536 && cmax % S == 0)                                         \
+    return launch(fine_reg_kernel<S>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel, \
+                  sel_n)
+    PK_FREG(4);
+    PK_FREG(8);
+    PK_FREG(16);
+    PK_FREG(32);
+#undef PK_FREG
     return launch(fine_mem_kernel, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
                   sel_n);
 }

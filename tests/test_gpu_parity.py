@@ -69,6 +69,14 @@ def test_gqa_128k_batch4_planted():
     assert torch.isfinite(out).all()
 
 
+def test_fine_selection_30k_candidates():
+    """200K tokens with a 15 % coarse budget: about 30000 candidates per unit, past
+    what the fused selection holds, so the fine top-k keeps 32 candidates per
+    thread in registers (and the hot rows go to the attention launch)."""
+    wl = W.gqa_bf16(N=200000, top_k=2048, permille=150, threads=16)
+    _full_check(wl, units=[0, 6], tag="30k-candidates")
+
+
 def test_all_keys_kept_is_full_attention():
     wl = W.gqa_bf16(N=3000, top_k=4096, permille=1000, n_local=64)
     pkv = gc.make_ctx(wl)
