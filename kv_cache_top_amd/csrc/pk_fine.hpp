@@ -180,11 +180,12 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
     const int b0 = tid * SEG;
     const int bl = b0 < C ? b0 : 0;          // a segment past C loads the row's start
     // up to 16 candidates per thread the positions stay in registers too; with
-    // more, only the selected ones are read back at the end
+    // more, they are read (all at once) after the threshold is known
     constexpr bool kPosReg = SEG <= 16;
     const int32_t* upos = cand_pos + (int64_t)u * cmax;
     uint32_t key[SEG];
     int32_t pos[kPosReg ? SEG : 1];
+    int32_t pos2[kPosReg ? 1 : SEG];   // read back after the threshold (SEG > 16)
     {
         const float4* e4 = reinterpret_cast<const float4*>(cand_est + (int64_t)u * cmax + bl);
         const int4* p4 = reinterpret_cast<const int4*>(upos + bl);
@@ -240,6 +241,17 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
     uint32_t r = packed >> 16;                 // ties at kth before this segment
     uint32_t o = (packed & 0xffffu) + (r < remaining ? r : remaining);
     int32_t* usel = sel + (int64_t)u * top_k;
+    if constexpr (!kPosReg) {                  // this run's positions, all requested at once
+        const int4* p4 = reinterpret_cast<const int4*>(upos + bl);
+#pragma unroll
+        for (int q = 0; q < SEG / 4; ++q) {
+            const int4 x = p4[q];
+            pos2[4 * q] = x.x;
+            pos2[4 * q + 1] = x.y;
+            pos2[4 * q + 2] = x.z;
+            pos2[4 * q + 3] = x.w;
+        }
+    }
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
         const bool eq = j < nv && !all && key[j] == kth;
@@ -247,7 +259,7 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
         r += eq ? 1u : 0u;
         if (in && o < (uint32_t)k_eff) {
             if constexpr (kPosReg) usel[o] = pos[j];
-            else usel[o] = upos[b0 + j];
+            else usel[o] = pos2[j];
         }
         o += in ? 1u : 0u;
     }

@@ -438,9 +438,14 @@ __global__ __launch_bounds__(kFBlock) void fine_reg_kernel(const int32_t* __rest
     fine_reg_body<SEG>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n, blockIdx.x, sh);
 }
 
-// more candidates than registers hold: every pass streams the estimates from
-// memory, kMemBatch loads in flight per thread; thread t compacts [t*seg, t*seg+seg)
-constexpr int kMemBatch = 8;
+// more candidates than registers hold: the threshold passes stream the
+// estimates from memory (coalesced, kMemBatch loads in flight per thread);
+// the compaction goes through LDS in tiles of kMemTile keys and positions,
+// loaded coalesced, thread t taking the contiguous run [t*8, t*8+8) of a tile,
+// so the output stays in candidate order.
+constexpr int kMemBatch = 32;
+constexpr int kMemTile = 8 * kFBlock;
+constexpr int kMemOut = 8192;   // selections staged in LDS and stored at the end (k <= 8192)
 __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __restrict__ cand_pos,
                                                            const float* __restrict__ cand_est,
                                                            int64_t cmax, int C, int top_k,
@@ -448,37 +453,33 @@ __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ sel_n) {
     const int u = blockIdx.x, tid = threadIdx.x;
     __shared__ FineShared sh;
+    __shared__ __align__(16) uint32_t s_tile[kMemTile];
+    __shared__ __align__(16) int32_t s_tpos[kMemTile];
+    __shared__ int32_t s_out[kMemOut];
+    __shared__ uint32_t s_red[2 * kFBlock / 64];
     const float* est = cand_est + (int64_t)u * cmax;
     const int32_t* cpos = cand_pos + (int64_t)u * cmax;
     const int k_eff = C < top_k ? C : top_k;
-    const int seg = (C + kFBlock - 1) / kFBlock;
-    const int b0 = tid * seg;
+    // 16-byte loads, four estimates each (rows hold a multiple of 64 entries, so
+    // a vector starting below C stays in the row); few CUs run this kernel, and
+    // a CU's bytes in flight bound each pass
+    const int C4 = (C + 3) / 4;
+    const float4* est4 = reinterpret_cast<const float4*>(est);
     auto for_all = [&](auto&& f) {
-        for (int i0 = tid; i0 < C; i0 += kMemBatch * kFBlock) {
-            float e[kMemBatch];
+        for (int q0 = tid; q0 < C4; q0 += (kMemBatch / 4) * kFBlock) {
+            float4 e[kMemBatch / 4];
 #pragma unroll
-            for (int k = 0; k < kMemBatch; ++k) {
-                const int i = i0 + k * kFBlock;
-                e[k] = est[i < C ? i : C - 1];        // clamped: a real element
+            for (int k = 0; k < kMemBatch / 4; ++k) {
+                const int q = q0 + k * kFBlock;
+                e[k] = est4[q < C4 ? q : C4 - 1];      // clamped: a real vector
             }
 #pragma unroll
-            for (int k = 0; k < kMemBatch; ++k)
-                if (i0 + k * kFBlock < C) f(f32_order_key(e[k]));
-        }
-    };
-    // f(i, key) for this thread's segment [b0, b0 + seg), in order
-    auto for_segment = [&](auto&& f) {
-        for (int j0 = 0; j0 < seg; j0 += kMemBatch) {
-            float e[kMemBatch];
-#pragma unroll
-            for (int k = 0; k < kMemBatch; ++k) {
-                const int i = b0 + j0 + k;
-                e[k] = est[(j0 + k < seg && i < C) ? i : C - 1];
-            }
-#pragma unroll
-            for (int k = 0; k < kMemBatch; ++k) {
-                const int i = b0 + j0 + k;
-                if (j0 + k < seg && i < C) f(i, f32_order_key(e[k]));
+            for (int k = 0; k < kMemBatch / 4; ++k) {
+                const int i = 4 * (q0 + k * kFBlock);
+                if (i < C) f(f32_order_key(e[k].x));
+                if (i + 1 < C) f(f32_order_key(e[k].y));
+                if (i + 2 < C) f(f32_order_key(e[k].z));
+                if (i + 3 < C) f(f32_order_key(e[k].w));
             }
         }
     };
@@ -492,28 +493,89 @@ __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __rest
         });
         fine_threshold(sh, kmax, kmin_inv, k_eff, for_all, kth, remaining);
     }
-    uint32_t eqc = 0, gtc = 0;
-    for_segment([&](int, uint32_t key) {
-        gtc += (all || key > kth) ? 1u : 0u;
-        eqc += (!all && key == kth) ? 1u : 0u;
-    });
-    uint32_t tot, r, gt_before;
-    if (C < 65536) {
-        const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, sh.tmp, &tot);
-        r = packed >> 16;
-        gt_before = packed & 0xffffu;
-    } else {
-        r = block_excl_scan_t<kFBlock>(eqc, sh.tmp, &tot);
-        gt_before = block_excl_scan_t<kFBlock>(gtc, sh.tmp, &tot);
+    // compaction, tile by tile: ties at kth before this thread's run and keys
+    // above kth before it, from one scan per tile plus the earlier tiles' totals
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t gt_carry = 0, eq_carry = 0;
+    int32_t* usel = sel + (int64_t)u * top_k;
+    // the next tile is requested while the current one is compacted
+    constexpr int kPer4 = kMemTile / (4 * kFBlock);   // 16-byte vectors per thread per tile
+    float4 e[kPer4];
+    int4 pv[kPer4];
+    const int4* cpos4 = reinterpret_cast<const int4*>(cpos);
+    auto fetch = [&](int base) {
+#pragma unroll
+        for (int k = 0; k < kPer4; ++k) {
+            const int q = base / 4 + k * kFBlock + tid;
+            e[k] = est4[q < C4 ? q : C4 - 1];
+            pv[k] = cpos4[q < C4 ? q : C4 - 1];
+        }
+    };
+    fetch(0);
+    for (int base = 0; base < C; base += kMemTile) {
+#pragma unroll
+        for (int k = 0; k < kPer4; ++k) {
+            reinterpret_cast<uint4*>(s_tile)[k * kFBlock + tid] =
+                make_uint4(f32_order_key(e[k].x), f32_order_key(e[k].y), f32_order_key(e[k].z),
+                           f32_order_key(e[k].w));
+            reinterpret_cast<int4*>(s_tpos)[k * kFBlock + tid] = pv[k];
+        }
+        lds_sync();
+        if (base + kMemTile < C) fetch(base + kMemTile);
+        uint32_t key[8];
+        int32_t kp[8];
+        {
+            // 16-byte reads: eight consecutive words per thread without 8-way bank conflicts
+            const uint4 k0 = reinterpret_cast<const uint4*>(s_tile)[2 * tid];
+            const uint4 k1 = reinterpret_cast<const uint4*>(s_tile)[2 * tid + 1];
+            const int4 p0 = reinterpret_cast<const int4*>(s_tpos)[2 * tid];
+            const int4 p1 = reinterpret_cast<const int4*>(s_tpos)[2 * tid + 1];
+            key[0] = k0.x; key[1] = k0.y; key[2] = k0.z; key[3] = k0.w;
+            key[4] = k1.x; key[5] = k1.y; key[6] = k1.z; key[7] = k1.w;
+            kp[0] = p0.x; kp[1] = p0.y; kp[2] = p0.z; kp[3] = p0.w;
+            kp[4] = p1.x; kp[5] = p1.y; kp[6] = p1.z; kp[7] = p1.w;
+        }
+        int nv = C - base - tid * 8;
+        nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
+        uint32_t gtc = 0, eqc = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            gtc += (j < nv && (all || key[j] > kth)) ? 1u : 0u;
+            eqc += (j < nv && !all && key[j] == kth) ? 1u : 0u;
+        }
+        // block scan of (gtc, eqc): both fit 16 bits within a tile of 8192
+        const uint32_t v = (eqc << 16) | gtc;
+        const uint32_t x = wave_incl_scan(v);
+        if (lane == 63) s_red[wave] = x;
+        lds_sync();
+        uint32_t before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kFBlock / 64; ++w) {
+            const uint32_t t = s_red[w];
+            before += w < wave ? t : 0u;
+            tot += t;
+        }
+        const uint32_t packed = before + x - v;
+        uint32_t r = eq_carry + (packed >> 16);                 // ties before this run
+        uint32_t o = gt_carry + (packed & 0xffffu) + (r < remaining ? r : remaining);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool eq = j < nv && !all && key[j] == kth;
+            const bool in = j < nv && (all || key[j] > kth || (eq && r < remaining));
+            r += eq ? 1u : 0u;
+            if (in && o < (uint32_t)k_eff) {
+                // staged: a store here would sit ahead of the next tile's load waits
+                if (k_eff <= kMemOut) s_out[o] = kp[j];
+                else usel[o] = kp[j];
+            }
+            o += in ? 1u : 0u;
+        }
+        gt_carry += tot & 0xffffu;
+        eq_carry += tot >> 16;
+        lds_sync();                            // the tile and s_red are rewritten next
     }
-    uint32_t o = gt_before + (r < remaining ? r : remaining);
-    for_segment([&](int i, uint32_t key) {
-        const bool eq = !all && key == kth;
-        const bool in = all || key > kth || (eq && r < remaining);
-        r += eq ? 1u : 0u;
-        if (in && o < (uint32_t)k_eff) sel[(int64_t)u * top_k + o] = cpos[i];
-        o += in ? 1u : 0u;
-    });
+    if (k_eff <= kMemOut)
+        for (int i = tid; i < k_eff; i += kFBlock) usel[i] = s_out[i];
     if (tid == 0) sel_n[u] = k_eff;
 }
 
