@@ -360,6 +360,31 @@ def counts(layer):
                 fine=512 * hot * units if fused else 0, keys=n_r * units)
 
 
+def dense_reference(torch, layer, ms_step, reps=20):
+    """Full attention over every stored token of the layer (pk_dense_attend, same
+    split kernel and merge), the decode attention the retrieval path replaces:
+    its time per call, its rate over the K/V bytes it reads, and the whole sparse
+    decode step's speedup over it."""
+    ctx = layer.ctx
+    q = layer.q[0] if layer.q.dim() == 4 else layer.q
+    out = torch.empty((ctx.batch, ctx.n_q, 128), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        ctx.dense_attend(q, out)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        ctx.dense_attend(q, out)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    n = ctx.window()[0]
+    nbytes = 512 * n * layer.wl.n_units
+    return {"us_per_call": us, "bytes_per_call": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "sparse_step_speedup": us / (ms_step * 1e3)}
+
+
 def cpu_baseline(args, layer, budget_s=10.0):
     """The oracle (plain numpy, single thread) on a bounded sample: decode steps of
     `cpu_units` of the (batch, kv-head) units of one layer (their keys encoded
@@ -523,6 +548,7 @@ def main():
             stages[k]["GBps"] = gbs(k)
 
     rec, planted = recall(layers[(base + args.profile_steps - 1) % nl])
+    dense = dense_reference(torch, layers[0], ms_step)
     sref = stream_reference(torch)
     cpu = None
     if not args.no_cpu_baseline:
@@ -566,6 +592,7 @@ def main():
                           "frac_of_stream_read": comb_gbs / sref["read_GBps"] if comb_gbs else None,
                           "bytes_per_step": int(comb_bytes), "kernel_us_per_step": comb_us},
         "stream_reference": sref,
+        "dense_attention": dense,
         "stages": stages,
         "keys_scanned_per_s": keys_per_step * 1e3 / ms_step,
         "host_submit_ms_per_step": 1e3 * host_s / args.steps,

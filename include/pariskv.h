@@ -126,6 +126,17 @@ pk_status pk_retrieve(pk_ctx* ctx, const void* q, int32_t* sel, int32_t* sel_n, 
 pk_status pk_sparse_attend(pk_ctx* ctx, const void* q, const int32_t* sel, const int32_t* sel_n,
                            float* out, void* stream);
 
+/* Full attention over every stored token of each unit (no retrieval): the
+ * dense GQA decode attention the sparse path replaces, kept as the comparison
+ * baseline.  q device [batch][n_q][d] in the store dtype, out device float32
+ * [batch][n_q][d]; the same split kernel and merge as pk_sparse_attend with
+ * all n tokens as one zone.  The first call allocates its partial buffer
+ * (units x ceil(n / 128) x G x 130 floats).  Device stores only.
+ * ParisKV page, "Problem definition" (full attention reads every KV vector).
+ * Errors: PK_ERR_INVALID (NULL pointer, no prefill), PK_ERR_UNSUPPORTED
+ * (host-memory store), PK_ERR_OOM. */
+pk_status pk_dense_attend(pk_ctx* ctx, const void* q, float* out, void* stream);
+
 /* One whole decode step: pk_append_decode_keys(k_new, v_new) followed by
  * pk_retrieve(q) and pk_sparse_attend(q) over the retrieved set, with the
  * append carried out by the retrieval's first kernel.  Same arguments,

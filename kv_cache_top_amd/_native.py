@@ -52,6 +52,7 @@ SIGNATURES = {
                                 _c_void_p]),
     "pk_decode_step": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p]),
+    "pk_dense_attend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "pk_codebook": (_i32, [_i32, _i32, ctypes.POINTER(ctypes.c_float),
                            ctypes.POINTER(ctypes.c_float)]),
     "pk_status_string": (ctypes.c_char_p, [_i32]),

@@ -45,6 +45,8 @@ struct pk_ctx {
     int32_t* cand_pos = nullptr;  // [units][cmax]
     float* cand_est = nullptr;    // [units][cmax]
     float* part = nullptr;        // [units][max_splits][G][130]
+    float* dense_part = nullptr;  // partials of pk_dense_attend, allocated on its first use
+    size_t dense_bytes = 0;
     pk::HotRing ring;             // device rows of the hot zone (host-memory stores only)
     // optional per-stage timing
     bool profiling = false;
@@ -150,7 +152,8 @@ void free_all(pk_ctx* c) {
     for (hipEvent_t e : c->event_pool) (void)hipEventDestroy(e);
     c->event_pool.clear();
     void* bufs[] = {c->ids,  c->rec,      c->lut,      c->ysum, c->scores, c->hist,   c->tot,
-                    c->meta, c->cand_pos, c->cand_est, c->part, c->ring.k, c->ring.v};
+                    c->meta, c->cand_pos, c->cand_est, c->part, c->ring.k, c->ring.v,
+                    c->dense_part};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
 }
@@ -483,6 +486,29 @@ pk_status pk_sparse_attend(pk_ctx* c, const void* q, const int32_t* sel, const i
     if (!c || !q || !sel || !sel_n || !out) return PK_ERR_INVALID;
     if (!c->prefilled) return PK_ERR_INVALID;
     return run_attend(c, q, sel, sel_n, out, (hipStream_t)stream);
+}
+
+pk_status pk_dense_attend(pk_ctx* c, const void* q, float* out, void* stream) {
+    if (!c || !q || !out) return PK_ERR_INVALID;
+    if (!c->prefilled || c->n < 1) return PK_ERR_INVALID;
+    if (c->ring.k != nullptr) return PK_ERR_UNSUPPORTED;
+    const int64_t n_splits = ceil_div(c->n, pk::attend_split_keys());
+    if (n_splits > pk::attend_max_splits()) return PK_ERR_UNSUPPORTED;
+    const size_t need = (size_t)c->units * n_splits * c->G * (pk::kD + 2) * sizeof(float);
+    if (need > c->dense_bytes) {
+        if (c->dense_part) (void)hipFree(c->dense_part);
+        c->dense_part = nullptr;
+        c->dense_bytes = 0;
+        if (hipMalloc((void**)&c->dense_part, need) != hipSuccess) return PK_ERR_OOM;
+        c->dense_bytes = need;
+    }
+    const hipStream_t st = (hipStream_t)stream;
+    // every token as one zone read straight from the store: sink_end = r_end = n
+    PK_HIP(pk::launch_attend(c->dt == PK_BF16, c->G, c->K, c->V, c->cap, c->units, q, c->n, c->n,
+                             c->n, nullptr, nullptr, c->cfg.top_k, (int)n_splits, (int)n_splits,
+                             0, c->dense_part, pk::HotRing{}, st));
+    PK_HIP(pk::launch_combine(c->dense_part, c->units, c->G, (int)n_splits, out, st));
+    return PK_OK;
 }
 
 pk_status pk_decode_step(pk_ctx* c, const void* k_new, const void* v_new, const void* q,

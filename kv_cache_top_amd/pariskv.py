@@ -118,6 +118,17 @@ class ParisKV:
                                            _stream(stream)), "pk_sparse_attend")
         return out
 
+    def dense_attend(self, q: torch.Tensor, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+        """Full attention over every stored token (pk_dense_attend): the dense
+        decode attention the retrieval replaces, for comparison."""
+        self._check_rows(q, (self.batch, self.n_q, 128))
+        if out is None:
+            out = torch.empty((self.batch, self.n_q, 128), dtype=torch.float32, device=q.device)
+        nat.check(nat.lib.pk_dense_attend(self._ctx, _ptr(q), _ptr(out), _stream(stream)),
+                  "pk_dense_attend")
+        return out
+
     def step(self, q: torch.Tensor, stream=None):
         """Retrieve then attend; returns (out, sel, sel_n)."""
         sel, sel_n = self.retrieve(q, stream=stream)

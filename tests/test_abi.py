@@ -108,6 +108,8 @@ def test_calls_reject_null_context():
     assert nat.lib.pk_append_decode_keys(None, p, p, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_retrieve(None, p, p, p, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_sparse_attend(None, p, p, p, p, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_dense_attend(None, p, p, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_decode_step(None, p, p, p, p, p, p, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_debug_copy(None, 0, p, 1, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_debug_size(None, 0) == 0
     nat.lib.pk_destroy(None)

@@ -77,6 +77,21 @@ def test_fine_selection_30k_candidates():
     _full_check(wl, units=[0, 6], tag="30k-candidates")
 
 
+def test_dense_attention_matches_oracle():
+    """pk_dense_attend: full attention over every stored token of each unit, against
+    the oracle's attention over all positions; ragged last split."""
+    wl = W.gqa_bf16(N=20011, batch=2, top_k=512)
+    pkv = gc.make_ctx(wl)
+    pkv.encode_keys(wl.n_tokens)
+    q = gc.queries(wl)
+    out = pkv.dense_attend(q).cpu().numpy().reshape(wl.n_units, wl.group, 128)
+    for u in (0, 9, 15):
+        K, V, Qg = gc.unit_view(wl, u)
+        ref = ok.sparse_attention(Qg, K, V, np.arange(wl.n_tokens))
+        e = float(np.max(np.abs(out[u] - ref)))
+        assert e <= gc.ATT_TOL["bf16"], f"unit {u}: dense attention max-abs err {e:.3g}"
+
+
 def test_all_keys_kept_is_full_attention():
     wl = W.gqa_bf16(N=3000, top_k=4096, permille=1000, n_local=64)
     pkv = gc.make_ctx(wl)
