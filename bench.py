@@ -51,6 +51,11 @@ def parse():
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--sweep", choices=("capacity", "variants"), default=None,
+                    help="capacity: sparse decode step vs dense attention at 128K..1M tokens, "
+                         "batch 4; variants: probe count, vote weights and coarse fraction at "
+                         "128K, batch 4 (time, bytes and recall per setting); one JSON line each")
+    ap.add_argument("--sweep-steps", type=int, default=256)
     ap.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
                     help="3: 128K context, batch 4 (default); 4: 1M context, K/V store in pinned "
                          "host memory; 5: 16384 drifting decode steps after a 32K prefill")
@@ -257,16 +262,22 @@ def calibrate_copy():
 
 
 class Layer:
-    """One layer replica: its ParisKV context, query and token pools, outputs."""
+    """One layer replica: its ParisKV context, query and token pools, outputs.
+    `wl` reuses an already drawn workload; `override` replaces method parameters
+    (rho, vote_weights, coarse_permille)."""
 
-    def __init__(self, args, layer, pool=8):
+    def __init__(self, args, layer, pool=8, wl=None, **override):
+        import dataclasses
         import torch
         from kv_cache_top_amd import ParisKV
         from synth import workloads as W
         t0 = time.time()
-        wl = W.gqa_bf16(N=args.context, batch=args.batch, layer=layer, n_plant=64,
-                        buf_tokens=args.buf_tokens, threads=args.threads,
-                        name=f"gqa_{args.context // 1024}k_b{args.batch}_planted_bf16")
+        if wl is None:
+            wl = W.gqa_bf16(N=args.context, batch=args.batch, layer=layer, n_plant=64,
+                            buf_tokens=args.buf_tokens, threads=args.threads,
+                            name=f"gqa_{args.context // 1024}k_b{args.batch}_planted_bf16")
+        if override:
+            wl = dataclasses.replace(wl, params=dataclasses.replace(wl.params, **override))
         self.wl = wl
         p = wl.params
         steps_here = (args.warmup + args.steps + args.profile_steps) // args.layers + 2
@@ -456,6 +467,165 @@ def recall(layer):
     return float(np.mean(rec)), float(np.mean(pl))
 
 
+class DeviceLayer:
+    """A layer replica for the capacity sweep: the gqa_bf16 recipe (no planted set)
+    drawn on the GPU at any context length, with the same step interface as Layer."""
+
+    def __init__(self, N, batch, layer, steps_here, buf_tokens, pool=8):
+        import types
+        import torch
+        from kv_cache_top_amd import ParisKV
+        from synth import workloads as W
+        p = W.Params(buf_tokens=buf_tokens)
+        self.wl = types.SimpleNamespace(params=p, n_units=batch * 8, dtype="bf16", group=4,
+                                        batch=batch, n_kv=8)
+        dt = torch.bfloat16
+        self.ctx = ParisKV(batch=batch, n_kv=8, n_q=32, capacity=N + steps_here + 8, dtype=dt,
+                           rho=p.rho, vote_weights=p.vote_weights,
+                           coarse_permille=p.coarse_permille, top_k=p.top_k, n_sink=p.n_sink,
+                           n_local=p.n_local, buf_tokens=p.buf_tokens,
+                           sign_bits=tuple(int(x) for x in W.sign_bits(0, layer)))
+        qp, kp, vp = W.fill_gqa_device(self.ctx.K, self.ctx.V, N, seed=0, layer=layer, pool=pool)
+        self.q = torch.from_numpy(qp).to(dt).cuda()
+        self.kn = torch.from_numpy(kp).to(dt).cuda()
+        self.vn = torch.from_numpy(vp).to(dt).cuda()
+        self.sel = torch.empty((batch, 8, p.top_k), dtype=torch.int32, device="cuda")
+        self.sel_n = torch.empty((batch, 8), dtype=torch.int32, device="cuda")
+        self.out = torch.empty((batch, 32, 128), dtype=torch.float32, device="cuda")
+        self.pool, self.t = pool, 0
+        self.ctx.encode_keys(N)
+        self._stream = torch.cuda.current_stream().cuda_stream
+
+    def step(self):
+        i = self.t % self.pool
+        self.t += 1
+        self.ctx.decode_step_raw(self.kn[i].data_ptr(), self.vn[i].data_ptr(), self.q[i].data_ptr(),
+                                 self.sel.data_ptr(), self.sel_n.data_ptr(), self.out.data_ptr(),
+                                 self._stream)
+
+
+def time_steps(torch, layers, warmup, steps):
+    """ms per decode step over `steps` steps cycling the layers (after `warmup`)."""
+    nl = len(layers)
+    for i in range(warmup):
+        layers[i % nl].step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        layers[(warmup + i) % nl].step()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def profiled_stages(torch, nat, layers, n):
+    """Average per-stage kernel durations (us) over n more steps."""
+    for L in layers:
+        L.ctx.profile(True)
+    for i in range(n):
+        layers[i % len(layers)].step()
+    torch.cuda.synchronize()
+    ms, cnt = {k: 0.0 for k in nat.STAGES}, {k: 0 for k in nat.STAGES}
+    for L in layers:
+        for k, (m, c) in L.ctx.profile_read().items():
+            ms[k] += m
+            cnt[k] += c
+        L.ctx.profile(False)
+    return {k: round(1e3 * ms[k] / cnt[k], 2) for k in nat.STAGES if cnt[k]}
+
+
+def run_capacity_sweep(args):
+    """Sparse decode step against dense attention over every stored token, at 128K,
+    256K, 384K and 1M tokens, batch 4 x 8 kv heads (G = 4, bf16, top-k 2048, coarse
+    5 %), K/V drawn on the GPU; layer replicas are cycled while one step's working
+    set is below twice the 256 MB last-level cache.  Also the batch that 288 GB-class
+    HBM holds at each context, from the bytes each design keeps per token: dense
+    attention K/V only (512 B), the retrieval path with the store in HBM (K/V + 16 B
+    ids + 128 B records), and with the store in host memory (ids + records)."""
+    import torch
+    import kv_cache_top_amd._native as nat
+    free, total = torch.cuda.mem_get_info()
+    B = args.batch
+    units = 8 * B
+    for N in (131072, 262144, 393216, 1 << 20):
+        t0 = time.time()
+        ws = units * (16 * N + 128 * max(2048, N // 20) + 512 * (2048 + 516))
+        nl = max(1, min(4, -(-(512 << 20) // ws)))
+        steps_here = (16 + args.sweep_steps + 32) // nl + 2
+        layers = [DeviceLayer(N, B, l, steps_here, args.buf_tokens) for l in range(nl)]
+        torch.cuda.synchronize()
+        ms = time_steps(torch, layers, 16, args.sweep_steps)
+        st = profiled_stages(torch, nat, layers, 32)
+        c = counts(layers[0])
+        dense = dense_reference(torch, layers[0], ms, reps=5)
+        per_tok = {"dense_kv": 512, "paris_store_in_hbm": 512 + 144, "paris_store_in_host": 144}
+        max_batch = {k: int(total // (8 * N * v)) for k, v in per_tok.items()}
+        print(json.dumps({
+            "sweep": "capacity", "context": N, "batch": B, "layers_cycled": nl,
+            "sparse_us_per_step": round(1e3 * ms, 2), "sparse_steps_per_s": round(1e3 / ms, 1),
+            "stages_us": st,
+            "sparse_alg_bytes_per_step": int(c["scan"] + c["rerank"] + c["attend"] + c["fine"]),
+            "dense_us_per_call": round(dense["us_per_call"], 1),
+            "dense_bytes_per_call": dense["bytes_per_call"], "dense_GBps": round(dense["GBps"], 1),
+            "sparse_step_speedup_over_dense": round(dense["sparse_step_speedup"], 2),
+            "max_batch_by_hbm_bytes": max_batch, "hbm_total_bytes": int(total),
+            "wall_s": round(time.time() - t0, 1)}), flush=True)
+        for L in layers:
+            L.ctx.close()
+        del layers
+        torch.cuda.empty_cache()
+
+
+def run_variant_sweep(args):
+    """The knobs the page leaves open (probe count rho, the hierarchical vote weights,
+    the coarse fraction) at 128K, batch 4, planted workload: step time, per-stage
+    durations, algorithmic bytes and recall@k / planted recall (mean over one step
+    per layer replica, every fourth unit) per setting."""
+    import copy
+    import torch
+    import kv_cache_top_amd._native as nat
+    from synth import workloads as W
+    a = copy.copy(args)
+    a.steps, a.warmup, a.profile_steps = args.sweep_steps, 16, 32
+    wls = [W.gqa_bf16(N=a.context, batch=a.batch, layer=l, n_plant=64, buf_tokens=a.buf_tokens,
+                      threads=a.threads, name=f"gqa_{a.context // 1024}k_b{a.batch}_planted_bf16")
+           for l in range(a.layers)]
+    variants = [dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50),
+                dict(rho=1, vote_weights=(1,), coarse_permille=50),
+                dict(rho=2, vote_weights=(2, 1), coarse_permille=50),
+                dict(rho=8, vote_weights=(8, 7, 6, 5, 4, 3, 2, 1), coarse_permille=50),
+                dict(rho=4, vote_weights=(8, 4, 2, 1), coarse_permille=50),
+                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=100)]
+    for v in variants:
+        layers = [Layer(a, l, wl=wls[l], **v) for l in range(a.layers)]
+        for L in layers:
+            L.ctx.encode_keys(L.wl.n_tokens)
+        torch.cuda.synchronize()
+        ms = time_steps(torch, layers, a.warmup, a.steps)
+        st = profiled_stages(torch, nat, layers, a.profile_steps)
+        c = counts(layers[0])
+        rec, pl = [], []
+        for L in layers:
+            L.step()
+            torch.cuda.synchronize()
+            r, p_ = recall(L)
+            rec.append(r)
+            pl.append(p_)
+        print(json.dumps({
+            "sweep": "variants", "context": a.context, "batch": a.batch,
+            "rho": v["rho"], "vote_weights": list(v["vote_weights"]),
+            "coarse_permille": v["coarse_permille"],
+            "us_per_step": round(1e3 * ms, 2), "steps_per_s": round(1e3 / ms, 1), "stages_us": st,
+            "alg_bytes_per_step": int(c["scan"] + c["rerank"] + c["attend"] + c["fine"]),
+            "recall_at_k": round(float(np.mean(rec)), 4),
+            "planted_recall": round(float(np.mean(pl)), 4)}), flush=True)
+        for L in layers:
+            L.ctx.close()
+        del layers
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -471,6 +641,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.sweep == "capacity":
+        return run_capacity_sweep(args)
+    if args.sweep == "variants":
+        return run_variant_sweep(args)
     if args.config == 4:
         return run_config4(args)
     if args.config == 5:

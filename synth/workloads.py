@@ -228,6 +228,40 @@ def decode_stream(w: Workload, n_steps: int, drift_sigma: float = 2.0, seed: int
     return Kn, Vn, Qn
 
 
+def fill_gqa_device(K, V, n_tokens: int, seed: int = 0, layer: int = 0, pool: int = 8):
+    """The gqa_bf16 recipe drawn on the GPU, for contexts whose host-side draw would
+    take minutes (capacity sweeps).  K, V: device tensors [batch, n_kv, cap, d]
+    (bf16 or fp32) whose first n_tokens rows are filled: keys s * z with the unit's
+    channel scales s (drawn exactly as gqa_bf16 draws them: lognormal(0, 0.5), 4
+    outlier channels x20), values z, z ~ N(0, 1) from torch's generator on the
+    device seeded per (seed, layer, unit).  Returns host float32 pools of `pool`
+    query sets [pool, batch, n_kv*4, d] drawn like the keys, and of `pool` new
+    tokens' keys and values [pool, batch, n_kv, d] (rounded to K's dtype)."""
+    batch, n_kv, _, d = K.shape
+    group = 4
+    qp = np.empty((pool, batch, n_kv * group, d), np.float32)
+    kp = np.empty((pool, batch, n_kv, d), np.float32)
+    vp = np.empty((pool, batch, n_kv, d), np.float32)
+    g = torch.Generator(device=K.device)
+    for u in range(batch * n_kv):
+        b, h = divmod(u, n_kv)
+        s_k = _channel_scales(_rng(seed, layer, u, _S_SCALE), d, 4)
+        g.manual_seed(int(np.random.SeedSequence(entropy=seed, spawn_key=(layer, u, 7)).generate_state(1)[0]))
+        st = torch.from_numpy(s_k).to(K.device)
+        for lo in range(0, n_tokens, 1 << 18):
+            hi = min(n_tokens, lo + (1 << 18))
+            z = torch.randn((hi - lo, d), generator=g, device=K.device)
+            K[b, h, lo:hi].copy_(z * st)
+            V[b, h, lo:hi].copy_(torch.randn((hi - lo, d), generator=g, device=K.device))
+        r = _rng(seed, layer, u, 1000 + _S_QUERY)
+        qp[:, b, h * group:(h + 1) * group] = r.standard_normal((pool, group, d)) * s_k
+        kp[:, b, h] = r.standard_normal((pool, d)) * s_k
+        vp[:, b, h] = r.standard_normal((pool, d))
+    if K.dtype == torch.bfloat16:
+        qp, kp, vp = round_bf16(qp), round_bf16(kp), round_bf16(vp)
+    return qp, kp, vp
+
+
 def query_pool(w: Workload, n: int, plant_cos: float = 0.3) -> np.ndarray:
     """n further query sets drawn with the workload's recipe (new draws, same
     channel scales; planted workloads: new noisy copies of the planted

@@ -163,6 +163,22 @@ def test_saturated_coarse_scores():
     assert meta[0][0] == 256 and meta[5][0] == 256, meta[:, 0]
 
 
+@pytest.mark.parametrize("rho,weights,permille", [
+    (1, (1,), 50),                          # top centroid only
+    (2, (2, 1), 100),                       # 10 % coarse budget
+    (4, (8, 4, 2, 1), 50),                  # powers-of-two weights: 513 score bins
+    (8, (8, 7, 6, 5, 4, 3, 2, 1), 80),      # widest probe, linear weights
+])
+def test_vote_variants(rho, weights, permille):
+    """The page leaves the probe count, the hierarchical weights and the coarse
+    fraction open: every stage stays bit-exact (ids, tables, scores, candidate
+    sets) and within tolerance for other settings of them."""
+    import dataclasses
+    wl = W.gqa_bf16(N=24000, top_k=512, permille=permille)
+    wl.params = dataclasses.replace(wl.params, rho=rho, vote_weights=tuple(weights))
+    _full_check(wl, units=[0, 3, 6], tag=f"rho{rho}-w{'-'.join(map(str, weights))}-p{permille}")
+
+
 def test_fine_ties_periodic_keys():
     """64 distinct keys repeated along the context: large groups of exactly tied
     estimates around the k-th (the bucket of the k-th holds a whole group)."""
