@@ -228,6 +228,17 @@ def decode_stream(w: Workload, n_steps: int, drift_sigma: float = 2.0, seed: int
     return Kn, Vn, Qn
 
 
+def kmeans_init_positions(n_units: int, n_tokens: int, seed: int = 0, layer: int = 0,
+                          k: int = 256) -> np.ndarray:
+    """k distinct token positions in [0, n_tokens) per unit, uniformly drawn: the
+    initial centroids of the learned-centroid comparator.  int32 [n_units, k]."""
+    out = np.empty((n_units, k), np.int32)
+    for u in range(n_units):
+        r = _rng(seed, layer, u, 2000)
+        out[u] = np.sort(r.choice(n_tokens, size=k, replace=False))
+    return out
+
+
 def fill_gqa_device(K, V, n_tokens: int, seed: int = 0, layer: int = 0, pool: int = 8):
     """The gqa_bf16 recipe drawn on the GPU, for contexts whose host-side draw would
     take minutes (capacity sweeps).  K, V: device tensors [batch, n_kv, cap, d]
