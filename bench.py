@@ -56,6 +56,12 @@ def parse():
                          "batch 4; variants: probe count, vote weights and coarse fraction at "
                          "128K, batch 4 (time, bytes and recall per setting); one JSON line each")
     ap.add_argument("--sweep-steps", type=int, default=256)
+    ap.add_argument("--centroids", choices=("analytic", "learned"), default="analytic",
+                    help="--config 5 only: the page's analytic centroids, or the comparison "
+                         "stage with centroids fitted by k-means to the prefill keys")
+    ap.add_argument("--kmeans-iters", type=int, default=10)
+    ap.add_argument("--drift-sigma", type=float, default=2.0,
+                    help="--config 5 only: drift of the key/query mean over the decode steps")
     ap.add_argument("--config", type=int, default=3, choices=(3, 4, 5),
                     help="3: 128K context, batch 4 (default); 4: 1M context, K/V store in pinned "
                          "host memory; 5: 16384 drifting decode steps after a 32K prefill")
@@ -199,7 +205,7 @@ def run_config5(args):
     wl = W.gqa_bf16(N=N0, top_k=1024, buf_tokens=256, threads=args.threads,
                     name="gqa_32k_drift16k_bf16")
     p = wl.params
-    Kn, Vn, Qn = W.decode_stream(wl, T)
+    Kn, Vn, Qn = W.decode_stream(wl, T, drift_sigma=args.drift_sigma)
     dt = torch.bfloat16
     ctx = ParisKV(batch=1, n_kv=8, n_q=32, capacity=N0 + T, dtype=dt, rho=p.rho,
                   vote_weights=p.vote_weights, coarse_permille=p.coarse_permille, top_k=p.top_k,
@@ -207,6 +213,17 @@ def run_config5(args):
                   sign_bits=tuple(int(x) for x in wl.sign_bits))
     ctx.K[:, :, :N0].copy_(torch.from_numpy(wl.K).to(dt))
     ctx.V[:, :, :N0].copy_(torch.from_numpy(wl.V).to(dt))
+    fit_ms = None
+    if args.centroids == "learned":
+        init = torch.from_numpy(W.kmeans_init_positions(8, N0)).cuda()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        ctx.fit_centroids(N0, init, args.kmeans_iters)
+        f1.record()
+        torch.cuda.synchronize()
+        fit_ms = f0.elapsed_time(f1)
+        log(f"k-means fit ({args.kmeans_iters} iterations, {8 * N0} keys): {fit_ms:.2f} ms")
     ctx.encode_keys(N0)
     Kd, Vd, Qd = (torch.from_numpy(x).to(dt).cuda() for x in (Kn, Vn, Qn))
     Kall = np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2)
@@ -238,11 +255,13 @@ def run_config5(args):
         "ms_per_step": total_ms / T, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": 1, "kv_heads": 8, "q_heads": 32, "head_dim": 128,
-                   "prefill": N0, "decode_steps": T, "drift_sigma": 2.0, "top_k": p.top_k,
+                   "prefill": N0, "decode_steps": T, "drift_sigma": args.drift_sigma, "top_k": p.top_k,
                    "coarse_permille": p.coarse_permille, "sink": p.n_sink, "local": p.n_local,
-                   "update_buffer": p.buf_tokens},
+                   "update_buffer": p.buf_tokens, "centroids": args.centroids},
         "recall_at_k_per_1k_steps": curve,
     }
+    if fit_ms is not None:
+        result["kmeans_fit"] = {"iterations": args.kmeans_iters, "keys": 8 * N0, "ms": fit_ms}
     print(json.dumps(result), flush=True)
 
 

@@ -137,6 +137,28 @@ pk_status pk_sparse_attend(pk_ctx* ctx, const void* q, const int32_t* sel, const
  * (host-memory store), PK_ERR_OOM. */
 pk_status pk_dense_attend(pk_ctx* ctx, const void* q, float* out, void* stream);
 
+/* Comparison coarse stage: replaces the analytic sign-pattern centroids of
+ * every unit and subspace by 256 centroids fitted with k-means to the rotated
+ * keys of positions [0, n_tokens) of the store (the keys a model holds after
+ * prefill), the design the ParisKV page sets its data-independent centroids
+ * against ("Problem definition"; "Drift-robust analytic centroids").  Call it
+ * after writing the prefill K and before pk_encode_keys; from then on the
+ * context's bucket ids (prefill and every later eviction) and the queries'
+ * top-rho centroids use the fitted tables, and everything else is unchanged.
+ * Fitting: init_pos device int32 [units][256] (positions < n_tokens, checked
+ * on the host after a synchronising copy) give the initial centroids, the
+ * normalised subspace vectors of those keys; then `iters` Lloyd rounds of
+ * assignment (most similar centroid by the fp32 pairwise tree of the products
+ * c_j x_j, ties to the lower index) and update (centroid = S / ||S||, S the
+ * exact integer sum of the assigned vectors with coordinates rounded to
+ * multiples of 2^-20; a centroid with no members keeps its value).  The first
+ * call allocates the tables (units x 16 x 256 x 8 floats, and as many 64-bit
+ * sums).
+ * Errors: PK_ERR_INVALID (NULL, keys already encoded, n_tokens < 256, a
+ * position out of range, iters outside 0..1000), PK_ERR_CAPACITY, PK_ERR_OOM. */
+pk_status pk_fit_centroids(pk_ctx* ctx, int64_t n_tokens, const int32_t* init_pos, int32_t iters,
+                           void* stream);
+
 /* One whole decode step: pk_append_decode_keys(k_new, v_new) followed by
  * pk_retrieve(q) and pk_sparse_attend(q) over the retrieved set, with the
  * append carried out by the retrieval's first kernel.  Same arguments,
@@ -189,9 +211,10 @@ pk_status pk_profile_read(pk_ctx* ctx, double* ms, int64_t* launches);
  *   PK_DBG_SCORES  uint8  [units][cap]              min(coarse score, 255) of retrieval position sink_end + i
  *   PK_DBG_CAND    int32  [units][cmax]             candidate positions (ascending), first n_cand valid
  *   PK_DBG_EST     float  [units][cmax]             RSQ-IP estimate of each candidate
- *   PK_DBG_NCAND   int32  [units][4]                {threshold score, ties taken, n_cand, k_eff}  */
+ *   PK_DBG_NCAND   int32  [units][4]                {threshold score, ties taken, n_cand, k_eff}
+ *   PK_DBG_CENTROIDS float [units][B][256][8]       fitted centroids (after pk_fit_centroids only) */
 enum { PK_DBG_IDS = 0, PK_DBG_REC = 1, PK_DBG_LUT = 2, PK_DBG_SCORES = 3, PK_DBG_CAND = 4,
-       PK_DBG_EST = 5, PK_DBG_NCAND = 6 };
+       PK_DBG_EST = 5, PK_DBG_NCAND = 6, PK_DBG_CENTROIDS = 7 };
 size_t pk_debug_size(const pk_ctx* ctx, int32_t what);
 pk_status pk_debug_copy(pk_ctx* ctx, int32_t what, void* host_dst, size_t bytes, void* stream);
 

@@ -19,7 +19,7 @@ PK_F32, PK_BF16 = 0, 1
 PK_MEM_DEVICE, PK_MEM_HOST_MAPPED = 0, 1
 STAGES = ("encode", "append", "qprep", "scan", "select", "rerank", "fine", "attend", "combine")
 (PK_DBG_IDS, PK_DBG_REC, PK_DBG_LUT, PK_DBG_SCORES, PK_DBG_CAND, PK_DBG_EST,
- PK_DBG_NCAND) = range(7)
+ PK_DBG_NCAND, PK_DBG_CENTROIDS) = range(8)
 
 # every function the header declares, with its ctypes signature
 _c_void_p, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -53,6 +53,7 @@ SIGNATURES = {
     "pk_decode_step": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p]),
     "pk_dense_attend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "pk_fit_centroids": (_i32, [_c_void_p, _i64, _c_void_p, _i32, _c_void_p]),
     "pk_codebook": (_i32, [_i32, _i32, ctypes.POINTER(ctypes.c_float),
                            ctypes.POINTER(ctypes.c_float)]),
     "pk_status_string": (ctypes.c_char_p, [_i32]),

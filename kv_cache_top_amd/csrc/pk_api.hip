@@ -47,6 +47,9 @@ struct pk_ctx {
     float* part = nullptr;        // [units][max_splits][G][130]
     float* dense_part = nullptr;  // partials of pk_dense_attend, allocated on its first use
     size_t dense_bytes = 0;
+    float* cents = nullptr;       // [units][16][256][8] learned centroids (pk_fit_centroids), else
+                                  // null: the analytic sign-pattern centroids
+    long long* km_sums = nullptr; // [units][16][256][8] fixed-point sums of the fit
     pk::HotRing ring;             // device rows of the hot zone (host-memory stores only)
     // optional per-stage timing
     bool profiling = false;
@@ -153,7 +156,7 @@ void free_all(pk_ctx* c) {
     c->event_pool.clear();
     void* bufs[] = {c->ids,  c->rec,      c->lut,      c->ysum, c->scores, c->hist,   c->tot,
                     c->meta, c->cand_pos, c->cand_est, c->part, c->ring.k, c->ring.v,
-                    c->dense_part};
+                    c->dense_part, c->cents, c->km_sums};
     for (void* p : bufs)
         if (p) (void)hipFree(p);
 }
@@ -209,6 +212,9 @@ pk_status evict(pk_ctx* c, hipStream_t st) {
         StageTimer tm(c, PK_STAGE_ENCODE, st);
         PK_HIP(pk::launch_encode(c->dt == PK_BF16, c->K, c->cap, c->units, c->r_end, move, c->ids,
                                  c->rec, c->cfg.sign_bits, c->tab, st));
+        if (c->cents)
+            PK_HIP(pk::launch_km_ids(c->dt == PK_BF16, c->K, c->cap, c->units, c->r_end, move,
+                                     c->cfg.sign_bits, c->cents, c->ids, st));
     }
     c->r_end += move;
     c->buf = 0;
@@ -235,7 +241,7 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     {
         StageTimer tm(c, PK_STAGE_QPREP, st);
         PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
-                                c->cfg.vote_weight, c->lut, c->ysum, k_new, v_new, c->K, c->V,
+                                c->cfg.vote_weight, c->cents, c->lut, c->ysum, k_new, v_new, c->K, c->V,
                                 row, c->cap, c->n - 1, c->ring, st));
     }
     const int64_t n_r = c->r_end - c->sink_end;
@@ -445,6 +451,10 @@ pk_status pk_encode_keys(pk_ctx* c, int64_t n_tokens, void* stream) {
     StageTimer tm(c, PK_STAGE_ENCODE, (hipStream_t)stream);
     PK_HIP(pk::launch_encode(c->dt == PK_BF16, c->K, c->cap, c->units, sink_end, r_end - sink_end,
                              c->ids, c->rec, c->cfg.sign_bits, c->tab, (hipStream_t)stream));
+    if (c->cents)
+        PK_HIP(pk::launch_km_ids(c->dt == PK_BF16, c->K, c->cap, c->units, sink_end,
+                                 r_end - sink_end, c->cfg.sign_bits, c->cents, c->ids,
+                                 (hipStream_t)stream));
     PK_HIP(pk::launch_ring_fill(c->K, c->V, (int64_t)pk::kD * dtype_size(c->dt), c->cap, c->units,
                                 sink_end, r_end, n_tokens, c->ring, (hipStream_t)stream));
     c->n = n_tokens;
@@ -452,6 +462,39 @@ pk_status pk_encode_keys(pk_ctx* c, int64_t n_tokens, void* stream) {
     c->r_end = r_end;
     c->buf = 0;
     c->prefilled = true;
+    return PK_OK;
+}
+
+pk_status pk_fit_centroids(pk_ctx* c, int64_t n_tokens, const int32_t* init_pos, int32_t iters,
+                           void* stream) {
+    if (!c || !init_pos || iters < 0 || iters > 1000) return PK_ERR_INVALID;
+    if (c->prefilled) return PK_ERR_INVALID;          // ids of encoded keys would be stale
+    if (n_tokens < 256) return PK_ERR_INVALID;
+    if (n_tokens > c->cap) return PK_ERR_CAPACITY;
+    const hipStream_t st = (hipStream_t)stream;
+    // the initial positions index the store: checked on the host before any launch
+    std::vector<int32_t> pos((size_t)c->units * 256);
+    PK_HIP(hipMemcpyAsync(pos.data(), init_pos, pos.size() * sizeof(int32_t),
+                          hipMemcpyDeviceToHost, st));
+    PK_HIP(hipStreamSynchronize(st));
+    for (int32_t p : pos)
+        if (p < 0 || p >= n_tokens) return PK_ERR_INVALID;
+    const size_t n = (size_t)c->units * pk::kSub * 256 * 8;
+    if (!c->cents) {
+        float* ct = nullptr;
+        long long* sm = nullptr;
+        if (hipMalloc((void**)&ct, n * sizeof(float)) != hipSuccess) return PK_ERR_OOM;
+        if (hipMalloc((void**)&sm, n * sizeof(long long)) != hipSuccess) {
+            (void)hipFree(ct);
+            return PK_ERR_OOM;
+        }
+        c->cents = ct;
+        c->km_sums = sm;
+    }
+    PK_HIP(hipMemsetAsync(c->cents, 0, n * sizeof(float), st));
+    StageTimer tm(c, PK_STAGE_ENCODE, st);
+    PK_HIP(pk::launch_km_fit(c->dt == PK_BF16, c->K, c->cap, c->units, n_tokens, init_pos, iters,
+                             c->cfg.sign_bits, c->cents, c->km_sums, st));
     return PK_OK;
 }
 
@@ -565,6 +608,7 @@ size_t pk_debug_size(const pk_ctx* c, int32_t what) {
         case PK_DBG_CAND: return U * (size_t)c->cmax * 4;
         case PK_DBG_EST: return U * (size_t)c->cmax * 4;
         case PK_DBG_NCAND: return U * 16;
+        case PK_DBG_CENTROIDS: return c->cents ? U * pk::kSub * 256 * 8 * sizeof(float) : 0;
     }
     return 0;
 }
@@ -582,6 +626,7 @@ pk_status pk_debug_copy(pk_ctx* c, int32_t what, void* host_dst, size_t bytes, v
         case PK_DBG_CAND: src = c->cand_pos; break;
         case PK_DBG_EST: src = c->cand_est; break;
         case PK_DBG_NCAND: src = c->meta; break;
+        case PK_DBG_CENTROIDS: src = c->cents; break;
     }
     const hipStream_t st = (hipStream_t)stream;
     if (what == PK_DBG_SCORES) {

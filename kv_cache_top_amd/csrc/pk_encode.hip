@@ -98,7 +98,7 @@ constexpr int kQMaxBlock = 512;  // G <= 8 waves
 template <typename T>
 __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
     const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
-    uint8_t* __restrict__ lut, float* __restrict__ ysum,
+    const float* __restrict__ cents, uint8_t* __restrict__ lut, float* __restrict__ ysum,
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new, uint8_t* __restrict__ K,
     uint8_t* __restrict__ V, int64_t row_bytes, int64_t cap, int64_t new_pos, uint4* __restrict__ rk,
     uint4* __restrict__ rv, int64_t ring_rows, int64_t ring_slot) {
@@ -135,16 +135,29 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
     float y[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) y[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[r]), b));
-    const float t0 = (lane & 1) ? -y[0] : y[0], t1 = (lane & 2) ? -y[1] : y[1];
-    const float t2 = (lane & 4) ? -y[2] : y[2], t3 = (lane & 8) ? -y[3] : y[3];
-    const float t4 = (lane & 16) ? -y[4] : y[4], t5 = (lane & 32) ? -y[5] : y[5];
-    const float lo = (t0 + t1) + (t2 + t3);
-    const float p45 = t4 + t5;
     uint32_t key[4];
+    if (cents == nullptr) {
+        const float t0 = (lane & 1) ? -y[0] : y[0], t1 = (lane & 2) ? -y[1] : y[1];
+        const float t2 = (lane & 4) ? -y[2] : y[2], t3 = (lane & 8) ? -y[3] : y[3];
+        const float t4 = (lane & 16) ? -y[4] : y[4], t5 = (lane & 32) ? -y[5] : y[5];
+        const float lo = (t0 + t1) + (t2 + t3);
+        const float p45 = t4 + t5;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const float t6 = (t & 1) ? -y[6] : y[6], t7 = (t & 2) ? -y[7] : y[7];
-        key[t] = f32_order_key(lo + (p45 + (t6 + t7)));  // > 0 for every finite score
+        for (int t = 0; t < 4; ++t) {
+            const float t6 = (t & 1) ? -y[6] : y[6], t7 = (t & 2) ? -y[7] : y[7];
+            key[t] = f32_order_key(lo + (p45 + (t6 + t7)));  // > 0 for every finite score
+        }
+    } else {
+        // learned centroids (comparison stage): the fp32 tree of fl32(c_j y_j)
+        const float4* ct = reinterpret_cast<const float4*>(cents + ((int64_t)u * kSub + b) * 256 * 8);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float4 c0 = ct[2 * (64 * t + lane)], c1 = ct[2 * (64 * t + lane) + 1];
+            const float p[8] = {__fmul_rn(c0.x, y[0]), __fmul_rn(c0.y, y[1]), __fmul_rn(c0.z, y[2]),
+                                __fmul_rn(c0.w, y[3]), __fmul_rn(c1.x, y[4]), __fmul_rn(c1.y, y[5]),
+                                __fmul_rn(c1.z, y[6]), __fmul_rn(c1.w, y[7])};
+            key[t] = f32_order_key(tree8(p));
+        }
     }
     lds_sync();
 
@@ -271,7 +284,7 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 }
 
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
-                        int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
+                        int rho, const uint8_t* weights, const float* cents, uint8_t* lut, float* ysum,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
                         int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st) {
     const int64_t slot = new_pos < ring.n_sink ? new_pos : ring.n_sink + new_pos % ring.span;
@@ -280,11 +293,11 @@ hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64
     const dim3 grid(kSub, units), blk(64 * G);
     if (bf16)
         return launch(qprep_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)q, G, sign[0],
-                      sign[1], rho, w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new,
+                      sign[1], rho, w, cents, lut, ysum, (const uint4*)k_new, (const uint4*)v_new,
                       (uint8_t*)K, (uint8_t*)V, row_bytes, cap, new_pos, (uint4*)ring.k,
                       (uint4*)ring.v, ring.rows, slot);
     return launch(qprep_kernel<float>, grid, blk, 0, st, (const float*)q, G, sign[0], sign[1], rho,
-                  w, lut, ysum, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V,
+                  w, cents, lut, ysum, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V,
                   row_bytes, cap, new_pos, (uint4*)ring.k, (uint4*)ring.v, ring.rows, slot);
 }
 

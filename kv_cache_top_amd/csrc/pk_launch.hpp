@@ -61,9 +61,18 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
                          const CodeTables& tab, hipStream_t st);
 // query rotation, vote tables and summed query (plus the step's append)
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
-                        int rho, const uint8_t* weights, uint8_t* lut, float* ysum,
+                        int rho, const uint8_t* weights, const float* cents, uint8_t* lut,
+                        float* ysum,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
                         int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st);
+// learned-centroid comparison stage: fit (seed, then iters rounds of assign +
+// normalise) and bucket ids of keys [p0, p0 + count) under the fitted tables
+hipError_t launch_km_fit(bool bf16, const void* K, int64_t cap, int units, int64_t n_fit,
+                         const int32_t* init_pos, int iters, const uint64_t sign[2], float* cents,
+                         long long* S, hipStream_t st);
+hipError_t launch_km_ids(bool bf16, const void* K, int64_t cap, int units, int64_t p0,
+                         int64_t count, const uint64_t sign[2], const float* cents, uint8_t* ids,
+                         hipStream_t st);
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
                          int64_t row_bytes, int64_t cap, int64_t pos, int units,
                          const HotRing& ring, hipStream_t st);

@@ -88,6 +88,16 @@ class ParisKV:
     def encode_keys(self, n_tokens: int, stream=None) -> None:
         nat.check(nat.lib.pk_encode_keys(self._ctx, n_tokens, _stream(stream)), "pk_encode_keys")
 
+    def fit_centroids(self, n_tokens: int, init_pos: torch.Tensor, iters: int, stream=None) -> None:
+        """Learned-centroid comparison stage (pk_fit_centroids): k-means tables from
+        the first n_tokens stored keys; call before encode_keys.  init_pos: device
+        int32 [batch * n_kv, 256] initial positions."""
+        if (init_pos.dtype != torch.int32 or init_pos.device.type != "cuda"
+                or tuple(init_pos.shape) != (self.batch * self.n_kv, 256) or not init_pos.is_contiguous()):
+            raise ValueError("init_pos must be a contiguous cuda int32 tensor [units, 256]")
+        nat.check(nat.lib.pk_fit_centroids(self._ctx, n_tokens, _ptr(init_pos), iters, _stream(stream)),
+                  "pk_fit_centroids")
+
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
         self._check_rows(k_new, (self.batch, self.n_kv, 128))
         self._check_rows(v_new, (self.batch, self.n_kv, 128))
@@ -181,7 +191,7 @@ class ParisKV:
 
     _DBG_DTYPE = {nat.PK_DBG_IDS: np.uint8, nat.PK_DBG_REC: np.uint8, nat.PK_DBG_LUT: np.uint8,
                   nat.PK_DBG_SCORES: np.uint8, nat.PK_DBG_CAND: np.int32, nat.PK_DBG_EST: np.float32,
-                  nat.PK_DBG_NCAND: np.int32}
+                  nat.PK_DBG_NCAND: np.int32, nat.PK_DBG_CENTROIDS: np.float32}
 
     def debug(self, what: int, stream=None) -> np.ndarray:
         n = nat.lib.pk_debug_size(self._ctx, what)

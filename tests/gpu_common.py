@@ -75,8 +75,10 @@ class UnitReport:
         self.lines.append(s)
 
 
-def check_encode(wl, pkv, units, ids_all=None, rec_all=None):
-    """ids and nibbles bit-exact, w within W_RTOL, for the retrieval zone of `units`."""
+def check_encode(wl, pkv, units, ids_all=None, rec_all=None, ids_fn=None):
+    """ids and nibbles bit-exact, w within W_RTOL, for the retrieval zone of `units`.
+    ids_fn(u, keys) gives the expected ids when they are not the analytic ones
+    (the learned-centroid comparison stage)."""
     n, sink_end, r_end, _ = pkv.window()
     ids_all = pkv.debug(0) if ids_all is None else ids_all
     rec_all = pkv.debug(1) if rec_all is None else rec_all
@@ -86,6 +88,8 @@ def check_encode(wl, pkv, units, ids_all=None, rec_all=None):
         K, _, _ = unit_view(wl, u)
         pos = np.arange(sink_end, r_end)
         i_o, n_o, w_o = ok.encode_keys(K[pos], s, LEVELS, SQ_T)
+        if ids_fn is not None:
+            i_o = ids_fn(u, K[pos])
         ids_g = ids_all[u].reshape(-1, 16)[pos]
         rec_g = rec_all[u].reshape(-1, 128)[pos]
         nib_g = rec_g[:, :64]
@@ -98,8 +102,9 @@ def check_encode(wl, pkv, units, ids_all=None, rec_all=None):
     return out
 
 
-def check_retrieval(wl, pkv, units, sel, sel_n, enc):
+def check_retrieval(wl, pkv, units, sel, sel_n, enc, vote_fn=None):
     """LUT, scores, candidates bit-exact; estimates within EST_RTOL; fine sets by the tie rule.
+    vote_fn(u, Qg) gives the expected vote table when it is not the analytic one.
     Returns per-unit oracle results."""
     n, sink_end, r_end, _ = pkv.window()
     lut = pkv.debug(2)
@@ -117,7 +122,7 @@ def check_retrieval(wl, pkv, units, sel, sel_n, enc):
         i_o, n_o, w_o = enc[u]
         pos = np.arange(sink_end, r_end)
         N_r = pos.size
-        L, _ = ok.vote_table(Qg, s, p.rho, p.vote_weights)
+        L = ok.vote_table(Qg, s, p.rho, p.vote_weights)[0] if vote_fn is None else vote_fn(u, Qg)
         assert np.array_equal(lut[u].reshape(16, 256).astype(np.int64), L.astype(np.int64)), \
             f"unit {u}: vote table differs"
         sc_o = ok.coarse_scores(i_o, L) if N_r else np.zeros(0, np.int64)

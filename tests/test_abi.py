@@ -109,6 +109,7 @@ def test_calls_reject_null_context():
     assert nat.lib.pk_retrieve(None, p, p, p, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_sparse_attend(None, p, p, p, p, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_dense_attend(None, p, p, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_fit_centroids(None, 4096, p, 3, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_decode_step(None, p, p, p, p, p, p, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_debug_copy(None, 0, p, 1, None) == nat.PK_ERR_INVALID
     assert nat.lib.pk_debug_size(None, 0) == 0

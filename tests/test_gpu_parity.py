@@ -315,6 +315,54 @@ def test_decode_window_append_evict():
         win.end_step()
 
 
+def test_learned_centroids_match_oracle():
+    """Comparison stage with centroids fitted by k-means to the prefill keys: the
+    fitted tables are bit-exact against the oracle's fit, and so are the bucket ids
+    of the prefill keys and of keys evicted during decoding, the vote tables, the
+    coarse scores and candidate sets; estimates, selection and attention to the
+    usual bars."""
+    from oracle import kmeans as km
+    T, N0, iters = 140, 3000, 3
+    wl = W.gqa_bf16(N=N0, top_k=256, n_local=128, buf_tokens=64)
+    Kn, Vn, Qn = W.decode_stream(wl, T)
+    init = W.kmeans_init_positions(wl.n_units, N0)
+    pkv = gc.make_ctx(wl, capacity=N0 + T)
+    pkv.fit_centroids(N0, torch.from_numpy(init).cuda(), iters)
+    pkv.encode_keys(N0)
+    torch.cuda.synchronize()
+    s = wl.signs()
+    p = wl.params
+    units = [0, 3, 6]
+    import kv_cache_top_amd._native as nat
+    cents = pkv.debug(nat.PK_DBG_CENTROIDS).reshape(wl.n_units, 16, 256, 8)
+    ref = {}
+    for u in units:
+        K, _, _ = gc.unit_view(wl, u)
+        c_o, _ = km.fit(K[:N0], s, init[u], iters)
+        assert np.array_equal(cents[u], c_o), \
+            f"unit {u}: centroids differ at {np.argwhere(cents[u] != c_o)[:4]}"
+        ref[u] = c_o
+    ids_fn = lambda u, keys: km.encode_ids(keys, s, ref[u])
+    vote_fn = lambda u, Qg: km.vote_table(Qg, s, ref[u], p.rho, p.vote_weights)
+    dt = gc.torch_dtype(wl)
+    Kall = np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2)
+    Vall = np.concatenate([wl.V, np.moveaxis(Vn, 0, 2)], axis=2)
+    full = W.Workload(wl.name, wl.batch, wl.n_kv, wl.group, N0 + T, wl.dtype, wl.params,
+                      wl.sign_bits, Kall, Vall, wl.Q)
+    for t in range(T):
+        pkv.append(torch.from_numpy(Kn[t]).to(dt).cuda(), torch.from_numpy(Vn[t]).to(dt).cuda())
+        q = torch.from_numpy(Qn[t]).to(dt).cuda()
+        sel, sel_n = pkv.retrieve(q)
+        out = pkv.sparse_attend(q, sel, sel_n)
+        if t in (0, 64, 65, 129):
+            torch.cuda.synchronize()
+            full.Q = Qn[t]
+            enc = gc.check_encode(full, pkv, units, ids_fn=ids_fn)
+            gc.check_retrieval(full, pkv, units, sel, sel_n, enc, vote_fn=vote_fn)
+            gc.check_attention(full, pkv, units, sel, sel_n, out)
+            gc.log(f"[learned] step {t}: window {pkv.window()} ok")
+
+
 def test_decode_step_matches_separate_calls():
     """pk_decode_step (append fused into the first retrieval kernel) gives the same
     window, selection and output as append + retrieve + attend, across an eviction."""
