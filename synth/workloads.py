@@ -177,14 +177,15 @@ def single_head_f32(N=4096, seed=0, layer=0, top_k=128, threads=8) -> Workload:
 
 def gqa_bf16(N=32768, batch=1, seed=0, layer=0, top_k=2048, permille=50,
              n_sink=4, n_local=512, buf_tokens=0, n_plant=0, threads=8,
-             name=None) -> Workload:
-    """8B-class GQA layer: 8 KV heads, 4 query heads each, bf16; keys with 4
-    outlier channels (x20) on top of lognormal channel scales, values N(0,1),
-    queries drawn like the keys of their head (or planted noisy copies)."""
+             name=None, group=4, dtype="bf16") -> Workload:
+    """8B-class GQA layer: 8 KV heads, 4 query heads each (`group`), bf16 (or
+    `dtype` "f32"); keys with 4 outlier channels (x20) on top of lognormal
+    channel scales, values N(0,1), queries drawn like the keys of their head
+    (or planted noisy copies)."""
     p = Params(coarse_permille=permille, top_k=top_k, n_sink=n_sink, n_local=n_local,
                buf_tokens=buf_tokens)
-    nm = name or f"gqa_{N // 1024}k_b{batch}_bf16"
-    return _build(nm, batch, 8, 4, N, "bf16", p, seed, layer, n_outlier=4,
+    nm = name or f"gqa_{N // 1024}k_b{batch}_{dtype}" + ("" if group == 4 else f"_g{group}")
+    return _build(nm, batch, 8, group, N, dtype, p, seed, layer, n_outlier=4,
                   gqa_values_std_normal=True, n_plant=n_plant, threads=threads)
 
 

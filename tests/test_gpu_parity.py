@@ -179,6 +179,32 @@ def test_vote_variants(rho, weights, permille):
     _full_check(wl, units=[0, 3, 6], tag=f"rho{rho}-w{'-'.join(map(str, weights))}-p{permille}")
 
 
+@pytest.mark.parametrize("group,dtype", [(1, "bf16"), (2, "bf16"), (8, "bf16"), (4, "f32")])
+def test_group_sizes_and_fp32(group, dtype):
+    """Other query-group sizes (1, 2 and 8 query heads per kv head: the vote
+    tables, the summed rerank query and the attention kernels for those widths)
+    and an fp32 store with G = 4, through the separate calls and the fused decode
+    step."""
+    wl = W.gqa_bf16(N=12000, top_k=512, permille=80, group=group, dtype=dtype, buf_tokens=32,
+                    n_local=64)
+    pkv, sel, sel_n, out = _full_check(wl, units=[0, 5], capacity=12100, tag=f"g{group}-{dtype}")
+    # one fused decode step (append + retrieve + attend) against the oracle too
+    dt = gc.torch_dtype(wl)
+    Kn, Vn, Qn = W.decode_stream(wl, 1)
+    k = torch.from_numpy(Kn[0]).to(dt).cuda()
+    v = torch.from_numpy(Vn[0]).to(dt).cuda()
+    q = torch.from_numpy(Qn[0]).to(dt).cuda()
+    out, sel, sel_n = pkv.decode_step(k, v, q)
+    torch.cuda.synchronize()
+    Kall = np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2)
+    Vall = np.concatenate([wl.V, np.moveaxis(Vn, 0, 2)], axis=2)
+    full = W.Workload(wl.name, wl.batch, wl.n_kv, wl.group, wl.n_tokens + 1, wl.dtype, wl.params,
+                      wl.sign_bits, Kall, Vall, Qn[0])
+    enc = gc.check_encode(full, pkv, [0, 5])
+    gc.check_retrieval(full, pkv, [0, 5], sel, sel_n, enc)
+    gc.check_attention(full, pkv, [0, 5], sel, sel_n, out)
+
+
 def test_fine_ties_periodic_keys():
     """64 distinct keys repeated along the context: large groups of exactly tied
     estimates around the k-th (the bucket of the k-th holds a whole group)."""
