@@ -70,8 +70,21 @@ def lloyd_max(m: int = 8, n_levels: int = 8, tol: float = 1e-15, max_iter: int =
     return c, t
 
 
-def spec_tables(m: int = 8, n_levels: int = 8):
+def quantile_codebook(m: int = 8, n_levels: int = 8):
+    """The alternative reading of the Beta-prior codebook: equal-probability bins
+    (threshold t_l is the l/n quantile of |u_j|) with each level the conditional
+    mean of its bin.  Returns (levels c[0..n-1], thresholds t[0..n-2])."""
+    a, b = _beta_params(m)
+    t = np.sqrt(special.betaincinv(a, b, np.arange(1, n_levels) / n_levels))
+    edges = np.concatenate([[0.0], t, [1.0]])
+    c = np.array([bin_first_moment(edges[i], edges[i + 1], m) /
+                  bin_mass(edges[i], edges[i + 1], m) for i in range(n_levels)])
+    return c, t
+
+
+def spec_tables(m: int = 8, n_levels: int = 8, kind: str = "lloyd_max"):
     """The two fp32 tables the coding rule uses: levels fp32(c_i) and squared
-    thresholds fp32(t_l^2) (t_l^2 formed in float64, then rounded once)."""
-    c, t = lloyd_max(m, n_levels)
+    thresholds fp32(t_l^2) (t_l^2 formed in float64, then rounded once).
+    kind: "lloyd_max" (the default reading) or "quantile"."""
+    c, t = (lloyd_max if kind == "lloyd_max" else quantile_codebook)(m, n_levels)
     return c.astype(np.float32), (t * t).astype(np.float32)

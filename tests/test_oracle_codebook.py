@@ -87,3 +87,46 @@ def test_spec_tables_are_rounded_once():
     assert np.array_equal(c32, c.astype(np.float32))
     assert np.array_equal(T32, (t * t).astype(np.float32))
     assert np.all(np.diff(T32) > 0)
+
+
+# ----------------------------------------------------------- quantile reading
+
+def check_quantile_conditions(levels, thresholds):
+    """Equal-probability bins (each 1/8 of the mass, by quadrature of the density)
+    and every level the conditional mean of its bin (quadrature)."""
+    edges = np.concatenate([[0.0], thresholds, [1.0]])
+    for i, c in enumerate(levels):
+        den, _ = integrate.quad(density, edges[i], edges[i + 1], epsabs=1e-15, epsrel=1e-14)
+        if abs(den - 1.0 / len(levels)) > 1e-11:
+            return False
+        num, _ = integrate.quad(lambda a: a * density(a), edges[i], edges[i + 1],
+                                epsabs=1e-15, epsrel=1e-14)
+        if abs(num / den - c) > 1e-12:
+            return False
+    return True
+
+
+def test_quantile_codebook_conditions():
+    from oracle.codebook import quantile_codebook
+    c, t = quantile_codebook(M)
+    assert np.all(np.diff(c) > 0) and np.all(np.diff(t) > 0)
+    assert np.all((t > c[:-1]) & (t < c[1:]))          # each threshold between its levels
+    assert check_quantile_conditions(c, t)
+
+
+def test_quantile_bins_against_monte_carlo():
+    from oracle.codebook import quantile_codebook
+    _, t = quantile_codebook(M)
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((400_000, M))
+    u = np.abs(z / np.linalg.norm(z, axis=1, keepdims=True)).ravel()
+    frac = np.bincount(np.searchsorted(t, u, side="right"), minlength=8) / u.size
+    sd = math.sqrt(0.125 * 0.875 / u.size) * math.sqrt(M)
+    assert np.all(np.abs(frac - 0.125) < 5 * sd)
+
+
+def test_mutation_quantile_midpoint_thresholds_is_caught():
+    """Lloyd-Max thresholds (midpoints) do not give equal bins: the quantile pin
+    rejects them."""
+    c, t = lloyd_max(M)
+    assert not check_quantile_conditions(c, t)
