@@ -306,7 +306,8 @@ class Layer:
                            dtype=dt, rho=p.rho, vote_weights=p.vote_weights,
                            coarse_permille=p.coarse_permille, top_k=p.top_k, n_sink=p.n_sink,
                            n_local=p.n_local, buf_tokens=p.buf_tokens,
-                           sign_bits=tuple(int(x) for x in wl.sign_bits))
+                           sign_bits=tuple(int(x) for x in wl.sign_bits),
+                           codebook=0 if p.codebook == "lloyd_max" else 1)
         N = wl.n_tokens
         self.ctx.K[:, :, :N].copy_(torch.from_numpy(wl.K).to(dt))
         self.ctx.V[:, :, :N].copy_(torch.from_numpy(wl.V).to(dt))
@@ -596,6 +597,24 @@ def run_capacity_sweep(args):
         torch.cuda.empty_cache()
 
 
+def estimate_error(layer):
+    """RMS error of the last step's RSQ-IP estimates against the exact summed inner
+    products sum_g <k_i, q_g> of the candidates, relative to the RMS of the exact
+    values (every fourth unit); a quality measure of the codes, not part of the path."""
+    wl = layer.wl
+    cand, est, meta = (layer.ctx.debug(i) for i in (4, 5, 6))
+    q = layer.q[(layer.t - 1) % layer.pool].float().cpu().numpy()
+    num = den = 0.0
+    for u in range(0, wl.n_units, 4):
+        b, h = divmod(u, wl.n_kv)
+        C = int(meta[u][2])
+        pos = cand[u][:C]
+        exact = wl.K[b, h][pos].astype(np.float64) @ q[b, 4 * h:4 * h + 4].astype(np.float64).sum(0)
+        num += float(np.sum((est[u][:C].astype(np.float64) - exact) ** 2))
+        den += float(np.sum(exact ** 2))
+    return math.sqrt(num / den) if den else None
+
+
 def run_variant_sweep(args):
     """The knobs the page leaves open (probe count rho, the hierarchical vote weights,
     the coarse fraction) at 128K, batch 4, planted workload: step time, per-stage
@@ -615,7 +634,8 @@ def run_variant_sweep(args):
                 dict(rho=2, vote_weights=(2, 1), coarse_permille=50),
                 dict(rho=8, vote_weights=(8, 7, 6, 5, 4, 3, 2, 1), coarse_permille=50),
                 dict(rho=4, vote_weights=(8, 4, 2, 1), coarse_permille=50),
-                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=100)]
+                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=100),
+                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, codebook="quantile")]
     for v in variants:
         layers = [Layer(a, l, wl=wls[l], **v) for l in range(a.layers)]
         for L in layers:
@@ -624,21 +644,23 @@ def run_variant_sweep(args):
         ms = time_steps(torch, layers, a.warmup, a.steps)
         st = profiled_stages(torch, nat, layers, a.profile_steps)
         c = counts(layers[0])
-        rec, pl = [], []
+        rec, pl, ee = [], [], []
         for L in layers:
             L.step()
             torch.cuda.synchronize()
             r, p_ = recall(L)
             rec.append(r)
             pl.append(p_)
+            ee.append(estimate_error(L))
         print(json.dumps({
             "sweep": "variants", "context": a.context, "batch": a.batch,
             "rho": v["rho"], "vote_weights": list(v["vote_weights"]),
-            "coarse_permille": v["coarse_permille"],
+            "coarse_permille": v["coarse_permille"], "codebook": v.get("codebook", "lloyd_max"),
             "us_per_step": round(1e3 * ms, 2), "steps_per_s": round(1e3 / ms, 1), "stages_us": st,
             "alg_bytes_per_step": int(c["scan"] + c["rerank"] + c["attend"] + c["fine"]),
             "recall_at_k": round(float(np.mean(rec)), 4),
-            "planted_recall": round(float(np.mean(pl)), 4)}), flush=True)
+            "planted_recall": round(float(np.mean(pl)), 4),
+            "estimate_rel_rms_error": round(float(np.mean(ee)), 5)}), flush=True)
         for L in layers:
             L.ctx.close()
         del layers

@@ -71,6 +71,8 @@ typedef struct {
     int32_t n_local;           /* most recent tokens always attended                  */
     int32_t buf_tokens;        /* update buffer U (0 = static context, no appends)    */
     uint64_t sign_bits[2];     /* SRHT diagonal: D_jj = -1 where bit j is set         */
+    int32_t codebook;          /* magnitude codebook: 0 = Lloyd-Max (pk_codebook), 1 = */
+                               /* equal-probability bins (pk_codebook_quantile)       */
 } pk_config;
 
 typedef struct pk_ctx pk_ctx;  /* opaque; owned by the library */
@@ -173,6 +175,13 @@ pk_status pk_decode_step(pk_ctx* ctx, const void* k_new, const void* v_new, cons
  * = fp32 levels, sq_thresholds[n_levels-1] = fp32(t^2) of the thresholds.
  * ParisKV page: "Quantization".  Errors: PK_ERR_INVALID (m < 2, n_levels != 8, NULL). */
 pk_status pk_codebook(int32_t sub_dim, int32_t n_levels, float* levels, float* sq_thresholds);
+
+/* Host only.  The other reading of the page's Beta-prior codebook: the same
+ * law of |u_j|, cut into n_levels bins of equal probability (threshold l =
+ * the l/n_levels quantile), each level the conditional mean of its bin.  Same
+ * outputs and errors as pk_codebook.  ParisKV page: "Quantization". */
+pk_status pk_codebook_quantile(int32_t sub_dim, int32_t n_levels, float* levels,
+                               float* sq_thresholds);
 
 /* Human-readable name of a status code (static string). */
 const char* pk_status_string(pk_status s);

@@ -38,6 +38,7 @@ class PkConfig(ctypes.Structure):
         ("n_local", ctypes.c_int32),
         ("buf_tokens", ctypes.c_int32),
         ("sign_bits", ctypes.c_uint64 * 2),
+        ("codebook", ctypes.c_int32),
     ]
 
 
@@ -56,6 +57,8 @@ SIGNATURES = {
     "pk_fit_centroids": (_i32, [_c_void_p, _i64, _c_void_p, _i32, _c_void_p]),
     "pk_codebook": (_i32, [_i32, _i32, ctypes.POINTER(ctypes.c_float),
                            ctypes.POINTER(ctypes.c_float)]),
+    "pk_codebook_quantile": (_i32, [_i32, _i32, ctypes.POINTER(ctypes.c_float),
+                                    ctypes.POINTER(ctypes.c_float)]),
     "pk_status_string": (ctypes.c_char_p, [_i32]),
     "pk_get_window": (_i32, [_c_void_p, ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                              ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
@@ -108,18 +111,20 @@ def check(status: int, where: str) -> None:
         raise PkError(status, where)
 
 
-def codebook(sub_dim: int = 8):
-    """(levels fp32[8], squared thresholds fp32[7]) as computed by the library (host only)."""
+def codebook(sub_dim: int = 8, kind: str = "lloyd_max"):
+    """(levels fp32[8], squared thresholds fp32[7]) as computed by the library (host
+    only); kind "lloyd_max" (pk_codebook) or "quantile" (pk_codebook_quantile)."""
     import numpy as np
     lv = (ctypes.c_float * 8)()
     th = (ctypes.c_float * 7)()
-    check(lib.pk_codebook(sub_dim, 8, lv, th), "pk_codebook")
+    fn = lib.pk_codebook if kind == "lloyd_max" else lib.pk_codebook_quantile
+    check(fn(sub_dim, 8, lv, th), "pk_codebook")
     return np.array(lv[:], np.float32), np.array(th[:], np.float32)
 
 
 def make_config(*, rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, top_k=2048, n_sink=4,
                 n_local=512, buf_tokens=0, sign_bits=(0, 0), head_dim=128, n_sub=16,
-                sub_dim=8) -> PkConfig:
+                sub_dim=8, codebook=0) -> PkConfig:
     cfg = PkConfig()
     cfg.head_dim, cfg.n_sub, cfg.sub_dim, cfg.rho = head_dim, n_sub, sub_dim, rho
     for i in range(8):
@@ -127,4 +132,5 @@ def make_config(*, rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, top_k=2
     cfg.coarse_permille, cfg.top_k = coarse_permille, top_k
     cfg.n_sink, cfg.n_local, cfg.buf_tokens = n_sink, n_local, buf_tokens
     cfg.sign_bits[0], cfg.sign_bits[1] = int(sign_bits[0]), int(sign_bits[1])
+    cfg.codebook = codebook
     return cfg

@@ -174,6 +174,7 @@ pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capac
     if (cfg->head_dim != 128 || cfg->n_sub != 16 || cfg->sub_dim != 8) return PK_ERR_UNSUPPORTED;
     if (cfg->rho < 1 || cfg->rho > pk::kRhoMax) return PK_ERR_INVALID;
     if (cfg->coarse_permille < 1 || cfg->coarse_permille > 1000) return PK_ERR_INVALID;
+    if (cfg->codebook != 0 && cfg->codebook != 1) return PK_ERR_INVALID;
     if (cfg->top_k < 1 || cfg->n_sink < 0 || cfg->n_local < 0 || cfg->buf_tokens < 0)
         return PK_ERR_INVALID;
     if (cfg->buf_tokens > 0 && cfg->buf_tokens > cfg->n_local) return PK_ERR_INVALID;
@@ -358,7 +359,8 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     c->nbins = nbins;
     c->hstride = (nbins + 7) / 8 * 8;
     c->sstride = (capacity + 7) / 8 * 8;
-    if (pk_codebook(cfg->sub_dim, 8, c->tab.levels, c->tab.sq_thr) != PK_OK) {
+    if ((cfg->codebook == 0 ? pk_codebook : pk_codebook_quantile)(cfg->sub_dim, 8, c->tab.levels,
+                                                                    c->tab.sq_thr) != PK_OK) {
         delete c;
         return PK_ERR_INVALID;
     }

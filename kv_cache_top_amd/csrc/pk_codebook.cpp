@@ -46,6 +46,35 @@ struct AbsCoordLaw {
 
 }  // namespace
 
+// Alternative reading: equal-probability bins (threshold l = the l/n quantile of
+// a, found by bisection on the closed-form law) with conditional-mean levels.
+extern "C" pk_status pk_codebook_quantile(int32_t sub_dim, int32_t n_levels, float* levels,
+                                          float* sq_thresholds) {
+    if (sub_dim < 2 || n_levels != 8 || !levels || !sq_thresholds) return PK_ERR_INVALID;
+    const AbsCoordLaw law(sub_dim);
+    const int n = n_levels;
+    double t[8];
+    for (int i = 0; i < n - 1; ++i) {
+        const double target = (i + 1.0) / n;
+        double lo = 0.0, hi = 1.0;
+        for (int it = 0; it < 200 && hi - lo > 0.0; ++it) {
+            const double mid = 0.5 * (lo + hi);
+            if (mid <= lo || mid >= hi) break;   // adjacent doubles
+            (law.cdf(mid) < target ? lo : hi) = mid;
+        }
+        t[i] = 0.5 * (lo + hi);
+    }
+    double lo = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const double hi = (i == n - 1) ? 1.0 : t[i];
+        levels[i] = (float)((law.partial_moment(hi) - law.partial_moment(lo)) /
+                            (law.cdf(hi) - law.cdf(lo)));
+        lo = hi;
+    }
+    for (int i = 0; i < n - 1; ++i) sq_thresholds[i] = (float)(t[i] * t[i]);
+    return PK_OK;
+}
+
 extern "C" pk_status pk_codebook(int32_t sub_dim, int32_t n_levels, float* levels,
                                  float* sq_thresholds) {
     if (sub_dim < 2 || n_levels != 8 || !levels || !sq_thresholds) return PK_ERR_INVALID;

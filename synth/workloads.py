@@ -48,6 +48,7 @@ class Params:
     n_sink: int = 4
     n_local: int = 512
     buf_tokens: int = 0      # U (update buffer); 0 = static context
+    codebook: str = "lloyd_max"   # magnitude codebook reading: "lloyd_max" or "quantile"
 
 
 @dataclasses.dataclass

@@ -12,6 +12,12 @@ from oracle import pariskv as ok
 from oracle.codebook import spec_tables
 
 LEVELS, SQ_T = spec_tables()
+_TABLES = {"lloyd_max": (LEVELS, SQ_T), "quantile": spec_tables(kind="quantile")}
+
+
+def tables(wl):
+    """(levels, squared thresholds) of the workload's codebook reading."""
+    return _TABLES[getattr(wl.params, "codebook", "lloyd_max")]
 
 # acceptance bars
 W_RTOL = 1e-6          # calibration scale (fp32 on both sides; derivation in the design notes)
@@ -33,7 +39,8 @@ def make_ctx(wl, capacity=None, host_mapped=False, **override):
     p = wl.params
     kw = dict(rho=p.rho, vote_weights=p.vote_weights, coarse_permille=p.coarse_permille,
               top_k=p.top_k, n_sink=p.n_sink, n_local=p.n_local, buf_tokens=p.buf_tokens,
-              sign_bits=tuple(int(x) for x in wl.sign_bits))
+              sign_bits=tuple(int(x) for x in wl.sign_bits),
+              codebook=0 if p.codebook == "lloyd_max" else 1)
     kw.update(override)
     cap = capacity or wl.n_tokens
     dt = torch_dtype(wl)
@@ -55,9 +62,9 @@ def unit_view(wl, u):
     return wl.K[b, h], wl.V[b, h], wl.Q[b, h * wl.group:(h + 1) * wl.group]
 
 
-def est_scale(nib, w, Qg, signs):
+def est_scale(nib, w, Qg, signs, levels=LEVELS):
     """sum_g sum_b |w_b <v_b, (R q_g)_b>|: the magnitude the estimate error is measured against."""
-    v = ok.dequantize(ok.unpack_nibbles(nib, 16, 8), LEVELS)
+    v = ok.dequantize(ok.unpack_nibbles(nib, 16, 8), levels)
     R = ok.srht_matrix(signs)
     w = np.asarray(w, np.float64)
     s = np.zeros(v.shape[0])
@@ -87,7 +94,7 @@ def check_encode(wl, pkv, units, ids_all=None, rec_all=None, ids_fn=None):
     for u in units:
         K, _, _ = unit_view(wl, u)
         pos = np.arange(sink_end, r_end)
-        i_o, n_o, w_o = ok.encode_keys(K[pos], s, LEVELS, SQ_T)
+        i_o, n_o, w_o = ok.encode_keys(K[pos], s, *tables(wl))
         if ids_fn is not None:
             i_o = ids_fn(u, K[pos])
         ids_g = ids_all[u].reshape(-1, 16)[pos]
@@ -134,8 +141,8 @@ def check_retrieval(wl, pkv, units, sel, sel_n, enc, vote_fn=None):
         cand_o = ok.top_by_key(sc_o, pos, C)
         assert np.array_equal(cand[u][:C], cand_o), f"unit {u}: coarse candidate set differs"
         rel = cand_o - sink_end
-        e_o = ok.rsq_ip(n_o[rel], w_o[rel], Qg, s, LEVELS) if C else np.zeros(0)
-        scale = est_scale(n_o[rel], w_o[rel], Qg, s) if C else np.zeros(0)
+        e_o = ok.rsq_ip(n_o[rel], w_o[rel], Qg, s, tables(wl)[0]) if C else np.zeros(0)
+        scale = est_scale(n_o[rel], w_o[rel], Qg, s, tables(wl)[0]) if C else np.zeros(0)
         err = np.abs(est[u][:C].astype(np.float64) - e_o)
         assert np.all(err <= EST_RTOL * np.maximum(scale, 1e-30)), \
             f"unit {u}: est rel err {np.max(err / np.maximum(scale, 1e-30)):.3g}"

@@ -42,11 +42,12 @@ def test_status_strings():
 
 
 def test_library_codebook_matches_oracle_bit_exact():
-    for m in (4, 8, 16):
-        lv, th = nat.codebook(m)
-        c32, T32 = spec_tables(m)
-        assert np.array_equal(lv.view(np.uint32), c32.view(np.uint32))
-        assert np.array_equal(th.view(np.uint32), T32.view(np.uint32))
+    for kind in ("lloyd_max", "quantile"):
+        for m in (4, 8, 16):
+            lv, th = nat.codebook(m, kind)
+            c32, T32 = spec_tables(m, kind=kind)
+            assert np.array_equal(lv.view(np.uint32), c32.view(np.uint32)), (kind, m)
+            assert np.array_equal(th.view(np.uint32), T32.view(np.uint32)), (kind, m)
 
 
 def test_codebook_rejects_bad_arguments():

@@ -205,6 +205,16 @@ def test_group_sizes_and_fp32(group, dtype):
     gc.check_attention(full, pkv, [0, 5], sel, sel_n, out)
 
 
+def test_quantile_codebook():
+    """The other reading of the Beta-prior codebook (equal-probability bins):
+    nibbles bit-exact, w and the estimates within tolerance, sets and attention
+    as usual, with the library's own quantile tables."""
+    import dataclasses
+    wl = W.gqa_bf16(N=20000, top_k=512, permille=80)
+    wl.params = dataclasses.replace(wl.params, codebook="quantile")
+    _full_check(wl, units=[0, 4, 7], tag="quantile-codebook")
+
+
 def test_fine_ties_periodic_keys():
     """64 distinct keys repeated along the context: large groups of exactly tied
     estimates around the k-th (the bucket of the k-th holds a whole group)."""
