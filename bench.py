@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=4)
     ap.add_argument("--buf-tokens", type=int, default=256)
     ap.add_argument("--profile-steps", type=int, default=40)
+    ap.add_argument("--warm-steps", type=int, default=256,
+                    help="steps timed on one layer replica only (its working set can stay in "
+                         "the last-level cache), reported beside the graded cycled figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=4)
     ap.add_argument("--threads", type=int, default=16)
@@ -299,7 +302,8 @@ class Layer:
             wl = dataclasses.replace(wl, params=dataclasses.replace(wl.params, **override))
         self.wl = wl
         p = wl.params
-        steps_here = (args.warmup + args.steps + args.profile_steps) // args.layers + 2
+        steps_here = (args.warmup + args.steps + args.profile_steps) // args.layers + 2 + \
+            (args.warm_steps + 16 if layer == 0 else 0)
         self.cap = args.context + steps_here + 8
         dt = torch.bfloat16
         self.ctx = ParisKV(batch=wl.batch, n_kv=wl.n_kv, n_q=wl.n_kv * wl.group, capacity=self.cap,
@@ -764,6 +768,10 @@ def main():
 
     rec, planted = recall(layers[(base + args.profile_steps - 1) % nl])
     dense = dense_reference(torch, layers[0], ms_step)
+    warm = None
+    if args.warm_steps > 0:
+        ms_warm = time_steps(torch, [layers[0]], 16, args.warm_steps)
+        warm = {"steps": args.warm_steps, "us_per_step": 1e3 * ms_warm, "steps_per_s": 1e3 / ms_warm}
     sref = stream_reference(torch)
     cpu = None
     if not args.no_cpu_baseline:
@@ -808,6 +816,7 @@ def main():
                           "bytes_per_step": int(comb_bytes), "kernel_us_per_step": comb_us},
         "stream_reference": sref,
         "dense_attention": dense,
+        "warm_single_layer": warm,
         "stages": stages,
         "keys_scanned_per_s": keys_per_step * 1e3 / ms_step,
         "host_submit_ms_per_step": 1e3 * host_s / args.steps,
