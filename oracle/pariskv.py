@@ -116,6 +116,16 @@ def _tree8(t: np.ndarray) -> np.ndarray:
            ((t[..., 4] + t[..., 5]) + (t[..., 6] + t[..., 7]))
 
 
+def _tree(t: np.ndarray) -> np.ndarray:
+    """The spec's pairwise fp32 sum over the last axis (m = 8: _tree8; m = 4:
+    (t0+t1)+(t2+t3))."""
+    t = np.asarray(t, np.float32)
+    if t.shape[-1] == 8:
+        return _tree8(t)
+    assert t.shape[-1] == 4, "spec trees exist for m = 4 and m = 8"
+    return (t[..., 0] + t[..., 1]) + (t[..., 2] + t[..., 3])
+
+
 def quantize_codes(x: np.ndarray, sq_thresholds: np.ndarray, n_sub: int, m: int):
     """Sign + 3-bit magnitude code of every coordinate of every subspace direction.
 
@@ -126,10 +136,10 @@ def quantize_codes(x: np.ndarray, sq_thresholds: np.ndarray, n_sub: int, m: int)
     ss_b is zero gets all-zero nibbles.  Returns uint8 [n, n_sub, m] and the
     fp32 ss [n, n_sub].
     """
-    assert m == 8, "the spec tree is written for m = 8"
+    assert m in (4, 8), "spec trees exist for m = 4 and m = 8"
     xb = np.asarray(x, np.float32).reshape(-1, n_sub, m)
     sq = xb * xb
-    ss = _tree8(sq)
+    ss = _tree(sq)
     T = np.asarray(sq_thresholds, np.float32)
     mag = np.zeros(xb.shape, np.int64)
     for l in range(T.shape[0]):
@@ -206,16 +216,17 @@ def encode_keys(K: np.ndarray, signs: np.ndarray, levels: np.ndarray,
 
 
 def centroid_scores(y_b: np.ndarray) -> np.ndarray:
-    """fp32 similarity of a rotated query subspace y_b (m = 8) to all 256 centroids.
+    """fp32 similarity of a rotated query subspace y_b (m = 8 or 4) to all 2^m centroids.
 
     Score(c) = pairwise fp32 sum of t_j, t_j = -y_j if bit j of c is set else
     y_j.  This is sqrt(m) times the inner product with centroid c; the dropped
     positive factors do not change the ranking.
     """
-    bits = ((np.arange(256)[:, None] >> np.arange(8)[None, :]) & 1).astype(bool)
     y = np.asarray(y_b, np.float32)
+    m = y.shape[0]
+    bits = ((np.arange(1 << m)[:, None] >> np.arange(m)[None, :]) & 1).astype(bool)
     t = np.where(bits, -y[None, :], y[None, :]).astype(np.float32)
-    return _tree8(t)
+    return _tree(t)
 
 
 def top_rho(scores: np.ndarray, rho: int) -> np.ndarray:

@@ -319,3 +319,75 @@ def test_window_partitions_sequence():
 
 def test_recall_definition():
     assert pk.recall(np.array([1, 2, 3]), np.array([2, 3, 4, 5])) == 0.5
+
+
+# ------------------------------------------------------ subspaces of m = 4
+
+def check_m4_ids_and_top_rho(bucket_ids, centroid_scores, top_rho):
+    """m = 4 (32 subspaces of 4 coordinates, 16 sign-pattern centroids each):
+    ids by brute force over the 16 centroids (exact zeros present), and on
+    integer queries the spec scores equal the exact scaled inner products with
+    top-rho ties to the lower index."""
+    r = np.random.default_rng(11)
+    x = r.standard_normal((30, D)).astype(np.float32)
+    x[r.random(x.shape) < 0.1] = 0.0
+    ids = bucket_ids(x, 32, 4)
+    C = np.stack([pk.centroid(c, 4) for c in range(16)])
+    for i in range(x.shape[0]):
+        for b in range(32):
+            dots = C @ x[i, 4 * b:4 * b + 4].astype(np.float64)
+            if ids[i, b] != max(range(16), key=lambda c: (dots[c], -c)):
+                return False
+    C2 = C * 2.0
+    for _ in range(200):
+        y = r.integers(-3, 4, size=4).astype(np.float32)
+        sc = centroid_scores(y)
+        if sc.shape != (16,) or not np.array_equal(sc.astype(np.float64), C2 @ y.astype(np.float64)):
+            return False
+        if list(top_rho(sc, 4)) != sorted(range(16), key=lambda c: (-float(C2[c] @ y), c))[:4]:
+            return False
+    return True
+
+
+def test_m4_ids_and_top_rho():
+    assert check_m4_ids_and_top_rho(pk.bucket_ids, pk.centroid_scores, pk.top_rho)
+
+
+def test_m4_codes_follow_the_real_number_rule():
+    """m = 4 codes with the m = 4 codebook: the fp32 rule agrees with the
+    real-number bin rule |u_j| >= t_l away from the thresholds."""
+    from oracle.codebook import lloyd_max
+    _, t = lloyd_max(4)
+    T32 = (t * t).astype(np.float32)
+    r = np.random.default_rng(12)
+    x = r.standard_normal((500, D)).astype(np.float32)
+    nib, ss = pk.quantize_codes(x, T32, 32, 4)
+    xb = x.reshape(-1, 32, 4).astype(np.float64)
+    u = np.abs(xb) / np.linalg.norm(xb, axis=2, keepdims=True)
+    mag = np.sum(u[..., None] >= t[None, None, None, :], axis=-1)
+    far = np.min(np.abs(u[..., None] - t), axis=-1) > 1e-6
+    assert np.array_equal((nib & 7)[far], mag[far])
+    assert np.array_equal((nib >> 3) & 1, (xb < 0).astype(np.uint8))
+
+
+def test_m4_rsq_ip_identity():
+    """With identity quantisation (v = u) the m = 4 estimate is the exact
+    summed inner product."""
+    r = np.random.default_rng(13)
+    s = _signs(13)
+    K = r.standard_normal((50, D))
+    Qg = r.standard_normal((4, D))
+    x = pk.srht_matrix(s) @ K.T * math.sqrt(D)
+    xb = x.T.reshape(-1, 32, 4)
+    u = xb / np.linalg.norm(xb, axis=2, keepdims=True)
+    w = pk.calibrate_w(x.T, u, np.ones((50, 32)), 32, 4)
+    est = pk.rsq_ip_directions(u, w, Qg, s)
+    assert np.allclose(est, K @ Qg.sum(0), rtol=1e-12, atol=1e-10)
+
+
+def test_mutation_m4_tree_dropping_a_term_is_caught():
+    def bad(y_b):
+        y = np.asarray(y_b, np.float32).copy()
+        y[3] = 0.0
+        return pk.centroid_scores(y)
+    assert not check_m4_ids_and_top_rho(pk.bucket_ids, bad, pk.top_rho)
