@@ -311,7 +311,8 @@ class Layer:
                            coarse_permille=p.coarse_permille, top_k=p.top_k, n_sink=p.n_sink,
                            n_local=p.n_local, buf_tokens=p.buf_tokens,
                            sign_bits=tuple(int(x) for x in wl.sign_bits),
-                           codebook=0 if p.codebook == "lloyd_max" else 1)
+                           codebook=0 if p.codebook == "lloyd_max" else 1, n_sub=p.n_sub,
+                           sub_dim=p.sub_dim)
         N = wl.n_tokens
         self.ctx.K[:, :, :N].copy_(torch.from_numpy(wl.K).to(dt))
         self.ctx.V[:, :, :N].copy_(torch.from_numpy(wl.V).to(dt))
@@ -376,8 +377,8 @@ def measured_traffic():
 
 def counts(layer):
     """Algorithmic HBM bytes of one step's scan / rerank / attention on this layer at
-    its current window: scan 16 B per retrieval-zone key, rerank 128 B per
-    candidate, attention one bf16 K row and one V row (512 B) per attended key.  The
+    its current window: scan 16 B per retrieval-zone key, rerank one record per
+    candidate (64 B of codes + 4 B per subspace: 128 B for m = 8), attention one bf16 K row and one V row (512 B) per attended key.  The
     hot-zone rows (sink, local, buffer) are gathered by the fine-selection launch
     (bf16 device stores, G <= 4, at most 16384 candidates), the selected rows by
     the attention launch."""
@@ -390,7 +391,7 @@ def counts(layer):
     hot = sink_end + (n - r_end)
     fused = layer.wl.dtype == "bf16" and layer.wl.group <= 4 and C <= 16384 and \
         not getattr(layer, "host_mapped", False)
-    return dict(scan=16 * n_r * units, rerank=128 * C * units,
+    return dict(scan=16 * n_r * units, rerank=(64 + 4 * p.n_sub) * C * units,
                 attend=512 * (k_eff + (0 if fused else hot)) * units,
                 fine=512 * hot * units if fused else 0, keys=n_r * units)
 
@@ -621,7 +622,7 @@ def estimate_error(layer):
 
 def run_variant_sweep(args):
     """The knobs the page leaves open (probe count rho, the hierarchical vote weights,
-    the coarse fraction) at 128K, batch 4, planted workload: step time, per-stage
+    the coarse fraction, the codebook, the subspace width m) at 128K, batch 4, planted workload: step time, per-stage
     durations, algorithmic bytes and recall@k / planted recall (mean over one step
     per layer replica, every fourth unit) per setting."""
     import copy
@@ -639,7 +640,8 @@ def run_variant_sweep(args):
                 dict(rho=8, vote_weights=(8, 7, 6, 5, 4, 3, 2, 1), coarse_permille=50),
                 dict(rho=4, vote_weights=(8, 4, 2, 1), coarse_permille=50),
                 dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=100),
-                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, codebook="quantile")]
+                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, codebook="quantile"),
+                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, n_sub=32, sub_dim=4)]
     for v in variants:
         layers = [Layer(a, l, wl=wls[l], **v) for l in range(a.layers)]
         for L in layers:
@@ -660,6 +662,7 @@ def run_variant_sweep(args):
             "sweep": "variants", "context": a.context, "batch": a.batch,
             "rho": v["rho"], "vote_weights": list(v["vote_weights"]),
             "coarse_permille": v["coarse_permille"], "codebook": v.get("codebook", "lloyd_max"),
+            "subspaces": v.get("n_sub", 16), "sub_dim": v.get("sub_dim", 8),
             "us_per_step": round(1e3 * ms, 2), "steps_per_s": round(1e3 / ms, 1), "stages_us": st,
             "alg_bytes_per_step": int(c["scan"] + c["rerank"] + c["attend"] + c["fine"]),
             "recall_at_k": round(float(np.mean(rec)), 4),

@@ -9,7 +9,7 @@
  * attention over sink + local + update buffer + the retrieved keys.
  *
  * Terms used below:
- *   d      head dimension (128)           B   subspaces (16)     m  coordinates per subspace (8)
+ *   d      head dimension (128)           B   subspaces (16 or 32) m  coordinates per subspace (8 or 4)
  *   unit   one (batch, kv head) sequence  G   query heads per kv head (grouped-query attention)
  *   cap    capacity in tokens per unit    N   tokens currently held per unit
  *
@@ -58,11 +58,15 @@ typedef enum { PK_MEM_DEVICE = 0, PK_MEM_HOST_MAPPED = 1 } pk_mem;
 
 /* Method parameters.  ParisKV page: "Analytic centroids" (B, m), "Coarse
  * candidate generation" (rho, vote weights, candidate fraction), "Sliding-window
- * update mechanism" (zones).  Supported: head_dim 128, n_sub 16, sub_dim 8. */
+ * update mechanism" (zones).  Supported: head_dim 128 and (n_sub, sub_dim) =
+ * (16, 8) or (32, 4); n_sub * sub_dim != head_dim is PK_ERR_INVALID, other
+ * widths PK_ERR_UNSUPPORTED.  With m = 4 the 2^4 sign-pattern centroids of a
+ * subspace give 4-bit ids, two per id byte, and G * max(weight) <= 127. */
 typedef struct {
     int32_t head_dim;          /* d = 128                                             */
-    int32_t n_sub;             /* B = 16                                              */
-    int32_t sub_dim;           /* m = 8 (256 sign-pattern centroids per subspace)     */
+    int32_t n_sub;             /* B = 16 (or 32)                                      */
+    int32_t sub_dim;           /* m = 8: 256 sign-pattern centroids per subspace;     */
+                               /* m = 4: 16 of them                                   */
     int32_t rho;               /* centroids picked per subspace and query head, 1..8  */
     uint8_t vote_weight[8];    /* vote of a rank-r pick (r = 0 is the best), 1..255   */
     int32_t coarse_permille;   /* candidates kept = max(top_k, ceil(p * N_r / 1000)), capped at N_r */
@@ -78,11 +82,12 @@ typedef struct {
 typedef struct pk_ctx pk_ctx;  /* opaque; owned by the library */
 
 /* Create a context over the caller's K/V store.
- * Owns: the per-key metadata (16 B of bucket ids and a 128 B record of codes
- * and scales per token), the window counters and all scratch.  The caller
+ * Owns: the per-key metadata (16 B of bucket ids and a record of codes and
+ * scales per token: 64 B of 4-bit codes + 4 B per subspace, so 128 B for m = 8
+ * and 192 B for m = 4), the window counters and all scratch.  The caller
  * keeps ownership of k_store / v_store, which must outlive the context.
  * Requires n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8} (other G up to 16
- * are valid but PK_ERR_UNSUPPORTED), G * max(weight) <= 255, buf_tokens <=
+ * are valid but PK_ERR_UNSUPPORTED), G * max(weight) <= 255 (m = 8; 127 for m = 4), buf_tokens <=
  * n_local, capacity <= 2^24.  Allocates device memory and synchronises the device.
  * Errors: PK_ERR_INVALID, PK_ERR_UNSUPPORTED, PK_ERR_NO_DEVICE, PK_ERR_OOM. */
 pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,
@@ -157,7 +162,8 @@ pk_status pk_dense_attend(pk_ctx* ctx, const void* q, float* out, void* stream);
  * call allocates the tables (units x 16 x 256 x 8 floats, and as many 64-bit
  * sums).
  * Errors: PK_ERR_INVALID (NULL, keys already encoded, n_tokens < 256, a
- * position out of range, iters outside 0..1000), PK_ERR_CAPACITY, PK_ERR_OOM. */
+ * position out of range, iters outside 0..1000), PK_ERR_UNSUPPORTED (m != 8),
+ * PK_ERR_CAPACITY, PK_ERR_OOM. */
 pk_status pk_fit_centroids(pk_ctx* ctx, int64_t n_tokens, const int32_t* init_pos, int32_t iters,
                            void* stream);
 
@@ -214,9 +220,10 @@ pk_status pk_profile_read(pk_ctx* ctx, double* ms, int64_t* launches);
 /* Debug read-back for tests: copies an internal buffer to host memory and
  * synchronises the stream.  `bytes` must equal the size reported by
  * pk_debug_size for `what`.
- *   PK_DBG_IDS     uint8  [units][cap][B]           bucket ids
- *   PK_DBG_REC     uint8  [units][cap][128]         64 B nibbles (coord 2i in low half of byte i) + float32 w[B]
- *   PK_DBG_LUT     uint8  [units][B][256]           vote table of the last pk_retrieve
+ *   PK_DBG_IDS     uint8  [units][cap][16]          bucket ids (m = 4: subspace 2i in the low half of byte i)
+ *   PK_DBG_REC     uint8  [units][cap][64 + 4B]     64 B nibbles (coord 2i in low half of byte i) + float32 w[B]
+ *   PK_DBG_LUT     uint8  [units][16][256]          vote of each id-byte value, last pk_retrieve (m = 4:
+ *                                                   row i entry c = L[2i][c & 15] + L[2i+1][c >> 4])
  *   PK_DBG_SCORES  uint8  [units][cap]              min(coarse score, 255) of retrieval position sink_end + i
  *   PK_DBG_CAND    int32  [units][cmax]             candidate positions (ascending), first n_cand valid
  *   PK_DBG_EST     float  [units][cmax]             RSQ-IP estimate of each candidate

@@ -163,6 +163,10 @@ void free_all(pk_ctx* c) {
 
 // attention splits: the hot tokens (at most sink + local + buffer) and the
 // selection are split separately
+size_t rec_bytes(int sub_dim) {
+    return sub_dim == 4 ? (size_t)pk::rec_bytes<4>() : (size_t)pk::rec_bytes<8>();
+}
+
 int64_t max_attend_splits(const pk_config& cfg) {
     const int64_t hot = (int64_t)cfg.n_sink + cfg.n_local + cfg.buf_tokens;
     return ceil_div(hot, pk::attend_split_keys()) + ceil_div(cfg.top_k, pk::attend_split_keys());
@@ -171,7 +175,9 @@ int64_t max_attend_splits(const pk_config& cfg) {
 pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capacity, int* G_out,
                           int* nbins_out) {
     if (!cfg || n_kv < 1 || n_q < 1 || capacity < 1) return PK_ERR_INVALID;
-    if (cfg->head_dim != 128 || cfg->n_sub != 16 || cfg->sub_dim != 8) return PK_ERR_UNSUPPORTED;
+    if (cfg->head_dim != 128) return PK_ERR_UNSUPPORTED;
+    if (cfg->n_sub * cfg->sub_dim != cfg->head_dim) return PK_ERR_INVALID;
+    if (cfg->sub_dim != 8 && cfg->sub_dim != 4) return PK_ERR_UNSUPPORTED;
     if (cfg->rho < 1 || cfg->rho > pk::kRhoMax) return PK_ERR_INVALID;
     if (cfg->coarse_permille < 1 || cfg->coarse_permille > 1000) return PK_ERR_INVALID;
     if (cfg->codebook != 0 && cfg->codebook != 1) return PK_ERR_INVALID;
@@ -187,7 +193,8 @@ pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capac
         if (cfg->vote_weight[r] < 1) return PK_ERR_INVALID;
         if (cfg->vote_weight[r] > wmax) wmax = cfg->vote_weight[r];
     }
-    if (G * wmax > 255) return PK_ERR_INVALID;
+    // a vote-table byte holds the votes of one subspace (m = 8) or of two (m = 4)
+    if (G * wmax * (8 / cfg->sub_dim) > 255) return PK_ERR_INVALID;
     const int nbins = cfg->n_sub * G * wmax + 1;
     if (nbins > pk::kMaxBins) return PK_ERR_UNSUPPORTED;
     if (capacity > (int64_t)1 << 24) return PK_ERR_UNSUPPORTED;
@@ -242,7 +249,8 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     {
         StageTimer tm(c, PK_STAGE_QPREP, st);
         PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
-                                c->cfg.vote_weight, c->cents, c->lut, c->ysum, k_new, v_new, c->K, c->V,
+                                c->cfg.vote_weight, c->cents, c->lut, c->ysum, c->cfg.sub_dim, k_new,
+                                v_new, c->K, c->V,
                                 row, c->cap, c->n - 1, c->ring, st));
     }
     const int64_t n_r = c->r_end - c->sink_end;
@@ -364,6 +372,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         delete c;
         return PK_ERR_INVALID;
     }
+    c->tab.sub_dim = cfg->sub_dim;
     c->max_chunks = (int)std::min<int64_t>(pk::kMaxChunks, ceil_div(capacity, 256));
     // candidate rows hold a multiple of 64 entries: the fine selection reads a
     // thread's (up to 64) candidates in 16-byte vectors
@@ -377,7 +386,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         size_t bytes;
     } allocs[] = {
         {(void**)&c->ids, (size_t)(U * capacity * pk::kSub)},
-        {(void**)&c->rec, (size_t)(U * capacity * pk::kRec)},
+        {(void**)&c->rec, (size_t)(U * capacity * rec_bytes(cfg->sub_dim))},
         {(void**)&c->lut, (size_t)(U * pk::kSub * 256)},
         {(void**)&c->ysum, (size_t)(U * pk::kD * 4)},
         // score rows padded to 16 B; the tail pad covers vector reads past the last row
@@ -471,6 +480,7 @@ pk_status pk_fit_centroids(pk_ctx* c, int64_t n_tokens, const int32_t* init_pos,
                            void* stream) {
     if (!c || !init_pos || iters < 0 || iters > 1000) return PK_ERR_INVALID;
     if (c->prefilled) return PK_ERR_INVALID;          // ids of encoded keys would be stale
+    if (c->cfg.sub_dim != 8) return PK_ERR_UNSUPPORTED;   // 256 fitted centroids of 8 coordinates
     if (n_tokens < 256) return PK_ERR_INVALID;
     if (n_tokens > c->cap) return PK_ERR_CAPACITY;
     const hipStream_t st = (hipStream_t)stream;
@@ -604,7 +614,7 @@ size_t pk_debug_size(const pk_ctx* c, int32_t what) {
     const size_t U = (size_t)c->units, cap = (size_t)c->cap;
     switch (what) {
         case PK_DBG_IDS: return U * cap * pk::kSub;
-        case PK_DBG_REC: return U * cap * pk::kRec;
+        case PK_DBG_REC: return U * cap * rec_bytes(c->cfg.sub_dim);
         case PK_DBG_LUT: return U * pk::kSub * 256;
         case PK_DBG_SCORES: return U * cap;
         case PK_DBG_CAND: return U * (size_t)c->cmax * 4;

@@ -13,9 +13,15 @@
 namespace pk {
 
 constexpr int kD = 128;          // head dim
-constexpr int kSub = 16;         // B
-constexpr int kSubDim = 8;       // m
-constexpr int kRec = 128;        // record bytes per key: 64 B nibbles + 16 x f32 w
+constexpr int kSub = 16;         // bucket-id bytes per key = rows of the scan's vote table
+// Subspaces: B = 16 of m = 8 coordinates (one id byte each), or B = 32 of m = 4
+// (two 4-bit ids per byte: subspace 2i in the low half of byte i).  Either way
+// a key has 16 id bytes, and the vote table the scan reads has one 256-entry
+// row per id byte (for m = 4 an entry is the sum of the two subspaces' votes).
+// Record of a key: 64 B of nibbles (coordinate 2i in the low half of byte i),
+// then B fp32 scales w.
+template <int M>
+constexpr int rec_bytes() { return 64 + 4 * (kD / M); }   // 128 (m = 8), 192 (m = 4)
 constexpr int kRhoMax = 8;
 constexpr int kMaxBins = 4096;   // coarse-score histogram bins (B * G * max weight + 1)
 constexpr int kMaxChunks = 2048; // scan chunks per unit
@@ -24,6 +30,7 @@ constexpr int kBlock = 256;      // threads per block of the streaming kernels
 struct CodeTables {
     float sq_thr[7];   // fp32(t_l^2), ascending
     float levels[8];   // fp32 Lloyd-Max levels
+    int32_t sub_dim;   // m: 8 or 4
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -12,14 +12,20 @@ namespace pk {
 
 // ---------------------------------------------------------------------------
 // encode: one 16-lane group per key.  Reads the key row once (256 B bf16 /
-// 512 B fp32) and writes 16 B of ids and a 128 B record.
+// 512 B fp32) and writes 16 B of ids and a record (128 B for m = 8, 192 B for
+// m = 4).  Lane l holds rotated coordinates 8l..8l+7: one subspace of m = 8,
+// or the two subspaces 2l, 2l+1 of m = 4.  Either way its id byte is the sign
+// bits of its 8 coordinates (bit r = [x_{8l+r} < 0]) and its nibble word the
+// 8 codes; for m = 4 the magnitudes of each half are coded against that
+// half's own squared norm and each half gets its own w.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int M>
 __global__ __launch_bounds__(kBlock) void encode_kernel(const T* __restrict__ K, int64_t cap,
                                                          int64_t p0, int64_t count, int64_t total,
                                                          uint8_t* __restrict__ ids,
                                                          uint8_t* __restrict__ rec, uint64_t sign_lo,
                                                          uint64_t sign_hi, CodeTables tab) {
+    constexpr int kHalves = 8 / M;   // subspaces per lane
     __shared__ float s_lev[8];
     if (threadIdx.x < 8) s_lev[threadIdx.x] = tab.levels[threadIdx.x];
     lds_sync();
@@ -44,48 +50,67 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(const T* __restrict__ K,
         float sq[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) sq[r] = __fmul_rn(v[r], v[r]);
-        const float ss = tree8(sq);
-        float bound[7];
-#pragma unroll
-        for (int l = 0; l < 7; ++l) bound[l] = __fmul_rn(tab.sq_thr[l], ss);
-
-        uint32_t packed = 0;
-        double s2 = 0.0, s1 = 0.0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            uint32_t mag = 0;
-#pragma unroll
-            for (int l = 0; l < 7; ++l) mag += (sq[r] >= bound[l]) ? 1u : 0u;
-            packed |= ((((id >> r) & 1u) << 3) | mag) << (4 * r);
-            const double ax = fabs((double)v[r]);
-            s2 += ax * ax;
-            s1 += (double)s_lev[mag] * ax;
-        }
-        float w = 0.0f;
-        if (ss == 0.0f) {
-            packed = 0;
+        // squared norm of each subspace: the spec's pairwise tree
+        float ss[kHalves];
+        if constexpr (M == 8) {
+            ss[0] = tree8(sq);
         } else {
+            ss[0] = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+            ss[1] = (sq[4] + sq[5]) + (sq[6] + sq[7]);
+        }
+        uint32_t packed = 0;
+        float w[kHalves];
+#pragma unroll
+        for (int h = 0; h < kHalves; ++h) {
+            float bound[7];
+#pragma unroll
+            for (int l = 0; l < 7; ++l) bound[l] = __fmul_rn(tab.sq_thr[l], ss[h]);
+            uint32_t part = 0;
+            double s2 = 0.0, s1 = 0.0;
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                const int r = h * M + j;
+                uint32_t mag = 0;
+#pragma unroll
+                for (int l = 0; l < 7; ++l) mag += (sq[r] >= bound[l]) ? 1u : 0u;
+                part |= ((((id >> r) & 1u) << 3) | mag) << (4 * r);
+                const double ax = fabs((double)v[r]);
+                s2 += ax * ax;
+                s1 += (double)s_lev[mag] * ax;
+            }
+            // ss = 0: all codes of the subspace 0 and w = 0; otherwise
             // w = ||x_b|| / sqrt(d) / <v_b, x_b / ||x_b||> = ||x_b||^2 / (sqrt(d) <v_b, x_b>)
-            w = (float)(s2 / (11.313708498984761 * s1));
+            w[h] = 0.0f;
+            if (ss[h] != 0.0f) {
+                packed |= part;
+                w[h] = (float)(s2 / (11.313708498984761 * s1));
+            }
         }
         ids[row * kSub + l16] = (uint8_t)id;
-        uint8_t* r = rec + row * kRec;
+        uint8_t* r = rec + row * rec_bytes<M>();
         reinterpret_cast<uint32_t*>(r)[l16] = packed;
-        reinterpret_cast<float*>(r + 64)[l16] = w;
+        if constexpr (M == 8)
+            reinterpret_cast<float*>(r + 64)[l16] = w[0];
+        else
+            reinterpret_cast<float2*>(r + 64)[l16] = make_float2(w[0], w[1]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// query preparation: one block of G waves per (subspace b, unit).
+// query preparation: one block of G waves per (id byte b, unit).
 //   y_g = H D q_g (spec arithmetic); wave g rotates query head g (the four
 //   16-lane groups of the wave compute the same transform) and reads the 8
-//   coordinates of subspace b from lane b, so y_{g,b} is wave-uniform;
-//   the 256 centroid scores of (g, b): lane l scores c = l + 64 t, t < 4, as
+//   coordinates 8b..8b+7 from lane b, so they are wave-uniform.
+//   m = 8 (subspace b): lane l scores the centroids c = l + 64 t, t < 4, as
 //   the pairwise fp32 tree ((t0+t1)+(t2+t3)) + ((t4+t5)+(t6+t7)) of the
-//   signed coordinates;
-//   top-rho by (score desc, c asc): rho rounds of a wave maximum of the
-//   order keys, the lowest index among the lanes holding it, and removal;
-//   vote table row L[b][c] = sum_g weight(rank of c in head g's picks).
+//   signed coordinates; top-rho by (score desc, c asc): rho rounds of a wave
+//   maximum of the order keys, the lowest index among the lanes holding it by
+//   ballot, and removal; vote table row L[b][c] = sum_g weight(rank of c in
+//   head g's picks).
+//   m = 4 (subspaces 2b, 2b+1): lanes 0..15 score the 16 centroids of 2b from
+//   coordinates 0..3 with the tree (t0+t1)+(t2+t3), lanes 16..31 those of
+//   2b+1 from coordinates 4..7; top-rho in each half the same way; the row the
+//   scan reads for id byte b is L[2b][c & 15] + L[2b+1][c >> 4].
 // Block (0, u) also writes Ysum = sum_g y_g (for the rerank) and may copy the
 // step's new K/V token into the store.
 // ---------------------------------------------------------------------------
@@ -95,7 +120,7 @@ struct VoteWeights {
 
 constexpr int kQMaxBlock = 512;  // G <= 8 waves
 
-template <typename T>
+template <typename T, int M>
 __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
     const T* __restrict__ q, int G, uint64_t sign_lo, uint64_t sign_hi, int rho, VoteWeights wts,
     const float* __restrict__ cents, uint8_t* __restrict__ lut, float* __restrict__ ysum,
@@ -136,7 +161,16 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
 #pragma unroll
     for (int r = 0; r < 8; ++r) y[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[r]), b));
     uint32_t key[4];
-    if (cents == nullptr) {
+    if constexpr (M == 4) {
+        // lane l < 32 holds centroid l & 15 of subspace 2b + (l >> 4)
+        const int h = (lane >> 4) & 1;
+        const float a0 = h ? y[4] : y[0], a1 = h ? y[5] : y[1];
+        const float a2 = h ? y[6] : y[2], a3 = h ? y[7] : y[3];
+        const float t0 = (lane & 1) ? -a0 : a0, t1 = (lane & 2) ? -a1 : a1;
+        const float t2 = (lane & 4) ? -a2 : a2, t3 = (lane & 8) ? -a3 : a3;
+        key[0] = lane < 32 ? f32_order_key((t0 + t1) + (t2 + t3)) : 0u;
+        key[1] = key[2] = key[3] = 0u;
+    } else if (cents == nullptr) {
         const float t0 = (lane & 1) ? -y[0] : y[0], t1 = (lane & 2) ? -y[1] : y[1];
         const float t2 = (lane & 4) ? -y[2] : y[2], t3 = (lane & 8) ? -y[3] : y[3];
         const float t4 = (lane & 16) ? -y[4] : y[4], t5 = (lane & 32) ? -y[5] : y[5];
@@ -161,24 +195,44 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
     }
     lds_sync();
 
-    for (int r = 0; r < rho; ++r) {
-        const uint32_t m = wave_max(max(max(key[0], key[1]), max(key[2], key[3])));
-        int c = 256;
+    if constexpr (M == 4) {
+        // each half separately; s_row[16 h + c] = vote of centroid c of subspace 2b + h
 #pragma unroll
-        for (int t = 3; t >= 0; --t) {
-            const uint64_t bal = __ballot(key[t] == m);
-            if (bal != 0) c = 64 * t + (__ffsll((unsigned long long)bal) - 1);
+        for (int h = 0; h < 2; ++h) {
+            uint32_t kk = ((lane >> 4) == h) ? key[0] : 0u;
+            for (int r = 0; r < rho; ++r) {
+                const uint32_t m = wave_max(kk);
+                const uint64_t bal = __ballot(kk == m);
+                const int c = __ffsll((unsigned long long)bal) - 1;   // lane 16 h + centroid
+                if (lane == c) kk = 0;  // removed
+                if (lane == 0) atomicAdd(&s_row[c], wts.w[r]);
+            }
         }
+    } else {
+        for (int r = 0; r < rho; ++r) {
+            const uint32_t m = wave_max(max(max(key[0], key[1]), max(key[2], key[3])));
+            int c = 256;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (c == 64 * t + lane) key[t] = 0;  // removed
-        if (lane == 0) atomicAdd(&s_row[c], wts.w[r]);
+            for (int t = 3; t >= 0; --t) {
+                const uint64_t bal = __ballot(key[t] == m);
+                if (bal != 0) c = 64 * t + (__ffsll((unsigned long long)bal) - 1);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (c == 64 * t + lane) key[t] = 0;  // removed
+            if (lane == 0) atomicAdd(&s_row[c], wts.w[r]);
+        }
     }
     lds_sync();
     if (tid < 64) {
+        // vote of id-byte value c (at most 255: checked on the host)
+        auto entry = [&](int c) -> uint32_t {
+            if constexpr (M == 4) return s_row[c & 15] + s_row[16 + (c >> 4)];
+            return s_row[c];
+        };
         uint32_t* out = reinterpret_cast<uint32_t*>(lut + ((int64_t)u * kSub + b) * 256);
-        out[tid] = (s_row[4 * tid] & 0xffu) | ((s_row[4 * tid + 1] & 0xffu) << 8) |
-                   ((s_row[4 * tid + 2] & 0xffu) << 16) | ((s_row[4 * tid + 3] & 0xffu) << 24);
+        out[tid] = (entry(4 * tid) & 0xffu) | ((entry(4 * tid + 1) & 0xffu) << 8) |
+                   ((entry(4 * tid + 2) & 0xffu) << 16) | ((entry(4 * tid + 3) & 0xffu) << 24);
     }
     if (b == 0) {
         for (int i = tid; i < kD; i += 64 * G) {
@@ -276,29 +330,40 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
     int64_t blocks = (groups_needed + (kBlock / 16) - 1) / (kBlock / 16);
     if (blocks > 65536) blocks = 65536;
     const dim3 grid((unsigned)blocks), blk(kBlock);
-    if (bf16)
-        return launch(encode_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)K, cap, p0,
-                      count, total, ids, rec, sign[0], sign[1], tab);
-    return launch(encode_kernel<float>, grid, blk, 0, st, (const float*)K, cap, p0, count, total,
-                  ids, rec, sign[0], sign[1], tab);
+#define PK_ENC(TY, MM)                                                                        \
+    return launch(encode_kernel<TY, MM>, grid, blk, 0, st, (const TY*)K, cap, p0, count, total, \
+                  ids, rec, sign[0], sign[1], tab)
+    if (tab.sub_dim == 4) {
+        if (bf16) PK_ENC(uint16_t, 4);
+        PK_ENC(float, 4);
+    }
+    if (tab.sub_dim != 8) return hipErrorInvalidValue;
+    if (bf16) PK_ENC(uint16_t, 8);
+    PK_ENC(float, 8);
+#undef PK_ENC
 }
 
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
-                        int rho, const uint8_t* weights, const float* cents, uint8_t* lut, float* ysum,
+                        int rho, const uint8_t* weights, const float* cents, uint8_t* lut, float* ysum, int sub_dim,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
                         int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st) {
     const int64_t slot = new_pos < ring.n_sink ? new_pos : ring.n_sink + new_pos % ring.span;
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     const dim3 grid(kSub, units), blk(64 * G);
-    if (bf16)
-        return launch(qprep_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)q, G, sign[0],
-                      sign[1], rho, w, cents, lut, ysum, (const uint4*)k_new, (const uint4*)v_new,
-                      (uint8_t*)K, (uint8_t*)V, row_bytes, cap, new_pos, (uint4*)ring.k,
-                      (uint4*)ring.v, ring.rows, slot);
-    return launch(qprep_kernel<float>, grid, blk, 0, st, (const float*)q, G, sign[0], sign[1], rho,
-                  w, cents, lut, ysum, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V,
-                  row_bytes, cap, new_pos, (uint4*)ring.k, (uint4*)ring.v, ring.rows, slot);
+    if (sub_dim != 8 && (sub_dim != 4 || cents != nullptr)) return hipErrorInvalidValue;
+#define PK_QP(TY, MM)                                                                            \
+    return launch(qprep_kernel<TY, MM>, grid, blk, 0, st, (const TY*)q, G, sign[0], sign[1], rho, \
+                  w, cents, lut, ysum, (const uint4*)k_new, (const uint4*)v_new, (uint8_t*)K,      \
+                  (uint8_t*)V, row_bytes, cap, new_pos, (uint4*)ring.k, (uint4*)ring.v, ring.rows, \
+                  slot)
+    if (sub_dim == 4) {
+        if (bf16) PK_QP(uint16_t, 4);
+        PK_QP(float, 4);
+    }
+    if (bf16) PK_QP(uint16_t, 8);
+    PK_QP(float, 8);
+#undef PK_QP
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,

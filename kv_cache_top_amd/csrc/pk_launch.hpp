@@ -62,7 +62,7 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 // query rotation, vote tables and summed query (plus the step's append)
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, const float* cents, uint8_t* lut,
-                        float* ysum,
+                        float* ysum, int sub_dim,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
                         int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st);
 // learned-centroid comparison stage: fit (seed, then iters rounds of assign +

@@ -21,6 +21,8 @@
 //  fine    one 1024-thread block per unit: the k-th largest estimate by
 //          value bucketing (radix select as the fallback), ties to the lower
 //          position, compaction in order.
+#include <type_traits>
+
 #include "pk_device.hpp"
 #include "pk_fine.hpp"
 #include "pk_launch.hpp"
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
 // need = C - ge[T+1] in position order.  Chunk c holds gt_c = sfx_c[T+1]
 // keys above T and eq_c = sfx_c[T] - gt_c ties; this chunk's candidates start
 // after the earlier chunks' keys above T and the ties taken among theirs.
-template <int KPT>
+template <int KPT, int M>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void rerank_kernel(
     const uint8_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
     const uint8_t* __restrict__ ids, const uint8_t* __restrict__ lut,
@@ -375,39 +377,56 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     lds_sync();
 
     // RSQ-IP: est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g;
-    // 16 lanes per candidate, lane b reading subspace b's nibble word and w.
-    // A group fetches the records of up to kBatch candidates before using any.
+    // 16 lanes per candidate, lane l reading the nibble word of coordinates
+    // 8l..8l+7 and their w (one subspace for m = 8, two for m = 4).
+    // A group fetches the records of up to kBatch candidates before using any
+    // (8 for m = 4, whose lanes read 12 B each: the same registers as 16 x 8 B).
     // Codes are dequantised two at a time from the byte-indexed level pairs.
     // Record offsets within the unit fit 32 bits (capacity <= 2^24 keys).
-    constexpr int kBatch = 16;
+    constexpr int kBatch = M == 8 ? 16 : 8;
+    constexpr uint32_t kRecB = (uint32_t)rec_bytes<M>();
+    using WT = typename std::conditional<M == 8, float, float2>::type;   // a lane's w
     const float inv_sqrt_d = 0.08838834764831845f;
     const int grp = tid >> 4;
-    const uint8_t* urec = rec + (int64_t)u * cap * kRec;
+    const uint8_t* urec = rec + (int64_t)u * cap * kRecB;
     int32_t* upos = cand_pos + (int64_t)u * cmax;
     float* uest = cand_est + (int64_t)u * cmax;
     for (int i0 = grp; i0 < (int)n_mem; i0 += kBatch * (kBlock / 16)) {
         uint32_t nib[kBatch];
-        float w[kBatch];
+        WT w[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int i = i0 + k * (kBlock / 16);
             const int32_t p = s_list[i < (int)n_mem ? i : i0];
-            const uint32_t ro = (uint32_t)p * (uint32_t)kRec + 4u * (uint32_t)l16;
-            nib[k] = *reinterpret_cast<const uint32_t*>(urec + ro);
-            w[k] = *reinterpret_cast<const float*>(urec + ro + 64u);
+            const uint32_t ro = (uint32_t)p * kRecB;
+            nib[k] = *reinterpret_cast<const uint32_t*>(urec + ro + 4u * (uint32_t)l16);
+            w[k] = reinterpret_cast<const WT*>(urec + ro + 64u)[l16];
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int i = i0 + k * (kBlock / 16);
             if (i >= (int)n_mem) break;          // uniform in the 16-lane group
-            float dot = 0.0f;
+            float part;
+            if constexpr (M == 8) {
+                float dot = 0.0f;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float2 lv = s_pair[(nib[k] >> (8 * b)) & 255u];
-                dot = fmaf(lv.x, y[2 * b], dot);
-                dot = fmaf(lv.y, y[2 * b + 1], dot);
+                for (int b = 0; b < 4; ++b) {
+                    const float2 lv = s_pair[(nib[k] >> (8 * b)) & 255u];
+                    dot = fmaf(lv.x, y[2 * b], dot);
+                    dot = fmaf(lv.y, y[2 * b + 1], dot);
+                }
+                part = w[k] * dot;
+            } else {
+                float dot[2] = {0.0f, 0.0f};
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float2 lv = s_pair[(nib[k] >> (8 * b)) & 255u];
+                    dot[b >> 1] = fmaf(lv.x, y[2 * b], dot[b >> 1]);
+                    dot[b >> 1] = fmaf(lv.y, y[2 * b + 1], dot[b >> 1]);
+                }
+                part = fmaf(w[k].x, dot[0], w[k].y * dot[1]);
             }
-            const float e = sum16(w[k] * dot);
+            const float e = sum16(part);
             const uint32_t o = cand_before + (uint32_t)i;
             if (l16 == 0 && (int64_t)o < cmax) {
                 upos[o] = s_list[i];
@@ -632,10 +651,15 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
         return hipErrorInvalidValue;
     const dim3 grid(n_chunks, units), blk(kBlock);
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
-#define PK_RERANK(K)                                                                          \
-    return launch(rerank_kernel<K>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, lut,  \
-                  cap, sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, C,      \
-                  top_k, ysum, tab, cand_pos, cand_est, cmax, meta)
+    if (tab.sub_dim != 8 && tab.sub_dim != 4) return hipErrorInvalidValue;
+#define PK_RERANK(K)                                                                               \
+    return tab.sub_dim == 8                                                                        \
+               ? launch(rerank_kernel<K, 8>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, \
+                        lut, cap, sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, \
+                        C, top_k, ysum, tab, cand_pos, cand_est, cmax, meta)                       \
+               : launch(rerank_kernel<K, 4>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, \
+                        lut, cap, sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, \
+                        C, top_k, ysum, tab, cand_pos, cand_est, cmax, meta)
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1);
         case 2: PK_RERANK(2);

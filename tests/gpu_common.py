@@ -12,12 +12,34 @@ from oracle import pariskv as ok
 from oracle.codebook import spec_tables
 
 LEVELS, SQ_T = spec_tables()
-_TABLES = {"lloyd_max": (LEVELS, SQ_T), "quantile": spec_tables(kind="quantile")}
 
 
 def tables(wl):
-    """(levels, squared thresholds) of the workload's codebook reading."""
-    return _TABLES[getattr(wl.params, "codebook", "lloyd_max")]
+    """(levels, squared thresholds) of the workload's codebook reading and subspace width."""
+    return spec_tables(m=wl.params.sub_dim, kind=getattr(wl.params, "codebook", "lloyd_max"))
+
+
+def sub_shape(wl):
+    return wl.params.n_sub, wl.params.sub_dim
+
+
+def pack_ids(ids: np.ndarray, m: int) -> np.ndarray:
+    """The library's 16 id bytes per key: one id per byte for m = 8; for m = 4
+    subspace 2i in the low half of byte i and 2i + 1 in the high half."""
+    ids = np.asarray(ids, np.uint8)
+    if m == 8:
+        return ids
+    return (ids[:, 0::2] | (ids[:, 1::2] << 4)).astype(np.uint8)
+
+
+def byte_vote_table(L: np.ndarray, m: int) -> np.ndarray:
+    """The table the scan reads, [16][256]: the vote table itself for m = 8;
+    for m = 4, entry c of row i = L[2i][c & 15] + L[2i + 1][c >> 4]."""
+    L = np.asarray(L, np.int64)
+    if m == 8:
+        return L
+    c = np.arange(256)
+    return L[0::2][:, c & 15] + L[1::2][:, c >> 4]
 
 # acceptance bars
 W_RTOL = 1e-6          # calibration scale (fp32 on both sides; derivation in the design notes)
@@ -40,7 +62,7 @@ def make_ctx(wl, capacity=None, host_mapped=False, **override):
     kw = dict(rho=p.rho, vote_weights=p.vote_weights, coarse_permille=p.coarse_permille,
               top_k=p.top_k, n_sink=p.n_sink, n_local=p.n_local, buf_tokens=p.buf_tokens,
               sign_bits=tuple(int(x) for x in wl.sign_bits),
-              codebook=0 if p.codebook == "lloyd_max" else 1)
+              codebook=0 if p.codebook == "lloyd_max" else 1, n_sub=p.n_sub, sub_dim=p.sub_dim)
     kw.update(override)
     cap = capacity or wl.n_tokens
     dt = torch_dtype(wl)
@@ -62,14 +84,14 @@ def unit_view(wl, u):
     return wl.K[b, h], wl.V[b, h], wl.Q[b, h * wl.group:(h + 1) * wl.group]
 
 
-def est_scale(nib, w, Qg, signs, levels=LEVELS):
+def est_scale(nib, w, Qg, signs, levels=LEVELS, n_sub=16, m=8):
     """sum_g sum_b |w_b <v_b, (R q_g)_b>|: the magnitude the estimate error is measured against."""
-    v = ok.dequantize(ok.unpack_nibbles(nib, 16, 8), levels)
+    v = ok.dequantize(ok.unpack_nibbles(nib, n_sub, m), levels)
     R = ok.srht_matrix(signs)
     w = np.asarray(w, np.float64)
     s = np.zeros(v.shape[0])
     for q in np.atleast_2d(np.asarray(Qg, np.float64)):
-        y = (R @ q).reshape(16, 8)
+        y = (R @ q).reshape(n_sub, m)
         s += np.sum(np.abs(w * np.einsum("nbj,bj->nb", v, y)), axis=1)
     return s
 
@@ -90,18 +112,20 @@ def check_encode(wl, pkv, units, ids_all=None, rec_all=None, ids_fn=None):
     ids_all = pkv.debug(0) if ids_all is None else ids_all
     rec_all = pkv.debug(1) if rec_all is None else rec_all
     s = wl.signs()
+    n_sub, m = sub_shape(wl)
     out = {}
     for u in units:
         K, _, _ = unit_view(wl, u)
         pos = np.arange(sink_end, r_end)
-        i_o, n_o, w_o = ok.encode_keys(K[pos], s, *tables(wl))
+        i_o, n_o, w_o = ok.encode_keys(K[pos], s, *tables(wl), n_sub=n_sub, m=m)
         if ids_fn is not None:
             i_o = ids_fn(u, K[pos])
         ids_g = ids_all[u].reshape(-1, 16)[pos]
-        rec_g = rec_all[u].reshape(-1, 128)[pos]
+        rec_g = rec_all[u].reshape(-1, 64 + 4 * n_sub)[pos]
         nib_g = rec_g[:, :64]
         w_g = rec_g[:, 64:].copy().view(np.float32)
-        assert np.array_equal(ids_g, i_o), f"unit {u}: bucket ids differ at {np.argwhere(ids_g != i_o)[:5]}"
+        i_p = pack_ids(i_o, m)
+        assert np.array_equal(ids_g, i_p), f"unit {u}: bucket ids differ at {np.argwhere(ids_g != i_p)[:5]}"
         assert np.array_equal(nib_g, n_o), f"unit {u}: nibbles differ at {np.argwhere(nib_g != n_o)[:5]}"
         rel = np.abs(w_g.astype(np.float64) - w_o) / np.maximum(np.abs(w_o), 1e-30)
         assert np.all(rel <= W_RTOL), f"unit {u}: w rel err {rel.max():.3g}"
@@ -123,14 +147,16 @@ def check_retrieval(wl, pkv, units, sel, sel_n, enc, vote_fn=None):
     sel_n = sel_n.cpu().numpy().reshape(-1)
     s = wl.signs()
     p = wl.params
+    n_sub, m = sub_shape(wl)
     res = {}
     for u in units:
         K, V, Qg = unit_view(wl, u)
         i_o, n_o, w_o = enc[u]
         pos = np.arange(sink_end, r_end)
         N_r = pos.size
-        L = ok.vote_table(Qg, s, p.rho, p.vote_weights)[0] if vote_fn is None else vote_fn(u, Qg)
-        assert np.array_equal(lut[u].reshape(16, 256).astype(np.int64), L.astype(np.int64)), \
+        L = (ok.vote_table(Qg, s, p.rho, p.vote_weights, n_sub, m)[0] if vote_fn is None
+             else vote_fn(u, Qg))
+        assert np.array_equal(lut[u].reshape(16, 256).astype(np.int64), byte_vote_table(L, m)), \
             f"unit {u}: vote table differs"
         sc_o = ok.coarse_scores(i_o, L) if N_r else np.zeros(0, np.int64)
         # scores are stored saturated at 255 (the threshold logic rescores saturated keys)
@@ -141,8 +167,9 @@ def check_retrieval(wl, pkv, units, sel, sel_n, enc, vote_fn=None):
         cand_o = ok.top_by_key(sc_o, pos, C)
         assert np.array_equal(cand[u][:C], cand_o), f"unit {u}: coarse candidate set differs"
         rel = cand_o - sink_end
-        e_o = ok.rsq_ip(n_o[rel], w_o[rel], Qg, s, tables(wl)[0]) if C else np.zeros(0)
-        scale = est_scale(n_o[rel], w_o[rel], Qg, s, tables(wl)[0]) if C else np.zeros(0)
+        e_o = ok.rsq_ip(n_o[rel], w_o[rel], Qg, s, tables(wl)[0], n_sub, m) if C else np.zeros(0)
+        scale = (est_scale(n_o[rel], w_o[rel], Qg, s, tables(wl)[0], n_sub, m) if C
+                 else np.zeros(0))
         err = np.abs(est[u][:C].astype(np.float64) - e_o)
         assert np.all(err <= EST_RTOL * np.maximum(scale, 1e-30)), \
             f"unit {u}: est rel err {np.max(err / np.maximum(scale, 1e-30)):.3g}"

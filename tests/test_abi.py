@@ -67,8 +67,8 @@ def _create(cfg, batch=1, n_kv=8, n_q=32, cap=1000, dtype=nat.PK_BF16, k=16, v=1
 
 @pytest.mark.parametrize("field,value,expect", [
     ("head_dim", 64, nat.PK_ERR_UNSUPPORTED),
-    ("n_sub", 8, nat.PK_ERR_UNSUPPORTED),
-    ("sub_dim", 16, nat.PK_ERR_UNSUPPORTED),
+    ("n_sub", 8, nat.PK_ERR_INVALID),            # B * m != d
+    ("sub_dim", 16, nat.PK_ERR_INVALID),
     ("rho", 0, nat.PK_ERR_INVALID),
     ("rho", 9, nat.PK_ERR_INVALID),
     ("coarse_permille", 0, nat.PK_ERR_INVALID),
@@ -101,6 +101,12 @@ def test_create_validates_shapes_and_pointers():
     assert _create(big)[0] == nat.PK_ERR_INVALID                  # G * weight > 255
     zero = nat.make_config(vote_weights=(4, 3, 0, 1))
     assert _create(zero)[0] == nat.PK_ERR_INVALID
+    # subspace widths: m = 8 and m = 4 are built, m = 16 (B = 8) is valid but not built
+    assert _create(nat.make_config(n_sub=8, sub_dim=16))[0] == nat.PK_ERR_UNSUPPORTED
+    assert _create(nat.make_config(n_sub=64, sub_dim=2))[0] == nat.PK_ERR_UNSUPPORTED
+    # m = 4: a vote-table byte sums two subspaces' votes, so 2 * G * weight <= 255
+    assert _create(nat.make_config(n_sub=32, sub_dim=4, vote_weights=(32, 1, 1, 1)))[0] == \
+        nat.PK_ERR_INVALID
 
 
 def test_calls_reject_null_context():
@@ -123,3 +129,5 @@ def test_no_device_is_reported_without_a_gpu():
         pytest.skip("a GPU is present")
     st, ctx = _create(nat.make_config())
     assert st == nat.PK_ERR_NO_DEVICE and not ctx.value
+    st, ctx = _create(nat.make_config(n_sub=32, sub_dim=4, vote_weights=(31, 1, 1, 1)))
+    assert st == nat.PK_ERR_NO_DEVICE and not ctx.value   # a valid m = 4 configuration

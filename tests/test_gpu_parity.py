@@ -215,6 +215,40 @@ def test_quantile_codebook():
     _full_check(wl, units=[0, 4, 7], tag="quantile-codebook")
 
 
+@pytest.mark.parametrize("dtype,group", [("bf16", 4), ("f32", 2)])
+def test_subspaces_of_width_4(dtype, group):
+    """32 subspaces of m = 4 (16 sign-pattern centroids each, two 4-bit ids per
+    id byte, 32 scales in a 192-byte record, the m = 4 codebook): ids, codes,
+    vote tables, scores and candidate sets bit-exact, w and estimates within
+    tolerance, attention as usual; then 70 fused decode steps through two
+    buffer fills, so the device also encodes evicted keys with m = 4."""
+    import dataclasses
+    wl = W.gqa_bf16(N=20011, top_k=512, permille=50, group=group, dtype=dtype, buf_tokens=32,
+                    n_local=64)
+    wl.params = dataclasses.replace(wl.params, n_sub=32, sub_dim=4)
+    steps = 70
+    units = [0, 5]
+    pkv, sel, sel_n, out = _full_check(wl, units=units, capacity=wl.n_tokens + steps,
+                                       tag=f"m4-{dtype}-g{group}")
+    dt = gc.torch_dtype(wl)
+    Kn, Vn, Qn = W.decode_stream(wl, steps)
+    for t in range(steps):
+        out, sel, sel_n = pkv.decode_step(torch.from_numpy(Kn[t]).to(dt).cuda(),
+                                          torch.from_numpy(Vn[t]).to(dt).cuda(),
+                                          torch.from_numpy(Qn[t]).to(dt).cuda())
+    torch.cuda.synchronize()
+    n, sink_end, r_end, _ = pkv.window()
+    assert n == wl.n_tokens + steps and r_end == wl.n_tokens - 64 + 2 * 32   # two evictions
+    Kall = np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2)
+    Vall = np.concatenate([wl.V, np.moveaxis(Vn, 0, 2)], axis=2)
+    full = W.Workload(wl.name, wl.batch, wl.n_kv, wl.group, n, wl.dtype, wl.params, wl.sign_bits,
+                      Kall, Vall, Qn[-1])
+    enc = gc.check_encode(full, pkv, units)
+    gc.check_retrieval(full, pkv, units, sel, sel_n, enc)
+    gc.check_attention(full, pkv, units, sel, sel_n, out)
+    gc.log(f"[m4-{dtype}-g{group}] decode steps ok (r_end {r_end})")
+
+
 def test_fine_ties_periodic_keys():
     """64 distinct keys repeated along the context: large groups of exactly tied
     estimates around the k-th (the bucket of the k-th holds a whole group)."""
