@@ -117,12 +117,16 @@ def _tree8(t: np.ndarray) -> np.ndarray:
 
 
 def _tree(t: np.ndarray) -> np.ndarray:
-    """The spec's pairwise fp32 sum over the last axis (m = 8: _tree8; m = 4:
-    (t0+t1)+(t2+t3))."""
+    """The spec's pairwise fp32 sum over the last axis, terms paired in index
+    order at every level (m = 8: _tree8; m = 4: (t0+t1)+(t2+t3); m = 16: the
+    m = 8 tree of t0..t7 plus the m = 8 tree of t8..t15)."""
     t = np.asarray(t, np.float32)
-    if t.shape[-1] == 8:
+    m = t.shape[-1]
+    if m == 8:
         return _tree8(t)
-    assert t.shape[-1] == 4, "spec trees exist for m = 4 and m = 8"
+    if m == 16:
+        return _tree8(t[..., :8]) + _tree8(t[..., 8:])
+    assert m == 4, "spec trees exist for m = 4, 8 and 16"
     return (t[..., 0] + t[..., 1]) + (t[..., 2] + t[..., 3])
 
 
@@ -136,7 +140,7 @@ def quantize_codes(x: np.ndarray, sq_thresholds: np.ndarray, n_sub: int, m: int)
     ss_b is zero gets all-zero nibbles.  Returns uint8 [n, n_sub, m] and the
     fp32 ss [n, n_sub].
     """
-    assert m in (4, 8), "spec trees exist for m = 4 and m = 8"
+    assert m in (4, 8, 16), "spec trees exist for m = 4, 8 and 16"
     xb = np.asarray(x, np.float32).reshape(-1, n_sub, m)
     sq = xb * xb
     ss = _tree(sq)
@@ -216,7 +220,7 @@ def encode_keys(K: np.ndarray, signs: np.ndarray, levels: np.ndarray,
 
 
 def centroid_scores(y_b: np.ndarray) -> np.ndarray:
-    """fp32 similarity of a rotated query subspace y_b (m = 8 or 4) to all 2^m centroids.
+    """fp32 similarity of a rotated query subspace y_b (m = 4, 8 or 16) to all 2^m centroids.
 
     Score(c) = pairwise fp32 sum of t_j, t_j = -y_j if bit j of c is set else
     y_j.  This is sqrt(m) times the inner product with centroid c; the dropped

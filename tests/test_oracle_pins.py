@@ -391,3 +391,120 @@ def test_mutation_m4_tree_dropping_a_term_is_caught():
         y[3] = 0.0
         return pk.centroid_scores(y)
     assert not check_m4_ids_and_top_rho(pk.bucket_ids, bad, pk.top_rho)
+
+
+# ------------------------------------------------------ subspaces of m = 16
+
+def check_m16_ids_and_top_rho(bucket_ids, centroid_scores, top_rho):
+    """m = 16 (8 subspaces of 16 coordinates, 65536 sign-pattern centroids each):
+    ids by brute force over all 65536 centroids (exact zeros present), 16-bit;
+    on integer queries the spec scores equal the exact scaled inner products
+    (4 <c, y>), top-rho ties go to the lower index, rank 1 is the query's own
+    sign pattern and rank 2 flips its smallest coordinate."""
+    r = np.random.default_rng(21)
+    x = r.standard_normal((5, D)).astype(np.float32)
+    x[r.random(x.shape) < 0.1] = 0.0
+    ids = bucket_ids(x, 8, 16)
+    if ids.dtype != np.uint16 or ids.shape != (5, 8):
+        return False
+    C = np.stack([pk.centroid(c, 16) for c in range(1 << 16)])
+    for i in range(x.shape[0]):
+        for b in range(8):
+            dots = C @ x[i, 16 * b:16 * b + 16].astype(np.float64)
+            best = np.flatnonzero(dots == dots.max())[0]      # lowest index among the maxima
+            if ids[i, b] != best:
+                return False
+    C4 = C * 4.0
+    for t in range(12):
+        y = r.integers(-3, 4, size=16).astype(np.float32)
+        if t % 3 == 0:
+            y = (r.permutation(16) + 1) * r.choice([-1, 1], 16)   # distinct magnitudes
+            y = y.astype(np.float32)
+        sc = centroid_scores(y)
+        exact = C4 @ y.astype(np.float64)
+        if sc.shape != (1 << 16,) or not np.array_equal(sc.astype(np.float64), exact):
+            return False
+        want = np.lexsort((np.arange(1 << 16), -exact))[:6]
+        if list(top_rho(sc, 6)) != list(want):
+            return False
+        if t % 3 == 0:
+            own = int(np.sum((y < 0).astype(np.int64) << np.arange(16)))
+            small = int(np.argmin(np.abs(y)))
+            if list(top_rho(sc, 2)) != [own, own ^ (1 << small)]:
+                return False
+    return True
+
+
+def test_m16_ids_and_top_rho():
+    assert check_m16_ids_and_top_rho(pk.bucket_ids, pk.centroid_scores, pk.top_rho)
+
+
+def test_m16_codes_follow_the_real_number_rule():
+    """m = 16 codes with the m = 16 codebook: the fp32 rule agrees with the
+    real-number bin rule |u_j| >= t_l away from the thresholds."""
+    from oracle.codebook import lloyd_max
+    _, t = lloyd_max(16)
+    T32 = (t * t).astype(np.float32)
+    r = np.random.default_rng(22)
+    x = r.standard_normal((500, D)).astype(np.float32)
+    nib, ss = pk.quantize_codes(x, T32, 8, 16)
+    xb = x.reshape(-1, 8, 16).astype(np.float64)
+    assert np.allclose(ss, np.sum(xb * xb, axis=2), rtol=1e-6)
+    u = np.abs(xb) / np.linalg.norm(xb, axis=2, keepdims=True)
+    mag = np.sum(u[..., None] >= t[None, None, None, :], axis=-1)
+    far = np.min(np.abs(u[..., None] - t), axis=-1) > 1e-6
+    assert np.array_equal((nib & 7)[far], mag[far])
+    assert np.array_equal((nib >> 3) & 1, (xb < 0).astype(np.uint8))
+
+
+def test_m16_rsq_ip_identity():
+    """With identity quantisation (v = u) the m = 16 estimate is the exact
+    summed inner product."""
+    r = np.random.default_rng(23)
+    s = _signs(23)
+    K = r.standard_normal((50, D))
+    Qg = r.standard_normal((4, D))
+    x = pk.srht_matrix(s) @ K.T * math.sqrt(D)
+    xb = x.T.reshape(-1, 8, 16)
+    u = xb / np.linalg.norm(xb, axis=2, keepdims=True)
+    w = pk.calibrate_w(x.T, u, np.ones((50, 8)), 8, 16)
+    est = pk.rsq_ip_directions(u, w, Qg, s)
+    assert np.allclose(est, K @ Qg.sum(0), rtol=1e-12, atol=1e-10)
+
+
+def test_m16_vote_table_follows_the_flip_structure():
+    """m = 16 vote table: in real arithmetic a centroid's score is sum |y_j|
+    minus twice the |y_j| of the coordinates where it differs from the query's
+    own sign pattern, so a head's top 3 are its sign pattern, then the flips of
+    its smallest and of its second-smallest coordinate (random normal queries:
+    no near ties for fp32 rounding to reorder); weighted by rank and summed
+    over the heads."""
+    r = np.random.default_rng(24)
+    s = _signs(24)
+    Qg = r.standard_normal((2, D)).astype(np.float32)
+    L, picks = pk.vote_table(Qg, s, 3, (3, 2, 1), n_sub=8, m=16)
+    y = pk.srht_matrix(s) @ Qg.astype(np.float64).T * math.sqrt(D)
+    want = np.zeros((8, 1 << 16), np.int64)
+    for g in range(2):
+        for b in range(8):
+            yb = y[16 * b:16 * b + 16, g]
+            # best flip sets of the own sign pattern: smallest sums of |y_j|
+            a = np.abs(yb)
+            own = int(np.sum((yb < 0).astype(np.int64) << np.arange(16)))
+            order = np.argsort(a)
+            sets = [(), (order[0],), (order[1],), (order[0], order[1]), (order[2],)]
+            sets.sort(key=lambda f: sum(a[list(f)]))
+            for rank, f in enumerate(sets[:3]):
+                c = own
+                for j in f:
+                    c ^= 1 << int(j)
+                want[b, c] += (3, 2, 1)[rank]
+    assert np.array_equal(L.astype(np.int64), want)
+
+
+def test_mutation_m16_tree_dropping_a_term_is_caught():
+    def bad(y_b):
+        y = np.asarray(y_b, np.float32).copy()
+        y[11] = 0.0
+        return pk.centroid_scores(y)
+    assert not check_m16_ids_and_top_rho(pk.bucket_ids, bad, pk.top_rho)
