@@ -641,7 +641,8 @@ def run_variant_sweep(args):
                 dict(rho=4, vote_weights=(8, 4, 2, 1), coarse_permille=50),
                 dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=100),
                 dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, codebook="quantile"),
-                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, n_sub=32, sub_dim=4)]
+                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, n_sub=32, sub_dim=4),
+                dict(rho=4, vote_weights=(4, 3, 2, 1), coarse_permille=50, n_sub=8, sub_dim=16)]
     for v in variants:
         layers = [Layer(a, l, wl=wls[l], **v) for l in range(a.layers)]
         for L in layers:

@@ -164,7 +164,14 @@ void free_all(pk_ctx* c) {
 // attention splits: the hot tokens (at most sink + local + buffer) and the
 // selection are split separately
 size_t rec_bytes(int sub_dim) {
-    return sub_dim == 4 ? (size_t)pk::rec_bytes<4>() : (size_t)pk::rec_bytes<8>();
+    return sub_dim == 4    ? (size_t)pk::rec_bytes<4>()
+           : sub_dim == 16 ? (size_t)pk::rec_bytes<16>()
+                           : (size_t)pk::rec_bytes<8>();
+}
+
+// vote table bytes per unit: byte rows (m = 4, 8) or hash tables (m = 16)
+size_t lut_bytes(int sub_dim) {
+    return sub_dim == 16 ? (size_t)pk::lut_bytes<16>() : (size_t)pk::lut_bytes<8>();
 }
 
 int64_t max_attend_splits(const pk_config& cfg) {
@@ -177,7 +184,7 @@ pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capac
     if (!cfg || n_kv < 1 || n_q < 1 || capacity < 1) return PK_ERR_INVALID;
     if (cfg->head_dim != 128) return PK_ERR_UNSUPPORTED;
     if (cfg->n_sub * cfg->sub_dim != cfg->head_dim) return PK_ERR_INVALID;
-    if (cfg->sub_dim != 8 && cfg->sub_dim != 4) return PK_ERR_UNSUPPORTED;
+    if (cfg->sub_dim != 8 && cfg->sub_dim != 4 && cfg->sub_dim != 16) return PK_ERR_UNSUPPORTED;
     if (cfg->rho < 1 || cfg->rho > pk::kRhoMax) return PK_ERR_INVALID;
     if (cfg->coarse_permille < 1 || cfg->coarse_permille > 1000) return PK_ERR_INVALID;
     if (cfg->codebook != 0 && cfg->codebook != 1) return PK_ERR_INVALID;
@@ -193,8 +200,9 @@ pk_status validate_config(const pk_config* cfg, int n_kv, int n_q, int64_t capac
         if (cfg->vote_weight[r] < 1) return PK_ERR_INVALID;
         if (cfg->vote_weight[r] > wmax) wmax = cfg->vote_weight[r];
     }
-    // a vote-table byte holds the votes of one subspace (m = 8) or of two (m = 4)
-    if (G * wmax * (8 / cfg->sub_dim) > 255) return PK_ERR_INVALID;
+    // a vote-table byte holds the votes of one subspace (m = 8) or of two (m = 4);
+    // an m = 16 table entry holds one centroid's votes in 8 bits
+    if (G * wmax * (cfg->sub_dim == 4 ? 2 : 1) > 255) return PK_ERR_INVALID;
     const int nbins = cfg->n_sub * G * wmax + 1;
     if (nbins > pk::kMaxBins) return PK_ERR_UNSUPPORTED;
     if (capacity > (int64_t)1 << 24) return PK_ERR_UNSUPPORTED;
@@ -269,7 +277,7 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
         StageTimer tm(c, PK_STAGE_SCAN, st);
         PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
                                c->max_chunks, c->lut, c->scores, c->sstride, c->hist, c->hstride,
-                               tot_now, c->nbins, st));
+                               tot_now, c->nbins, c->cfg.sub_dim, st));
     }
     {
         StageTimer tm(c, PK_STAGE_RERANK, st);
@@ -387,7 +395,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     } allocs[] = {
         {(void**)&c->ids, (size_t)(U * capacity * pk::kSub)},
         {(void**)&c->rec, (size_t)(U * capacity * rec_bytes(cfg->sub_dim))},
-        {(void**)&c->lut, (size_t)(U * pk::kSub * 256)},
+        {(void**)&c->lut, (size_t)U * lut_bytes(cfg->sub_dim)},
         {(void**)&c->ysum, (size_t)(U * pk::kD * 4)},
         // score rows padded to 16 B; the tail pad covers vector reads past the last row
         {(void**)&c->scores, (size_t)(U * c->sstride + 8192)},   // last chunk read whole
@@ -419,7 +427,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
         hipMemset(c->tot, 0, 2 * U * ((c->nbins + 1) & ~1) * 4) != hipSuccess ||
         hipMemset(c->scores, 0, U * c->sstride + 8192) != hipSuccess ||
-        hipMemset(c->lut, 0, U * pk::kSub * 256) != hipSuccess ||
+        hipMemset(c->lut, 0, (size_t)U * lut_bytes(cfg->sub_dim)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         free_all(c);
         delete c;
@@ -615,7 +623,7 @@ size_t pk_debug_size(const pk_ctx* c, int32_t what) {
     switch (what) {
         case PK_DBG_IDS: return U * cap * pk::kSub;
         case PK_DBG_REC: return U * cap * rec_bytes(c->cfg.sub_dim);
-        case PK_DBG_LUT: return U * pk::kSub * 256;
+        case PK_DBG_LUT: return U * lut_bytes(c->cfg.sub_dim);
         case PK_DBG_SCORES: return U * cap;
         case PK_DBG_CAND: return U * (size_t)c->cmax * 4;
         case PK_DBG_EST: return U * (size_t)c->cmax * 4;

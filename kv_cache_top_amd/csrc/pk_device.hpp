@@ -21,7 +21,31 @@ constexpr int kSub = 16;         // bucket-id bytes per key = rows of the scan's
 // Record of a key: 64 B of nibbles (coordinate 2i in the low half of byte i),
 // then B fp32 scales w.
 template <int M>
-constexpr int rec_bytes() { return 64 + 4 * (kD / M); }   // 128 (m = 8), 192 (m = 4)
+constexpr int rec_bytes() { return 64 + 4 * (kD / M); }   // 128 (m = 8), 192 (m = 4), 96 (m = 16)
+// B = 8 subspaces of m = 16 also keep the 16 sign bytes (the id of subspace b
+// is the little-endian 16-bit word at byte 2b), but 65536 centroids per
+// subspace leave no room for a dense vote row: each subspace gets a 256-slot
+// hash table of its (at most G * rho) voted centroids instead, 1 KB of u32
+// entries (vote << 16 | centroid; 0 = empty), linear probing from hash16(id).
+template <int M>
+constexpr int lut_bytes() { return M == 16 ? 8192 : 4096; }   // vote table per unit
+
+__device__ __forceinline__ uint32_t hash16(uint32_t id) {      // Fibonacci hash to 8 bits
+    return ((id * 40503u) & 0xffffu) >> 8;
+}
+
+// votes of centroid `id` in one subspace's hash table (a bounded probe: the
+// table never holds more than 64 of its 256 slots, so an empty slot ends it)
+__device__ __forceinline__ uint32_t hashed_vote(const uint32_t* tab, uint32_t id) {
+    uint32_t slot = hash16(id);
+    uint32_t e = tab[slot];
+    for (int k = 0; k < 256 && e != 0u; ++k) {
+        if ((e & 0xffffu) == id) return e >> 16;
+        slot = (slot + 1u) & 255u;
+        e = tab[slot];
+    }
+    return 0u;
+}
 constexpr int kRhoMax = 8;
 constexpr int kMaxBins = 4096;   // coarse-score histogram bins (B * G * max weight + 1)
 constexpr int kMaxChunks = 2048; // scan chunks per unit
@@ -30,7 +54,7 @@ constexpr int kBlock = 256;      // threads per block of the streaming kernels
 struct CodeTables {
     float sq_thr[7];   // fp32(t_l^2), ascending
     float levels[8];   // fp32 Lloyd-Max levels
-    int32_t sub_dim;   // m: 8 or 4
+    int32_t sub_dim;   // m: 8, 4 or 16
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -260,6 +284,10 @@ __device__ __forceinline__ float wave_sum_f(float x) {
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
     const uint32_t b = __float_as_uint(f + 0.0f);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+// its inverse (a zero comes back as +0)
+__device__ __forceinline__ float order_key_f32(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // Block-wide exclusive scan of one uint32 per thread for a block of NT

@@ -86,7 +86,7 @@ hipError_t launch_ring_fill(const void* K, const void* V, int64_t row_bytes, int
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
                        uint8_t* scores, int64_t sstride, uint16_t* hist, int hstride,
-                       uint32_t* tot, int nbins, hipStream_t st);
+                       uint32_t* tot, int nbins, int sub_dim, hipStream_t st);
 // coarse threshold and candidates (meta = {T, ties taken, C, k_eff} per unit),
 // then the RSQ-IP estimates of the candidates; ids and lut rescore the keys
 // whose stored score saturated when the threshold reaches 255; tot_clear (the

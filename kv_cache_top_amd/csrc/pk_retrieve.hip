@@ -29,20 +29,26 @@
 
 namespace pk {
 
-template <int KPT>
+// M = 8: the vote table holds one 256-entry byte row per id byte (also m = 4,
+// whose rows sum two subspaces); M = 16: one hash table per 16-bit id.
+template <int KPT, int M>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8 ? 8 : 1))) void scan_kernel(
     const uint8_t* __restrict__ ids, int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks,
     const uint8_t* __restrict__ lut, uint8_t* __restrict__ scores, int64_t sstride,
     uint16_t* __restrict__ hist, int hstride, uint32_t* __restrict__ tot, int nbins) {
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
-    __shared__ uint32_t s_lut[kSub * 256 / 4];
+    constexpr int kLutParts = lut_bytes<M>() / (16 * kBlock);   // 16-byte pieces per thread
+    __shared__ uint32_t s_lut[lut_bytes<M>() / 4];
     extern __shared__ uint32_t s_hist[];  // nbins entries (sized at launch)
     const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_lut);
 
     // The vote table is requested first and the key id rows right after, all
     // before any is used: scoring key j then waits only for its own row.
-    const uint4 lut_part = reinterpret_cast<const uint4*>(lut + (int64_t)u * kSub * 256)[tid];
+    uint4 lut_part[kLutParts];
+#pragma unroll
+    for (int i = 0; i < kLutParts; ++i)
+        lut_part[i] = reinterpret_cast<const uint4*>(lut + (int64_t)u * lut_bytes<M>())[tid + i * kBlock];
     const int64_t start = (int64_t)ch * chunk;
     const uint4* idrow = reinterpret_cast<const uint4*>(ids) + u * cap + sink_end;
     // loads are unconditional (index clamped to the last key, n_r >= 1) so the
@@ -53,7 +59,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         const int64_t i = start + j * kBlock + tid;
         v[j] = load_nt(idrow + (i < n_r ? i : n_r - 1));
     }
-    reinterpret_cast<uint4*>(s_lut)[tid] = lut_part;
+#pragma unroll
+    for (int i = 0; i < kLutParts; ++i) reinterpret_cast<uint4*>(s_lut)[tid + i * kBlock] = lut_part[i];
     for (int b = tid; b < nbins; b += kBlock) s_hist[b] = 0;
     lds_sync();
 
@@ -71,10 +78,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         const bool valid = j * kBlock + tid < nval;
         const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint32_t sc = 0;
+        if constexpr (M == 16) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+            for (int b = 0; b < 8; ++b)
+                sc += hashed_vote(s_lut + 256 * b, (w[b >> 1] >> (16 * (b & 1))) & 0xffffu);
+        } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((w[a] >> (8 * k)) & 255u)];
+            for (int a = 0; a < 4; ++a) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((w[a] >> (8 * k)) & 255u)];
+            }
         }
         scv[j] = sc;
         c8 += (valid && sc < 8u) ? (1ull << (sc << 3)) : 0ull;
@@ -170,7 +183,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     constexpr int chunk = KPT * kBlock;
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int l16 = tid & 15;
-    __shared__ __align__(16) int32_t s_list[chunk < 1024 ? 1024 : chunk];   // also the vote table
+    constexpr int kLutWords = (M == 16 ? lut_bytes<16>() : lut_bytes<8>()) / 4;
+    __shared__ __align__(16) int32_t s_list[chunk < kLutWords ? kLutWords : chunk];   // also the vote table
     __shared__ float2 s_pair[256];     // nibble byte (code of coord 2i+1 << 4 | code of 2i)
     {
         // signed level of a 4-bit code: sign bit 3, magnitude index bits 0..2
@@ -300,8 +314,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     // a stored 255 stands for 255 or more: when the threshold is that high the
     // saturated keys are rescored from their bucket ids (block-uniform branch)
     if (T >= 255) {
-        reinterpret_cast<uint4*>(s_list)[tid] =
-            reinterpret_cast<const uint4*>(lut + (int64_t)u * kSub * 256)[tid];
+        constexpr int kTabB = M == 16 ? lut_bytes<16>() : lut_bytes<8>();
+        for (int i = tid; i < kTabB / 16; i += kBlock)
+            reinterpret_cast<uint4*>(s_list)[i] = reinterpret_cast<const uint4*>(lut + (int64_t)u * kTabB)[i];
         lds_sync();
         const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_list);
         const uint4* idrow = reinterpret_cast<const uint4*>(ids) + u * cap + sink_end;
@@ -311,10 +326,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
                 const uint4 v = idrow[kbase + j];
                 const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
                 uint32_t sc = 0;
+                if constexpr (M == 16) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+                    for (int b = 0; b < 8; ++b)
+                        sc += hashed_vote(reinterpret_cast<const uint32_t*>(s_list) + 256 * b,
+                                          (wv[b >> 1] >> (16 * (b & 1))) & 0xffffu);
+                } else {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((wv[a] >> (8 * k)) & 255u)];
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) sc += lut8[(4 * a + k) * 256 + ((wv[a] >> (8 * k)) & 255u)];
+                }
                 s[j] = sc;
             }
         }
@@ -378,14 +400,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
 
     // RSQ-IP: est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g;
     // 16 lanes per candidate, lane l reading the nibble word of coordinates
-    // 8l..8l+7 and their w (one subspace for m = 8, two for m = 4).
+    // 8l..8l+7 and their w (one subspace for m = 8, two for m = 4, half of
+    // subspace l / 2 for m = 16).
     // A group fetches the records of up to kBatch candidates before using any
     // (8 for m = 4, whose lanes read 12 B each: the same registers as 16 x 8 B).
     // Codes are dequantised two at a time from the byte-indexed level pairs.
     // Record offsets within the unit fit 32 bits (capacity <= 2^24 keys).
-    constexpr int kBatch = M == 8 ? 16 : 8;
+    constexpr int kBatch = M == 4 ? 8 : 16;
     constexpr uint32_t kRecB = (uint32_t)rec_bytes<M>();
-    using WT = typename std::conditional<M == 8, float, float2>::type;   // a lane's w
+    using WT = typename std::conditional<M == 4, float2, float>::type;   // a lane's w
     const float inv_sqrt_d = 0.08838834764831845f;
     const int grp = tid >> 4;
     const uint8_t* urec = rec + (int64_t)u * cap * kRecB;
@@ -400,14 +423,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
             const int32_t p = s_list[i < (int)n_mem ? i : i0];
             const uint32_t ro = (uint32_t)p * kRecB;
             nib[k] = *reinterpret_cast<const uint32_t*>(urec + ro + 4u * (uint32_t)l16);
-            w[k] = reinterpret_cast<const WT*>(urec + ro + 64u)[l16];
+            w[k] = reinterpret_cast<const WT*>(urec + ro + 64u)[M == 16 ? (l16 >> 1) : l16];
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int i = i0 + k * (kBlock / 16);
             if (i >= (int)n_mem) break;          // uniform in the 16-lane group
             float part;
-            if constexpr (M == 8) {
+            if constexpr (M != 4) {   // one w for the lane's 8 coordinates
                 float dot = 0.0f;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -617,16 +640,20 @@ hipError_t probe_kernel_image() {
 hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_end, int64_t n_r,
                        int chunk, int n_chunks, int max_chunks, const uint8_t* lut,
                        uint8_t* scores, int64_t sstride, uint16_t* hist, int hstride,
-                       uint32_t* tot, int nbins, hipStream_t st) {
+                       uint32_t* tot, int nbins, int sub_dim, hipStream_t st) {
     if (nbins < 1 || nbins > kMaxBins || hstride < nbins || n_chunks > max_chunks)
         return hipErrorInvalidValue;
+    if (sub_dim != 4 && sub_dim != 8 && sub_dim != 16) return hipErrorInvalidValue;
     const dim3 grid(n_chunks, units), blk(kBlock);
     // the histogram is the only dynamic LDS: small vote tables keep the
     // block small enough for eight resident blocks per CU
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
-#define PK_SCAN(K)                                                                         \
-    return launch(scan_kernel<K>, grid, blk, hist_bytes, st, ids, cap, sink_end, n_r,        \
-                  max_chunks, lut, scores, sstride, hist, hstride, tot, nbins)
+#define PK_SCAN(K)                                                                              \
+    return sub_dim == 16                                                                          \
+               ? launch(scan_kernel<K, 16>, grid, blk, hist_bytes, st, ids, cap, sink_end, n_r,   \
+                        max_chunks, lut, scores, sstride, hist, hstride, tot, nbins)              \
+               : launch(scan_kernel<K, 8>, grid, blk, hist_bytes, st, ids, cap, sink_end, n_r,    \
+                        max_chunks, lut, scores, sstride, hist, hstride, tot, nbins)
     switch (chunk / kBlock) {
         case 1: PK_SCAN(1);
         case 2: PK_SCAN(2);
@@ -651,15 +678,14 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
         return hipErrorInvalidValue;
     const dim3 grid(n_chunks, units), blk(kBlock);
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
-    if (tab.sub_dim != 8 && tab.sub_dim != 4) return hipErrorInvalidValue;
+    if (tab.sub_dim != 8 && tab.sub_dim != 4 && tab.sub_dim != 16) return hipErrorInvalidValue;
+#define PK_RERANK_M(K, MM)                                                                         \
+    launch(rerank_kernel<K, MM>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, lut, cap,   \
+           sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, C, top_k, ysum, tab,   \
+           cand_pos, cand_est, cmax, meta)
 #define PK_RERANK(K)                                                                               \
-    return tab.sub_dim == 8                                                                        \
-               ? launch(rerank_kernel<K, 8>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, \
-                        lut, cap, sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, \
-                        C, top_k, ysum, tab, cand_pos, cand_est, cmax, meta)                       \
-               : launch(rerank_kernel<K, 4>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, \
-                        lut, cap, sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, \
-                        C, top_k, ysum, tab, cand_pos, cand_est, cmax, meta)
+    return tab.sub_dim == 8 ? PK_RERANK_M(K, 8)                                                    \
+                            : (tab.sub_dim == 4 ? PK_RERANK_M(K, 4) : PK_RERANK_M(K, 16))
     switch (chunk / kBlock) {
         case 1: PK_RERANK(1);
         case 2: PK_RERANK(2);
@@ -670,6 +696,7 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
         default: return hipErrorInvalidValue;
     }
 #undef PK_RERANK
+#undef PK_RERANK_M
 }
 
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,

@@ -25,11 +25,41 @@ def sub_shape(wl):
 
 def pack_ids(ids: np.ndarray, m: int) -> np.ndarray:
     """The library's 16 id bytes per key: one id per byte for m = 8; for m = 4
-    subspace 2i in the low half of byte i and 2i + 1 in the high half."""
+    subspace 2i in the low half of byte i and 2i + 1 in the high half; for
+    m = 16 the 16-bit id of subspace b little-endian at bytes 2b, 2b + 1."""
+    if m == 16:
+        ids = np.ascontiguousarray(np.asarray(ids, np.uint16).astype("<u2"))
+        return ids.view(np.uint8).reshape(ids.shape[0], 16)
     ids = np.asarray(ids, np.uint8)
     if m == 8:
         return ids
     return (ids[:, 0::2] | (ids[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _hash16(c: int) -> int:
+    return ((c * 40503) & 0xFFFF) >> 8
+
+
+def check_hashed_votes(table_bytes: np.ndarray, L: np.ndarray, u: int) -> None:
+    """m = 16: the 8 hash tables of a unit hold exactly the oracle's nonzero
+    votes (entry = vote << 16 | centroid, 0 = empty), each centroid once, and
+    each entry is reachable by linear probing from its home slot (no empty slot
+    on the way), so the scan's probe finds it."""
+    tab = np.ascontiguousarray(table_bytes).view(np.uint32).reshape(8, 256)
+    for b in range(8):
+        got = {}
+        for slot in np.flatnonzero(tab[b]):
+            e = int(tab[b, slot])
+            c, vote = e & 0xFFFF, e >> 16
+            assert c not in got, f"unit {u}, subspace {b}: centroid {c} twice"
+            got[c] = vote
+            h = _hash16(c)
+            k = h
+            while k != slot:
+                assert tab[b, k] != 0, f"unit {u}, subspace {b}: {c} unreachable from slot {h}"
+                k = (k + 1) & 255
+        want = {int(c): int(L[b, c]) for c in np.flatnonzero(L[b])}
+        assert got == want, f"unit {u}, subspace {b}: votes {got} != {want}"
 
 
 def byte_vote_table(L: np.ndarray, m: int) -> np.ndarray:
@@ -156,8 +186,11 @@ def check_retrieval(wl, pkv, units, sel, sel_n, enc, vote_fn=None):
         N_r = pos.size
         L = (ok.vote_table(Qg, s, p.rho, p.vote_weights, n_sub, m)[0] if vote_fn is None
              else vote_fn(u, Qg))
-        assert np.array_equal(lut[u].reshape(16, 256).astype(np.int64), byte_vote_table(L, m)), \
-            f"unit {u}: vote table differs"
+        if m == 16:
+            check_hashed_votes(lut[u], L, u)
+        else:
+            assert np.array_equal(lut[u].reshape(16, 256).astype(np.int64), byte_vote_table(L, m)), \
+                f"unit {u}: vote table differs"
         sc_o = ok.coarse_scores(i_o, L) if N_r else np.zeros(0, np.int64)
         # scores are stored saturated at 255 (the threshold logic rescores saturated keys)
         assert np.array_equal(scores[u][:N_r].astype(np.int64), np.minimum(sc_o, 255)), \

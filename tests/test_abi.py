@@ -101,8 +101,7 @@ def test_create_validates_shapes_and_pointers():
     assert _create(big)[0] == nat.PK_ERR_INVALID                  # G * weight > 255
     zero = nat.make_config(vote_weights=(4, 3, 0, 1))
     assert _create(zero)[0] == nat.PK_ERR_INVALID
-    # subspace widths: m = 8 and m = 4 are built, m = 16 (B = 8) is valid but not built
-    assert _create(nat.make_config(n_sub=8, sub_dim=16))[0] == nat.PK_ERR_UNSUPPORTED
+    # subspace widths: m = 4, 8 and 16 are built, m = 2 (B = 64) is valid but not built
     assert _create(nat.make_config(n_sub=64, sub_dim=2))[0] == nat.PK_ERR_UNSUPPORTED
     # m = 4: a vote-table byte sums two subspaces' votes, so 2 * G * weight <= 255
     assert _create(nat.make_config(n_sub=32, sub_dim=4, vote_weights=(32, 1, 1, 1)))[0] == \
@@ -131,3 +130,5 @@ def test_no_device_is_reported_without_a_gpu():
     assert st == nat.PK_ERR_NO_DEVICE and not ctx.value
     st, ctx = _create(nat.make_config(n_sub=32, sub_dim=4, vote_weights=(31, 1, 1, 1)))
     assert st == nat.PK_ERR_NO_DEVICE and not ctx.value   # a valid m = 4 configuration
+    st, ctx = _create(nat.make_config(n_sub=8, sub_dim=16, vote_weights=(63, 1, 1, 1)))
+    assert st == nat.PK_ERR_NO_DEVICE and not ctx.value   # a valid m = 16 configuration

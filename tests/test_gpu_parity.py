@@ -215,21 +215,24 @@ def test_quantile_codebook():
     _full_check(wl, units=[0, 4, 7], tag="quantile-codebook")
 
 
-@pytest.mark.parametrize("dtype,group", [("bf16", 4), ("f32", 2)])
-def test_subspaces_of_width_4(dtype, group):
-    """32 subspaces of m = 4 (16 sign-pattern centroids each, two 4-bit ids per
-    id byte, 32 scales in a 192-byte record, the m = 4 codebook): ids, codes,
-    vote tables, scores and candidate sets bit-exact, w and estimates within
-    tolerance, attention as usual; then 70 fused decode steps through two
-    buffer fills, so the device also encodes evicted keys with m = 4."""
+@pytest.mark.parametrize("m,dtype,group", [(4, "bf16", 4), (4, "f32", 2), (16, "bf16", 4),
+                                           (16, "f32", 8)])
+def test_subspace_widths(m, dtype, group):
+    """Other subspace widths.  m = 4: 32 subspaces of 16 sign-pattern centroids,
+    two 4-bit ids per id byte, 32 scales in a 192-byte record.  m = 16: 8
+    subspaces of 65536 centroids, 16-bit ids, hashed vote tables, 8 scales in
+    a 96-byte record.  Each with its own codebook.  ids, codes, votes, scores
+    and candidate sets bit-exact, w and estimates within tolerance, attention
+    as usual; then 70 fused decode steps through two buffer fills, so the
+    device also encodes evicted keys at that width."""
     import dataclasses
     wl = W.gqa_bf16(N=20011, top_k=512, permille=50, group=group, dtype=dtype, buf_tokens=32,
                     n_local=64)
-    wl.params = dataclasses.replace(wl.params, n_sub=32, sub_dim=4)
+    wl.params = dataclasses.replace(wl.params, n_sub=128 // m, sub_dim=m)
     steps = 70
     units = [0, 5]
     pkv, sel, sel_n, out = _full_check(wl, units=units, capacity=wl.n_tokens + steps,
-                                       tag=f"m4-{dtype}-g{group}")
+                                       tag=f"m{m}-{dtype}-g{group}")
     dt = gc.torch_dtype(wl)
     Kn, Vn, Qn = W.decode_stream(wl, steps)
     for t in range(steps):
@@ -246,7 +249,7 @@ def test_subspaces_of_width_4(dtype, group):
     enc = gc.check_encode(full, pkv, units)
     gc.check_retrieval(full, pkv, units, sel, sel_n, enc)
     gc.check_attention(full, pkv, units, sel, sel_n, out)
-    gc.log(f"[m4-{dtype}-g{group}] decode steps ok (r_end {r_end})")
+    gc.log(f"[m{m}-{dtype}-g{group}] decode steps ok (r_end {r_end})")
 
 
 def test_fine_ties_periodic_keys():
