@@ -34,17 +34,34 @@ __device__ __forceinline__ uint32_t hash16(uint32_t id) {      // Fibonacci hash
     return ((id * 40503u) & 0xffffu) >> 8;
 }
 
-// votes of centroid `id` in one subspace's hash table (a bounded probe: the
-// table never holds more than 64 of its 256 slots, so an empty slot ends it)
-__device__ __forceinline__ uint32_t hashed_vote(const uint32_t* tab, uint32_t id) {
+// votes of centroid `id` in one subspace's hash table, given the entry `e`
+// at its home slot (a bounded probe: the table never holds more than 64 of
+// its 256 slots, so an empty slot ends it; an empty home slot reads as vote 0)
+__device__ __forceinline__ uint32_t hashed_vote(const uint32_t* tab, uint32_t id, uint32_t e) {
+    if ((e & 0xffffu) == id || e == 0u) return e >> 16;
     uint32_t slot = hash16(id);
-    uint32_t e = tab[slot];
-    for (int k = 0; k < 256 && e != 0u; ++k) {
-        if ((e & 0xffffu) == id) return e >> 16;
+    for (int k = 0; k < 255; ++k) {
         slot = (slot + 1u) & 255u;
         e = tab[slot];
+        if (e == 0u) return 0u;
+        if ((e & 0xffffu) == id) return e >> 16;
     }
     return 0u;
+}
+
+// coarse score of one key over the 8 hash tables: the 8 home slots are read
+// before any is resolved
+__device__ __forceinline__ uint32_t hashed_score(const uint32_t* tabs, const uint32_t w[4]) {
+    uint32_t id[8], e[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        id[b] = (w[b >> 1] >> (16 * (b & 1))) & 0xffffu;
+        e[b] = tabs[256 * b + hash16(id[b])];
+    }
+    uint32_t sc = 0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) sc += hashed_vote(tabs + 256 * b, id[b], e[b]);
+    return sc;
 }
 constexpr int kRhoMax = 8;
 constexpr int kMaxBins = 4096;   // coarse-score histogram bins (B * G * max weight + 1)

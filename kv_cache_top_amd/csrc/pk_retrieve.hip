@@ -79,9 +79,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
         uint32_t sc = 0;
         if constexpr (M == 16) {
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-                sc += hashed_vote(s_lut + 256 * b, (w[b >> 1] >> (16 * (b & 1))) & 0xffffu);
+            sc = hashed_score(s_lut, w);
         } else {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -327,10 +325,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
                 const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
                 uint32_t sc = 0;
                 if constexpr (M == 16) {
-#pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        sc += hashed_vote(reinterpret_cast<const uint32_t*>(s_list) + 256 * b,
-                                          (wv[b >> 1] >> (16 * (b & 1))) & 0xffffu);
+                    sc = hashed_score(reinterpret_cast<const uint32_t*>(s_list), wv);
                 } else {
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
