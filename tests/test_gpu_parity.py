@@ -252,6 +252,28 @@ def test_subspace_widths(m, dtype, group):
     gc.log(f"[m{m}-{dtype}-g{group}] decode steps ok (r_end {r_end})")
 
 
+@pytest.mark.parametrize("m", [4, 8, 16])
+def test_tied_centroid_scores(m):
+    """Queries whose rotated coordinates are exactly -1, 0 or +1, with whole
+    subspaces zero: many centroid scores tie exactly (all 2^m of them in a zero
+    subspace), so every width's top-rho must fall back to the lower index, and
+    the m = 16 selection takes its widest pair search.  fp32 store, so that
+    q = D H y / 128 is exact and rotates back to exactly y."""
+    import dataclasses
+    wl = W.gqa_bf16(N=12000, top_k=256, permille=50, dtype="f32", n_local=64)
+    wl.params = dataclasses.replace(wl.params, n_sub=128 // m, sub_dim=m)
+    r = np.random.default_rng(5)
+    H = ok.sylvester_hadamard(128)
+    Y = r.integers(-1, 2, size=wl.Q.shape).astype(np.float64)
+    Y[..., 0:16] = 0.0                        # the first 16 rotated coordinates of every head
+    Y[:, ::3, 48:64] = 0.0                    # and another block on every third head
+    Q = (Y @ H.T) * wl.signs().astype(np.float64) / 128.0
+    assert np.array_equal(ok.rotate_spec(Q.reshape(-1, 128).astype(np.float32), wl.signs()),
+                          Y.reshape(-1, 128).astype(np.float32))
+    wl.Q = Q.astype(np.float32)
+    _full_check(wl, units=[0, 3, 7], tag=f"tied-m{m}")
+
+
 def test_fine_ties_periodic_keys():
     """64 distinct keys repeated along the context: large groups of exactly tied
     estimates around the k-th (the bucket of the k-th holds a whole group)."""
