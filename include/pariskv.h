@@ -220,10 +220,14 @@ pk_status pk_profile_read(pk_ctx* ctx, double* ms, int64_t* launches);
 /* Debug read-back for tests: copies an internal buffer to host memory and
  * synchronises the stream.  `bytes` must equal the size reported by
  * pk_debug_size for `what`.
- *   PK_DBG_IDS     uint8  [units][cap][16]          bucket ids (m = 4: subspace 2i in the low half of byte i)
+ *   PK_DBG_IDS     uint8  [units][cap][16]          bucket ids (m = 4: subspace 2i in the low half of byte i;
+ *                                                   m = 16: little-endian uint16 per subspace)
  *   PK_DBG_REC     uint8  [units][cap][64 + 4B]     64 B nibbles (coord 2i in low half of byte i) + float32 w[B]
  *   PK_DBG_LUT     uint8  [units][16][256]          vote of each id-byte value, last pk_retrieve (m = 4:
- *                                                   row i entry c = L[2i][c & 15] + L[2i+1][c >> 4])
+ *                                                   row i entry c = L[2i][c & 15] + L[2i+1][c >> 4]);
+ *                  m = 16: uint32 [units][8][256]   per subspace a linear-probing hash table of the voted
+ *                                                   centroids: vote << 16 | centroid, 0 = empty, home slot
+ *                                                   ((c * 40503) & 0xffff) >> 8
  *   PK_DBG_SCORES  uint8  [units][cap]              min(coarse score, 255) of retrieval position sink_end + i
  *   PK_DBG_CAND    int32  [units][cmax]             candidate positions (ascending), first n_cand valid
  *   PK_DBG_EST     float  [units][cmax]             RSQ-IP estimate of each candidate
