@@ -101,6 +101,60 @@ def stream_reference(torch):
     return out
 
 
+def gather_reference(torch, layer, reps=8):
+    """Plain random gathers on this GPU with the library's gather-read reference
+    kernel (pk_gather_read), in the access patterns of the step's gather stages
+    on this layer's window: the rerank's records (C random retrieval-zone
+    positions per unit, ascending, 128-byte records over an array the size of
+    the records) and the attention's rows (2 k random positions per unit,
+    256-byte rows over an array the size of the K store).  A 1 GiB streaming
+    read before each timed gather evicts the last-level cache; the gather alone
+    is timed with HIP events on the stream it runs on."""
+    import ctypes
+    import kv_cache_top_amd._native as nat
+    wl, p = layer.wl, layer.wl.params
+    units, cap = wl.n_units, layer.cap
+    n, sink_end, r_end, _ = layer.ctx.window()
+    n_r = r_end - sink_end
+    C = min(n_r, max(p.top_k, (p.coarse_permille * n_r + 999) // 1000))
+    k = min(p.top_k, C)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    base = (torch.arange(units, device="cuda", dtype=torch.int64) * cap + sink_end)[:, None]
+    out = {}
+    for name, rec_bytes, per_unit in (("records_128B", 128, C), ("rows_256B", 256, 2 * k)):
+        arr = torch.empty(units * cap * rec_bytes, dtype=torch.uint8, device="cuda")
+        sets = []
+        for _ in range(reps):
+            pos = torch.rand(units, n_r, device="cuda", generator=gen).argsort(dim=1)[:, :per_unit]
+            sets.append((pos.sort(dim=1).values + base).to(torch.int32).contiguous())
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for i in range(reps + 1):
+            nat.check(nat.lib.pk_stream_read(ctypes.c_void_p(flush.data_ptr()), 1 << 30,
+                                             ctypes.c_void_p(sink.data_ptr()), st), "pk_stream_read")
+            if i > 0:
+                evs[i - 1][0].record(stream)
+            nat.check(nat.lib.pk_gather_read(ctypes.c_void_p(arr.data_ptr()), units * cap, rec_bytes,
+                                             ctypes.c_void_p(sets[i % reps].data_ptr()),
+                                             units * per_unit, ctypes.c_void_p(sink.data_ptr()), st),
+                      "pk_gather_read")
+            if i > 0:
+                evs[i - 1][1].record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        nbytes = units * per_unit * rec_bytes
+        out[name] = {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
+        del arr, sets
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def stage_times(ctx_list, steps_fn, n_steps, torch, nat):
     """Per-stage kernel durations (dispatch-attached HIP events) over n_steps."""
     for c in ctx_list:
@@ -777,6 +831,10 @@ def main():
         ms_warm = time_steps(torch, [layers[0]], 16, args.warm_steps)
         warm = {"steps": args.warm_steps, "us_per_step": 1e3 * ms_warm, "steps_per_s": 1e3 / ms_warm}
     sref = stream_reference(torch)
+    gref = gather_reference(torch, layers[0])
+    for k, ref in (("rerank", "records_128B"), ("attend", "rows_256B")):
+        if stages.get(k, {}).get("GBps"):
+            stages[k]["frac_of_gather_reference"] = stages[k]["GBps"] / gref[ref]["GBps"]
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -819,6 +877,7 @@ def main():
                           "frac_of_stream_read": comb_gbs / sref["read_GBps"] if comb_gbs else None,
                           "bytes_per_step": int(comb_bytes), "kernel_us_per_step": comb_us},
         "stream_reference": sref,
+        "gather_reference": gref,
         "dense_attention": dense,
         "warm_single_layer": warm,
         "stages": stages,

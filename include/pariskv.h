@@ -204,6 +204,18 @@ pk_status pk_get_window(const pk_ctx* ctx, int64_t* n_tokens, int64_t* sink_end,
  * Errors: PK_ERR_INVALID (NULL, misaligned or zero size). */
 pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement reference, not part of the method: gathers `count` records of
+ * `rec_bytes` bytes (a multiple of 16, at most 1024), record i being row
+ * idx[i] of the array at `src` (device memory, 16-byte aligned, n_rows rows of
+ * rec_bytes; idx device int32, values clamped to [0, n_rows) on the device),
+ * 16 bytes per lane, so that the path's gather stages (the rerank's 128-byte
+ * records, the attention's 256-byte K/V rows) can be set against this device's
+ * random-gather rate for the same access pattern.  *sink (device, 4 bytes) is
+ * written only in the unlikely case that the checksum equals a fixed constant.
+ * Errors: PK_ERR_INVALID (NULL, misaligned, sizes out of range). */
+pk_status pk_gather_read(const void* src, int64_t n_rows, int32_t rec_bytes, const int32_t* idx,
+                         int64_t count, uint32_t* sink, void* stream);
+
 /* Per-stage kernel timing.  While enabled, every kernel the context launches
  * is bracketed by HIP events recorded on the stream it runs on.
  * pk_profile_read synchronises those events and returns, per stage, the

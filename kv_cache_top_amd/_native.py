@@ -67,6 +67,7 @@ SIGNATURES = {
     "pk_debug_size": (_sz, [_c_void_p, _i32]),
     "pk_debug_copy": (_i32, [_c_void_p, _i32, _c_void_p, _sz, _c_void_p]),
     "pk_stream_read": (_i32, [_c_void_p, _sz, _c_void_p, _c_void_p]),
+    "pk_gather_read": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _i64, _c_void_p, _c_void_p]),
 }
 
 

@@ -452,6 +452,16 @@ pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* st
     return PK_OK;
 }
 
+pk_status pk_gather_read(const void* src, int64_t n_rows, int32_t rec_bytes, const int32_t* idx,
+                         int64_t count, uint32_t* sink, void* stream) {
+    if (!src || !idx || !sink || n_rows < 1 || count < 1 || rec_bytes < 16 || rec_bytes > 1024 ||
+        (rec_bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) ||
+        n_rows > (int64_t)1 << 40 || count > ((int64_t)1 << 40) / rec_bytes)
+        return PK_ERR_INVALID;
+    PK_HIP(pk::launch_gather_read(src, n_rows, rec_bytes, idx, count, sink, (hipStream_t)stream));
+    return PK_OK;
+}
+
 pk_status pk_get_window(const pk_ctx* c, int64_t* n_tokens, int64_t* sink_end, int64_t* r_end,
                         int64_t* buf) {
     if (!c) return PK_ERR_INVALID;

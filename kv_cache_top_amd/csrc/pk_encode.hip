@@ -505,6 +505,38 @@ __global__ __launch_bounds__(kBlock) void stream_read_kernel(const uint4* __rest
 }
 
 // ---------------------------------------------------------------------------
+// random gather of records (measurement reference): lane t reads the 16-byte
+// piece t % per of record t / per, record i at row idx[i] (clamped to the
+// array); four pieces per thread in flight, folded into a checksum stored only
+// if it matches an improbable value
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void gather_read_kernel(const uint4* __restrict__ src,
+                                                              int64_t n_rows, int per,
+                                                              const int32_t* __restrict__ idx,
+                                                              int64_t total,
+                                                              uint32_t* __restrict__ sink) {
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t t0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; t0 < total; t0 += 4 * stride) {
+        int64_t off[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t t = t0 + k * stride < total ? t0 + k * stride : total - 1;
+            const int64_t rec = t / per;
+            int64_t row = idx[rec];
+            row = row < 0 ? 0 : (row >= n_rows ? n_rows - 1 : row);
+            off[k] = row * per + (t - rec * per);
+        }
+        uint4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = src[off[k]];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64_t p0,
@@ -570,6 +602,16 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
     return launch(append_kernel, dim3(blocks), dim3(kBlock), 0, st, (const uint4*)k_new,
                   (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap, pos, units,
                   (uint4*)ring.k, (uint4*)ring.v, ring.rows, slot);
+}
+
+hipError_t launch_gather_read(const void* src, int64_t n_rows, int rec_bytes, const int32_t* idx,
+                              int64_t count, uint32_t* sink, hipStream_t st) {
+    const int per = rec_bytes / 16;
+    const int64_t total = count * per;
+    int64_t blocks = (total + 4 * kBlock - 1) / (4 * kBlock);
+    if (blocks > 16384) blocks = 16384;
+    return launch(gather_read_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                  (const uint4*)src, n_rows, per, idx, total, sink);
 }
 
 hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, hipStream_t st) {

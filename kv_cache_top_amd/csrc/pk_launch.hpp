@@ -77,6 +77,8 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
                          int64_t row_bytes, int64_t cap, int64_t pos, int units,
                          const HotRing& ring, hipStream_t st);
 hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, hipStream_t st);
+hipError_t launch_gather_read(const void* src, int64_t n_rows, int rec_bytes, const int32_t* idx,
+                              int64_t count, uint32_t* sink, hipStream_t st);
 // copy rows [0, sink_end) and [r_end, n) of every unit from the store into the ring
 hipError_t launch_ring_fill(const void* K, const void* V, int64_t row_bytes, int64_t cap,
                             int units, int64_t sink_end, int64_t r_end, int64_t n,

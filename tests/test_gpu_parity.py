@@ -557,3 +557,23 @@ def test_append_past_capacity_is_rejected():
     with pytest.raises(PkError):
         pkv.append(k, k)
     assert pkv.window() == before
+
+
+def test_gather_reference_kernel():
+    """The random-gather measurement reference runs for the record and row sizes
+    the bench uses and leaves the sink alone (its checksum of zeros is 0)."""
+    import ctypes
+    import kv_cache_top_amd._native as nat
+    arr = torch.zeros(1000 * 512, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+    for rec_bytes in (16, 128, 256, 512):
+        rows = arr.numel() // rec_bytes
+        idx = torch.randint(0, rows, (5003,), device="cuda", generator=g, dtype=torch.int32)
+        st = nat.lib.pk_gather_read(ctypes.c_void_p(arr.data_ptr()), rows, rec_bytes,
+                                    ctypes.c_void_p(idx.data_ptr()), idx.numel(),
+                                    ctypes.c_void_p(sink.data_ptr()), None)
+        assert st == nat.PK_OK
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
