@@ -71,9 +71,12 @@ def parse():
     return ap.parse_args()
 
 
-def stream_reference(torch):
+def stream_reference(torch, scan_bytes=None):
     """Plain streaming kernels on this GPU over 1 GiB: the library's streaming-read
-    reference kernel (pk_stream_read) and a torch device copy (read + write bytes)."""
+    reference kernel (pk_stream_read) and a torch device copy (read + write bytes).
+    With scan_bytes, also the streaming read of exactly that many bytes (the scan's
+    algorithmic bytes per launch), timed cold: a 1 GiB read of another buffer
+    before each timed read evicts the last-level cache."""
     import ctypes
     import kv_cache_top_amd._native as nat
     x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
@@ -96,6 +99,23 @@ def stream_reference(torch):
         b.record()
         torch.cuda.synchronize()
         out[name] = nbytes * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    if scan_bytes:
+        nb = int(scan_bytes) // 16 * 16
+        part = y.view(torch.uint8)[:nb]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(8)]
+        for i in range(9):
+            read()                                   # evicts: 1 GiB of x
+            if i > 0:
+                evs[i - 1][0].record()
+            nat.check(nat.lib.pk_stream_read(ctypes.c_void_p(part.data_ptr()), nb,
+                                             ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)),
+                      "pk_stream_read")
+            if i > 0:
+                evs[i - 1][1].record()
+        torch.cuda.synchronize()
+        us = 1e3 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        out["read_scan_bytes"] = {"bytes": nb, "us": us, "GBps": nb / (us * 1e-6) / 1e9}
     del x, y
     torch.cuda.empty_cache()
     return out
@@ -830,8 +850,10 @@ def main():
     if args.warm_steps > 0:
         ms_warm = time_steps(torch, [layers[0]], 16, args.warm_steps)
         warm = {"steps": args.warm_steps, "us_per_step": 1e3 * ms_warm, "steps_per_s": 1e3 / ms_warm}
-    sref = stream_reference(torch)
+    sref = stream_reference(torch, scan_bytes=stages.get("scan", {}).get("alg_bytes"))
     gref = gather_reference(torch, layers[0])
+    if stages.get("scan", {}).get("GBps") and "read_scan_bytes" in sref:
+        stages["scan"]["frac_of_same_size_read"] = stages["scan"]["GBps"] / sref["read_scan_bytes"]["GBps"]
     for k, ref in (("rerank", "records_128B"), ("attend", "rows_256B")):
         if stages.get(k, {}).get("GBps"):
             stages[k]["frac_of_gather_reference"] = stages[k]["GBps"] / gref[ref]["GBps"]
