@@ -69,6 +69,17 @@ def test_gqa_128k_batch4_planted():
     assert torch.isfinite(out).all()
 
 
+@pytest.mark.parametrize("m", [4, 16])
+def test_gqa_128k_batch4_planted_subspace_widths(m):
+    """The full 128K-token, batch-4 planted workload with m = 4 and m = 16
+    subspaces, in the launch configuration the variant sweep times; two units
+    against the oracle."""
+    import dataclasses
+    wl = W.gqa_128k_planted()
+    wl.params = dataclasses.replace(wl.params, n_sub=128 // m, sub_dim=m)
+    _full_check(wl, units=[5, 26], tag=f"gqa-128k-m{m}")
+
+
 def test_fine_selection_30k_candidates():
     """200K tokens with a 15 % coarse budget: about 30000 candidates per unit, past
     what the fused selection holds, so the fine top-k keeps 32 candidates per
