@@ -263,6 +263,18 @@ def test_subspace_widths(m, dtype, group):
     gc.log(f"[m{m}-{dtype}-g{group}] decode steps ok (r_end {r_end})")
 
 
+@pytest.mark.parametrize("m,rho,group", [(16, 8, 8), (4, 8, 2), (16, 1, 1)])
+def test_subspace_width_probe_counts(m, rho, group):
+    """Edges of the m = 4 and m = 16 query preparation: 8 probes of 16
+    centroids (m = 4), 8 probes by 8 heads merged into one m = 16 table (64
+    picks, every lane of the merge wave), and a single probe of a single head."""
+    import dataclasses
+    wl = W.gqa_bf16(N=16000, top_k=512, permille=60, group=group)
+    wl.params = dataclasses.replace(wl.params, n_sub=128 // m, sub_dim=m, rho=rho,
+                                    vote_weights=tuple(range(rho, 0, -1)))
+    _full_check(wl, units=[1, 6], tag=f"m{m}-rho{rho}-g{group}")
+
+
 @pytest.mark.parametrize("m", [4, 8, 16])
 def test_tied_centroid_scores(m):
     """Queries whose rotated coordinates are exactly -1, 0 or +1, with whole
