@@ -893,6 +893,9 @@ def main():
             "unit": "GB/s",
             "frac": (scan_gbs / HBM_PEAK_GBS) if scan_gbs else None,
             "traffic": measured_traffic(),
+            # a plain cold streaming read of the same bytes on this GPU
+            "same_size_read_GBps": sref.get("read_scan_bytes", {}).get("GBps"),
+            "frac_of_same_size_read": stages.get("scan", {}).get("frac_of_same_size_read"),
         },
         "retrieval_hbm": {"scan_rerank_gather_GBps": comb_gbs,
                           "frac": comb_gbs / HBM_PEAK_GBS if comb_gbs else None,
