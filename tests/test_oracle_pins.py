@@ -296,6 +296,24 @@ def test_decode_step_with_k_at_least_retrieval_is_full_attention():
         assert np.allclose(res["out"], _sdpa(Qg, K, V), atol=1e-12)
 
 
+@pytest.mark.parametrize("m", [4, 16])
+def test_decode_step_other_widths_keep_all_is_full_attention(m):
+    """The whole oracle step at m = 4 and m = 16 (their codebooks, vote tables,
+    scores and estimates) with every retrieval-zone key kept reproduces full
+    attention, and the candidate set is the whole zone."""
+    from oracle.codebook import spec_tables
+    from synth.workloads import gqa_bf16
+    wl = gqa_bf16(N=700, top_k=4096, permille=1000, n_local=64)
+    s = wl.signs()
+    lv, sq = spec_tables(m=m)
+    K, V, Qg = wl.K[0, 2], wl.V[0, 2], wl.Q[0, 8:12]
+    ids, nib, w = pk.encode_keys(K, s, lv, sq, n_sub=128 // m, m=m)
+    res = pk.decode_step(K, V, Qg, ids, nib, w, pk.Window(700, 4, 64, 0), s, lv, permille=1000,
+                         top_k=4096, n_sub=128 // m, m=m)
+    assert np.array_equal(res["cand"], np.arange(4, 700 - 64))
+    assert np.allclose(res["out"], _sdpa(Qg, K, V), atol=1e-12)
+
+
 # ---------------------------------------------------------------------- window
 
 def test_window_partitions_sequence():
