@@ -44,16 +44,8 @@ struct AbsCoordLaw {
     }
 };
 
-}  // namespace
-
-// Alternative reading: equal-probability bins (threshold l = the l/n quantile of
-// a, found by bisection on the closed-form law) with conditional-mean levels.
-extern "C" pk_status pk_codebook_quantile(int32_t sub_dim, int32_t n_levels, float* levels,
-                                          float* sq_thresholds) {
-    if (sub_dim < 2 || n_levels != 8 || !levels || !sq_thresholds) return PK_ERR_INVALID;
-    const AbsCoordLaw law(sub_dim);
-    const int n = n_levels;
-    double t[8];
+// thresholds t[0..n-2] at the l/n quantiles of the law (bisection)
+void quantile_thresholds(const AbsCoordLaw& law, int n, double* t) {
     for (int i = 0; i < n - 1; ++i) {
         const double target = (i + 1.0) / n;
         double lo = 0.0, hi = 1.0;
@@ -64,6 +56,19 @@ extern "C" pk_status pk_codebook_quantile(int32_t sub_dim, int32_t n_levels, flo
         }
         t[i] = 0.5 * (lo + hi);
     }
+}
+
+}  // namespace
+
+// Alternative reading: equal-probability bins (threshold l = the l/n quantile of
+// a, found by bisection on the closed-form law) with conditional-mean levels.
+extern "C" pk_status pk_codebook_quantile(int32_t sub_dim, int32_t n_levels, float* levels,
+                                          float* sq_thresholds) {
+    if (sub_dim < 2 || n_levels != 8 || !levels || !sq_thresholds) return PK_ERR_INVALID;
+    const AbsCoordLaw law(sub_dim);
+    const int n = n_levels;
+    double t[8];
+    quantile_thresholds(law, n, t);
     double lo = 0.0;
     for (int i = 0; i < n; ++i) {
         const double hi = (i == n - 1) ? 1.0 : t[i];
@@ -81,7 +86,11 @@ extern "C" pk_status pk_codebook(int32_t sub_dim, int32_t n_levels, float* level
     const AbsCoordLaw law(sub_dim);
     const int n = n_levels;
     double t[8], c[8];
-    for (int i = 0; i < n - 1; ++i) t[i] = (i + 1.0) / n;  // uniform start
+    // start from the equal-probability thresholds: every bin then has mass
+    // 1/n (from a uniform start on [0, 1] the top bins of a large-m law hold
+    // no mass in double precision, and their levels would be 0/0); the law
+    // is log-concave for m >= 3, so the Lloyd fixed point is unique
+    quantile_thresholds(law, n, t);
     for (int iter = 0; iter < 200000; ++iter) {
         double lo = 0.0;
         for (int i = 0; i < n; ++i) {
