@@ -26,7 +26,10 @@
  * void*, NULL = the null stream) and returns without synchronising.  Errors
  * found by host-side validation are returned before anything is launched and
  * leave the context unchanged.  A device fault surfaces as PK_ERR_HIP from a
- * later call.  A context is not thread-safe; calls on one context must be
+ * later call.  A runtime call that fails inside the library (an allocation, a
+ * launch) is reported only through the returned status: the library clears
+ * the calling thread's HIP last-error state before returning, so the caller's
+ * own later error checks do not see it.  A context is not thread-safe; calls on one context must be
  * issued from one host thread in order.
  */
 #ifndef PARISKV_H

@@ -72,9 +72,23 @@ namespace {
 
 bool g_verbose = std::getenv("PK_VERBOSE") != nullptr;
 
+// A failed runtime call also sets the calling thread's last-error state; it is
+// reported through the returned status and then cleared, so that the
+// caller's next error check of its own work does not pick it up.
 pk_status hip_fail(hipError_t e, const char* what) {
     if (g_verbose) std::fprintf(stderr, "pariskv: %s: %s\n", what, hipGetErrorString(e));
+    (void)hipGetLastError();
     return e == hipErrorOutOfMemory ? PK_ERR_OOM : PK_ERR_HIP;
+}
+
+pk_status alloc_fail() {
+    (void)hipGetLastError();
+    return PK_ERR_OOM;
+}
+
+pk_status runtime_fail() {
+    (void)hipGetLastError();
+    return PK_ERR_HIP;
 }
 
 #define PK_HIP(call)                                      \
@@ -410,7 +424,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         if (hipMalloc(a.p, a.bytes) != hipSuccess) {
             free_all(c);
             delete c;
-            return PK_ERR_OOM;
+            return alloc_fail();
         }
     }
     c->ring.n_sink = cfg->n_sink;
@@ -421,7 +435,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         if (hipMalloc(&c->ring.k, rb) != hipSuccess || hipMalloc(&c->ring.v, rb) != hipSuccess) {
             free_all(c);
             delete c;
-            return PK_ERR_OOM;
+            return alloc_fail();
         }
     }
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
@@ -431,7 +445,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         hipDeviceSynchronize() != hipSuccess) {
         free_all(c);
         delete c;
-        return PK_ERR_HIP;
+        return runtime_fail();
     }
     *out = c;
     return PK_OK;
@@ -513,10 +527,10 @@ pk_status pk_fit_centroids(pk_ctx* c, int64_t n_tokens, const int32_t* init_pos,
     if (!c->cents) {
         float* ct = nullptr;
         long long* sm = nullptr;
-        if (hipMalloc((void**)&ct, n * sizeof(float)) != hipSuccess) return PK_ERR_OOM;
+        if (hipMalloc((void**)&ct, n * sizeof(float)) != hipSuccess) return alloc_fail();
         if (hipMalloc((void**)&sm, n * sizeof(long long)) != hipSuccess) {
             (void)hipFree(ct);
-            return PK_ERR_OOM;
+            return alloc_fail();
         }
         c->cents = ct;
         c->km_sums = sm;
@@ -572,7 +586,7 @@ pk_status pk_dense_attend(pk_ctx* c, const void* q, float* out, void* stream) {
         if (c->dense_part) (void)hipFree(c->dense_part);
         c->dense_part = nullptr;
         c->dense_bytes = 0;
-        if (hipMalloc((void**)&c->dense_part, need) != hipSuccess) return PK_ERR_OOM;
+        if (hipMalloc((void**)&c->dense_part, need) != hipSuccess) return alloc_fail();
         c->dense_bytes = need;
     }
     const hipStream_t st = (hipStream_t)stream;
@@ -605,7 +619,7 @@ pk_status pk_decode_step(pk_ctx* c, const void* k_new, const void* v_new, const 
 
 pk_status pk_profile_enable(pk_ctx* c, int32_t on) {
     if (!c) return PK_ERR_INVALID;
-    if (hipDeviceSynchronize() != hipSuccess) return PK_ERR_HIP;
+    if (hipDeviceSynchronize() != hipSuccess) return runtime_fail();
     release_events(c);
     c->profiling = on != 0;
     return PK_OK;

@@ -600,3 +600,24 @@ def test_gather_reference_kernel():
         assert st == nat.PK_OK
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0
+
+
+def test_create_out_of_device_memory_is_reported():
+    """A context whose metadata cannot fit in device memory (64 x 8 units at
+    2^24 tokens: 137 GB of ids and 1.1 TB of records) fails with PK_ERR_OOM
+    before launching anything, frees what it had allocated, and a normal
+    context works afterwards.  The store pointers are never touched by
+    pk_create, so small tensors stand in for them."""
+    import ctypes
+    import kv_cache_top_amd._native as nat
+    small = torch.zeros(4096, dtype=torch.bfloat16, device="cuda")
+    cfg = nat.make_config()
+    ctx = ctypes.c_void_p()
+    free0, _ = torch.cuda.mem_get_info()
+    st = nat.lib.pk_create(ctypes.byref(cfg), 64, 8, 32, 1 << 24, nat.PK_BF16,
+                           ctypes.c_void_p(small.data_ptr()), ctypes.c_void_p(small.data_ptr()),
+                           nat.PK_MEM_DEVICE, ctypes.byref(ctx))
+    assert st == nat.PK_ERR_OOM and not ctx.value
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 >= free0 - (64 << 20), "partial allocations were not released"
+    _full_check(W.gqa_bf16(N=9000, top_k=256), units=[0], tag="after-oom")
