@@ -89,7 +89,8 @@ typedef struct pk_ctx pk_ctx;  /* opaque; owned by the library */
  * scales per token: 64 B of 4-bit codes + 4 B per subspace, so 128 B for m = 8
  * and 192 B for m = 4), the window counters and all scratch.  The caller
  * keeps ownership of k_store / v_store, which must outlive the context.
- * Requires n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8} (other G up to 16
+ * Requires batch * n_kv_heads <= 65535 (else PK_ERR_UNSUPPORTED) and
+ * n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8} (other G up to 16
  * are valid but PK_ERR_UNSUPPORTED), G * max(weight) <= 255 (m = 8; 127 for m = 4), buf_tokens <=
  * n_local, capacity <= 2^24.  Allocates device memory and synchronises the device.
  * Errors: PK_ERR_INVALID, PK_ERR_UNSUPPORTED, PK_ERR_NO_DEVICE, PK_ERR_OOM. */

@@ -357,6 +357,8 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     if (!out) return PK_ERR_INVALID;
     *out = nullptr;
     if (batch < 1 || !k_store || !v_store) return PK_ERR_INVALID;
+    // units index the grid's y dimension of most kernels (at most 65535)
+    if ((int64_t)batch * n_kv_heads > 65535) return PK_ERR_UNSUPPORTED;
     if (kv_dtype != PK_F32 && kv_dtype != PK_BF16) return PK_ERR_INVALID;
     if (store_mem != PK_MEM_DEVICE && store_mem != PK_MEM_HOST_MAPPED) return PK_ERR_INVALID;
     int G = 0, nbins = 0;

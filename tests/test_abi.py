@@ -93,6 +93,8 @@ def test_create_validates_shapes_and_pointers():
     assert _create(cfg, n_q=8 * 32)[0] == nat.PK_ERR_INVALID      # G = 32
     assert _create(cfg, cap=0)[0] == nat.PK_ERR_INVALID
     assert _create(cfg, cap=(1 << 24) + 1)[0] == nat.PK_ERR_UNSUPPORTED
+    assert _create(cfg, batch=70000, n_kv=1, n_q=4)[0] == nat.PK_ERR_UNSUPPORTED   # units > 65535
+    assert _create(cfg, batch=1 << 20, n_kv=1 << 12, n_q=1 << 14)[0] == nat.PK_ERR_UNSUPPORTED
     assert _create(cfg, dtype=7)[0] == nat.PK_ERR_INVALID
     assert _create(cfg, k=0)[0] == nat.PK_ERR_INVALID
     assert _create(cfg, k=24)[0] == nat.PK_ERR_INVALID            # not 16-byte aligned
