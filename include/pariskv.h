@@ -20,7 +20,8 @@
  *   sel           [batch][n_kv_heads][top_k]       int32 token positions, ascending
  *   sel_n         [batch][n_kv_heads]              int32 number of valid entries of sel
  *   out           [batch][n_q_heads][d]            float32
- * All device pointers must be 16-byte aligned; rows are contiguous.
+ * All device pointers must be 16-byte aligned (checked: PK_ERR_INVALID); rows
+ * are contiguous.
  *
  * Streams: every call that launches work takes a hipStream_t (passed as
  * void*, NULL = the null stream) and returns without synchronising.  Errors

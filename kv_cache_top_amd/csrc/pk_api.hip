@@ -99,6 +99,10 @@ pk_status runtime_fail() {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// every device pointer an entry point receives must be 16-byte aligned (the
+// kernels read and write them with 16-byte vector accesses)
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 hipEvent_t take_event(pk_ctx* c) {
     if (!c->event_pool.empty()) {
         hipEvent_t e = c->event_pool.back();
@@ -546,6 +550,7 @@ pk_status pk_fit_centroids(pk_ctx* c, int64_t n_tokens, const int32_t* init_pos,
 
 pk_status pk_append_decode_keys(pk_ctx* c, const void* k_new, const void* v_new, void* stream) {
     if (!c || !k_new || !v_new) return PK_ERR_INVALID;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PK_ERR_INVALID;
     if (!c->prefilled || c->cfg.buf_tokens == 0) return PK_ERR_INVALID;
     if (c->n + 1 > c->cap) return PK_ERR_CAPACITY;
     const hipStream_t st = (hipStream_t)stream;
@@ -566,6 +571,7 @@ pk_status pk_append_decode_keys(pk_ctx* c, const void* k_new, const void* v_new,
 
 pk_status pk_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, void* stream) {
     if (!c || !q || !sel || !sel_n) return PK_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(sel) || !aligned16(sel_n)) return PK_ERR_INVALID;
     if (!c->prefilled) return PK_ERR_INVALID;
     return run_retrieve(c, q, sel, sel_n, nullptr, nullptr, (hipStream_t)stream);
 }
@@ -573,12 +579,15 @@ pk_status pk_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, vo
 pk_status pk_sparse_attend(pk_ctx* c, const void* q, const int32_t* sel, const int32_t* sel_n,
                            float* out, void* stream) {
     if (!c || !q || !sel || !sel_n || !out) return PK_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(sel) || !aligned16(sel_n) || !aligned16(out))
+        return PK_ERR_INVALID;
     if (!c->prefilled) return PK_ERR_INVALID;
     return run_attend(c, q, sel, sel_n, out, (hipStream_t)stream);
 }
 
 pk_status pk_dense_attend(pk_ctx* c, const void* q, float* out, void* stream) {
     if (!c || !q || !out) return PK_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(out)) return PK_ERR_INVALID;
     if (!c->prefilled || c->n < 1) return PK_ERR_INVALID;
     if (c->ring.k != nullptr) return PK_ERR_UNSUPPORTED;
     const int64_t n_splits = ceil_div(c->n, pk::attend_split_keys());
@@ -603,6 +612,9 @@ pk_status pk_dense_attend(pk_ctx* c, const void* q, float* out, void* stream) {
 pk_status pk_decode_step(pk_ctx* c, const void* k_new, const void* v_new, const void* q,
                          int32_t* sel, int32_t* sel_n, float* out, void* stream) {
     if (!c || !k_new || !v_new || !q || !sel || !sel_n || !out) return PK_ERR_INVALID;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(sel) ||
+        !aligned16(sel_n) || !aligned16(out))
+        return PK_ERR_INVALID;
     if (!c->prefilled || c->cfg.buf_tokens == 0) return PK_ERR_INVALID;
     if (c->n + 1 > c->cap) return PK_ERR_CAPACITY;
     const hipStream_t st = (hipStream_t)stream;

@@ -602,6 +602,42 @@ def test_gather_reference_kernel():
     assert int(sink.abs().sum()) == 0
 
 
+def test_misaligned_pointers_are_rejected():
+    """A device pointer that is not 16-byte aligned (a query taken one element
+    into a buffer) is refused on the host with PK_ERR_INVALID by every per-step
+    entry point, nothing is launched, and the context is unchanged: the next
+    call with aligned buffers matches the oracle."""
+    import ctypes
+    import kv_cache_top_amd._native as nat
+    wl = W.gqa_bf16(N=9000, top_k=256, buf_tokens=16, n_local=64)
+    pkv = gc.make_ctx(wl, capacity=9100)
+    pkv.encode_keys(wl.n_tokens)
+    q = gc.queries(wl)
+    big = torch.empty(q.numel() + 8, dtype=q.dtype, device="cuda")
+    qm = big[1:1 + q.numel()]                       # 2 bytes past an aligned address
+    sel = torch.empty((1, 8, 256), dtype=torch.int32, device="cuda")
+    sel_n = torch.empty((1, 8), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+    kv = torch.empty((1, 8, 128), dtype=q.dtype, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    before = pkv.window()
+    lib, ctx = nat.lib, pkv._ctx
+    assert lib.pk_retrieve(ctx, P(qm), P(sel), P(sel_n), None) == nat.PK_ERR_INVALID
+    assert lib.pk_sparse_attend(ctx, P(qm), P(sel), P(sel_n), P(out), None) == nat.PK_ERR_INVALID
+    assert lib.pk_dense_attend(ctx, P(qm), P(out), None) == nat.PK_ERR_INVALID
+    assert lib.pk_decode_step(ctx, P(kv), P(kv), P(qm), P(sel), P(sel_n), P(out),
+                              None) == nat.PK_ERR_INVALID
+    kvm = torch.empty(kv.numel() + 8, dtype=kv.dtype, device="cuda")[3:3 + kv.numel()]
+    assert lib.pk_append_decode_keys(ctx, P(kvm), P(kv), None) == nat.PK_ERR_INVALID
+    assert pkv.window() == before
+    sel, sel_n = pkv.retrieve(q)
+    out = pkv.sparse_attend(q, sel, sel_n)
+    torch.cuda.synchronize()
+    enc = gc.check_encode(wl, pkv, [2])
+    gc.check_retrieval(wl, pkv, [2], sel, sel_n, enc)
+    gc.check_attention(wl, pkv, [2], sel, sel_n, out)
+
+
 def test_create_out_of_device_memory_is_reported():
     """A context whose metadata cannot fit in device memory (64 x 8 units at
     2^24 tokens: 137 GB of ids and 1.1 TB of records) fails with PK_ERR_OOM
