@@ -156,12 +156,18 @@ def test_fine_ties_identical_keys():
     assert np.array_equal(s[0], np.arange(sink_end, sink_end + 512))
 
 
-def test_saturated_coarse_scores():
+@pytest.mark.parametrize("m", [8, 4, 16])
+def test_saturated_coarse_scores(m):
     """A fifth of the keys equal to the query shared by the whole GQA group: those
-    score the maximum 256 (every subspace's top centroid for every head), above
-    the 255 a stored score holds, and they are more than the coarse budget, so
-    the threshold is 256 and the saturated keys are rescored from their ids."""
+    score the maximum B G w_max (every subspace's top centroid for every head):
+    256 for m = 8 and 512 for m = 4, above the 255 a stored score holds, and
+    they are more than the coarse budget, so the threshold is that maximum and
+    the saturated keys are rescored from their ids (with the pair tables for
+    m = 4).  For m = 16 the maximum is 128: no saturation, but thousands of
+    keys tie at the threshold in the hashed tables."""
+    import dataclasses
     wl = W.gqa_bf16(N=20000, top_k=512, permille=100)
+    wl.params = dataclasses.replace(wl.params, n_sub=128 // m, sub_dim=m)
     G = wl.group
     for h in range(wl.n_kv):
         wl.Q[:, h * G:(h + 1) * G] = wl.Q[:, h * G:h * G + 1]
@@ -169,9 +175,10 @@ def test_saturated_coarse_scores():
     hit = pos[pos % 5 == 0]
     for h in range(wl.n_kv):
         wl.K[:, h, hit] = wl.Q[:, h * G][:, None, :]
-    pkv, sel, sel_n, _ = _full_check(wl, units=[0, 5], tag="saturated")
+    pkv, sel, sel_n, _ = _full_check(wl, units=[0, 5], tag=f"saturated-m{m}")
     meta = pkv.debug(6)
-    assert meta[0][0] == 256 and meta[5][0] == 256, meta[:, 0]
+    top = (128 // m) * G * 4
+    assert meta[0][0] == top and meta[5][0] == top, meta[:, 0]
 
 
 @pytest.mark.parametrize("rho,weights,permille", [
