@@ -244,6 +244,16 @@ def run_config4(args):
     ms_step = a.elapsed_time(b) / args.steps
     stages = stage_times([ctx], steps, min(args.profile_steps, 32), torch, nat)
     n, sink_end, r_end, _ = ctx.window()
+    # recall@k of the last step's selection against the exact top-k of the
+    # retrieval zone (appended and evicted tokens included, read from the store)
+    torch.cuda.synchronize()
+    q_last = q[(state["t"] - 1) % pool].float().cpu().numpy()
+    sel_h, sel_nh = sel.cpu().numpy().reshape(8, -1), sel_n.cpu().numpy().reshape(-1)
+    pos = np.arange(sink_end, r_end)
+    rec = [recall_at_k(sel_h[h][:sel_nh[h]],
+                       exact_topk(ctx.K[0, h, :r_end].float().numpy(), q_last[0, 4 * h:4 * h + 4],
+                                  pos, p.top_k))
+           for h in range(8)]
     n_r = r_end - sink_end
     C = min(n_r, max(p.top_k, (p.coarse_permille * n_r + 999) // 1000))
     scan_b, rerank_b = 16 * n_r * 8, 128 * C * 8
@@ -266,6 +276,7 @@ def run_config4(args):
                       "retrieved_GBps": host_b / st("attend") / 1e9},
         "stages": stages,
         "encode": {"keys": 8 * n_r, "ms": enc_ms, "host_read_GBps": 8 * n_r * 256 / (enc_ms * 1e-3) / 1e9},
+        "recall_at_k": float(np.mean(rec)),
     }
     print(json.dumps(result), flush=True)
 
