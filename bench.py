@@ -893,6 +893,7 @@ def main():
             "batch": wl.batch, "kv_heads": wl.n_kv, "q_heads": wl.n_kv * wl.group, "head_dim": 128,
             "context": wl.n_tokens, "kv_dtype": "bf16", "top_k": wl.params.top_k,
             "coarse_permille": wl.params.coarse_permille, "rho": wl.params.rho,
+            "subspaces": wl.params.n_sub, "sub_dim": wl.params.sub_dim,
             "sink": wl.params.n_sink, "local": wl.params.n_local,
             "update_buffer": wl.params.buf_tokens, "layers_cycled": nl,
         },
