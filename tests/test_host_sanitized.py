@@ -12,11 +12,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
 def test_codebook_host_code_under_sanitizers(tmp_path):
-    exe = str(tmp_path / "codebook_driver")
+    exe = str(tmp_path / "codebook_check")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I", os.path.join(ROOT, "include"),
-           os.path.join(ROOT, "tests", "host", "codebook_driver.cpp"),
+           os.path.join(ROOT, "tests", "host", "codebook_check.cpp"),
            os.path.join(ROOT, "kv_cache_top_amd", "csrc", "pk_codebook.cpp"), "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
