@@ -609,6 +609,28 @@ def test_gather_reference_kernel():
     assert int(sink.abs().sum()) == 0
 
 
+@pytest.mark.parametrize("m", [4, 16])
+def test_learned_centroids_need_width_8(m):
+    """The learned-centroid comparison stage fits 256 centroids of 8
+    coordinates: other widths are refused (PK_ERR_UNSUPPORTED) before any
+    device access, and the context then works as usual."""
+    import ctypes
+    import dataclasses
+    import kv_cache_top_amd._native as nat
+    wl = W.gqa_bf16(N=6000, top_k=256)
+    wl.params = dataclasses.replace(wl.params, n_sub=128 // m, sub_dim=m)
+    pkv = gc.make_ctx(wl)
+    init = torch.zeros((wl.n_units, 256), dtype=torch.int32, device="cuda")
+    st = nat.lib.pk_fit_centroids(pkv._ctx, wl.n_tokens, ctypes.c_void_p(init.data_ptr()), 3, None)
+    assert st == nat.PK_ERR_UNSUPPORTED
+    pkv.encode_keys(wl.n_tokens)
+    q = gc.queries(wl)
+    sel, sel_n = pkv.retrieve(q)
+    torch.cuda.synchronize()
+    enc = gc.check_encode(wl, pkv, [3])
+    gc.check_retrieval(wl, pkv, [3], sel, sel_n, enc)
+
+
 def test_misaligned_pointers_are_rejected():
     """A device pointer that is not 16-byte aligned (a query taken one element
     into a buffer) is refused on the host with PK_ERR_INVALID by every per-step
