@@ -30,7 +30,15 @@
  * later call.  A runtime call that fails inside the library (an allocation, a
  * launch) is reported only through the returned status: the library clears
  * the calling thread's HIP last-error state before returning, so the caller's
- * own later error checks do not see it.  A context is not thread-safe; calls on one context must be
+ * own later error checks do not see it.
+ *
+ * HIP graph capture: each call takes its launch decisions on the host from
+ * host-side state (the window, and for pk_retrieve / pk_decode_step which of
+ * two device tables the coarse-score histogram is accumulated into; the calls
+ * alternate between them).  A captured call replays the decisions it was
+ * captured with, so a graph holding one pk_retrieve gives wrong coarse counts
+ * from its second replay on.  The calls are meant to be issued eagerly: they
+ * allocate nothing and never synchronise.  A context is not thread-safe; calls on one context must be
  * issued from one host thread in order.
  */
 #ifndef PARISKV_H
