@@ -80,6 +80,71 @@ def test_gqa_128k_batch4_planted_subspace_widths(m):
     _full_check(wl, units=[5, 26], tag=f"gqa-128k-m{m}")
 
 
+def test_maximum_capacity_single_head():
+    """The largest context the library accepts: 2^24 tokens in one fp32 unit.
+    Record offsets reach 2^31 bytes, the scan and rerank run 2048 chunks of
+    8192 keys, and the 10 % coarse budget gives 1.68M candidates (the streaming
+    fine selection).  Against the oracle: ids, codes and w of 4096 random
+    positions, the vote table, those positions' coarse scores, the estimates of
+    4096 random candidates, and the attention over the library's selection.
+    Over all positions, exactly: the candidate set is the keys above the
+    threshold plus the first ties in position order, and the fine set is the
+    top-k of the candidates' estimates (ties to the lower position)."""
+    N = 1 << 24
+    wl = W.single_head_f32(N=N, threads=16)
+    p = wl.params
+    gc.log(f"[max-capacity] {wl.name} N={N}")
+    pkv = gc.make_ctx(wl)
+    pkv.encode_keys(N)
+    q = gc.queries(wl)
+    sel, sel_n = pkv.retrieve(q)
+    out = pkv.sparse_attend(q, sel, sel_n)
+    torch.cuda.synchronize()
+    n, sink_end, r_end, _ = pkv.window()
+    K, V, Qg = gc.unit_view(wl, 0)
+    s = wl.signs()
+    levels, sq_t = gc.tables(wl)
+    r = np.random.default_rng(7)
+    # encode, vote table and coarse scores at sampled positions
+    P = np.sort(r.choice(np.arange(sink_end, r_end), 4096, replace=False))
+    i_o, n_o, w_o = ok.encode_keys(K[P], s, levels, sq_t)
+    ids = pkv.debug(0)[0].reshape(-1, 16)
+    rec = pkv.debug(1)[0].reshape(-1, 128)
+    assert np.array_equal(ids[P], i_o), "bucket ids differ"
+    assert np.array_equal(rec[P, :64], n_o), "nibbles differ"
+    w_g = rec[P, 64:].copy().view(np.float32).astype(np.float64)
+    assert np.all(np.abs(w_g - w_o) <= gc.W_RTOL * np.maximum(np.abs(w_o), 1e-30)), "w differ"
+    L, _ = ok.vote_table(Qg, s, p.rho, p.vote_weights)
+    assert np.array_equal(pkv.debug(2)[0].reshape(16, 256).astype(np.int64), L.astype(np.int64))
+    sc = pkv.debug(3)[0][:r_end - sink_end].astype(np.int64)
+    assert np.array_equal(sc[P - sink_end], np.minimum(ok.coarse_scores(i_o, L), 255))
+    # the candidate set over all positions, from the (sample-checked) scores
+    meta = pkv.debug(6)[0]
+    T, need, C = int(meta[0]), int(meta[1]), int(meta[2])
+    N_r = r_end - sink_end
+    assert C == ok.coarse_count(N_r, p.coarse_permille, p.top_k) and sc.max() < 255
+    above = np.flatnonzero(sc > T)
+    ties = np.flatnonzero(sc == T)
+    assert above.size < C <= above.size + ties.size and need == C - above.size
+    cand_want = np.sort(np.concatenate([above, ties[:need]])) + sink_end
+    cand = pkv.debug(4)[0][:C]
+    assert np.array_equal(cand, cand_want), "candidate set differs"
+    # estimates at sampled candidates
+    est = pkv.debug(5)[0][:C].astype(np.float64)
+    Ci = np.sort(r.choice(C, 4096, replace=False))
+    _, n_c, w_c = ok.encode_keys(K[cand[Ci]], s, levels, sq_t)
+    e_o = ok.rsq_ip(n_c, w_c, Qg, s, levels)
+    scale = gc.est_scale(n_c, w_c, Qg, s, levels)
+    assert np.all(np.abs(est[Ci] - e_o) <= gc.EST_RTOL * np.maximum(scale, 1e-30)), "estimates differ"
+    # the fine set from the (sample-checked) estimates
+    k_eff = min(p.top_k, C)
+    sel_g = sel.cpu().numpy().reshape(-1)[:k_eff]
+    assert int(sel_n.cpu().item()) == k_eff
+    assert np.array_equal(sel_g, np.sort(ok.top_by_key(est, cand, k_eff))), "fine set differs"
+    err = gc.check_attention(wl, pkv, [0], sel, sel_n, out)
+    gc.log(f"[max-capacity] ok: C={C}, T={T}, ties taken {need}, attention max-abs {err:.3g}")
+
+
 def test_fine_selection_30k_candidates():
     """200K tokens with a 15 % coarse budget: about 30000 candidates per unit, past
     what the fused selection holds, so the fine top-k keeps 32 candidates per
