@@ -145,6 +145,27 @@ def test_maximum_capacity_single_head():
     gc.log(f"[max-capacity] ok: C={C}, T={T}, ties taken {need}, attention max-abs {err:.3g}")
 
 
+def test_many_units():
+    """Batch 128 x 8 kv heads = 1024 units (the units are the grid's y
+    dimension of most kernels), short contexts; units spread over the batch
+    against the oracle, through the separate calls and one fused decode step."""
+    wl = W.gqa_bf16(N=2500, batch=128, top_k=64, n_local=128, buf_tokens=16)
+    pkv, sel, sel_n, out = _full_check(wl, units=[0, 517, 1023], capacity=2600, tag="1024-units")
+    dt = gc.torch_dtype(wl)
+    Kn, Vn, Qn = W.decode_stream(wl, 1)
+    out, sel, sel_n = pkv.decode_step(torch.from_numpy(Kn[0]).to(dt).cuda(),
+                                      torch.from_numpy(Vn[0]).to(dt).cuda(),
+                                      torch.from_numpy(Qn[0]).to(dt).cuda())
+    torch.cuda.synchronize()
+    Kall = np.concatenate([wl.K, np.moveaxis(Kn, 0, 2)], axis=2)
+    Vall = np.concatenate([wl.V, np.moveaxis(Vn, 0, 2)], axis=2)
+    full = W.Workload(wl.name, wl.batch, wl.n_kv, wl.group, wl.n_tokens + 1, wl.dtype, wl.params,
+                      wl.sign_bits, Kall, Vall, Qn[0])
+    enc = gc.check_encode(full, pkv, [3, 1000])
+    gc.check_retrieval(full, pkv, [3, 1000], sel, sel_n, enc)
+    gc.check_attention(full, pkv, [3, 1000], sel, sel_n, out)
+
+
 def test_fine_selection_30k_candidates():
     """200K tokens with a 15 % coarse budget: about 30000 candidates per unit, past
     what the fused selection holds, so the fine top-k keeps 32 candidates per
