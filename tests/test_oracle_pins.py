@@ -526,3 +526,22 @@ def test_mutation_m16_tree_dropping_a_term_is_caught():
         y[11] = 0.0
         return pk.centroid_scores(y)
     assert not check_m16_ids_and_top_rho(pk.bucket_ids, bad, pk.top_rho)
+
+
+@pytest.mark.parametrize("m", [4, 8, 16])
+def test_zero_query_subspace_picks_lowest_centroids(m):
+    """A rotated query subspace that is exactly zero ties all 2^m centroids, so
+    each head picks centroids 0..rho-1 there and the vote table holds G times
+    the rank weights on them (and nothing else in that subspace)."""
+    r = np.random.default_rng(31)
+    s = _signs(31)
+    Y = r.integers(-2, 3, size=(3, D)).astype(np.float64)
+    Y[:, 0:m] = 0.0                                        # subspace 0 of every head
+    Qg = (Y @ scipy.linalg.hadamard(D).T) * s / D          # rotates back to exactly Y
+    assert np.array_equal(pk.rotate_spec(Qg.astype(np.float32), s), Y.astype(np.float32))
+    w = (5, 3, 2, 1)
+    L, picks = pk.vote_table(Qg.astype(np.float32), s, 4, w, n_sub=D // m, m=m)
+    assert np.array_equal(picks[:, 0], np.tile(np.arange(4), (3, 1)))
+    want = np.zeros(1 << m, np.int64)
+    want[:4] = 3 * np.array(w)
+    assert np.array_equal(L[0].astype(np.int64), want)
