@@ -114,3 +114,39 @@ def test_attention_missing_scale_is_caught():
 def test_codebook_wrong_prior_is_caught():
     c, t = lloyd_max(6)                     # codebook of the wrong dimension
     assert not check_lloyd_max_conditions(c, t)
+
+
+def _w_alignment_variant(kind):
+    """calibrate_w with the alignment <v_b, u_b> used in another way than the
+    page's division: multiplied in, or the least-squares scale <v,u>/||v||^2."""
+    def bad(x, v, ss32, n_sub, m):
+        xb = np.asarray(x, np.float64).reshape(-1, n_sub, m)
+        norm = np.sqrt(np.sum(xb * xb, axis=-1))
+        u = xb / np.where(norm > 0, norm, 1.0)[..., None]
+        v = np.asarray(v, np.float64)
+        align = np.sum(v * u, axis=-1)
+        if kind == "multiply":
+            f = align
+        else:
+            f = align / np.sum(v * v, axis=-1)
+        return np.where(np.asarray(ss32) != 0, norm / math.sqrt(n_sub * m) * f, 0.0)
+    return bad
+
+
+def test_w_alignment_multiplied_is_caught():
+    for m in (8, 4, 16):
+        assert not pins.check_rsq_ip_parallel_query(_w_alignment_variant("multiply"),
+                                                    pk.rsq_ip_directions, 128 // m, m)
+
+
+def test_w_least_squares_is_caught():
+    for m in (8, 4, 16):
+        assert not pins.check_rsq_ip_parallel_query(_w_alignment_variant("least_squares"),
+                                                    pk.rsq_ip_directions, 128 // m, m)
+
+
+def test_w_least_squares_passes_the_identity_pin():
+    """Why the parallel-query pin is needed: with v = u both wrong forms equal
+    the page's w, so the identity-quantisation pin cannot tell them apart."""
+    assert pins.check_rsq_ip_identity(_w_alignment_variant("least_squares"), pk.rsq_ip_directions)
+    assert pins.check_rsq_ip_identity(_w_alignment_variant("multiply"), pk.rsq_ip_directions)

@@ -231,6 +231,48 @@ def test_rsq_ip_identity_quantisation():
     assert check_rsq_ip_identity(pk.calibrate_w, pk.rsq_ip_directions)
 
 
+def check_rsq_ip_parallel_query(calibrate_w, rsq_ip_directions, n_sub=16, m=8):
+    """Real 4-bit codes, queries parallel to the key's own subspace directions.
+
+    For a key with rotated subspaces x_b (x = sqrt(d) R k), u_b = x_b / ||x_b||
+    and v_b its dequantised code, take the query whose rotated subspaces are
+    alpha_b u_b (q = R^T y).  Then <k, q> = sum_b alpha_b ||x_b|| / sqrt(d), and
+    the estimator gives sum_b w_b alpha_b <v_b, u_b>: with the calibration of
+    the page ("Candidate reranking (RSQ-IP)", Calibration), w_b = ||(R k)_b|| /
+    <v_b, u_b>, the two agree exactly although v_b != u_b.  Any other use of the
+    alignment <v_b, u_b> (multiplying by it, or a least-squares scale
+    <v_b, u_b> / ||v_b||^2) misses by the codes' alignment loss (~0.3 % per
+    subspace), far outside the 1e-12 bar."""
+    levels, sq_t = spec_tables(m=m)
+    r = np.random.default_rng(31 + m)
+    s = _signs(32 + m)
+    R = pk.srht_matrix(s)
+    n = 48
+    K = r.standard_normal((n, D)) * r.lognormal(0, 0.5, D)
+    x = K @ R.T * math.sqrt(D)                      # exact sqrt(d) R k (float64)
+    nib, ss = pk.quantize_codes(x.astype(np.float32), sq_t, n_sub, m)
+    v = pk.dequantize(nib, levels)
+    assert np.all(ss != 0)
+    xb = x.reshape(n, n_sub, m)
+    u = xb / np.linalg.norm(xb, axis=-1, keepdims=True)
+    assert np.min(np.abs(np.sum(v * u, axis=-1) - 1.0)) > 1e-6   # the codes are not exact
+    w = calibrate_w(x, v, ss, n_sub, m)
+    ok = True
+    for i in range(n):
+        alpha = r.uniform(-2.0, 2.0, n_sub)
+        y = (alpha[:, None] * u[i]).reshape(D)
+        q = R.T @ y                                  # rotated query = y
+        est = rsq_ip_directions(v[i:i + 1], w[i:i + 1], q[None, :], s)[0]
+        ref = float(K[i] @ q)
+        ok &= abs(est - ref) <= 1e-12 * float(np.abs(K[i]) @ np.abs(q))
+    return ok
+
+
+@pytest.mark.parametrize("m", [8, 4, 16])
+def test_rsq_ip_exact_for_parallel_queries(m):
+    assert check_rsq_ip_parallel_query(pk.calibrate_w, pk.rsq_ip_directions, D // m, m)
+
+
 def test_rsq_ip_estimates_inner_products():
     """With the 4-bit codes the estimate tracks <k, q> closely (the per-coordinate
     Lloyd-Max error is under 1e-3); a statistical sanity bound, not a pin."""
