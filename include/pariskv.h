@@ -9,7 +9,8 @@
  * attention over sink + local + update buffer + the retrieved keys.
  *
  * Terms used below:
- *   d      head dimension (128)           B   subspaces (16 or 32) m  coordinates per subspace (8 or 4)
+ *   d      head dimension (128)           B   subspaces (16, 32 or 8)  m  coordinates per subspace
+ *                                                                        (8, 4 or 16; B * m = d)
  *   unit   one (batch, kv head) sequence  G   query heads per kv head (grouped-query attention)
  *   cap    capacity in tokens per unit    N   tokens currently held per unit
  *
@@ -71,14 +72,22 @@ typedef enum { PK_MEM_DEVICE = 0, PK_MEM_HOST_MAPPED = 1 } pk_mem;
 /* Method parameters.  ParisKV page: "Analytic centroids" (B, m), "Coarse
  * candidate generation" (rho, vote weights, candidate fraction), "Sliding-window
  * update mechanism" (zones).  Supported: head_dim 128 and (n_sub, sub_dim) =
- * (16, 8) or (32, 4); n_sub * sub_dim != head_dim is PK_ERR_INVALID, other
- * widths PK_ERR_UNSUPPORTED.  With m = 4 the 2^4 sign-pattern centroids of a
- * subspace give 4-bit ids, two per id byte, and G * max(weight) <= 127. */
+ * (16, 8), (32, 4) or (8, 16); n_sub * sub_dim != head_dim is PK_ERR_INVALID,
+ * other widths PK_ERR_UNSUPPORTED.  Every width keeps the 16 sign bytes of the
+ * rotated key as its bucket ids:
+ *   m = 8   one id per byte; the vote table has a 256-entry byte row per subspace;
+ *   m = 4   the 2^4 sign-pattern centroids give 4-bit ids, two per id byte, the
+ *           vote table's byte row i sums subspaces 2i and 2i + 1, and
+ *           G * max(weight) <= 127;
+ *   m = 16  the 16-bit id of subspace b is the little-endian word at bytes 2b,
+ *           2b + 1; of its 65536 centroids only the G * rho voted ones have a
+ *           vote, kept per subspace in a 256-slot hash table (see PK_DBG_LUT),
+ *           and G * max(weight) <= 255. */
 typedef struct {
     int32_t head_dim;          /* d = 128                                             */
-    int32_t n_sub;             /* B = 16 (or 32)                                      */
+    int32_t n_sub;             /* B = 16 (or 32, or 8)                                */
     int32_t sub_dim;           /* m = 8: 256 sign-pattern centroids per subspace;     */
-                               /* m = 4: 16 of them                                   */
+                               /* m = 4: 16 of them; m = 16: 65536                    */
     int32_t rho;               /* centroids picked per subspace and query head, 1..8  */
     uint8_t vote_weight[8];    /* vote of a rank-r pick (r = 0 is the best), 1..255   */
     int32_t coarse_permille;   /* candidates kept = max(top_k, ceil(p * N_r / 1000)), capped at N_r */
@@ -95,12 +104,12 @@ typedef struct pk_ctx pk_ctx;  /* opaque; owned by the library */
 
 /* Create a context over the caller's K/V store.
  * Owns: the per-key metadata (16 B of bucket ids and a record of codes and
- * scales per token: 64 B of 4-bit codes + 4 B per subspace, so 128 B for m = 8
- * and 192 B for m = 4), the window counters and all scratch.  The caller
+ * scales per token: 64 B of 4-bit codes + 4 B per subspace, so 128 B for m = 8,
+ * 192 B for m = 4 and 96 B for m = 16), the window counters and all scratch.  The caller
  * keeps ownership of k_store / v_store, which must outlive the context.
  * Requires batch * n_kv_heads <= 65535 (else PK_ERR_UNSUPPORTED) and
  * n_q_heads = G * n_kv_heads with G in {1, 2, 4, 8} (other G up to 16
- * are valid but PK_ERR_UNSUPPORTED), G * max(weight) <= 255 (m = 8; 127 for m = 4), buf_tokens <=
+ * are valid but PK_ERR_UNSUPPORTED), G * max(weight) <= 255 (m = 8, 16; 127 for m = 4), buf_tokens <=
  * n_local, capacity <= 2^24.  Allocates device memory and synchronises the device.
  * Errors: PK_ERR_INVALID, PK_ERR_UNSUPPORTED, PK_ERR_NO_DEVICE, PK_ERR_OOM. */
 pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int32_t n_q_heads,

@@ -277,7 +277,8 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
         PK_HIP(pk::launch_qprep(bf16, q, c->units, c->G, c->cfg.sign_bits, c->cfg.rho,
                                 c->cfg.vote_weight, c->cents, c->lut, c->ysum, c->cfg.sub_dim, k_new,
                                 v_new, c->K, c->V,
-                                row, c->cap, c->n - 1, c->ring, st));
+                                row, c->cap, c->n - 1, pk::ring_slot(c->ring, c->sink_end, c->n - 1),
+                                c->ring, st));
     }
     const int64_t n_r = c->r_end - c->sink_end;
     if (n_r <= 0) {
@@ -561,8 +562,8 @@ pk_status pk_append_decode_keys(pk_ctx* c, const void* k_new, const void* v_new,
     const int64_t row = (int64_t)pk::kD * dtype_size(c->dt);
     {
         StageTimer tm(c, PK_STAGE_APPEND, st);
-        PK_HIP(pk::launch_append(k_new, v_new, c->K, c->V, row, c->cap, c->n, c->units, c->ring,
-                                 st));
+        PK_HIP(pk::launch_append(k_new, v_new, c->K, c->V, row, c->cap, c->n,
+                                 pk::ring_slot(c->ring, c->sink_end, c->n), c->units, c->ring, st));
     }
     c->n += 1;
     c->buf += 1;

@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void ring_fill_kernel(const uint4* __restri
         const int64_t j = i % per_row, t = i / per_row;
         const int64_t u = t / hot, h = t - u * hot;
         const int64_t p = h < sink_end ? h : r_end + (h - sink_end);
-        const int64_t slot = p < n_sink ? p : n_sink + p % span;
+        const int64_t slot = p < sink_end ? p : n_sink + p % span;   // as ring_slot()
         const int64_t src = (u * cap + p) * per_row + j, dst = (u * ring_rows + slot) * per_row + j;
         rk[dst] = K[src];
         rv[dst] = V[src];
@@ -568,8 +568,8 @@ hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64
 hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64_t sign[2],
                         int rho, const uint8_t* weights, const float* cents, uint8_t* lut, float* ysum, int sub_dim,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
-                        int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st) {
-    const int64_t slot = new_pos < ring.n_sink ? new_pos : ring.n_sink + new_pos % ring.span;
+                        int64_t cap, int64_t new_pos, int64_t slot, const HotRing& ring,
+                        hipStream_t st) {
     VoteWeights w;
     for (int i = 0; i < kRhoMax; ++i) w.w[i] = (i < rho) ? weights[i] : 0u;
     const dim3 grid(sub_dim == 16 ? 8 : kSub, units), blk(64 * G);
@@ -594,11 +594,10 @@ hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64
 }
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
-                         int64_t row_bytes, int64_t cap, int64_t pos, int units,
+                         int64_t row_bytes, int64_t cap, int64_t pos, int64_t slot, int units,
                          const HotRing& ring, hipStream_t st) {
     const int64_t n = (int64_t)units * (row_bytes / 16);
     const int blocks = (int)((n + kBlock - 1) / kBlock);
-    const int64_t slot = pos < ring.n_sink ? pos : ring.n_sink + pos % ring.span;
     return launch(append_kernel, dim3(blocks), dim3(kBlock), 0, st, (const uint4*)k_new,
                   (const uint4*)v_new, (uint8_t*)K, (uint8_t*)V, row_bytes, cap, pos, units,
                   (uint4*)ring.k, (uint4*)ring.v, ring.rows, slot);

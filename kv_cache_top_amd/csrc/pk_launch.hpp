@@ -55,6 +55,15 @@ struct HotRing {
     int64_t n_sink = 0;
     int64_t span = 1;
 };
+// Ring row of position p given the window's sink end: the sink rows hold
+// positions [0, sink_end); every later position (local window, update buffer)
+// cycles through the span rows after the n_sink reserved ones.  A prefill
+// shorter than n_sink leaves sink_end < n_sink, and the tokens appended after
+// it are local tokens, read by the attention from the span rows.
+inline int64_t ring_slot(const HotRing& r, int64_t sink_end, int64_t p) {
+    return p < sink_end ? p : r.n_sink + p % r.span;
+}
+
 
 hipError_t launch_encode(bool bf16, const void* K, int64_t cap, int units, int64_t p0,
                          int64_t count, uint8_t* ids, uint8_t* rec, const uint64_t sign[2],
@@ -64,7 +73,8 @@ hipError_t launch_qprep(bool bf16, const void* q, int units, int G, const uint64
                         int rho, const uint8_t* weights, const float* cents, uint8_t* lut,
                         float* ysum, int sub_dim,
                         const void* k_new, const void* v_new, void* K, void* V, int64_t row_bytes,
-                        int64_t cap, int64_t new_pos, const HotRing& ring, hipStream_t st);
+                        int64_t cap, int64_t new_pos, int64_t ring_slot, const HotRing& ring,
+                        hipStream_t st);
 // learned-centroid comparison stage: fit (seed, then iters rounds of assign +
 // normalise) and bucket ids of keys [p0, p0 + count) under the fitted tables
 hipError_t launch_km_fit(bool bf16, const void* K, int64_t cap, int units, int64_t n_fit,
@@ -74,7 +84,7 @@ hipError_t launch_km_ids(bool bf16, const void* K, int64_t cap, int units, int64
                          int64_t count, const uint64_t sign[2], const float* cents, uint8_t* ids,
                          hipStream_t st);
 hipError_t launch_append(const void* k_new, const void* v_new, void* K, void* V,
-                         int64_t row_bytes, int64_t cap, int64_t pos, int units,
+                         int64_t row_bytes, int64_t cap, int64_t pos, int64_t ring_slot, int units,
                          const HotRing& ring, hipStream_t st);
 hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, hipStream_t st);
 hipError_t launch_gather_read(const void* src, int64_t n_rows, int rec_bytes, const int32_t* idx,

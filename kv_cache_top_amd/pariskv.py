@@ -111,6 +111,7 @@ class ParisKV:
             sel = torch.empty((self.batch, self.n_kv, self.cfg.top_k), dtype=torch.int32, device=q.device)
         if sel_n is None:
             sel_n = torch.empty((self.batch, self.n_kv), dtype=torch.int32, device=q.device)
+        self._check_sel(sel, sel_n)
         nat.check(nat.lib.pk_retrieve(self._ctx, _ptr(q), _ptr(sel), _ptr(sel_n), _stream(stream)),
                   "pk_retrieve")
         return sel, sel_n
@@ -118,12 +119,10 @@ class ParisKV:
     def sparse_attend(self, q: torch.Tensor, sel: torch.Tensor, sel_n: torch.Tensor,
                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         self._check_rows(q, (self.batch, self.n_q, 128))
-        if sel.dtype != torch.int32 or tuple(sel.shape) != (self.batch, self.n_kv, self.cfg.top_k):
-            raise ValueError("sel must be int32 [batch, n_kv, top_k]")
-        if sel_n.dtype != torch.int32 or tuple(sel_n.shape) != (self.batch, self.n_kv):
-            raise ValueError("sel_n must be int32 [batch, n_kv]")
+        self._check_sel(sel, sel_n)
         if out is None:
             out = torch.empty((self.batch, self.n_q, 128), dtype=torch.float32, device=q.device)
+        self._check_out(out)
         nat.check(nat.lib.pk_sparse_attend(self._ctx, _ptr(q), _ptr(sel), _ptr(sel_n), _ptr(out),
                                            _stream(stream)), "pk_sparse_attend")
         return out
@@ -135,6 +134,7 @@ class ParisKV:
         self._check_rows(q, (self.batch, self.n_q, 128))
         if out is None:
             out = torch.empty((self.batch, self.n_q, 128), dtype=torch.float32, device=q.device)
+        self._check_out(out)
         nat.check(nat.lib.pk_dense_attend(self._ctx, _ptr(q), _ptr(out), _stream(stream)),
                   "pk_dense_attend")
         return out
@@ -159,6 +159,8 @@ class ParisKV:
             sel_n = torch.empty((self.batch, self.n_kv), dtype=torch.int32, device=dev)
         if out is None:
             out = torch.empty((self.batch, self.n_q, 128), dtype=torch.float32, device=dev)
+        self._check_sel(sel, sel_n)
+        self._check_out(out)
         nat.check(nat.lib.pk_decode_step(self._ctx, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(sel),
                                          _ptr(sel_n), _ptr(out), _stream(stream)), "pk_decode_step")
         return out, sel, sel_n
@@ -201,6 +203,23 @@ class ParisKV:
         arr = buf.view(self._DBG_DTYPE[what])
         units = self.batch * self.n_kv
         return arr.reshape(units, -1)
+
+    def _check_sel(self, sel: torch.Tensor, sel_n: torch.Tensor):
+        """The kernels write top_k positions per unit into sel and a count per unit
+        into sel_n: both must be contiguous device int32 tensors of exactly that size."""
+        for t, shape, name in ((sel, (self.batch, self.n_kv, self.cfg.top_k), "sel"),
+                               (sel_n, (self.batch, self.n_kv), "sel_n")):
+            if (t.dtype != torch.int32 or tuple(t.shape) != shape or not t.is_contiguous()
+                    or t.device.type != "cuda"):
+                raise ValueError(f"{name} must be a contiguous cuda int32 tensor of shape {shape}, "
+                                 f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+
+    def _check_out(self, out: torch.Tensor):
+        shape = (self.batch, self.n_q, 128)
+        if (out.dtype != torch.float32 or tuple(out.shape) != shape or not out.is_contiguous()
+                or out.device.type != "cuda"):
+            raise ValueError(f"out must be a contiguous cuda float32 tensor of shape {shape}, "
+                             f"got {tuple(out.shape)} {out.dtype} on {out.device}")
 
     def _check_rows(self, t: torch.Tensor, shape):
         if tuple(t.shape) != shape or t.dtype != self.dtype or not t.is_contiguous():
