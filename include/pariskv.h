@@ -166,6 +166,23 @@ pk_status pk_sparse_attend(pk_ctx* ctx, const void* q, const int32_t* sel, const
  * (host-memory store), PK_ERR_OOM. */
 pk_status pk_dense_attend(pk_ctx* ctx, const void* q, float* out, void* stream);
 
+/* pk_dense_attend for callers that cannot allocate device memory during the
+ * call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): same arguments, layouts and results, but the split
+ * partials go to a scratch array the library keeps in device memory (one per
+ * GPU, pk_noalloc_scratch_bytes() = 64 MiB, held until the process ends;
+ * its device address is looked up by pk_create) instead of a buffer allocated
+ * on first use.  Calls no allocating routine.  All calls on one GPU share the
+ * array: calls that overlap on one GPU (other streams, other contexts, other
+ * host threads) race and must be ordered by the caller.  Each call rewrites
+ * every partial it reads, so nothing carries over from an earlier call.
+ * Errors: as pk_dense_attend, and PK_ERR_CAPACITY when the partials, batch *
+ * n_q_heads * ceil(n / 128) * 130 floats (n = tokens held), exceed the array. */
+pk_status pk_dense_attend_noalloc(pk_ctx* ctx, const void* q, float* out, void* stream);
+
+/* Size in bytes of the scratch array used by pk_dense_attend_noalloc. */
+size_t pk_noalloc_scratch_bytes(void);
+
 /* Comparison coarse stage: replaces the analytic sign-pattern centroids of
  * every unit and subspace by 256 centroids fitted with k-means to the rotated
  * keys of positions [0, n_tokens) of the store (the keys a model holds after

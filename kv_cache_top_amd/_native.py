@@ -54,6 +54,8 @@ SIGNATURES = {
     "pk_decode_step": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p]),
     "pk_dense_attend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "pk_dense_attend_noalloc": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "pk_noalloc_scratch_bytes": (_sz, []),
     "pk_fit_centroids": (_i32, [_c_void_p, _i64, _c_void_p, _i32, _c_void_p]),
     "pk_codebook": (_i32, [_i32, _i32, ctypes.POINTER(ctypes.c_float),
                            ctypes.POINTER(ctypes.c_float)]),

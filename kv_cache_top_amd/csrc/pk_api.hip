@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -23,6 +24,7 @@ struct pk_ctx {
     void* V = nullptr;
     pk_mem mem = PK_MEM_DEVICE;
     int device = 0;
+    float* scratch = nullptr;     // this device's address of the no-allocation scratch array
     CodeTables tab{};
     // window mirror (identical for every unit)
     bool prefilled = false;
@@ -61,6 +63,13 @@ struct pk_ctx {
     std::vector<hipEvent_t> event_pool;
 };
 
+// Scratch of pk_dense_attend_noalloc: the split partials of the dense
+// attention, in a file-scope device array instead of memory allocated per
+// call.  Every GPU the library runs on holds its own copy until the process
+// ends; calls on one GPU share it.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
 namespace pk {
 LaunchTiming& launch_timing() {
     static thread_local LaunchTiming t;
@@ -71,6 +80,26 @@ LaunchTiming& launch_timing() {
 namespace {
 
 bool g_verbose = std::getenv("PK_VERBOSE") != nullptr;
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (the host-side name of the array is not a device
+// address).  nullptr until looked up.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(int dev, float** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 // A failed runtime call also sets the calling thread's last-error state; it is
 // reported through the returned status and then cleared, so that the
@@ -86,9 +115,9 @@ pk_status alloc_fail() {
     return PK_ERR_OOM;
 }
 
-pk_status runtime_fail() {
+pk_status runtime_fail(pk_status s = PK_ERR_HIP) {
     (void)hipGetLastError();
-    return PK_ERR_HIP;
+    return s;
 }
 
 #define PK_HIP(call)                                      \
@@ -377,7 +406,12 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return PK_ERR_NO_DEVICE;
     // the kernels are built for gfx950 only: the current device must be able to load them
-    if (pk::probe_kernel_image() != hipSuccess) return PK_ERR_NO_DEVICE;
+    if (pk::probe_kernel_image() != hipSuccess) return runtime_fail(PK_ERR_NO_DEVICE);
+    float* scratch_ptr = nullptr;
+    {
+        const hipError_t e = scratch_address(dev, &scratch_ptr);
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    }
 
     pk_ctx* c = new (std::nothrow) pk_ctx();
     if (!c) return PK_ERR_OOM;
@@ -393,6 +427,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
     c->V = v_store;
     c->mem = store_mem;
     c->device = dev;
+    c->scratch = scratch_ptr;
     c->nbins = nbins;
     c->hstride = (nbins + 7) / 8 * 8;
     c->sstride = (capacity + 7) / 8 * 8;
@@ -609,6 +644,27 @@ pk_status pk_dense_attend(pk_ctx* c, const void* q, float* out, void* stream) {
     PK_HIP(pk::launch_combine(c->dense_part, c->units, c->G, (int)n_splits, out, st));
     return PK_OK;
 }
+
+pk_status pk_dense_attend_noalloc(pk_ctx* c, const void* q, float* out, void* stream) {
+    if (!c || !q || !out) return PK_ERR_INVALID;
+    if (!aligned16(q) || !aligned16(out)) return PK_ERR_INVALID;
+    if (!c->prefilled || c->n < 1) return PK_ERR_INVALID;
+    if (c->ring.k != nullptr) return PK_ERR_UNSUPPORTED;
+    const int64_t n_splits = ceil_div(c->n, pk::attend_split_keys());
+    if (n_splits > pk::attend_max_splits()) return PK_ERR_UNSUPPORTED;
+    const size_t need = (size_t)c->units * n_splits * c->G * (pk::kD + 2) * sizeof(float);
+    if (need > kNoAllocScratchBytes) return PK_ERR_CAPACITY;
+    // every (unit, split, head) partial the merge reads is written by the
+    // attention launch before it: nothing of the scratch has to start at zero
+    const hipStream_t st = (hipStream_t)stream;
+    PK_HIP(pk::launch_attend(c->dt == PK_BF16, c->G, c->K, c->V, c->cap, c->units, q, c->n, c->n,
+                             c->n, nullptr, nullptr, c->cfg.top_k, (int)n_splits, (int)n_splits,
+                             0, c->scratch, pk::HotRing{}, st));
+    PK_HIP(pk::launch_combine(c->scratch, c->units, c->G, (int)n_splits, out, st));
+    return PK_OK;
+}
+
+size_t pk_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 pk_status pk_decode_step(pk_ctx* c, const void* k_new, const void* v_new, const void* q,
                          int32_t* sel, int32_t* sel_n, float* out, void* stream) {

@@ -148,3 +148,10 @@ def test_no_device_is_reported_without_a_gpu():
     assert st == nat.PK_ERR_NO_DEVICE and not ctx.value   # a valid m = 4 configuration
     st, ctx = _create(nat.make_config(n_sub=8, sub_dim=16, vote_weights=(63, 1, 1, 1)))
     assert st == nat.PK_ERR_NO_DEVICE and not ctx.value   # a valid m = 16 configuration
+
+
+def test_noalloc_entry_point_validates_without_a_device():
+    """pk_dense_attend_noalloc refuses a null context before any device work, and
+    reports the size of its scratch array."""
+    assert nat.lib.pk_noalloc_scratch_bytes() == 64 << 20
+    assert nat.lib.pk_dense_attend_noalloc(None, None, None, None) == nat.PK_ERR_INVALID
