@@ -68,6 +68,11 @@ constexpr int kMaxBins = 4096;   // coarse-score histogram bins (B * G * max wei
 constexpr int kMaxChunks = 2048; // scan chunks per unit
 constexpr int kBlock = 256;      // threads per block of the streaming kernels
 
+// Histogram bins per lane of the scan's suffix-count wave: the nbins bins
+// spread over 64 lanes in runs of a multiple of 4 (16-byte LDS reads, 8-byte
+// stores).  The scan's LDS histogram holds 64 * this many entries.
+__host__ __device__ constexpr int scan_bins_per_lane(int nbins) { return 4 * ((nbins + 255) / 256); }
+
 struct CodeTables {
     float sq_thr[7];   // fp32(t_l^2), ascending
     float levels[8];   // fp32 Lloyd-Max levels

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     constexpr int kLutParts = lut_bytes<M>() / (16 * kBlock);   // 16-byte pieces per thread
     __shared__ uint32_t s_lut[lut_bytes<M>() / 4];
-    extern __shared__ uint32_t s_hist[];  // nbins entries (sized at launch)
+    extern __shared__ uint32_t s_hist[];  // scan_hist_slots(nbins) entries (sized at launch)
     const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_lut);
 
     // The vote table is requested first and the key id rows right after, all
@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     }
 #pragma unroll
     for (int i = 0; i < kLutParts; ++i) reinterpret_cast<uint4*>(s_lut)[tid + i * kBlock] = lut_part[i];
-    for (int b = tid; b < nbins; b += kBlock) s_hist[b] = 0;
+    const int per = scan_bins_per_lane(nbins);
+    for (int b = tid; b < 64 * per; b += kBlock) s_hist[b] = 0;
     lds_sync();
 
     // histogram: scores 0..7, which most keys have, go to eight byte counters
@@ -133,8 +134,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     // waves 1..: add the chunk's counts to the unit's score histogram (zeroed
     // by the query preparation of this step).  wave 0: the chunk's suffix
     // counts sfx[b] = #{keys with score >= b} (a chunk holds at most 8192
-    // keys: uint16); lane l sums the bins ranked l*per .. l*per+per-1 in
-    // descending score order.
+    // keys: uint16).  Lane l owns the `per` consecutive bins [l*per,
+    // l*per + per) (per a multiple of 4): one wave scan of the lane totals
+    // gives the count above each lane's range, and each lane stores its
+    // entries as 8-byte pieces, adjacent lanes at adjacent addresses.
     const int wave = tid >> 6;
     if (wave > 0) {
         // two bins per 64-bit atomic (a count stays below 2^24: no carry
@@ -146,20 +149,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
             if (h != 0u) __hip_atomic_fetch_add(ut + i, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     } else {
-        const int lane = tid, per = (nbins + 63) / 64;
-        uint32_t seg = 0;
-        for (int j = 0; j < per; ++j) {
-            const int r = lane * per + j;
-            if (r < nbins) seg += s_hist[nbins - 1 - r];
+        const int lane = tid;
+        const uint4* mine = reinterpret_cast<const uint4*>(s_hist + lane * per);
+        uint32_t tl = 0;
+        for (int i = 0; i < per / 4; ++i) {
+            const uint4 h4 = mine[i];
+            tl += (h4.x + h4.y) + (h4.z + h4.w);
         }
-        uint32_t run = wave_incl_scan(seg) - seg;
-        uint16_t* myh = hist + ((int64_t)u * max_chunks + ch) * hstride;
-        for (int j = 0; j < per; ++j) {
-            const int r = lane * per + j;
-            if (r < nbins) {
-                run += s_hist[nbins - 1 - r];
-                myh[nbins - 1 - r] = (uint16_t)run;
-            }
+        const uint32_t incl = wave_incl_scan(tl);
+        // keys scoring above this lane's bins: the totals of the higher lanes
+        uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
+        uint2* myh = reinterpret_cast<uint2*>(hist + ((int64_t)u * max_chunks + ch) * hstride);
+        for (int i = per / 4 - 1; i >= 0; --i) {
+            const uint4 h4 = mine[i];
+            const uint32_t s3 = run + h4.w, s2 = s3 + h4.z, s1 = s2 + h4.y, s0 = s1 + h4.x;
+            run = s0;
+            // rows hold hstride entries (a multiple of 8): a piece is wholly inside or outside
+            if (lane * per + 4 * i < hstride)
+                myh[(lane * per) / 4 + i] = make_uint2(s0 | (s1 << 16), s2 | (s3 << 16));
         }
     }
 }
@@ -642,7 +649,7 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
     const dim3 grid(n_chunks, units), blk(kBlock);
     // the histogram is the only dynamic LDS: small vote tables keep the
     // block small enough for eight resident blocks per CU
-    const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
+    const size_t hist_bytes = (size_t)64 * scan_bins_per_lane(nbins) * sizeof(uint32_t);
 #define PK_SCAN(K)                                                                              \
     return sub_dim == 16                                                                          \
                ? launch(scan_kernel<K, 16>, grid, blk, hist_bytes, st, ids, cap, sink_end, n_r,   \
