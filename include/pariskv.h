@@ -33,14 +33,17 @@
  * the calling thread's HIP last-error state before returning, so the caller's
  * own later error checks do not see it.
  *
- * HIP graph capture: each call takes its launch decisions on the host from
- * host-side state (the window, and for pk_retrieve / pk_decode_step which of
- * two device tables the coarse-score histogram is accumulated into; the calls
- * alternate between them).  A captured call replays the decisions it was
- * captured with, so a graph holding one pk_retrieve gives wrong coarse counts
- * from its second replay on.  The calls are meant to be issued eagerly: they
- * allocate nothing and never synchronise.  A context is not thread-safe; calls on one context must be
- * issued from one host thread in order.
+ * HIP graph capture: each call takes its launch decisions (grid sizes, window
+ * bounds, the candidate count) on the host from the context's window, and a
+ * captured call replays the decisions it was captured with.  Device state
+ * carried between calls (the coarse-score histogram) is returned to zero by
+ * the call that consumes it, so pk_retrieve and pk_sparse_attend on a static
+ * context (no appends: the window does not move) can be captured once and
+ * replayed with new query contents.  Calls that move the window
+ * (pk_append_decode_keys, pk_decode_step) must be issued eagerly, one per
+ * token.  The decode-path calls allocate nothing and never synchronise.  A
+ * context is not thread-safe; calls on one context must be issued from one
+ * host thread in order.
  */
 #ifndef PARISKV_H
 #define PARISKV_H

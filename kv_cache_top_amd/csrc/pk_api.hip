@@ -39,10 +39,9 @@ struct pk_ctx {
     float* ysum = nullptr;        // [units][128]       sum of rotated queries
     uint8_t* scores = nullptr;    // [units][sstride] + pad   min(coarse score, 255) (retrieval offset)
     uint16_t* hist = nullptr;     // [units][max_chunks][hstride] per-chunk #{score >= s}
-    uint32_t* tot = nullptr;      // [2][units][nbins rounded up to even]  unit score histograms:
-                                  // the scan adds into tables[tot_cur], the rerank reads it
-                                  // and zeroes the other one for the next step
-    int tot_cur = 0;
+    uint32_t* tot = nullptr;      // [units][nbins rounded up to even]  unit score histograms:
+                                  // the scan adds into it, the rerank reads it, and the
+                                  // fine selection zeroes it for the next step
     int32_t* meta = nullptr;      // [units][4]          {T, ties taken, C, k_eff}
     int32_t* cand_pos = nullptr;  // [units][cmax]
     float* cand_est = nullptr;    // [units][cmax]
@@ -317,21 +316,18 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
     const int64_t C = coarse_count(n_r, c->cfg.coarse_permille, c->cfg.top_k);
     const int chunk = choose_chunk(c->units, n_r);
     const int n_chunks = (int)ceil_div(n_r, chunk);
-    const int64_t tstride = (c->nbins + 1) & ~1;
-    uint32_t* tot_now = c->tot + (int64_t)c->tot_cur * c->units * tstride;
-    uint32_t* tot_next = c->tot + (int64_t)(1 - c->tot_cur) * c->units * tstride;
-    c->tot_cur = 1 - c->tot_cur;
+    const int tstride = (c->nbins + 1) & ~1;
     {
         StageTimer tm(c, PK_STAGE_SCAN, st);
         PK_HIP(pk::launch_scan(c->ids, c->cap, c->units, c->sink_end, n_r, chunk, n_chunks,
                                c->max_chunks, c->lut, c->scores, c->sstride, c->hist, c->hstride,
-                               tot_now, c->nbins, c->cfg.sub_dim, st));
+                               c->tot, c->nbins, c->cfg.sub_dim, st));
     }
     {
         StageTimer tm(c, PK_STAGE_RERANK, st);
         PK_HIP(pk::launch_rerank(chunk, c->scores, c->sstride, c->rec, c->ids, c->lut, c->cap,
                                  c->units, c->sink_end, n_r, n_chunks, c->max_chunks, c->hist,
-                                 c->hstride, tot_now, tot_next, c->nbins, C, c->cfg.top_k,
+                                 c->hstride, c->tot, c->nbins, C, c->cfg.top_k,
                                  c->ysum, c->tab, c->cand_pos, c->cand_est, c->cmax, c->meta,
                                  st));
     }
@@ -342,12 +338,13 @@ pk_status run_retrieve(pk_ctx* c, const void* q, int32_t* sel, int32_t* sel_n, c
         pk::fine_hot_supported(bf16, c->G, c->ring.k != nullptr, (int)C, c->cmax)) {
         PK_HIP(pk::launch_fine_hot(c->cand_pos, c->cand_est, c->cmax, c->units, (int)C,
                                    c->cfg.top_k, sel, sel_n, c->G, c->K, c->V, c->cap, q,
-                                   c->sink_end, c->r_end, c->n, n_splits, n_hs, c->part, st));
+                                   c->sink_end, c->r_end, c->n, n_splits, n_hs, c->part, c->tot,
+                                   tstride, st));
         if (hot_done) *hot_done = true;
         return PK_OK;
     }
     PK_HIP(pk::launch_fine(c->cand_pos, c->cand_est, c->cmax, c->units, (int)C, c->cfg.top_k, sel,
-                           sel_n, st));
+                           sel_n, c->tot, tstride, st));
     return PK_OK;
 }
 
@@ -456,7 +453,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         // score rows padded to 16 B; the tail pad covers vector reads past the last row
         {(void**)&c->scores, (size_t)(U * c->sstride + 8192)},   // last chunk read whole
         {(void**)&c->hist, (size_t)(U * c->max_chunks * (int64_t)c->hstride * 2)},
-        {(void**)&c->tot, (size_t)(2 * U * ((c->nbins + 1) & ~1) * 4)},
+        {(void**)&c->tot, (size_t)(U * ((c->nbins + 1) & ~1) * 4)},
         {(void**)&c->meta, (size_t)(U * 4 * 4)},
         {(void**)&c->cand_pos, (size_t)(U * c->cmax * 4)},
         {(void**)&c->cand_est, (size_t)(U * c->cmax * 4)},
@@ -481,7 +478,7 @@ pk_status pk_create(const pk_config* cfg, int32_t batch, int32_t n_kv_heads, int
         }
     }
     if (hipMemset(c->meta, 0, U * 16) != hipSuccess ||
-        hipMemset(c->tot, 0, 2 * U * ((c->nbins + 1) & ~1) * 4) != hipSuccess ||
+        hipMemset(c->tot, 0, U * ((c->nbins + 1) & ~1) * 4) != hipSuccess ||
         hipMemset(c->scores, 0, U * c->sstride + 8192) != hipSuccess ||
         hipMemset(c->lut, 0, (size_t)U * lut_bytes(cfg->sub_dim)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {

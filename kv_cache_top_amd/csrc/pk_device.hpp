@@ -67,6 +67,10 @@ constexpr int kRhoMax = 8;
 constexpr int kMaxBins = 4096;   // coarse-score histogram bins (B * G * max weight + 1)
 constexpr int kMaxChunks = 2048; // scan chunks per unit
 constexpr int kBlock = 256;      // threads per block of the streaming kernels
+// Fourth word of a raw (untyped, stride 0) buffer resource descriptor on the
+// gfx9 family: 32-bit data format, offsets checked against the record count
+// (loads past it return zero).
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // Histogram bins per lane of the scan's suffix-count wave: the nbins bins
 // spread over 64 lanes in runs of a multiple of 4 (16-byte LDS reads, 8-byte

@@ -167,6 +167,15 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
     kth = prefix;
 }
 
+// The unit's coarse-score histogram row (tstride words) is read by every
+// rerank block of a step; the fine selection, which runs after all of them,
+// zeroes it for the next step's scan (no host-chosen table, so a captured
+// retrieval replays correctly).  Called after the block's last load.
+__device__ __forceinline__ void clear_unit_hist(uint32_t* tot, int tstride, int u) {
+    if (tot == nullptr) return;
+    for (int i = threadIdx.x; i < tstride; i += blockDim.x) tot[(int64_t)u * tstride + i] = 0u;
+}
+
 // candidates held in registers: C <= SEG * kFBlock, SEG in {4, 8, 16, 32, 64}
 // (C < 65536); the candidate rows hold a multiple of SEG entries, so the
 // 16-byte vector loads of a segment that starts below C stay inside the row
@@ -174,7 +183,8 @@ template <int SEG>
 __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_pos,
                                               const float* __restrict__ cand_est, int64_t cmax,
                                               int C, int top_k, int32_t* __restrict__ sel,
-                                              int32_t* __restrict__ sel_n, int u, FineShared& sh) {
+                                              int32_t* __restrict__ sel_n, int u, FineShared& sh,
+                                              uint32_t* unit_hist, int tstride) {
     const int tid = threadIdx.x;
     const int k_eff = C < top_k ? C : top_k;
     const int b0 = tid * SEG;
@@ -263,6 +273,7 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
         }
         o += in ? 1u : 0u;
     }
+    clear_unit_hist(unit_hist, tstride, u);
     if (tid == 0) sel_n[u] = k_eff;
 }
 

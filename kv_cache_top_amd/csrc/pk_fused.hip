@@ -23,13 +23,14 @@ __global__ __launch_bounds__(kFBlock) void fine_hot_kernel(const int32_t* __rest
                                                            int64_t cmax, int C, int top_k,
                                                            int32_t* __restrict__ sel,
                                                            int32_t* __restrict__ sel_n, int units,
+                                                           uint32_t* __restrict__ tot, int tstride,
                                                            AttendArgs<uint16_t> a) {
     constexpr size_t kFineBytes = sizeof(FineShared);
     constexpr size_t kAttBytes = sizeof(AttendLds<G>);
     __shared__ __align__(16) unsigned char s_raw[kFineBytes > kAttBytes ? kFineBytes : kAttBytes];
     if ((int)blockIdx.x < units) {
         fine_reg_body<SEG>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n, blockIdx.x,
-                           *reinterpret_cast<FineShared*>(s_raw));
+                           *reinterpret_cast<FineShared*>(s_raw), tot, tstride);
         return;
     }
     // hot split gs = unit * n_hot_splits + split
@@ -51,7 +52,8 @@ hipError_t launch_fine_hot(const int32_t* cand_pos, const float* cand_est, int64
                            int units, int C, int top_k, int32_t* sel, int32_t* sel_n, int G,
                            const void* K, const void* V, int64_t cap, const void* q,
                            int64_t sink_end, int64_t r_end, int64_t n_tok, int n_splits,
-                           int n_hot_splits, float* part, hipStream_t st) {
+                           int n_hot_splits, float* part, uint32_t* tot, int tstride,
+                           hipStream_t st) {
     if (!fine_hot_supported(true, G, false, C, cmax) || n_hot_splits < 1 ||
         n_hot_splits > n_splits || n_splits > kMaxSplits)
         return hipErrorInvalidValue;
@@ -62,7 +64,7 @@ hipError_t launch_fine_hot(const int32_t* cand_pos, const float* cand_est, int64
     const int seg = C <= 4 * kFBlock ? 4 : (C <= 8 * kFBlock ? 8 : 16);
 #define PK_FH(S, GG)                                                                          \
     return launch(fine_hot_kernel<S, GG>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, \
-                  sel, sel_n, units, a)
+                  sel, sel_n, units, tot, tstride, a)
 #define PK_FH_G(S)                      \
     switch (G) {                        \
         case 1: PK_FH(S, 1);            \

@@ -101,17 +101,19 @@ hipError_t launch_scan(const uint8_t* ids, int64_t cap, int units, int64_t sink_
                        uint32_t* tot, int nbins, int sub_dim, hipStream_t st);
 // coarse threshold and candidates (meta = {T, ties taken, C, k_eff} per unit),
 // then the RSQ-IP estimates of the candidates; ids and lut rescore the keys
-// whose stored score saturated when the threshold reaches 255; tot_clear (the
-// other histogram table) is zeroed for the next step
+// whose stored score saturated when the threshold reaches 255
 hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, const uint8_t* rec,
                          const uint8_t* ids, const uint8_t* lut,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
                          int max_chunks, const uint16_t* hist, int hstride, const uint32_t* tot,
-                         uint32_t* tot_clear, int nbins, int64_t C, int top_k, const float* ysum,
+                         int nbins, int64_t C, int top_k, const float* ysum,
                          const CodeTables& tab, int32_t* cand_pos, float* cand_est, int64_t cmax,
                          int32_t* meta, hipStream_t st);
+// fine top-k; also zeroes the units' coarse-score histogram rows tot[units][tstride]
+// (null: none) for the next step's scan
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
-                       int C, int top_k, int32_t* sel, int32_t* sel_n, hipStream_t st);
+                       int C, int top_k, int32_t* sel, int32_t* sel_n, uint32_t* tot, int tstride,
+                       hipStream_t st);
 hipError_t launch_empty_select(int units, int32_t* sel_n, int32_t* meta, hipStream_t st);
 // hipSuccess when the current device can run this library's code object
 hipError_t probe_kernel_image();
@@ -131,7 +133,8 @@ hipError_t launch_fine_hot(const int32_t* cand_pos, const float* cand_est, int64
                            int units, int C, int top_k, int32_t* sel, int32_t* sel_n, int G,
                            const void* K, const void* V, int64_t cap, const void* q,
                            int64_t sink_end, int64_t r_end, int64_t n_tok, int n_splits,
-                           int n_hot_splits, float* part, hipStream_t st);
+                           int n_hot_splits, float* part, uint32_t* tot, int tstride,
+                           hipStream_t st);
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st);
 

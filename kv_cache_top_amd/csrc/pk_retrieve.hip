@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     const uint8_t* __restrict__ scores, int64_t sstride, const uint8_t* __restrict__ rec,
     const uint8_t* __restrict__ ids, const uint8_t* __restrict__ lut,
     int64_t cap, int64_t sink_end, int64_t n_r, int max_chunks, const uint16_t* __restrict__ hist,
-    int hstride, const uint32_t* __restrict__ tot, uint32_t* __restrict__ tot_clear, int nbins,
+    int hstride, const uint32_t* __restrict__ tot, int nbins,
     int64_t C, int top_k,
     const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
     float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
@@ -413,9 +413,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     using WT = typename std::conditional<M == 4, float2, float>::type;   // a lane's w
     const float inv_sqrt_d = 0.08838834764831845f;
     const int grp = tid >> 4;
-    const uint8_t* urec = rec + (int64_t)u * cap * kRecB;
+    // the unit's records through a buffer descriptor: 32-bit offsets (a unit
+    // holds at most 2^24 records of <= 192 B), half the address registers of
+    // 64-bit pointers for the batch in flight
+    const __amdgpu_buffer_rsrc_t urec = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(rec + (int64_t)u * cap * kRecB), (short)0,
+        (int)(uint32_t)((uint64_t)cap * kRecB), kBufferRsrcWord3);
     int32_t* upos = cand_pos + (int64_t)u * cmax;
     float* uest = cand_est + (int64_t)u * cmax;
+    const uint32_t w_off = 64u + (M == 4 ? 8u * (uint32_t)l16 : 4u * (uint32_t)(M == 16 ? (l16 >> 1) : l16));
     for (int i0 = grp; i0 < (int)n_mem; i0 += kBatch * (kBlock / 16)) {
         uint32_t nib[kBatch];
         WT w[kBatch];
@@ -424,8 +430,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
             const int i = i0 + k * (kBlock / 16);
             const int32_t p = s_list[i < (int)n_mem ? i : i0];
             const uint32_t ro = (uint32_t)p * kRecB;
-            nib[k] = *reinterpret_cast<const uint32_t*>(urec + ro + 4u * (uint32_t)l16);
-            w[k] = reinterpret_cast<const WT*>(urec + ro + 64u)[M == 16 ? (l16 >> 1) : l16];
+            nib[k] = __builtin_amdgcn_raw_buffer_load_b32(urec, ro + 4u * (uint32_t)l16, 0, 0);
+            if constexpr (M == 4) {
+                const uint32_t a = __builtin_amdgcn_raw_buffer_load_b32(urec, ro + w_off, 0, 0);
+                const uint32_t b = __builtin_amdgcn_raw_buffer_load_b32(urec, ro + w_off + 4u, 0, 0);
+                w[k] = make_float2(__uint_as_float(a), __uint_as_float(b));
+            } else {
+                w[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(urec, ro + w_off, 0, 0));
+            }
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
@@ -460,10 +472,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         }
     }
     // (stored last: a store ahead of a load's wait would be waited for too)
-    if (ch == 0) {
-        const int tstride = (nbins + 1) & ~1;
-        for (int i = tid; i < tstride; i += kBlock) tot_clear[(int64_t)u * tstride + i] = 0u;
-    }
     if (ch == 0 && tid == 0) {
         meta[u * 4 + 0] = T;
         meta[u * 4 + 1] = (int32_t)need;
@@ -477,9 +485,12 @@ __global__ __launch_bounds__(kFBlock) void fine_reg_kernel(const int32_t* __rest
                                                            const float* __restrict__ cand_est,
                                                            int64_t cmax, int C, int top_k,
                                                            int32_t* __restrict__ sel,
-                                                           int32_t* __restrict__ sel_n) {
+                                                           int32_t* __restrict__ sel_n,
+                                                           uint32_t* __restrict__ tot,
+                                                           int tstride) {
     __shared__ FineShared sh;
-    fine_reg_body<SEG>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n, blockIdx.x, sh);
+    fine_reg_body<SEG>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n, blockIdx.x, sh, tot,
+                       tstride);
 }
 
 // more candidates than registers hold: the threshold passes stream the
@@ -494,7 +505,9 @@ __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __rest
                                                            const float* __restrict__ cand_est,
                                                            int64_t cmax, int C, int top_k,
                                                            int32_t* __restrict__ sel,
-                                                           int32_t* __restrict__ sel_n) {
+                                                           int32_t* __restrict__ sel_n,
+                                                           uint32_t* __restrict__ tot,
+                                                           int tstride) {
     const int u = blockIdx.x, tid = threadIdx.x;
     __shared__ FineShared sh;
     __shared__ __align__(16) uint32_t s_tile[kMemTile];
@@ -620,6 +633,7 @@ __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __rest
     }
     if (k_eff <= kMemOut)
         for (int i = tid; i < k_eff; i += kFBlock) usel[i] = s_out[i];
+    clear_unit_hist(tot, tstride, u);
     if (tid == 0) sel_n[u] = k_eff;
 }
 
@@ -672,7 +686,7 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
                          const uint8_t* ids, const uint8_t* lut,
                          int64_t cap, int units, int64_t sink_end, int64_t n_r, int n_chunks,
                          int max_chunks, const uint16_t* hist, int hstride, const uint32_t* tot,
-                         uint32_t* tot_clear, int nbins, int64_t C, int top_k, const float* ysum,
+                         int nbins, int64_t C, int top_k, const float* ysum,
                          const CodeTables& tab, int32_t* cand_pos, float* cand_est, int64_t cmax,
                          int32_t* meta, hipStream_t st) {
     if (nbins < 1 || nbins > kMaxBins || hstride < nbins || n_chunks > max_chunks || C < 1 ||
@@ -683,7 +697,7 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
     if (tab.sub_dim != 8 && tab.sub_dim != 4 && tab.sub_dim != 16) return hipErrorInvalidValue;
 #define PK_RERANK_M(K, MM)                                                                         \
     launch(rerank_kernel<K, MM>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, lut, cap,   \
-           sink_end, n_r, max_chunks, hist, hstride, tot, tot_clear, nbins, C, top_k, ysum, tab,   \
+           sink_end, n_r, max_chunks, hist, hstride, tot, nbins, C, top_k, ysum, tab,              \
            cand_pos, cand_est, cmax, meta)
 #define PK_RERANK(K)                                                                               \
     return tab.sub_dim == 8 ? PK_RERANK_M(K, 8)                                                    \
@@ -702,7 +716,8 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
 }
 
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
-                       int C, int top_k, int32_t* sel, int32_t* sel_n, hipStream_t st) {
+                       int C, int top_k, int32_t* sel, int32_t* sel_n, uint32_t* tot, int tstride,
+                       hipStream_t st) {
     // registers hold up to 32 candidates per thread (SEG of them in rows padded
     // to a multiple of SEG); beyond that the passes stream from memory
     if (C < 1 || C > cmax) return hipErrorInvalidValue;
@@ -710,14 +725,14 @@ hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t c
 #define PK_FREG(S)                                                                              \
     if (C <= S * kFBlock && C < 65536 && cmax % S == 0)                                         \
     return launch(fine_reg_kernel<S>, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel, \
-                  sel_n)
+                  sel_n, tot, tstride)
     PK_FREG(4);
     PK_FREG(8);
     PK_FREG(16);
     PK_FREG(32);
 #undef PK_FREG
     return launch(fine_mem_kernel, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
-                  sel_n);
+                  sel_n, tot, tstride);
 }
 
 hipError_t launch_empty_select(int units, int32_t* sel_n, int32_t* meta, hipStream_t st) {

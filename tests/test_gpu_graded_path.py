@@ -9,6 +9,7 @@ window edges the other tests do not reach.
 * Empty sink and/or local zones (no always-attended rows at all).
 * A pinned host-memory store whose prefill is shorter than the sink zone
   (the appended tokens are local tokens, kept in the device ring).
+* A static retrieval + attention captured in a HIP graph and replayed.
 
 Bars as in test_gpu_parity.py (ParisKV page, "Two-stage GPU-native retrieval
 pipeline", "Sliding-window update mechanism", "UVA offloading").
@@ -141,8 +142,8 @@ def test_prefill_shorter_than_sink(host_mapped):
     """A 2-token prefill with n_sink = 4: the sink zone holds 2 tokens and every
     appended token is local (with a host-memory store, kept in the device ring's
     local rows).  Decode steps until the local window overflows into the
-    retrieval zone; every step's attention against the oracle, and the host
-    store's outputs bit-identical to the device store's."""
+    retrieval zone; every step's attention against the oracle, for a device
+    store and for a host-memory store."""
     T = 44
     wl = W.gqa_bf16(N=2, top_k=8, permille=500, n_sink=4, n_local=16, buf_tokens=8)
     Kn, Vn, Qn = W.decode_stream(wl, T)
@@ -190,3 +191,59 @@ def test_binding_rejects_bad_output_buffers():
     out, sel, sel_n = pkv.decode_step(kn, kn, q, sel=good_sel, sel_n=good_n)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+def test_graph_replay_of_static_retrieval():
+    """pk_retrieve + pk_sparse_attend on a static context captured into a HIP
+    graph: every replay, with new queries copied into the captured query buffer
+    between replays and eager library calls on the same context in between,
+    gives the eager calls' selection and output bit for bit (the coarse-score
+    histogram is a single device table the fine selection zeroes, so nothing
+    host-chosen changes between steps).  One replay is also checked against the
+    oracle."""
+    wl = W.gqa_bf16(N=20011, batch=2, top_k=512)
+    pkv = gc.make_ctx(wl)
+    pkv.encode_keys(wl.n_tokens)
+    pool_np = W.query_pool(wl, 4)
+    pool = torch.from_numpy(pool_np).to(torch.bfloat16).cuda()
+    q = torch.empty_like(pool[0])
+    shp_sel = (wl.batch, wl.n_kv, wl.params.top_k)
+    sel = torch.empty(shp_sel, dtype=torch.int32, device="cuda")
+    sel_n = torch.empty(shp_sel[:2], dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.batch, wl.n_kv * wl.group, 128), dtype=torch.float32, device="cuda")
+    refs = []
+    for i in range(4):
+        q.copy_(pool[i])
+        pkv.retrieve(q, sel, sel_n)
+        pkv.sparse_attend(q, sel, sel_n, out)
+        torch.cuda.synchronize()
+        refs.append((sel.clone(), sel_n.clone(), out.clone()))
+    sel_g, n_g, out_g = torch.empty_like(sel), torch.empty_like(sel_n), torch.empty_like(out)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pkv.retrieve(q, sel_g, n_g, stream=side)
+        pkv.sparse_attend(q, sel_g, n_g, out_g, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        pkv.retrieve(q, sel_g, n_g, stream=st)
+        pkv.sparse_attend(q, sel_g, n_g, out_g, stream=st)
+    for rep in range(3):
+        for i in range(4):
+            q.copy_(pool[i])
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(sel_g, refs[i][0]) and torch.equal(n_g, refs[i][1]), (rep, i)
+            assert torch.equal(out_g, refs[i][2]), (rep, i)
+            pkv.retrieve(q, sel, sel_n)          # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(sel, refs[i][0])
+    wl.Q = pool_np[3]
+    units = [0, 11]
+    enc = gc.check_encode(wl, pkv, units)
+    gc.check_retrieval(wl, pkv, units, sel_g, n_g, enc)
+    gc.check_attention(wl, pkv, units, sel_g, n_g, out_g)
+    del g
