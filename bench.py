@@ -51,6 +51,8 @@ def parse():
                          "the last-level cache), reported beside the graded cycled figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=4)
+    ap.add_argument("--no-sub-configs", action="store_true",
+                    help="default run only: skip the compact 1M host-store and drift records")
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -192,6 +194,10 @@ def stage_times(ctx_list, steps_fn, n_steps, torch, nat):
 
 
 def run_config4(args):
+    print(json.dumps(config4_record(args, args.steps, args.warmup)), flush=True)
+
+
+def config4_record(args, n_steps, n_warmup):
     """1M-token context, batch 1 x 8 kv heads (G = 4), bf16, the K/V store in pinned host
     memory: ids and records in HBM, sink/local/buffer rows in a device ring, the
     retrieved rows read by the attention kernel over the host link."""
@@ -205,7 +211,7 @@ def run_config4(args):
                     name="gqa_1m_b1_host_store_bf16")
     p = wl.params
     dt = torch.bfloat16
-    ctx = ParisKV(batch=1, n_kv=8, n_q=32, capacity=N + args.steps + args.warmup + 64, dtype=dt,
+    ctx = ParisKV(batch=1, n_kv=8, n_q=32, capacity=N + n_steps + n_warmup + 96, dtype=dt,
                   host_mapped=True, rho=p.rho, vote_weights=p.vote_weights,
                   coarse_permille=p.coarse_permille, top_k=p.top_k, n_sink=p.n_sink,
                   n_local=p.n_local, buf_tokens=p.buf_tokens,
@@ -234,14 +240,14 @@ def run_config4(args):
             ctx.decode_step_raw(kn[i].data_ptr(), vn[i].data_ptr(), q[i].data_ptr(), sel.data_ptr(),
                                 sel_n.data_ptr(), out.data_ptr(), stream)
 
-    steps(args.warmup)
+    steps(n_warmup)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    steps(args.steps)
+    steps(n_steps)
     b.record()
     torch.cuda.synchronize()
-    ms_step = a.elapsed_time(b) / args.steps
+    ms_step = a.elapsed_time(b) / n_steps
     stages = stage_times([ctx], steps, min(args.profile_steps, 32), torch, nat)
     n, sink_end, r_end, _ = ctx.window()
     # recall@k of the last step's selection against the exact top-k of the
@@ -262,8 +268,8 @@ def run_config4(args):
     st = lambda k: stages[k]["avg_us"] * 1e-6
     result = {
         "metric": "decode retrieval+sparse-attn steps/s at 1M ctx, K/V store in host memory",
-        "value": 1e3 / ms_step, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "value": 1e3 / ms_step, "unit": "steps/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": n_warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": 1, "kv_heads": 8, "q_heads": 32, "head_dim": 128,
                    "context": N, "kv_store": "pinned host memory", "top_k": p.top_k,
@@ -277,11 +283,19 @@ def run_config4(args):
         "stages": stages,
         "encode": {"keys": 8 * n_r, "ms": enc_ms, "host_read_GBps": 8 * n_r * 256 / (enc_ms * 1e-3) / 1e9},
         "recall_at_k": float(np.mean(rec)),
+        "wall_s": round(time.time() - t0, 1),
     }
-    print(json.dumps(result), flush=True)
+    ctx.close()
+    del ctx, wl
+    torch.cuda.empty_cache()
+    return result
 
 
 def run_config5(args):
+    print(json.dumps(config5_record(args)), flush=True)
+
+
+def config5_record(args):
     """Drifting decode: 32768-token prefill (batch 1 x 8 kv heads, G = 4, bf16), then
     16384 decode steps whose key/query mean drifts by two standard deviations; U = 256,
     k = 1024.  Timed in 16 segments of 1024 steps; recall@k of every unit against the
@@ -290,6 +304,7 @@ def run_config5(args):
     from kv_cache_top_amd import ParisKV
     from synth import workloads as W
     N0, T, seg = 32768, 16384, 1024
+    t_wall = time.time()
     wl = W.gqa_bf16(N=N0, top_k=1024, buf_tokens=256, threads=args.threads,
                     name="gqa_32k_drift16k_bf16")
     p = wl.params
@@ -350,7 +365,11 @@ def run_config5(args):
     }
     if fit_ms is not None:
         result["kmeans_fit"] = {"iterations": args.kmeans_iters, "keys": 8 * N0, "ms": fit_ms}
-    print(json.dumps(result), flush=True)
+    result["wall_s"] = round(time.time() - t_wall, 1)
+    ctx.close()
+    del ctx, Kd, Vd, Qd
+    torch.cuda.empty_cache()
+    return result
 
 
 def calibrate_copy():
@@ -403,6 +422,7 @@ class Layer:
         self.ctx.V[:, :, :N].copy_(torch.from_numpy(wl.V).to(dt))
         qp = W.query_pool(wl, pool)
         kn, vn, _ = W.decode_stream(wl, pool, drift_sigma=0.0, layer=layer)
+        self.q_host, self.kn_host = qp, kn       # host copies (the recall reference reads them)
         self.q = torch.from_numpy(qp).to(dt).cuda()
         self.kn = torch.from_numpy(kn).to(dt).cuda()
         self.vn = torch.from_numpy(vn).to(dt).cuda()
@@ -575,6 +595,144 @@ def recall(layer):
         rec.append(recall_at_k(got, ref))
         pl.append(float(np.isin(wl.planted[b, h], got).mean()))
     return float(np.mean(rec)), float(np.mean(pl))
+
+
+def recall_all(layers, per_layer=2, threads=16):
+    """recall@k and planted recall of every unit over `per_layer` further decode steps
+    of each layer replica.  The exact top-k ranks the unit's whole retrieval zone at
+    that step (prefill keys and the decode tokens evicted into it: the token appended
+    at a layer's step t is its pool entry t mod pool) by sum_g <q_g, k_i> in float64,
+    ties to the lower position.  Returns (recall@k, planted recall, unit-steps)."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+    recs, plants = [], []
+    for L in layers:
+        wl = L.wl
+        N, G = wl.n_tokens, wl.group
+        snaps = []
+        for _ in range(per_layer):
+            L.step()
+            torch.cuda.synchronize()
+            snaps.append((L.ctx.window(), L.sel.cpu().numpy().reshape(wl.n_units, -1).copy(),
+                          L.sel_n.cpu().numpy().reshape(-1).copy(), L.q_host[(L.t - 1) % L.pool]))
+        r_max = max(w[2] for w, _, _, _ in snaps)
+
+        def unit(u):
+            b, h = divmod(u, wl.n_kv)
+            K = wl.K[b, h, :min(r_max, N)].astype(np.float64)
+            if r_max > N:
+                K = np.concatenate([K, L.kn_host[np.arange(r_max - N) % L.pool, b, h].astype(np.float64)])
+            out = []
+            for (n, sink_end, r_end, _), sel, sel_n, q in snaps:
+                pos = np.arange(sink_end, r_end)
+                sc = K[sink_end:r_end] @ q[b, G * h:G * h + G].astype(np.float64).sum(0)
+                ref = pos[np.lexsort((pos, -sc))[:min(wl.params.top_k, pos.size)]]
+                got = sel[u][:sel_n[u]]
+                out.append((recall_at_k(got, ref), float(np.isin(wl.planted[b, h], got).mean())))
+            return out
+        with ThreadPoolExecutor(threads) as ex:
+            for res in ex.map(unit, range(wl.n_units)):
+                for r, p_ in res:
+                    recs.append(r)
+                    plants.append(p_)
+    return float(np.mean(recs)), float(np.mean(plants)), len(recs)
+
+
+def cpu_threads():
+    """Host threads for the oracle's all-cores run: the process's CPU share, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline_all_cores(args, layer, budget_s=10.0):
+    """The oracle on every (batch, kv-head) unit of one layer, the units split over
+    the host's threads (one numpy thread each): every unit encoded first (untimed),
+    then whole-batch decode steps over the layer's query pool for about `budget_s`
+    seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    from oracle import pariskv as ok
+    from oracle.codebook import spec_tables
+    wl = layer.wl
+    p = wl.params
+    levels, sq_t = spec_tables()
+    s = wl.signs()
+    N = wl.n_tokens
+    win = ok.Window(N, p.n_sink, p.n_local, p.buf_tokens)
+    qpool = layer.q.float().cpu().numpy()
+    n_thr = cpu_threads()
+    G = wl.group
+
+    def enc(u):
+        b, h = divmod(u, wl.n_kv)
+        return ok.encode_keys(wl.K[b, h], s, levels, sq_t)
+
+    def step(args_):
+        u, i = args_
+        b, h = divmod(u, wl.n_kv)
+        ids, nib, w = metas[u]
+        ok.decode_step(wl.K[b, h], wl.V[b, h], qpool[i % len(qpool), b, G * h:G * h + G], ids, nib, w,
+                       win, s, levels, rho=p.rho, weights=p.vote_weights,
+                       permille=p.coarse_permille, top_k=p.top_k)
+    with threadpool_limits(limits=1), ThreadPoolExecutor(n_thr) as ex:
+        metas = list(ex.map(enc, range(wl.n_units)))
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(step, [(u, n) for u in range(wl.n_units)]))
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or n >= 200:
+                break
+    return {"value": n / dt, "unit": "steps/s", "cores": n_thr, "kind": "oracle",
+            "sample": f"{n} whole-batch oracle decode steps (query prep, vote scan, coarse, RSQ-IP "
+                      f"rerank, top-k, attention of all {wl.n_units} (batch, kv-head) units of one "
+                      f"layer at {N} tokens, the units split over {n_thr} threads), {dt:.1f}s"}
+
+
+def graph_replay_timing(torch, layer, reps=200):
+    """Static retrieval + sparse attention (no append: the window does not move) on
+    one layer replica, issued eagerly and as replays of a HIP graph capturing the same
+    two calls: microseconds per call pair, and whether the replays' outputs equal the
+    eager ones."""
+    ctx, q = layer.ctx, layer.q[0]
+    sel, sel_n, out = layer.sel, layer.sel_n, layer.out
+
+    def eager():
+        ctx.retrieve(q, sel, sel_n)
+        ctx.sparse_attend(q, sel, sel_n, out)
+    for _ in range(8):
+        eager()
+    torch.cuda.synchronize()
+    ref = (sel.clone(), out.clone())
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        eager()
+    b.record()
+    torch.cuda.synchronize()
+    us_eager = a.elapsed_time(b) / reps * 1e3
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        ctx.retrieve(q, sel, sel_n, stream=st)
+        ctx.sparse_attend(q, sel, sel_n, out, stream=st)
+    for _ in range(4):
+        g.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us_graph = a.elapsed_time(b) / reps * 1e3
+    same = bool(torch.equal(sel, ref[0]) and torch.equal(out, ref[1]))
+    del g
+    return {"us_eager": us_eager, "us_graph_replay": us_graph, "replay_equals_eager": same,
+            "calls": "pk_retrieve + pk_sparse_attend, static context (one layer replica)"}
 
 
 class DeviceLayer:
@@ -855,7 +1013,6 @@ def main():
             stages[k]["alg_bytes"] = int(sums[k] / n_prof)
             stages[k]["GBps"] = gbs(k)
 
-    rec, planted = recall(layers[(base + args.profile_steps - 1) % nl])
     dense = dense_reference(torch, layers[0], ms_step)
     warm = None
     if args.warm_steps > 0:
@@ -868,12 +1025,37 @@ def main():
     for k, ref in (("rerank", "records_128B"), ("attend", "rows_256B")):
         if stages.get(k, {}).get("GBps"):
             stages[k]["frac_of_gather_reference"] = stages[k]["GBps"] / gref[ref]["GBps"]
-    cpu = None
+    graph = graph_replay_timing(torch, layers[0])
+    log("recall over every unit ...")
+    rec, planted, rec_n = recall_all(layers, threads=cpu_threads())
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(args, layers[0])
+        log("timing the CPU oracle (all cores, then one core) on a bounded sample ...")
+        cpu = cpu_baseline_all_cores(args, layers[0])
+        cpu1 = cpu_baseline(args, layers[0])
 
     wl = layers[0].wl
+    sub_cfg = {}
+    if not args.no_sub_configs:
+        for L in layers:
+            L.ctx.close()
+        del layers
+        torch.cuda.empty_cache()
+        log("1M-token host-store record ...")
+        c4 = config4_record(args, 64, 8)
+        sub_cfg["config_1m_host_store"] = {
+            "workload": c4["config"]["workload"], "steps_per_s": c4["value"],
+            "us_per_step": 1e3 * c4["ms_per_step"], "steps": c4["steps"],
+            "stages_us": {k: round(v["avg_us"], 2) for k, v in c4["stages"].items()},
+            "hbm": c4["hbm"], "host_link": c4["host_link"], "recall_at_k": c4["recall_at_k"],
+            "wall_s": c4["wall_s"]}
+        log("drift record ...")
+        c5 = config5_record(args)
+        sub_cfg["config_drift_32k_16k_steps"] = {
+            "workload": c5["config"]["workload"], "steps_per_s": c5["value"],
+            "us_per_step": 1e3 * c5["ms_per_step"], "steps": c5["steps"],
+            "drift_sigma": c5["config"]["drift_sigma"],
+            "recall_at_k_per_1k_steps": c5["recall_at_k_per_1k_steps"], "wall_s": c5["wall_s"]}
     enc_keys = wl.n_units * (wl.n_tokens - wl.params.n_sink - wl.params.n_local)
     result = {
         "metric": METRIC,
@@ -924,7 +1106,11 @@ def main():
                    "GBps": enc_keys * 400 / (np.mean(enc_ms) * 1e-3) / 1e9},
         "recall_at_k": rec,
         "planted_recall": planted,
+        "recall_sample": f"{rec_n} unit-steps: every unit of every layer replica, 2 decode steps each",
+        "graph_replay": graph,
         "cpu_baseline": cpu,
+        "cpu_baseline_one_core": cpu1,
+        **sub_cfg,
     }
     print(json.dumps(result), flush=True)
 
