@@ -176,26 +176,117 @@ __device__ __forceinline__ void clear_unit_hist(uint32_t* tot, int tstride, int 
     for (int i = threadIdx.x; i < tstride; i += blockDim.x) tot[(int64_t)u * tstride + i] = 0u;
 }
 
+// Survivors of the sampled prefilter kept in LDS (keys and candidate indices).
+constexpr int kSurvMax = 8 * kFBlock;
+
+// The sampled prefilter of fine_reg_body (described there).  key[0..nv) are
+// this thread's candidates b0..b0+nv-1; writes the selection's positions to
+// usel[0..k_eff) and returns true, or returns false (nothing written) when
+// fewer than k_eff or more than kSurvMax keys survive.
+template <int SEG>
+__device__ __forceinline__ bool fine_sampled(const uint32_t (&key)[SEG], int nv, int b0, int C,
+                                          int k_eff, const int32_t* __restrict__ upos,
+                                          int32_t* __restrict__ usel, FineShared& sh,
+                                          uint32_t* surv) {
+    const int tid = threadIdx.x;
+    // the sample: the first key of every thread holding candidates
+    const int n_samp = (C + SEG - 1) / SEG;
+    int r = (int)(((int64_t)2 * k_eff * n_samp + C - 1) / C);
+    r = r < 1 ? 1 : (r > n_samp ? n_samp : r);
+    uint32_t t_low = 0, rem_s = 0;
+    fine_threshold(sh, nv > 0 ? key[0] : 0u, nv > 0 ? ~key[0] : 0u, r,
+                   [&](auto&& f) { if (nv > 0) f(key[0]); }, t_low, rem_s);
+    // survivors: keys >= t_low, counted and placed in candidate order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) cnt += (j < nv && key[j] >= t_low) ? 1u : 0u;
+    uint32_t n_sur;
+    uint32_t w = block_excl_scan_t<kFBlock>(cnt, sh.tmp, &n_sur);
+    if (n_sur < (uint32_t)k_eff || n_sur > (uint32_t)kSurvMax) return false;   // block-uniform
+    uint32_t* skey = surv;
+    uint32_t* sidx = surv + kSurvMax;
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        if (j < nv && key[j] >= t_low) {
+            skey[w] = key[j];
+            sidx[w] = (uint32_t)(b0 + j);
+            ++w;
+        }
+    }
+    lds_sync();
+    // exact selection over the survivors: thread t holds survivors [8t, 8t + 8)
+    constexpr int SS = kSurvMax / kFBlock;
+    const int s0 = tid * SS;
+    const int nv2 = (int)n_sur - s0 < 0 ? 0 : ((int)n_sur - s0 < SS ? (int)n_sur - s0 : SS);
+    uint32_t k2[SS];
+    uint32_t kmax = 0, kmin_inv = 0;
+#pragma unroll
+    for (int j = 0; j < SS; ++j) {
+        k2[j] = j < nv2 ? skey[s0 + j] : 0u;
+        kmax = max(kmax, j < nv2 ? k2[j] : 0u);
+        kmin_inv = max(kmin_inv, j < nv2 ? ~k2[j] : 0u);
+    }
+    uint32_t kth = 0, remaining = (uint32_t)k_eff;
+    fine_threshold(sh, kmax, kmin_inv, k_eff,
+                   [&](auto&& f) {
+#pragma unroll
+                       for (int j = 0; j < SS; ++j)
+                           if (j < nv2) f(k2[j]);
+                   },
+                   kth, remaining);
+    uint32_t eqc = 0, gtc = 0;
+#pragma unroll
+    for (int j = 0; j < SS; ++j) {
+        gtc += (j < nv2 && k2[j] > kth) ? 1u : 0u;
+        eqc += (j < nv2 && k2[j] == kth) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, sh.tmp, &tot);
+    uint32_t rr = packed >> 16;
+    uint32_t o = (packed & 0xffffu) + (rr < remaining ? rr : remaining);
+#pragma unroll
+    for (int j = 0; j < SS; ++j) {
+        const bool eq = j < nv2 && k2[j] == kth;
+        const bool in = j < nv2 && (k2[j] > kth || (eq && rr < remaining));
+        rr += eq ? 1u : 0u;
+        if (in && o < (uint32_t)k_eff) usel[o] = upos[sidx[s0 + j]];
+        o += in ? 1u : 0u;
+    }
+    return true;
+}
+
 // candidates held in registers: C <= SEG * kFBlock, SEG in {4, 8, 16, 32, 64}
 // (C < 65536); the candidate rows hold a multiple of SEG entries, so the
-// 16-byte vector loads of a segment that starts below C stay inside the row
+// 16-byte vector loads of a segment that starts below C stay inside the row.
+//
+// With many candidates per selected key (SEG >= 32, C >= 8 k), every pass
+// over all the register-held keys costs the block several microseconds of
+// VALU time, so the selection first narrows them: t_low = the r-th largest
+// of a systematic sample (each thread's first key, r about twice the
+// sample's share of k), the keys >= t_low (an upper set of the values, kept
+// in candidate order in LDS, at most kSurvMax), and the exact selection over
+// those alone.  It is exact whenever at least k keys survive: then the k-th
+// largest key and every key equal to it are survivors, so the threshold, the
+// ties taken (lowest positions first) and the selected set are those of the
+// full selection; otherwise (or with too many survivors) the full selection
+// runs.  surv: 2 * kSurvMax words of LDS (SEG >= 32).
 template <int SEG>
 __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_pos,
                                               const float* __restrict__ cand_est, int64_t cmax,
                                               int C, int top_k, int32_t* __restrict__ sel,
                                               int32_t* __restrict__ sel_n, int u, FineShared& sh,
-                                              uint32_t* unit_hist, int tstride) {
+                                              uint32_t* unit_hist, int tstride,
+                                              uint32_t* surv = nullptr) {
     const int tid = threadIdx.x;
     const int k_eff = C < top_k ? C : top_k;
     const int b0 = tid * SEG;
     const int bl = b0 < C ? b0 : 0;          // a segment past C loads the row's start
     // up to 16 candidates per thread the positions stay in registers too; with
-    // more, they are read (all at once) after the threshold is known
+    // more, only the selected ones are read, after the threshold is known
     constexpr bool kPosReg = SEG <= 16;
     const int32_t* upos = cand_pos + (int64_t)u * cmax;
     uint32_t key[SEG];
     int32_t pos[kPosReg ? SEG : 1];
-    int32_t pos2[kPosReg ? 1 : SEG];   // read back after the threshold (SEG > 16)
     {
         const float4* e4 = reinterpret_cast<const float4*>(cand_est + (int64_t)u * cmax + bl);
         const int4* p4 = reinterpret_cast<const int4*>(upos + bl);
@@ -223,6 +314,14 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
     const int nv = C - b0 < 0 ? 0 : (C - b0 < SEG ? C - b0 : SEG);   // valid entries
     const bool all = k_eff >= C;
     uint32_t kth = 0, remaining = (uint32_t)k_eff;
+    if constexpr (SEG >= 32) {
+        if (!all && surv != nullptr && C >= 8 * k_eff &&
+            fine_sampled(key, nv, b0, C, k_eff, upos, sel + (int64_t)u * top_k, sh, surv)) {
+            clear_unit_hist(unit_hist, tstride, u);
+            if (tid == 0) sel_n[u] = k_eff;
+            return;
+        }
+    }
     if (!all) {
         uint32_t kmax = 0, kmin_inv = 0;
 #pragma unroll
@@ -251,27 +350,31 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
     uint32_t r = packed >> 16;                 // ties at kth before this segment
     uint32_t o = (packed & 0xffffu) + (r < remaining ? r : remaining);
     int32_t* usel = sel + (int64_t)u * top_k;
-    if constexpr (!kPosReg) {                  // this run's positions, all requested at once
-        const int4* p4 = reinterpret_cast<const int4*>(upos + bl);
-#pragma unroll
-        for (int q = 0; q < SEG / 4; ++q) {
-            const int4 x = p4[q];
-            pos2[4 * q] = x.x;
-            pos2[4 * q + 1] = x.y;
-            pos2[4 * q + 2] = x.z;
-            pos2[4 * q + 3] = x.w;
-        }
-    }
+    // fresh copies of kth and nv for the emit loop: otherwise the compiler keeps
+    // every comparison of the counting loop alive across the scan's barriers
+    // (SEG of them), which no longer fits the registers for SEG = 64
+    const uint32_t kth_e = (uint32_t)__builtin_amdgcn_readfirstlane((int)kth);
+    int nv_e = nv;
+    asm volatile("" : "+v"(nv_e));
+    // positions not held in registers (SEG > 16): the selected candidates'
+    // indices go to LDS (the histogram's words, dead by now) and their
+    // positions are then gathered in one round, one output per thread and pass
+    const bool stage = !kPosReg && k_eff <= kRadixBins;
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
-        const bool eq = j < nv && !all && key[j] == kth;
-        const bool in = j < nv && (all || key[j] > kth || (eq && r < remaining));
+        const bool eq = j < nv_e && !all && key[j] == kth_e;
+        const bool in = j < nv_e && (all || key[j] > kth_e || (eq && r < remaining));
         r += eq ? 1u : 0u;
         if (in && o < (uint32_t)k_eff) {
             if constexpr (kPosReg) usel[o] = pos[j];
-            else usel[o] = pos2[j];
+            else if (stage) sh.h[o] = (uint32_t)(b0 + j);
+            else usel[o] = upos[b0 + j];
         }
         o += in ? 1u : 0u;
+    }
+    if (stage) {
+        lds_sync();
+        for (int i = tid; i < k_eff; i += kFBlock) usel[i] = upos[sh.h[i]];
     }
     clear_unit_hist(unit_hist, tstride, u);
     if (tid == 0) sel_n[u] = k_eff;

@@ -489,8 +489,9 @@ __global__ __launch_bounds__(kFBlock) void fine_reg_kernel(const int32_t* __rest
                                                            uint32_t* __restrict__ tot,
                                                            int tstride) {
     __shared__ FineShared sh;
+    __shared__ uint32_t s_surv[SEG >= 32 ? 2 * kSurvMax : 1];   // survivors of the sampled prefilter
     fine_reg_body<SEG>(cand_pos, cand_est, cmax, C, top_k, sel, sel_n, blockIdx.x, sh, tot,
-                       tstride);
+                       tstride, SEG >= 32 ? s_surv : nullptr);
 }
 
 // more candidates than registers hold: the threshold passes stream the
@@ -718,8 +719,8 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
 hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t cmax, int units,
                        int C, int top_k, int32_t* sel, int32_t* sel_n, uint32_t* tot, int tstride,
                        hipStream_t st) {
-    // registers hold up to 32 candidates per thread (SEG of them in rows padded
-    // to a multiple of SEG); beyond that the passes stream from memory
+    // registers hold up to 64 candidates per thread (SEG of them in rows padded
+    // to a multiple of SEG); beyond that (C >= 65536) the passes stream from memory
     if (C < 1 || C > cmax) return hipErrorInvalidValue;
     const dim3 grid(units), blk(kFBlock);
 #define PK_FREG(S)                                                                              \
@@ -730,6 +731,7 @@ hipError_t launch_fine(const int32_t* cand_pos, const float* cand_est, int64_t c
     PK_FREG(8);
     PK_FREG(16);
     PK_FREG(32);
+    PK_FREG(64);
 #undef PK_FREG
     return launch(fine_mem_kernel, grid, blk, 0, st, cand_pos, cand_est, cmax, C, top_k, sel,
                   sel_n, tot, tstride);

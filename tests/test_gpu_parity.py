@@ -174,6 +174,28 @@ def test_fine_selection_30k_candidates():
     _full_check(wl, units=[0, 6], tag="30k-candidates")
 
 
+def test_fine_selection_39k_candidates():
+    """A coarse budget of 39244 candidates (15 % of 261628): the register-held
+    fine selection at 64 candidates per thread, narrowed first by the sampled
+    threshold (about 4000 survivors of 39244)."""
+    wl = W.gqa_bf16(N=262144, top_k=2048, permille=150, threads=16)
+    C = ok.coarse_count(262144 - 4 - 512, 150, 2048)
+    assert 32 * 1024 < C < 65536
+    _full_check(wl, units=[2, 7], tag="fine-39k")
+
+
+def test_fine_selection_39k_identical_keys():
+    """39244 candidates whose estimates all tie: the sampled threshold keeps every
+    candidate, more than the survivor buffer holds, so the full selection over
+    the 64 register-held keys per thread decides (the lowest positions)."""
+    wl = W.gqa_bf16(N=262144, top_k=2048, permille=150, threads=16)
+    wl.K[:, :, 4:] = wl.K[:, :, 4:5]
+    pkv, sel, sel_n, _ = _full_check(wl, units=[5], tag="fine-39k-identical")
+    _, sink_end, _, _ = pkv.window()
+    s = sel.cpu().numpy().reshape(wl.n_units, -1)
+    assert np.array_equal(s[5], np.arange(sink_end, sink_end + 2048))
+
+
 def test_dense_attention_matches_oracle():
     """pk_dense_attend: full attention over every stored token of each unit, against
     the oracle's attention over all positions; ragged last split."""
