@@ -78,7 +78,8 @@ def stream_reference(torch, scan_bytes=None):
     reference kernel (pk_stream_read) and a torch device copy (read + write bytes).
     With scan_bytes, also the streaming read of exactly that many bytes (the scan's
     algorithmic bytes per launch), timed cold: a 1 GiB read of another buffer
-    before each timed read evicts the last-level cache."""
+    before each timed read evicts the last-level cache.  That read is timed by
+    events attached to its dispatch, as the step's stages are."""
     import ctypes
     import kv_cache_top_amd._native as nat
     x = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").normal_()
@@ -88,7 +89,8 @@ def stream_reference(torch, scan_bytes=None):
 
     def read():
         nat.check(nat.lib.pk_stream_read(ctypes.c_void_p(x.data_ptr()), 1 << 30,
-                                         ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)),
+                                         ctypes.c_void_p(sink.data_ptr()), None,
+                                         ctypes.c_void_p(st)),
                   "pk_stream_read")
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     out = {}
@@ -104,20 +106,19 @@ def stream_reference(torch, scan_bytes=None):
     if scan_bytes:
         nb = int(scan_bytes) // 16 * 16
         part = y.view(torch.uint8)[:nb]
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(8)]
+        kus = ctypes.c_float(0.0)
+        times = []
         for i in range(9):
             read()                                   # evicts: 1 GiB of x
-            if i > 0:
-                evs[i - 1][0].record()
             nat.check(nat.lib.pk_stream_read(ctypes.c_void_p(part.data_ptr()), nb,
-                                             ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st)),
+                                             ctypes.c_void_p(sink.data_ptr()), ctypes.byref(kus),
+                                             ctypes.c_void_p(st)),
                       "pk_stream_read")
             if i > 0:
-                evs[i - 1][1].record()
-        torch.cuda.synchronize()
-        us = 1e3 * float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-        out["read_scan_bytes"] = {"bytes": nb, "us": us, "GBps": nb / (us * 1e-6) / 1e9}
+                times.append(kus.value)
+        us = float(np.mean(times))
+        out["read_scan_bytes"] = {"bytes": nb, "us": us, "GBps": nb / (us * 1e-6) / 1e9,
+                                  "timing": "dispatch events, cold (mean of 8)"}
     del x, y
     torch.cuda.empty_cache()
     return out
@@ -131,7 +132,7 @@ def gather_reference(torch, layer, reps=8):
     the records) and the attention's rows (2 k random positions per unit,
     256-byte rows over an array the size of the K store).  A 1 GiB streaming
     read before each timed gather evicts the last-level cache; the gather alone
-    is timed with HIP events on the stream it runs on."""
+    is timed by events attached to its dispatch, as the step's stages are."""
     import ctypes
     import kv_cache_top_amd._native as nat
     wl, p = layer.wl, layer.wl.params
@@ -154,21 +155,21 @@ def gather_reference(torch, layer, reps=8):
         for _ in range(reps):
             pos = torch.rand(units, n_r, device="cuda", generator=gen).argsort(dim=1)[:, :per_unit]
             sets.append((pos.sort(dim=1).values + base).to(torch.int32).contiguous())
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
+        kus = ctypes.c_float(0.0)
+        times = []
         for i in range(reps + 1):
             nat.check(nat.lib.pk_stream_read(ctypes.c_void_p(flush.data_ptr()), 1 << 30,
-                                             ctypes.c_void_p(sink.data_ptr()), st), "pk_stream_read")
-            if i > 0:
-                evs[i - 1][0].record(stream)
+                                             ctypes.c_void_p(sink.data_ptr()), None, st),
+                      "pk_stream_read")
             nat.check(nat.lib.pk_gather_read(ctypes.c_void_p(arr.data_ptr()), units * cap, rec_bytes,
                                              ctypes.c_void_p(sets[i % reps].data_ptr()),
-                                             units * per_unit, ctypes.c_void_p(sink.data_ptr()), st),
+                                             units * per_unit, ctypes.c_void_p(sink.data_ptr()),
+                                             ctypes.byref(kus), st),
                       "pk_gather_read")
             if i > 0:
-                evs[i - 1][1].record(stream)
+                times.append(kus.value)
         torch.cuda.synchronize()
-        us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        us = float(np.mean(times))
         nbytes = units * per_unit * rec_bytes
         out[name] = {"bytes": nbytes, "us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
         del arr, sets

@@ -239,12 +239,17 @@ pk_status pk_get_window(const pk_ctx* ctx, int64_t* n_tokens, int64_t* sink_end,
                         int64_t* buf);
 
 /* Measurement reference, not part of the method: reads `bytes` bytes at `src`
- * (device memory, 16-byte aligned, a multiple of 16 bytes) with a plain
- * streaming kernel, so that the path's bandwidth can be set against this
- * device's streaming-read rate.  *sink (device, 4 bytes) is written only in the
- * unlikely case that the checksum of the data equals a fixed constant.
- * Errors: PK_ERR_INVALID (NULL, misaligned or zero size). */
-pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+ * (device memory, 16-byte aligned, a multiple of 16 bytes, at most 2^44) with a
+ * plain streaming kernel (each 256-thread block one contiguous 32 KB piece,
+ * eight 16-byte nontemporal loads per thread in flight), so that the path's
+ * bandwidth can be set against this device's streaming-read rate.  *sink
+ * (device, 4 bytes) is written only in the unlikely case that the checksum of
+ * the data equals a fixed constant.  kernel_us: NULL, or a host float that
+ * receives the kernel's duration in microseconds, timed by events attached to
+ * the dispatch (the per-stage profile's timing); the call then waits for the
+ * kernel.  Errors: PK_ERR_INVALID (NULL, misaligned or zero size), PK_ERR_HIP. */
+pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, float* kernel_us,
+                         void* stream);
 
 /* Measurement reference, not part of the method: gathers `count` records of
  * `rec_bytes` bytes (a multiple of 16, at most 1024), record i being row
@@ -254,9 +259,10 @@ pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* st
  * records, the attention's 256-byte K/V rows) can be set against this device's
  * random-gather rate for the same access pattern.  *sink (device, 4 bytes) is
  * written only in the unlikely case that the checksum equals a fixed constant.
- * Errors: PK_ERR_INVALID (NULL, misaligned, sizes out of range). */
+ * kernel_us: as for pk_stream_read.
+ * Errors: PK_ERR_INVALID (NULL, misaligned, sizes out of range), PK_ERR_HIP. */
 pk_status pk_gather_read(const void* src, int64_t n_rows, int32_t rec_bytes, const int32_t* idx,
-                         int64_t count, uint32_t* sink, void* stream);
+                         int64_t count, uint32_t* sink, float* kernel_us, void* stream);
 
 /* Per-stage kernel timing.  While enabled, every kernel the context launches
  * is bracketed by HIP events recorded on the stream it runs on.

@@ -68,8 +68,10 @@ SIGNATURES = {
     "pk_profile_read": (_i32, [_c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "pk_debug_size": (_sz, [_c_void_p, _i32]),
     "pk_debug_copy": (_i32, [_c_void_p, _i32, _c_void_p, _sz, _c_void_p]),
-    "pk_stream_read": (_i32, [_c_void_p, _sz, _c_void_p, _c_void_p]),
-    "pk_gather_read": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _i64, _c_void_p, _c_void_p]),
+    "pk_stream_read": (_i32, [_c_void_p, _sz, _c_void_p, ctypes.POINTER(ctypes.c_float),
+                              _c_void_p]),
+    "pk_gather_read": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _i64, _c_void_p,
+                              ctypes.POINTER(ctypes.c_float), _c_void_p]),
 }
 
 

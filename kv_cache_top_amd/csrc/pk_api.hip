@@ -365,6 +365,34 @@ pk_status run_attend(pk_ctx* c, const void* q, const int32_t* sel, const int32_t
     return PK_OK;
 }
 
+// Runs `launch_fn` (one kernel launch); with `kernel_us`, times that launch by
+// events attached to the dispatch itself (the same timing as the per-stage
+// profile), waits for it and stores its duration in microseconds.
+template <typename F>
+pk_status reference_launch(float* kernel_us, hipStream_t st, F&& launch_fn) {
+    if (kernel_us == nullptr) {
+        PK_HIP(launch_fn(st));
+        return PK_OK;
+    }
+    hipEvent_t a = nullptr, b = nullptr;
+    if (hipEventCreate(&a) != hipSuccess) return runtime_fail();
+    if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return runtime_fail();
+    }
+    pk::launch_timing() = {a, b};
+    hipError_t e = launch_fn(st);
+    pk::launch_timing() = {};
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventSynchronize(b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    if (e != hipSuccess) return hip_fail(e, "reference kernel");
+    *kernel_us = 1000.0f * ms;
+    return PK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -497,22 +525,25 @@ void pk_destroy(pk_ctx* ctx) {
     delete ctx;
 }
 
-pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+pk_status pk_stream_read(const void* src, size_t bytes, uint32_t* sink, float* kernel_us,
+                         void* stream) {
     if (!src || !sink || bytes == 0 || (bytes & 15) ||
-        (reinterpret_cast<uintptr_t>(src) & 15))
+        (reinterpret_cast<uintptr_t>(src) & 15) || bytes > ((size_t)1 << 44))
         return PK_ERR_INVALID;
-    PK_HIP(pk::launch_stream_read(src, (int64_t)(bytes / 16), sink, (hipStream_t)stream));
-    return PK_OK;
+    return reference_launch(kernel_us, (hipStream_t)stream, [&](hipStream_t st) {
+        return pk::launch_stream_read(src, (int64_t)(bytes / 16), sink, st);
+    });
 }
 
 pk_status pk_gather_read(const void* src, int64_t n_rows, int32_t rec_bytes, const int32_t* idx,
-                         int64_t count, uint32_t* sink, void* stream) {
+                         int64_t count, uint32_t* sink, float* kernel_us, void* stream) {
     if (!src || !idx || !sink || n_rows < 1 || count < 1 || rec_bytes < 16 || rec_bytes > 1024 ||
         (rec_bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) ||
         n_rows > (int64_t)1 << 40 || count > ((int64_t)1 << 40) / rec_bytes)
         return PK_ERR_INVALID;
-    PK_HIP(pk::launch_gather_read(src, n_rows, rec_bytes, idx, count, sink, (hipStream_t)stream));
-    return PK_OK;
+    return reference_launch(kernel_us, (hipStream_t)stream, [&](hipStream_t st) {
+        return pk::launch_gather_read(src, n_rows, rec_bytes, idx, count, sink, st);
+    });
 }
 
 pk_status pk_get_window(const pk_ctx* c, int64_t* n_tokens, int64_t* sink_end, int64_t* r_end,

@@ -126,16 +126,16 @@ def test_calls_reject_null_context():
 
 def test_measurement_references_validate_arguments():
     p, i = ctypes.c_void_p(16), ctypes.c_void_p(64)
-    assert nat.lib.pk_stream_read(None, 16, p, None) == nat.PK_ERR_INVALID
-    assert nat.lib.pk_stream_read(ctypes.c_void_p(24), 16, p, None) == nat.PK_ERR_INVALID
-    assert nat.lib.pk_stream_read(p, 24, p, None) == nat.PK_ERR_INVALID
-    assert nat.lib.pk_gather_read(None, 10, 128, i, 4, p, None) == nat.PK_ERR_INVALID
-    assert nat.lib.pk_gather_read(p, 10, 128, None, 4, p, None) == nat.PK_ERR_INVALID
-    assert nat.lib.pk_gather_read(ctypes.c_void_p(24), 10, 128, i, 4, p, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_stream_read(None, 16, p, None, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_stream_read(ctypes.c_void_p(24), 16, p, None, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_stream_read(p, 24, p, None, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_gather_read(None, 10, 128, i, 4, p, None, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_gather_read(p, 10, 128, None, 4, p, None, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_gather_read(ctypes.c_void_p(24), 10, 128, i, 4, p, None, None) == nat.PK_ERR_INVALID
     for rb in (0, 8, 24, 2048):
-        assert nat.lib.pk_gather_read(p, 10, rb, i, 4, p, None) == nat.PK_ERR_INVALID
-    assert nat.lib.pk_gather_read(p, 0, 128, i, 4, p, None) == nat.PK_ERR_INVALID
-    assert nat.lib.pk_gather_read(p, 10, 128, i, 0, p, None) == nat.PK_ERR_INVALID
+        assert nat.lib.pk_gather_read(p, 10, rb, i, 4, p, None, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_gather_read(p, 0, 128, i, 4, p, None, None) == nat.PK_ERR_INVALID
+    assert nat.lib.pk_gather_read(p, 10, 128, i, 0, p, None, None) == nat.PK_ERR_INVALID
 
 
 def test_no_device_is_reported_without_a_gpu():

@@ -711,8 +711,18 @@ def test_gather_reference_kernel():
         idx = torch.randint(0, rows, (5003,), device="cuda", generator=g, dtype=torch.int32)
         st = nat.lib.pk_gather_read(ctypes.c_void_p(arr.data_ptr()), rows, rec_bytes,
                                     ctypes.c_void_p(idx.data_ptr()), idx.numel(),
-                                    ctypes.c_void_p(sink.data_ptr()), None)
+                                    ctypes.c_void_p(sink.data_ptr()), None, None)
         assert st == nat.PK_OK
+    # timed forms: the call waits for the kernel and reports a positive duration
+    us = ctypes.c_float(0.0)
+    assert nat.lib.pk_gather_read(ctypes.c_void_p(arr.data_ptr()), arr.numel() // 256, 256,
+                                  ctypes.c_void_p(idx.data_ptr()), idx.numel(),
+                                  ctypes.c_void_p(sink.data_ptr()), ctypes.byref(us), None) == nat.PK_OK
+    assert 0.0 < us.value < 1e6
+    us.value = 0.0
+    assert nat.lib.pk_stream_read(ctypes.c_void_p(arr.data_ptr()), arr.numel() - 16,
+                                  ctypes.c_void_p(sink.data_ptr()), ctypes.byref(us), None) == nat.PK_OK
+    assert 0.0 < us.value < 1e6
     torch.cuda.synchronize()
     assert int(sink.abs().sum()) == 0
 
