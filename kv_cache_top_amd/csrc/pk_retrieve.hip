@@ -186,38 +186,45 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
     float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
     constexpr int chunk = KPT * kBlock;
+    static_assert(kBlock == 256, "one pair-table entry and one prefetched piece per thread");
     const int u = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int l16 = tid & 15;
     constexpr int kLutWords = (M == 16 ? lut_bytes<16>() : lut_bytes<8>()) / 4;
     __shared__ __align__(16) int32_t s_list[chunk < kLutWords ? kLutWords : chunk];   // also the vote table
     __shared__ float2 s_pair[256];     // nibble byte (code of coord 2i+1 << 4 | code of 2i)
-    {
-        // signed level of a 4-bit code: sign bit 3, magnitude index bits 0..2
-        auto level = [&](uint32_t c) {
-            float m = tab.levels[0];
+    __shared__ float s_lv[16];         // signed level of each 4-bit code
+    __shared__ __align__(16) uint4 s_pre[kBlock];   // prefetched suffix counts (below)
+    __shared__ uint32_t s_T, s_need, s_gt, s_eq;
+    __shared__ __align__(16) uint32_t s_wtot[kBlock / 64];
+    // Every block resident on a CU runs the part before the record gather at
+    // the same time, so its instructions are paid by all of them: work that
+    // one wave can do is done by one wave.
+    if (tid < 16) {
+        // signed level of code tid: sign bit 3, magnitude index bits 0..2
+        float m = tab.levels[0];
 #pragma unroll
-            for (int l = 1; l < 8; ++l) m = ((c & 7u) == (uint32_t)l) ? tab.levels[l] : m;
-            return (c & 8u) ? -m : m;
-        };
-        for (int b = tid; b < 256; b += kBlock) s_pair[b] = make_float2(level(b & 15u), level(b >> 4));
+        for (int l = 1; l < 8; ++l) m = ((tid & 7) == l) ? tab.levels[l] : m;
+        s_lv[tid] = (tid & 8) ? -m : m;
     }
 
-    // one round of loads: this chunk's scores (contiguous per thread, vector
-    // loads; rows are padded so these never leave the buffer), the summed
-    // rotated query, the unit histogram
-    // the unit histogram's first 512 bins are requested before anything else
+    // one round of loads: the unit histogram (its first 512 bins requested
+    // before anything else), the first W suffix counts of the earlier chunks
+    // (up to 64 of them; thread 4c + q holds entries 8q .. 8q+7 of chunk c,
+    // rows being hstride entries, a multiple of 8), this chunk's scores
+    // (contiguous per thread, vector loads; rows are padded so these never
+    // leave the buffer) and the summed rotated query
     const uint32_t* ut = tot + (int64_t)u * ((nbins + 1) & ~1);
     const uint32_t t0 = tid < nbins ? ut[tid] : 0u;
     const uint32_t t1 = tid + kBlock < nbins ? ut[tid + kBlock] : 0u;
-    // the first W suffix counts of the earlier chunks (up to 64 of them) come
-    // with the first loads: thread 4c + q holds entries 8q .. 8q+7 of chunk c.
-    // Rows are hstride (a multiple of 8) entries long.
     const int W = hstride < 32 ? hstride : 32;
-    const int pc = tid >> 2, pq = tid & 3;
-    const bool pre_ok = pc < ch && 8 * pq < W;
-    uint4 pre = make_uint4(0u, 0u, 0u, 0u);
-    if (pre_ok)
-        pre = *reinterpret_cast<const uint4*>(hist + ((int64_t)u * max_chunks + pc) * hstride + 8 * pq);
+    {
+        const int pc = tid >> 2, pq = tid & 3;
+        uint4 pre = make_uint4(0u, 0u, 0u, 0u);
+        if (pc < ch && 8 * pq < W)
+            pre = *reinterpret_cast<const uint4*>(hist + ((int64_t)u * max_chunks + pc) * hstride + 8 * pq);
+        s_pre[tid] = pre;
+    }
     const int64_t start = (int64_t)ch * chunk;
     const int kbase = (int)start + tid * KPT;   // retrieval zone < 2^24 keys
     uint32_t s[KPT];
@@ -244,76 +251,90 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         for (int j = 0; j < KPT; ++j) s[j] = (w[j >> 2] >> (8 * (j & 3))) & 255u;
     }
     float y[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) y[r] = ysum[(int64_t)u * kD + 8 * l16 + r];
+    load8(ysum + (int64_t)u * kD + 8 * l16, y);
     extern __shared__ uint32_t s_ut[];   // the unit histogram (nbins entries, sized at launch)
     if (tid < nbins) s_ut[tid] = t0;
     if (tid + kBlock < nbins) s_ut[tid + kBlock] = t1;
     for (int b = tid + 2 * kBlock; b < nbins; b += kBlock) s_ut[b] = ut[b];
     lds_sync();
+    s_pair[tid] = make_float2(s_lv[tid & 15], s_lv[tid >> 4]);   // read after later barriers
 
-    // T and need from the unit histogram: thread t owns the bins ranked
-    // t*per .. t*per+per-1 in descending score order; ge[s] = #{score >= s} is
-    // non-increasing in s, and the one bin where it reaches C is T
-    const int lane = tid & 63, wave = tid >> 6;
-    __shared__ uint32_t s_T, s_need;
-    __shared__ uint32_t s_red[3 * kBlock / 64];
-    if (tid == 0) {
-        s_T = 0;
-        s_need = 0;
-    }
-    {
-        const int per = (nbins + kBlock - 1) / kBlock;
-        uint32_t seg = 0;
-        for (int j = 0; j < per; ++j) {
-            const int r = tid * per + j;
-            if (r < nbins) seg += s_ut[nbins - 1 - r];
-        }
-        const uint32_t x = wave_incl_scan(seg);
-        if (lane == 63) s_red[wave] = x;
-        lds_sync();
-        uint32_t run = x - seg;
+    // Wave 0: T and need.  ge[s] = #{score >= s} is non-increasing in s, and T
+    // is the one bin where it reaches C.  Lane l sums the bins [l*per, l*per +
+    // per) (per = ceil(nbins / 64) <= 64); a wave scan of the lane sums gives
+    // the keys above each lane's bins, and each lane walks its own bins from
+    // the top: the one lane whose range holds T finds it there.
+    if (wave == 0) {
+        const uint32_t Cu = (uint32_t)C;   // 1 <= C <= n_r < 2^24
+        const int per = (nbins + 63) >> 6;
+        const int b0 = lane * per;
+        int tb = -1;
+        uint32_t nd = 0;
+        if (per <= 8) {
+            uint32_t h[8];
 #pragma unroll
-        for (int w = 0; w < kBlock / 64; ++w) run += w < wave ? s_red[w] : 0u;
-        for (int j = 0; j < per; ++j) {
-            const int r = tid * per + j;
-            if (r < nbins) {
-                const uint32_t before = run;   // ge of the next higher score
-                run += s_ut[nbins - 1 - r];
-                if ((int64_t)before < C && (int64_t)run >= C) {   // C <= n_r: exactly one bin
-                    s_T = (uint32_t)(nbins - 1 - r);
-                    s_need = (uint32_t)(C - (int64_t)before);
+            for (int j = 0; j < 8; ++j) h[j] = (j < per && b0 + j < nbins) ? s_ut[b0 + j] : 0u;
+            const uint32_t seg = ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
+            const uint32_t incl = wave_incl_scan(seg);
+            uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
+#pragma unroll
+            for (int j = 7; j >= 0; --j) {
+                if (tb < 0 && run < Cu && run + h[j] >= Cu) {
+                    tb = b0 + j;
+                    nd = Cu - run;
                 }
+                run += h[j];
+            }
+        } else {
+            uint32_t seg = 0;
+            for (int j = 0; j < per; ++j) seg += b0 + j < nbins ? s_ut[b0 + j] : 0u;
+            const uint32_t incl = wave_incl_scan(seg);
+            uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
+            for (int j = per - 1; j >= 0; --j) {
+                const uint32_t h = b0 + j < nbins ? s_ut[b0 + j] : 0u;
+                if (tb < 0 && run < Cu && run + h >= Cu) {
+                    tb = b0 + j;
+                    nd = Cu - run;
+                }
+                run += h;
             }
         }
-        lds_sync();
+        const uint64_t hit = __ballot(tb >= 0);
+        const int L = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+        const int Tw = hit ? __builtin_amdgcn_readlane(tb, L) : 0;
+        const uint32_t need_w = hit ? (uint32_t)__builtin_amdgcn_readlane((int)nd, L) : 0u;
+        if (lane == 0) {
+            s_T = (uint32_t)Tw;
+            s_need = need_w;
+        }
     }
+    lds_sync();
     const int T = (int)(s_T < (uint32_t)nbins ? s_T : (uint32_t)nbins - 1u);
     const uint32_t need = s_need;
-    // keys above T (sfx_c[T+1]) and ties at T (sfx_c[T] - sfx_c[T+1]) in the
-    // chunks before this one: from the early entries when T + 1 is among
-    // them, else loaded now
-    uint32_t gtb = 0, eqb = 0;
-    const int Wv = W < nbins ? W : nbins;
-    if (T + 1 < Wv && ch <= kBlock / 4) {
-        auto entry = [&](int e) -> uint32_t {   // entry e (0..7) of this thread's eight
-            const int w = e >> 1;
-            const uint32_t x = w == 0 ? pre.x : (w == 1 ? pre.y : (w == 2 ? pre.z : pre.w));
-            return (e & 1) ? (x >> 16) : (x & 0xffffu);
-        };
-        if (pre_ok && (T >> 3) == pq) eqb += entry(T & 7);
-        if (pre_ok && ((T + 1) >> 3) == pq) {
-            const uint32_t g = entry((T + 1) & 7);
-            gtb += g;
-            eqb -= g;                          // block sums wrap back to sfx[T] - sfx[T+1]
+
+    // Wave 0 again, while the others count their keys: the earlier chunks'
+    // keys above T and ties at T.  Chunk c holds sfx_c[T+1] keys above T and
+    // sfx_c[T] - sfx_c[T+1] ties, read from the prefetched entries when both
+    // are among them, else from memory.
+    uint32_t g_w = 0, e_w = 0;
+    if (wave == 0) {
+        const int Wv = W < nbins ? W : nbins;
+        const uint16_t* pre16 = reinterpret_cast<const uint16_t*>(s_pre);
+        for (int c = lane; c < ch; c += 64) {
+            uint32_t at_t, above_t;   // sfx_c[T], sfx_c[T+1]
+            if (c < kBlock / 4 && T + 1 < Wv) {
+                at_t = pre16[c * 32 + T];
+                above_t = pre16[c * 32 + T + 1];
+            } else {
+                const uint16_t* row = hist + ((int64_t)u * max_chunks + c) * hstride;
+                at_t = row[T];
+                above_t = T + 1 < nbins ? row[T + 1] : 0u;
+            }
+            g_w += above_t;
+            e_w += at_t - above_t;
         }
-    } else {
-        for (int c = tid; c < ch; c += kBlock) {
-            const uint16_t* row = hist + ((int64_t)u * max_chunks + c) * hstride;
-            const uint32_t g = (T >= 0 && T + 1 < nbins) ? row[T + 1] : 0u;
-            gtb += g;
-            eqb += T >= 0 ? (uint32_t)row[T] - g : 0u;
-        }
+        g_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(g_w), 63);
+        e_w = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(e_w), 63);
     }
 
     // a stored 255 stands for 255 or more: when the threshold is that high the
@@ -346,59 +367,59 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     }
 
     // this chunk's candidates, in position order: keys above T, and ties at T
-    // while the unit's tie budget lasts
+    // while the unit's tie budget lasts.  Keys past the zone's end (last chunk
+    // only) read as -1, which is neither above nor equal to T >= 0.
+    if (start + chunk > n_r) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (kbase + j >= (int)n_r) s[j] = 0xffffffffu;
+    }
     uint32_t eqc = 0, gtc = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        if (kbase + j >= (int)n_r) s[j] = 0xffffffffu;
-        gtc += (s[j] != 0xffffffffu && s[j] > (uint32_t)T) ? 1u : 0u;
-        eqc += (s[j] == (uint32_t)T) ? 1u : 0u;
+        gtc += (int)s[j] > T ? 1u : 0u;
+        eqc += (int)s[j] == T ? 1u : 0u;
     }
-    // one barrier for three block-wide sums: the packed (ties, above) scan of
-    // this chunk and the earlier chunks' totals
-    uint32_t packed, tot_c, gt_chunk, eq_chunk;
+    // packed (ties, above) exclusive scan over the block (a chunk holds at
+    // most 8192 keys: the halves never carry)
+    uint32_t packed, tot_c;
     {
         const uint32_t v = (eqc << 16) | gtc;
         const uint32_t x = wave_incl_scan(v);
-        const uint32_t gw = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(gtb), 63);
-        const uint32_t ew = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(eqb), 63);
-        if (lane == 63) s_red[wave] = x;
-        if (lane == 0) {
-            s_red[kBlock / 64 + wave] = gw;
-            s_red[2 * kBlock / 64 + wave] = ew;
+        if (lane == 63) s_wtot[wave] = x;
+        if (wave == 0 && lane == 0) {
+            s_gt = g_w;
+            s_eq = e_w;
         }
         lds_sync();
-        uint32_t before = 0, all = 0, ga = 0, ea = 0;
-#pragma unroll
-        for (int w = 0; w < kBlock / 64; ++w) {
-            const uint32_t t = s_red[w];
-            if (w < wave) before += t;
-            all += t;
-            ga += s_red[kBlock / 64 + w];
-            ea += s_red[2 * kBlock / 64 + w];
-        }
+        const uint4 wt = *reinterpret_cast<const uint4*>(s_wtot);
+        const uint32_t before = (wave > 0 ? wt.x : 0u) + (wave > 1 ? wt.y : 0u) + (wave > 2 ? wt.z : 0u);
         packed = before + x - v;
-        tot_c = all;
-        gt_chunk = ga;
-        eq_chunk = ea;
+        tot_c = (wt.x + wt.y) + (wt.z + wt.w);
     }
+    const uint32_t gt_chunk = s_gt, eq_chunk = s_eq;
     const uint32_t eq_t = packed >> 16, gt_t = packed & 0xffffu;
     const uint32_t taken_before_chunk = eq_chunk < need ? eq_chunk : need;
     auto taken = [&](uint32_t e) { return (e < need ? e : need) - taken_before_chunk; };
     uint32_t at = gt_t + taken(eq_chunk + eq_t);
-    const uint32_t n_mem = (tot_c & 0xffffu) + taken(eq_chunk + (tot_c >> 16));
     const uint32_t cand_before = gt_chunk + taken_before_chunk;
+    // each wave lists its own candidates (a contiguous range of the chunk's
+    // list) and estimates them itself, so no block barrier stands between the
+    // list and the record requests
+    const int w_lo = __builtin_amdgcn_readfirstlane((int)at);   // lane 0's first slot
     uint32_t rank = eq_chunk + eq_t;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        bool in = false;
-        if (s[j] != 0xffffffffu) {
-            if (s[j] > (uint32_t)T) in = true;
-            else if (s[j] == (uint32_t)T) in = (rank++ < need);
-        }
-        if (in) s_list[at++] = (int32_t)(sink_end + start + (int64_t)tid * KPT + j);
+        const bool in = (int)s[j] > T || ((int)s[j] == T && rank < need);
+        rank += (int)s[j] == T ? 1u : 0u;
+        if (in) s_list[at] = (int32_t)(sink_end + start + (int64_t)tid * KPT + j);
+        at += in ? 1u : 0u;
     }
-    lds_sync();
+    const int w_hi = __builtin_amdgcn_readlane((int)at, 63);   // past lane 63's last slot
+    (void)tot_c;
+    // the list entries other lanes of this wave wrote are complete before any is read
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
 
     // RSQ-IP: est = sum_b w_b <v_b, Ysum_b> / sqrt(d), Ysum = sum_g H D q_g;
     // 16 lanes per candidate, lane l reading the nibble word of coordinates
@@ -412,7 +433,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     constexpr uint32_t kRecB = (uint32_t)rec_bytes<M>();
     using WT = typename std::conditional<M == 4, float2, float>::type;   // a lane's w
     const float inv_sqrt_d = 0.08838834764831845f;
-    const int grp = tid >> 4;
+    const int grp = lane >> 4;         // 16-lane group within the wave
     // the unit's records through a buffer descriptor: 32-bit offsets (a unit
     // holds at most 2^24 records of <= 192 B), half the address registers of
     // 64-bit pointers for the batch in flight
@@ -422,13 +443,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     int32_t* upos = cand_pos + (int64_t)u * cmax;
     float* uest = cand_est + (int64_t)u * cmax;
     const uint32_t w_off = 64u + (M == 4 ? 8u * (uint32_t)l16 : 4u * (uint32_t)(M == 16 ? (l16 >> 1) : l16));
-    for (int i0 = grp; i0 < (int)n_mem; i0 += kBatch * (kBlock / 16)) {
+    for (int i0 = w_lo + grp; i0 < w_hi; i0 += kBatch * 4) {
         uint32_t nib[kBatch];
         WT w[kBatch];
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-            const int i = i0 + k * (kBlock / 16);
-            const int32_t p = s_list[i < (int)n_mem ? i : i0];
+            const int i = i0 + k * 4;
+            const int32_t p = s_list[i < w_hi ? i : i0];
             const uint32_t ro = (uint32_t)p * kRecB;
             nib[k] = __builtin_amdgcn_raw_buffer_load_b32(urec, ro + 4u * (uint32_t)l16, 0, 0);
             if constexpr (M == 4) {
@@ -441,8 +462,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         }
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
-            const int i = i0 + k * (kBlock / 16);
-            if (i >= (int)n_mem) break;          // uniform in the 16-lane group
+            const int i = i0 + k * 4;
+            if (i >= w_hi) break;                // uniform in the 16-lane group
             float part;
             if constexpr (M != 4) {   // one w for the lane's 8 coordinates
                 float dot = 0.0f;
