@@ -448,7 +448,7 @@ class Layer:
         self.ctx.decode_step_raw(*self._args[i], self._stream)
 
 
-KERNEL_SOURCES = ("kv_cache_top_amd/csrc/pk_retrieve.hip", "kv_cache_top_amd/csrc/pk_device.hpp")
+KERNEL_SOURCES = ("kv_cache_top_amd/csrc/pk_scan.hip", "kv_cache_top_amd/csrc/pk_device.hpp")
 TRAFFIC_PROFILE = "profiles/scan_kernel_gqa128k_b4_hbm_traffic.txt"
 
 

@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpariskv.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-HIP_SOURCES = ["pk_api.hip", "pk_encode.hip", "pk_retrieve.hip", "pk_attend.hip", "pk_fused.hip",
-               "pk_kmeans.hip"]
+HIP_SOURCES = ["pk_api.hip", "pk_encode.hip", "pk_scan.hip", "pk_retrieve.hip", "pk_attend.hip",
+               "pk_fused.hip", "pk_kmeans.hip"]
 CXX_SOURCES = ["pk_codebook.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
