@@ -13,15 +13,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs<T> a, in
 }
 
 // merge of the split partials: one 128-thread block per (query head, unit),
-// thread d owning output coordinate d.  Splits are folded in groups of kCGroup,
-// everything of a group requested before any is used: lane k of each wave
-// reads (m, l) of split s0 + k, the group maximum M' rescales the running
-// sums, lane k's weight e^(m - M') is broadcast to the wave, and
-// acc += o_s e^(m_s - M'), L += l_s e^(m_s - M').  out = acc / L.
-constexpr int kCGroup = 32;
-
+// thread d owning output coordinate d.  Splits are folded in groups of CG
+// (24 when that covers them all, as in a decode step with a few hot-zone
+// splits and the selection's 16; else 32), everything of a group requested
+// before any is used: lane k of each wave reads (m, l) of split s0 + k, the
+// group maximum M' rescales the running sums, lane k's weight e^(m - M') is
+// broadcast to the wave, and acc += o_s e^(m_s - M'), L += l_s e^(m_s - M').
+// out = acc / L.
+template <int CG>
 __global__ __launch_bounds__(kD) void combine_kernel(const float* __restrict__ part, int G,
                                                      int n_splits, float* __restrict__ out) {
+    constexpr int kCGroup = CG;
     const int g = blockIdx.x, u = blockIdx.y, d = threadIdx.x, lane = d & 63;
     const int64_t stride = (int64_t)G * (kD + 2);      // between splits
     const float* hp = part + (int64_t)u * n_splits * stride + (int64_t)g * (kD + 2);
@@ -79,7 +81,9 @@ int attend_max_splits() { return kMaxSplits; }
 
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st) {
-    return launch(combine_kernel, dim3(G, units), dim3(kD), 0, st, part, G, n_splits, out);
+    if (n_splits <= 24)
+        return launch(combine_kernel<24>, dim3(G, units), dim3(kD), 0, st, part, G, n_splits, out);
+    return launch(combine_kernel<32>, dim3(G, units), dim3(kD), 0, st, part, G, n_splits, out);
 }
 
 hipError_t launch_attend(bool bf16, int G, const void* K, const void* V, int64_t cap, int units,
