@@ -319,7 +319,8 @@ __device__ __forceinline__ float order_key_f32(uint32_t k) {
 // Block-wide exclusive scan of one uint32 per thread for a block of NT
 // threads.  `tmp` must hold NT / 64 entries.  Returns the exclusive prefix;
 // the block total goes to *total.  Contains two LDS barriers.
-template <int NT>
+// kReuse: a closing barrier, so that tmp can be written again right after
+template <int NT, bool kReuse = true>
 __device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* tmp, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t x = wave_incl_scan(v);
@@ -332,7 +333,7 @@ __device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* tmp,
         if (w < wave) before += t;
         all += t;
     }
-    lds_sync();
+    if constexpr (kReuse) lds_sync();
     *total = all;
     return before + x - v;
 }

@@ -80,6 +80,9 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
                                                int k_eff, ForAll&& for_all, uint32_t& kth,
                                                uint32_t& remaining) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the bucket histogram is zeroed ahead of the range's barrier (no pass of
+    // the caller reads sh.h past its own last barrier)
+    for (int b = tid; b < kRadixBins; b += kFBlock) sh.h[b] = 0;
     kmax = wave_max(kmax);
     kmin_inv = wave_max(kmin_inv);
     if (lane == 0) {
@@ -110,8 +113,6 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
         auto bucket = [&](uint32_t key) -> uint32_t {
             return (uint32_t)fminf((order_key_to_f32(key) - vmin) * scale, topb);
         };
-        for (int b = tid; b < kRadixBins; b += kFBlock) sh.h[b] = 0;
-        lds_sync();
         for_all([&](uint32_t key) { atomicAdd(&sh.h[bucket(key)], 1u); });
         lds_sync();
         if (wave == 0) digit_search(sh.h, kRadixBins, remaining, lane, &sh.digit, &sh.above);
@@ -143,6 +144,8 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
             remaining = rem - sh.gt;
             return;
         }
+        // every thread has read n_b before the radix passes rewrite sh.h
+        lds_sync();
     }
     // radix select over the order keys
     uint32_t prefix = 0, pmask = 0;
@@ -201,7 +204,7 @@ __device__ __forceinline__ bool fine_sampled(const uint32_t (&key)[SEG], int nv,
 #pragma unroll
     for (int j = 0; j < SEG; ++j) cnt += (j < nv && key[j] >= t_low) ? 1u : 0u;
     uint32_t n_sur;
-    uint32_t w = block_excl_scan_t<kFBlock>(cnt, sh.tmp, &n_sur);
+    uint32_t w = block_excl_scan_t<kFBlock, false>(cnt, sh.tmp, &n_sur);
     if (n_sur < (uint32_t)k_eff || n_sur > (uint32_t)kSurvMax) return false;   // block-uniform
     uint32_t* skey = surv;
     uint32_t* sidx = surv + kSurvMax;
@@ -241,7 +244,7 @@ __device__ __forceinline__ bool fine_sampled(const uint32_t (&key)[SEG], int nv,
         eqc += (j < nv2 && k2[j] == kth) ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, sh.tmp, &tot);
+    const uint32_t packed = block_excl_scan_t<kFBlock, false>((eqc << 16) | gtc, sh.tmp, &tot);
     uint32_t rr = packed >> 16;
     uint32_t o = (packed & 0xffffu) + (rr < remaining ? rr : remaining);
 #pragma unroll
@@ -346,7 +349,7 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
         eqc += (j < nv && !all && key[j] == kth) ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t packed = block_excl_scan_t<kFBlock>((eqc << 16) | gtc, sh.tmp, &tot);
+    const uint32_t packed = block_excl_scan_t<kFBlock, false>((eqc << 16) | gtc, sh.tmp, &tot);
     uint32_t r = packed >> 16;                 // ties at kth before this segment
     uint32_t o = (packed & 0xffffu) + (r < remaining ? r : remaining);
     int32_t* usel = sel + (int64_t)u * top_k;
