@@ -77,16 +77,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         if (valid && sc >= 8u) atomicAdd(&s_hist[sc], 1u);
     }
     // stored as bytes, saturated at 255 (the rerank rescores saturated keys in
-    // the rare case that the threshold reaches 255)
-    uint8_t* srow = scores + u * sstride + start + tid;
-    if (nval == chunk) {
+    // the rare case that the threshold reaches 255): staged in LDS in chunk
+    // order and written after the barrier below, each thread its KPT
+    // consecutive bytes in one piece
+    __shared__ __align__(16) uint8_t s_sc[chunk];
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) srow[j * kBlock] = (uint8_t)min(scv[j], 255u);
-    } else {
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (j * kBlock + tid < nval) srow[j * kBlock] = (uint8_t)min(scv[j], 255u);
-    }
+    for (int j = 0; j < KPT; ++j) s_sc[j * kBlock + tid] = (uint8_t)min(scv[j], 255u);
     {
         // bytes 0..7 of c8 = counts of scores 0..7; widen to 16-bit fields
         // (a wave holds at most 64 * 32 per score) and sum over the wave
@@ -114,6 +110,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
         }
     }
     lds_sync();
+    {
+        uint8_t* srow = scores + u * sstride + start;
+        const int b0 = tid * KPT;
+        if (b0 + KPT <= nval) {
+            if constexpr (KPT >= 8) {
+#pragma unroll
+                for (int q = 0; q < KPT / 8; ++q)
+                    reinterpret_cast<uint2*>(srow + b0)[q] = reinterpret_cast<const uint2*>(s_sc + b0)[q];
+            } else if constexpr (KPT == 4) {
+                *reinterpret_cast<uint32_t*>(srow + b0) = *reinterpret_cast<const uint32_t*>(s_sc + b0);
+            } else if constexpr (KPT == 2) {
+                *reinterpret_cast<uint16_t*>(srow + b0) = *reinterpret_cast<const uint16_t*>(s_sc + b0);
+            } else {
+                srow[b0] = s_sc[b0];
+            }
+        } else {
+            for (int j = 0; j < KPT && b0 + j < nval; ++j) srow[b0 + j] = s_sc[b0 + j];
+        }
+    }
 
     // waves 1..: add the chunk's counts to the unit's score histogram (zeroed
     // by the previous step's fine selection, or at creation).  wave 0: the chunk's suffix
