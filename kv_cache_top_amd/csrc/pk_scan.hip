@@ -13,6 +13,11 @@
 
 namespace pk {
 
+// key id rows requested before the vote table's barrier (A/B on the 128K
+// batch-4 workload: 8 rows 14.3 us, 4 rows 14.3, 2 rows 14.15, 1 row 13.9,
+// none 14.3: with none, memory idles until the tables have arrived)
+constexpr int kScanEarlyRows = 1;
+
 // M = 8: the vote table holds one 256-entry byte row per id byte (also m = 4,
 // whose rows sum two subspaces); M = 16: one hash table per 16-bit id.
 template <int KPT, int M>
@@ -27,8 +32,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     extern __shared__ uint32_t s_hist[];  // scan_hist_slots(nbins) entries (sized at launch)
     const uint8_t* lut8 = reinterpret_cast<const uint8_t*>(s_lut);
 
-    // The vote table is requested first and the key id rows right after, all
-    // before any is used: scoring key j then waits only for its own row.
+    // The vote table is requested first, then the first kEarly key id rows;
+    // the other rows only after the table is in LDS (the block's barrier).  A block's requests queue
+    // behind those of the blocks dispatched before it on the same CU, so
+    // holding back most rows until the table has arrived keeps that queue
+    // short; the early rows keep memory busy meanwhile.  Scoring key j waits
+    // only for its own row.
+    constexpr int kEarly = KPT < kScanEarlyRows ? KPT : kScanEarlyRows;
     uint4 lut_part[kLutParts];
 #pragma unroll
     for (int i = 0; i < kLutParts; ++i)
@@ -39,7 +49,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     // compiler can count them and wait for each row individually
     uint4 v[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
+    for (int j = 0; j < kEarly; ++j) {
         const int64_t i = start + j * kBlock + tid;
         v[j] = load_nt(idrow + (i < n_r ? i : n_r - 1));
     }
@@ -48,6 +58,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     const int per = scan_bins_per_lane(nbins);
     for (int b = tid; b < 64 * per; b += kBlock) s_hist[b] = 0;
     lds_sync();
+#pragma unroll
+    for (int j = kEarly; j < KPT; ++j) {
+        const int64_t i = start + j * kBlock + tid;
+        v[j] = load_nt(idrow + (i < n_r ? i : n_r - 1));
+    }
 
     // histogram: scores 0..7, which most keys have, go to eight byte counters
     // per thread (at most KPT <= 32 keys each, no overflow), summed over the
