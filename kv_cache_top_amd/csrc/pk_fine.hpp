@@ -18,12 +18,13 @@ namespace pk {
 // bits) decides instead.  Then compaction in candidate (= position) order,
 // each thread owning a contiguous segment; ties at the k-th go to the lower
 // positions.
-// Up to kFineReg candidates, thread t keeps its segment [t*SEG, t*SEG+SEG)
-// in registers for every pass; beyond that the passes stream the estimates
-// from memory.
+// Below 65536 candidates thread t keeps its segment [t*SEG, t*SEG+SEG) in
+// registers for every pass (SEG up to 64; up to kFineReg, 16 per thread, in
+// the launch fused with the hot-zone attention); beyond that the passes
+// stream the estimates from memory.
 // ---------------------------------------------------------------------------
 constexpr int kFBlock = 1024;
-constexpr int kFineReg = 16 * kFBlock;  // candidates held in registers
+constexpr int kFineReg = 16 * kFBlock;  // candidates the fused launch holds in registers
 constexpr int kRadixBins = 2048;
 constexpr int kRankMax = 1024;   // bucket members ranked directly
 
