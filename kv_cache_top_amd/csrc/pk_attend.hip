@@ -19,40 +19,41 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs<T> a, in
 // before any is used: lane k of each wave reads (m, l) of split s0 + k, the
 // group maximum M' rescales the running sums, lane k's weight e^(m - M') is
 // broadcast to the wave, and acc += o_s e^(m_s - M'), L += l_s e^(m_s - M').
-// out = acc / L.
+// out = acc / L.  No branch stands between a group's loads and their use (a
+// branch there lets the compiler sink the row loads below it: two memory
+// round trips instead of one).  A split with nothing attended has m = -inf,
+// l = 0, o = 0 and weight 0; a unit's partials span less than 2^31 floats,
+// so offsets are 32-bit.
 template <int CG>
 __global__ __launch_bounds__(kD) void combine_kernel(const float* __restrict__ part, int G,
                                                      int n_splits, float* __restrict__ out) {
-    constexpr int kCGroup = CG;
     const int g = blockIdx.x, u = blockIdx.y, d = threadIdx.x, lane = d & 63;
-    const int64_t stride = (int64_t)G * (kD + 2);      // between splits
-    const float* hp = part + (int64_t)u * n_splits * stride + (int64_t)g * (kD + 2);
+    const int stride = G * (kD + 2);      // floats between splits
+    const float* hp = part + (int64_t)u * n_splits * stride + g * (kD + 2);
     float M = -INFINITY, L = 0.0f, acc = 0.0f;
-    for (int s0 = 0; s0 < n_splits; s0 += kCGroup) {
-        const int nk = n_splits - s0 < kCGroup ? n_splits - s0 : kCGroup;
-        const int sl = s0 + (lane < nk ? lane : nk - 1);
-        float ml = hp[sl * stride];
-        float ll = hp[sl * stride + 1];
-        float ov[kCGroup];
+    for (int s0 = 0; s0 < n_splits; s0 += CG) {
+        const int nk = n_splits - s0 < CG ? n_splits - s0 : CG;
+        const float* gp = hp + s0 * stride;
+        const int sl = lane < nk ? lane : nk - 1;
+        float ml = gp[sl * stride];
+        float ll = gp[sl * stride + 1];
+        float ov[CG];
 #pragma unroll
-        for (int k = 0; k < kCGroup; ++k) {
-            const int s = s0 + (k < nk ? k : nk - 1);
-            ov[k] = hp[s * stride + 2 + d];
-        }
+        for (int k = 0; k < CG; ++k) ov[k] = gp[(k < nk ? k : nk - 1) * stride + 2 + d];
         if (lane >= nk) {
             ml = -INFINITY;
             ll = 0.0f;
         }
         const float Mg = fmaxf(M, wave_max_f(ml));
-        if (Mg == -INFINITY) continue;                  // nothing attended yet
         const float r = (M == -INFINITY) ? 0.0f : __expf(M - Mg);
         const float f = (ml == -INFINITY) ? 0.0f : __expf(ml - Mg);
         L = fmaf(L, r, wave_sum_f(ll * f));
+        // lanes k >= nk hold weight 0, and their ov[k] (a copy of split
+        // s0 + nk - 1) is finite, so every term is taken unconditionally
         float a = acc * r;
 #pragma unroll
-        for (int k = 0; k < kCGroup; ++k) {
-            if (k < nk) a = fmaf(ov[k], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k)), a);
-        }
+        for (int k = 0; k < CG; ++k)
+            a = fmaf(ov[k], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), k)), a);
         acc = a;
         M = Mg;
     }

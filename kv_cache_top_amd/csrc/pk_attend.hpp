@@ -121,23 +121,20 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
     // coordinates per lane.
     // Hot splits read neither sel nor sel_n (the fused kernel computes them
     // at the same time).
+    // The count and the positions are loaded without a branch (a branch per
+    // load lets the compiler wait for each before issuing the next): a hot
+    // split points its loads at the query instead and discards the values.
     const int64_t n_hot = sink_end + (n_tok - r_end);
     const bool hot_split = sp < a.n_hot_splits;
-    int64_t i0, end;
-    if (hot_split) {
-        i0 = (int64_t)sp * kSplit;
-        end = n_hot;
-    } else {
-        int nsel = a.sel_n[u];
-        nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
-        i0 = n_hot + (int64_t)(sp - a.n_hot_splits) * kSplit;
-        end = n_hot + nsel;
-    }
-    const int nk = active ? (int)((end - i0) < kSplit ? (end - i0 > 0 ? end - i0 : 0) : kSplit) : 0;
+    const int32_t* sel_row = hot_split ? reinterpret_cast<const int32_t*>(q)
+                                       : a.sel + (int64_t)u * top_k;
+    const int32_t* sel_cnt = hot_split ? reinterpret_cast<const int32_t*>(q) : a.sel_n + u;
+    const int64_t i0 = hot_split ? (int64_t)sp * kSplit
+                                 : n_hot + (int64_t)(sp - a.n_hot_splits) * kSplit;
     auto sel_at = [&](int kk) -> int32_t {
-        if (hot_split) return 0;
         const int64_t i = i0 + kk - n_hot;
-        return a.sel[(int64_t)u * top_k + (i < 0 ? 0 : (i < top_k ? i : top_k - 1))];
+        const int32_t c = sel_row[hot_split ? 0 : (i < 0 ? 0 : (i < top_k ? (int)i : top_k - 1))];
+        return hot_split ? 0 : c;
     };
     constexpr int kPerK = kMfma ? 1 : kPer;
     int32_t cand_v[kPerK], cand_k[2];
@@ -150,32 +147,55 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
 #pragma unroll
         for (int j = 0; j < kPer; ++j) cand_v[j] = sel_at(32 * wave + grp + 4 * j);
     }
-    // query operand.  bf16: A rows = heads (rows >= G zero), lane l holds head
-    // l16's dims 32s + 8 grp .. +8 of step s.  fp32: this lane's 8 dims of every head.
+    int nsel = *sel_cnt;
+    // query operand.  bf16: A rows = heads, lane l holds head l16's dims 32s +
+    // 8 grp .. +8 of step s; rows >= G load head G - 1 (no branch around the
+    // loads), and their products are never stored.  fp32: this lane's 8 dims
+    // of every head.
     uint4 qa[4];
     Raw8<T> qv[kMfma ? 1 : G];
     if constexpr (kMfma) {
+        const int qh = l16 < G ? l16 : G - 1;
 #pragma unroll
         for (int st = 0; st < 4; ++st)
-            qa[st] = (l16 < G) ? *reinterpret_cast<const uint4*>(
-                                     q + ((int64_t)u * G + l16) * kD + 32 * st + 8 * grp)
-                               : make_uint4(0u, 0u, 0u, 0u);
+            qa[st] = *reinterpret_cast<const uint4*>(q + ((int64_t)u * G + qh) * kD + 32 * st + 8 * grp);
     } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) qv[g].load(q + ((int64_t)u * G + g) * kD + 8 * l16);
     }
+    nsel = nsel < 0 ? 0 : (nsel > top_k ? top_k : nsel);
+    const int64_t end = hot_split ? n_hot : n_hot + nsel;
+    const int nk = active ? (int)((end - i0) < kSplit ? (end - i0 > 0 ? end - i0 : 0) : kSplit) : 0;
 
+    // position of attended key kk (out of range, or stale, for a masked key).
+    // Positions and list indices stay below 2^26 (capacity <= 2^24), so this
+    // is 32-bit selects, not a branch the position load could sink into.
+    const int n_hot32 = (int)n_hot, sink32 = (int)sink_end, i032 = (int)i0;
+    const int hot_off = (int)r_end - sink32;   // list index -> position past the sink
+    auto pos_of = [&](int kk, int32_t c) -> int64_t {
+        const int i = i032 + kk;
+        const int ph = i < sink32 ? i : i + hot_off;
+        return (int64_t)(i < n_hot32 ? ph : c);
+    };
+    // key kk is attended: inside the split's count and a valid position
+    auto attended = [&](int kk, int32_t c) -> bool {
+        const int64_t p = pos_of(kk, c);
+        return kk < nk && p >= 0 && p < n_tok;
+    };
     // row of attended key kk: from the device ring for the hot zone when the
-    // store is host memory, else from the store
-    auto place = [&](int kk, int32_t c, bool& ok, bool& hot) -> int64_t {
+    // store is host memory, else from the store.  With a device store the row
+    // depends only on the position's range (a masked key reads a valid row
+    // and its score is masked later), so the row requests need not wait for
+    // the split's count; with a host store a masked key reads a ring row, so
+    // nothing crosses the host link for it.
+    auto place = [&](int kk, int32_t c, bool& hot) -> int64_t {
         const int64_t i = i0 + kk;
-        const int64_t p = (i < n_hot) ? ((i < sink_end) ? i : r_end + (i - sink_end)) : (int64_t)c;
-        ok = kk < nk && p >= 0 && p < n_tok;
+        const int64_t p = pos_of(kk, c);
         if constexpr (!RING) {
             hot = false;
-            return (int64_t)u * cap + (ok ? p : 0);
+            return (int64_t)u * cap + ((p >= 0 && p < n_tok) ? p : 0);
         }
-        if (!ok) {                          // masked: any valid row, on the device
+        if (!attended(kk, c)) {
             hot = true;
             return (int64_t)u * ring_rows;
         }
@@ -188,17 +208,15 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
         }
         return (int64_t)u * cap + p;
     };
-    bool ok_v[kPerK], ok_k[2], hot_v[kPerK], hot_k[2], ok_r, hot_r;
+    bool hot_v[kPerK], hot_k[2], hot_r;
     int64_t row_v[kPerK], row_k[2];
-    const int64_t row_r = place(32 * wave + kl, cand_r, ok_r, hot_r);
+    const int64_t row_r = place(32 * wave + kl, cand_r, hot_r);
     if constexpr (kMfma) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            row_k[h] = place(32 * wave + 16 * h + l16, cand_k[h], ok_k[h], hot_k[h]);
+        for (int h = 0; h < 2; ++h) row_k[h] = place(32 * wave + 16 * h + l16, cand_k[h], hot_k[h]);
     } else {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            row_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], ok_v[j], hot_v[j]);
+        for (int j = 0; j < kPer; ++j) row_v[j] = place(32 * wave + grp + 4 * j, cand_v[j], hot_v[j]);
     }
     // every K and V row is requested before any is used
     uint4 kb[2][4];
@@ -231,6 +249,9 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
         const VPair* vr = reinterpret_cast<const VPair*>((hk ? rv : V) + r * kD);
         vw[k] = __builtin_nontemporal_load(vr + lane);
     }
+    // keep the scheduler from hoisting the first q k^T products (which wait
+    // for the first key rows) above the value-row requests
+    __builtin_amdgcn_sched_barrier(0);
 
     // scores / sqrt(d) into L.p[head][key]
     if constexpr (kMfma) {
@@ -244,23 +265,25 @@ __device__ __forceinline__ void attend_split(const AttendArgs<T>& a, int u, int 
                                                             c, 0, 0, 0);
             // lane holds rows (heads) 4 grp + i of column (key) l16
             const int kk = 32 * wave + 16 * h + l16;
+            const bool ok = attended(kk, cand_k[h]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int g = 4 * grp + i;
-                if (g < G) L.p[g][kk] = ok_k[h] ? c[i] * kInvSqrtD : -INFINITY;
+                if (g < G) L.p[g][kk] = ok ? c[i] * kInvSqrtD : -INFINITY;
             }
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int kk = 32 * wave + grp + 4 * j;
+            const bool ok = attended(kk, cand_v[j]);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float d = 0.0f;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) d = fmaf(qv[g][r], kv[j][r], d);
                 d = sum16(d) * kInvSqrtD;
-                if (l16 == 0) L.p[g][kk] = ok_v[j] ? d : -INFINITY;
+                if (l16 == 0) L.p[g][kk] = ok ? d : -INFINITY;
             }
         }
     }
