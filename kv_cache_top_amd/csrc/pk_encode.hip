@@ -380,6 +380,17 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
         }
         lds_sync();
 
+        // the vote weights as wave-uniform values (an indexed argument read
+        // inside the rounds is a scalar load and a wait per round)
+        uint32_t wv[kRhoMax];
+#pragma unroll
+        for (int k = 0; k < kRhoMax; ++k) wv[k] = (uint32_t)__builtin_amdgcn_readfirstlane((int)wts.w[k]);
+        auto weight = [&](int r) {
+            uint32_t w = wv[0];
+#pragma unroll
+            for (int k = 1; k < kRhoMax; ++k) w = (r == k) ? wv[k] : w;
+            return w;
+        };
         if constexpr (M == 4) {
             // each half separately; s_row[16 h + c] = vote of centroid c of subspace 2b + h
 #pragma unroll
@@ -390,7 +401,7 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
                     const uint64_t bal = __ballot(kk == m);
                     const int c = __ffsll((unsigned long long)bal) - 1;   // lane 16 h + centroid
                     if (lane == c) kk = 0;  // removed
-                    if (lane == 0) atomicAdd(&s_row[c], wts.w[r]);
+                    if (lane == 0) atomicAdd(&s_row[c], weight(r));
                 }
             }
         } else {
@@ -405,7 +416,7 @@ __global__ __launch_bounds__(kQMaxBlock) void qprep_kernel(
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     if (c == 64 * t + lane) key[t] = 0;  // removed
-                if (lane == 0) atomicAdd(&s_row[c], wts.w[r]);
+                if (lane == 0) atomicAdd(&s_row[c], weight(r));
             }
         }
         lds_sync();

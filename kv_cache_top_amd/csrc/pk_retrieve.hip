@@ -56,12 +56,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     // Every block resident on a CU runs the part before the record gather at
     // the same time, so its instructions are paid by all of them: work that
     // one wave can do is done by one wave.
-    if (tid < 16) {
-        // signed level of code tid: sign bit 3, magnitude index bits 0..2
-        float m = tab.levels[0];
+    // signed level of code tid < 16: sign bit 3, magnitude index bits 0..2.
+    // The levels are read as wave-uniform values outside the branch: a
+    // per-lane select over the argument entries otherwise compiles to a vector
+    // load of the argument segment and a wait ahead of wave 0's first requests.
+    {
+        float lv[8];
 #pragma unroll
-        for (int l = 1; l < 8; ++l) m = ((tid & 7) == l) ? tab.levels[l] : m;
-        s_lv[tid] = (tid & 8) ? -m : m;
+        for (int l = 0; l < 8; ++l)
+            lv[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tab.levels[l])));
+        if (tid < 16) {
+            float m = lv[0];
+#pragma unroll
+            for (int l = 1; l < 8; ++l) m = ((tid & 7) == l) ? lv[l] : m;
+            s_lv[tid] = (tid & 8) ? -m : m;
+        }
     }
 
     // one round of loads: the unit histogram (its first 512 bins requested
