@@ -66,8 +66,11 @@ __device__ __forceinline__ void digit_search(const uint32_t* s_h, int nb, uint32
 }
 
 // Shared steps of both variants.  Keys are f32 order keys (larger key =
-// larger estimate).  ForAll(f) calls f(key) for every candidate of this
-// thread; the result is kth and `remaining` = ties at kth to take.
+// larger estimate).  ForAll(f) calls f(key, j) for every candidate of this
+// thread, j its slot (0 <= j < NC) when the thread holds its candidates in
+// registers, in which case each key's bucket is kept in a register between
+// the histogram and the member passes (NC = 0: recomputed); the result is kth
+// and `remaining` = ties at kth to take.
 struct FineShared {
     uint32_t h[kRadixBins];
     uint32_t mem[kRankMax];
@@ -76,7 +79,7 @@ struct FineShared {
     uint32_t digit, above, cnt, kth, gt;
 };
 
-template <typename ForAll>
+template <int NC, typename ForAll>
 __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, uint32_t kmin_inv,
                                                int k_eff, ForAll&& for_all, uint32_t& kth,
                                                uint32_t& remaining) {
@@ -114,7 +117,12 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
         auto bucket = [&](uint32_t key) -> uint32_t {
             return (uint32_t)fminf((order_key_to_f32(key) - vmin) * scale, topb);
         };
-        for_all([&](uint32_t key) { atomicAdd(&sh.h[bucket(key)], 1u); });
+        uint32_t bc[NC > 0 ? NC : 1];
+        for_all([&](uint32_t key, int j) {
+            const uint32_t bk = bucket(key);
+            if constexpr (NC > 0) bc[j] = bk;
+            atomicAdd(&sh.h[bk], 1u);
+        });
         lds_sync();
         if (wave == 0) digit_search(sh.h, kRadixBins, remaining, lane, &sh.digit, &sh.above);
         lds_sync();
@@ -122,8 +130,11 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
         const uint32_t rem = remaining - sh.above;   // 1 <= rem <= members of bstar
         const uint32_t n_b = sh.h[bstar];
         if (n_b <= (uint32_t)kRankMax) {
-            for_all([&](uint32_t key) {
-                if (bucket(key) == bstar) sh.mem[atomicAdd(&sh.cnt, 1u)] = key;
+            for_all([&](uint32_t key, int j) {
+                uint32_t bk;
+                if constexpr (NC > 0) bk = bc[j];
+                else bk = bucket(key);
+                if (bk == bstar) sh.mem[atomicAdd(&sh.cnt, 1u)] = key;
             });
             lds_sync();
             // exact rank of every member: the k-th value has gt < rem <= ge
@@ -157,7 +168,7 @@ __device__ __forceinline__ void fine_threshold(FineShared& sh, uint32_t kmax, ui
         const int nb = 1 << width;
         for (int b = tid; b < nb; b += kFBlock) sh.h[b] = 0;
         lds_sync();
-        for_all([&](uint32_t key) {
+        for_all([&](uint32_t key, int) {
             if ((key & pmask) == prefix) atomicAdd(&sh.h[(key >> shift) & dmask], 1u);
         });
         lds_sync();
@@ -198,8 +209,8 @@ __device__ __forceinline__ bool fine_sampled(const uint32_t (&key)[SEG], int nv,
     int r = (int)(((int64_t)2 * k_eff * n_samp + C - 1) / C);
     r = r < 1 ? 1 : (r > n_samp ? n_samp : r);
     uint32_t t_low = 0, rem_s = 0;
-    fine_threshold(sh, nv > 0 ? key[0] : 0u, nv > 0 ? ~key[0] : 0u, r,
-                   [&](auto&& f) { if (nv > 0) f(key[0]); }, t_low, rem_s);
+    fine_threshold<1>(sh, nv > 0 ? key[0] : 0u, nv > 0 ? ~key[0] : 0u, r,
+                      [&](auto&& f) { if (nv > 0) f(key[0], 0); }, t_low, rem_s);
     // survivors: keys >= t_low, counted and placed in candidate order
     uint32_t cnt = 0;
 #pragma unroll
@@ -231,13 +242,13 @@ __device__ __forceinline__ bool fine_sampled(const uint32_t (&key)[SEG], int nv,
         kmin_inv = max(kmin_inv, j < nv2 ? ~k2[j] : 0u);
     }
     uint32_t kth = 0, remaining = (uint32_t)k_eff;
-    fine_threshold(sh, kmax, kmin_inv, k_eff,
-                   [&](auto&& f) {
+    fine_threshold<SS>(sh, kmax, kmin_inv, k_eff,
+                       [&](auto&& f) {
 #pragma unroll
-                       for (int j = 0; j < SS; ++j)
-                           if (j < nv2) f(k2[j]);
-                   },
-                   kth, remaining);
+                           for (int j = 0; j < SS; ++j)
+                               if (j < nv2) f(k2[j], j);
+                       },
+                       kth, remaining);
     uint32_t eqc = 0, gtc = 0;
 #pragma unroll
     for (int j = 0; j < SS; ++j) {
@@ -333,13 +344,13 @@ __device__ __forceinline__ void fine_reg_body(const int32_t* __restrict__ cand_p
             kmax = max(kmax, j < nv ? key[j] : 0u);
             kmin_inv = max(kmin_inv, j < nv ? ~key[j] : 0u);
         }
-        fine_threshold(sh, kmax, kmin_inv, k_eff,
-                       [&](auto&& f) {
+        fine_threshold<(SEG <= 16 ? SEG : 0)>(sh, kmax, kmin_inv, k_eff,
+                                              [&](auto&& f) {
 #pragma unroll
-                           for (int j = 0; j < SEG; ++j)
-                               if (j < nv) f(key[j]);
-                       },
-                       kth, remaining);
+                                                  for (int j = 0; j < SEG; ++j)
+                                                      if (j < nv) f(key[j], j);
+                                              },
+                                              kth, remaining);
     }
     // compaction: one block scan of (ties at kth, keys above kth) gives both
     // offsets (C < 65536: the halves never carry)

@@ -424,10 +424,10 @@ __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __rest
 #pragma unroll
             for (int k = 0; k < kMemBatch / 4; ++k) {
                 const int i = 4 * (q0 + k * kFBlock);
-                if (i < C) f(f32_order_key(e[k].x));
-                if (i + 1 < C) f(f32_order_key(e[k].y));
-                if (i + 2 < C) f(f32_order_key(e[k].z));
-                if (i + 3 < C) f(f32_order_key(e[k].w));
+                if (i < C) f(f32_order_key(e[k].x), 0);
+                if (i + 1 < C) f(f32_order_key(e[k].y), 0);
+                if (i + 2 < C) f(f32_order_key(e[k].z), 0);
+                if (i + 3 < C) f(f32_order_key(e[k].w), 0);
             }
         }
     };
@@ -435,11 +435,11 @@ __global__ __launch_bounds__(kFBlock) void fine_mem_kernel(const int32_t* __rest
     uint32_t kth = 0, remaining = (uint32_t)k_eff;
     if (!all) {
         uint32_t kmax = 0, kmin_inv = 0;
-        for_all([&](uint32_t key) {
+        for_all([&](uint32_t key, int) {
             kmax = max(kmax, key);
             kmin_inv = max(kmin_inv, ~key);
         });
-        fine_threshold(sh, kmax, kmin_inv, k_eff, for_all, kth, remaining);
+        fine_threshold<0>(sh, kmax, kmin_inv, k_eff, for_all, kth, remaining);
     }
     // compaction, tile by tile: ties at kth before this thread's run and keys
     // above kth before it, from one scan per tile plus the earlier tiles' totals
