@@ -5,11 +5,11 @@
 
 namespace pk {
 
-// splits sp0 + blockIdx.x of unit blockIdx.y
+// split sp0 + blockIdx.y of unit blockIdx.x (units fastest: a unit's blocks share an XCD)
 template <typename T, int G, bool RING>
 __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs<T> a, int sp0) {
     __shared__ AttendLds<G> lds;
-    attend_split<T, G, RING>(a, blockIdx.y, sp0 + blockIdx.x, threadIdx.x, true, lds);
+    attend_split<T, G, RING>(a, blockIdx.x, sp0 + blockIdx.y, threadIdx.x, true, lds);
 }
 
 // merge of the split partials: one 128-thread block per (query head, unit),
@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_kernel(AttendArgs<T> a, in
 template <int CG>
 __global__ __launch_bounds__(kD) void combine_kernel(const float* __restrict__ part, int G,
                                                      int n_splits, float* __restrict__ out) {
-    const int g = blockIdx.x, u = blockIdx.y, d = threadIdx.x, lane = d & 63;
+    const int g = blockIdx.y, u = blockIdx.x, d = threadIdx.x, lane = d & 63;
     const int stride = G * (kD + 2);      // floats between splits
     const float* hp = part + (int64_t)u * n_splits * stride + g * (kD + 2);
     float M = -INFINITY, L = 0.0f, acc = 0.0f;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kD) void combine_kernel(const float* __restrict__ p
 template <typename T>
 static hipError_t launch_attend_t(int G, const AttendArgs<T>& a, int units, int sp0, bool ring,
                                   hipStream_t st) {
-    const dim3 grid(a.n_splits - sp0, units), blk(kAttThreads);
+    const dim3 grid(units, a.n_splits - sp0), blk(kAttThreads);
 #define PK_ATT(GG)                                                                       \
     return ring ? launch(attend_kernel<T, GG, true>, grid, blk, 0, st, a, sp0)           \
                 : launch(attend_kernel<T, GG, false>, grid, blk, 0, st, a, sp0)
@@ -83,8 +83,8 @@ int attend_max_splits() { return kMaxSplits; }
 hipError_t launch_combine(const float* part, int units, int G, int n_splits, float* out,
                           hipStream_t st) {
     if (n_splits <= 24)
-        return launch(combine_kernel<24>, dim3(G, units), dim3(kD), 0, st, part, G, n_splits, out);
-    return launch(combine_kernel<32>, dim3(G, units), dim3(kD), 0, st, part, G, n_splits, out);
+        return launch(combine_kernel<24>, dim3(units, G), dim3(kD), 0, st, part, G, n_splits, out);
+    return launch(combine_kernel<32>, dim3(units, G), dim3(kD), 0, st, part, G, n_splits, out);
 }
 
 hipError_t launch_attend(bool bf16, int G, const void* K, const void* V, int64_t cap, int units,

@@ -25,7 +25,7 @@
 namespace pk {
 
 constexpr int kSplit = 128;
-constexpr int kMaxSplits = 65536;   // splits per unit (the dense pass takes n / kSplit)
+constexpr int kMaxSplits = 65535;   // splits per unit (the dense pass takes n / kSplit; a grid dimension)
 constexpr int kAttThreads = 256;   // threads of one split
 static_assert(kSplit % 64 == 0, "softmax statistics take 64 keys per wave pass");
 

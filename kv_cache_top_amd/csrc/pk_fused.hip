@@ -33,13 +33,13 @@ __global__ __launch_bounds__(kFBlock) void fine_hot_kernel(const int32_t* __rest
                            *reinterpret_cast<FineShared*>(s_raw), tot, tstride);
         return;
     }
-    // hot split gs = unit * n_hot_splits + split
+    // hot split gs = split * units + unit (units fastest: a unit's blocks share an XCD)
     if (threadIdx.x >= kAttThreads) {
         attend_split_idle();
         return;
     }
     const int gs = (int)blockIdx.x - units;
-    attend_split<uint16_t, G, false>(a, gs / a.n_hot_splits, gs % a.n_hot_splits, threadIdx.x,
+    attend_split<uint16_t, G, false>(a, gs % units, gs / units, threadIdx.x,
                                      true, *reinterpret_cast<AttendLds<G>*>(s_raw));
 }
 
