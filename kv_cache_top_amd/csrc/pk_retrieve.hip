@@ -40,10 +40,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(KPT <= 8
     int hstride, const uint32_t* __restrict__ tot, int nbins,
     int64_t C, int top_k,
     const float* __restrict__ ysum, CodeTables tab, int32_t* __restrict__ cand_pos,
-    float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta) {
+    float* __restrict__ cand_est, int64_t cmax, int32_t* __restrict__ meta, int units_fastest) {
     constexpr int chunk = KPT * kBlock;
     static_assert(kBlock == 256, "one pair-table entry and one prefetched piece per thread");
-    const int u = blockIdx.x, ch = blockIdx.y, tid = threadIdx.x;   // units fastest (XCD affinity)
+    const int u = units_fastest ? blockIdx.x : blockIdx.y;   // block order: see launch_rerank
+    const int ch = units_fastest ? blockIdx.y : blockIdx.x;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l16 = tid & 15;
     constexpr int kLutWords = (M == 16 ? lut_bytes<16>() : lut_bytes<8>()) / 4;
@@ -555,19 +557,25 @@ hipError_t launch_rerank(int chunk, const uint8_t* scores, int64_t sstride, cons
     if (nbins < 1 || nbins > kMaxBins || hstride < nbins || n_chunks > max_chunks || C < 1 ||
         C > n_r)
         return hipErrorInvalidValue;
-    // units fastest: blocks are dealt to the 8 XCDs round-robin in launch
-    // order, so all of a unit's blocks share one XCD and its L2, which then
-    // fetches the unit's histogram and suffix-count rows once instead of once
-    // per XCD (11.8 -> 10.3 us at 128K x 4; the selection, attention and merge
-    // launches take the same order).  The scan and the query preparation keep
-    // chunks fastest: the same order made each about 0.5 us slower.
-    const dim3 grid(units, n_chunks), blk(kBlock);
+    // Units fastest up to 64 chunks per unit: blocks are dealt to the 8 XCDs
+    // round-robin in launch order, so all of a unit's blocks share one XCD and
+    // its L2, which then fetches the unit's histogram and suffix-count rows
+    // once instead of once per XCD (11.8 -> 10.3 us at 128K x 4; also faster
+    // at 256K and 384K; the selection, attention and merge launches take the
+    // same order).  With more chunks (1M tokens x 4: 128 chunks of 8192 keys,
+    // four rounds of resident blocks) each XCD then holds whole units and the
+    // units' uneven candidate counts leave XCDs idle: 65.3 us chunk-major
+    // against 77.0 us, so chunks go fastest there.  The scan and the query
+    // preparation keep chunks fastest at every size: the unit order made each
+    // about 0.5 us slower at 128K.
+    const int uf = n_chunks <= 64 ? 1 : 0;
+    const dim3 grid(uf ? units : n_chunks, uf ? n_chunks : units), blk(kBlock);
     const size_t hist_bytes = (size_t)nbins * sizeof(uint32_t);
     if (tab.sub_dim != 8 && tab.sub_dim != 4 && tab.sub_dim != 16) return hipErrorInvalidValue;
 #define PK_RERANK_M(K, MM)                                                                         \
     launch(rerank_kernel<K, MM>, grid, blk, hist_bytes, st, scores, sstride, rec, ids, lut, cap,   \
            sink_end, n_r, max_chunks, hist, hstride, tot, nbins, C, top_k, ysum, tab,              \
-           cand_pos, cand_est, cmax, meta)
+           cand_pos, cand_est, cmax, meta, uf)
 #define PK_RERANK(K)                                                                               \
     return tab.sub_dim == 8 ? PK_RERANK_M(K, 8)                                                    \
                             : (tab.sub_dim == 4 ? PK_RERANK_M(K, 4) : PK_RERANK_M(K, 16))
