@@ -166,7 +166,7 @@ pk_status pk_sparse_attend(pk_ctx* ctx, const void* q, const int32_t* sel, const
  * (units x ceil(n / 128) x G x 130 floats).  Device stores only.
  * ParisKV page, "Problem definition" (full attention reads every KV vector).
  * Errors: PK_ERR_INVALID (NULL pointer, no prefill), PK_ERR_UNSUPPORTED
- * (host-memory store), PK_ERR_OOM. */
+ * (host-memory store, or more than 65535 x 128 tokens per unit), PK_ERR_OOM. */
 pk_status pk_dense_attend(pk_ctx* ctx, const void* q, float* out, void* stream);
 
 /* pk_dense_attend for callers that cannot allocate device memory during the
