@@ -82,9 +82,15 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(const T* __restrict__ K,
 #pragma unroll
             for (int j = 0; j < kCoords; ++j) {
                 const int r = h * kCoords + j;
-                uint32_t mag = 0;
-#pragma unroll
-                for (int l = 0; l < 7; ++l) mag += (sq[r] >= bound[l]) ? 1u : 0u;
+                // mag = #{l : sq >= bound[l]}; the bounds ascend (squared
+                // thresholds times ss >= 0, rounded monotonically), so three
+                // levels of a binary search give the same count, ties and NaN
+                // included
+                const float x = sq[r];
+                const bool c1 = x >= bound[3];
+                const bool c2 = x >= (c1 ? bound[5] : bound[1]);
+                const bool c3 = x >= (c1 ? (c2 ? bound[6] : bound[4]) : (c2 ? bound[2] : bound[0]));
+                const uint32_t mag = (c1 ? 4u : 0u) + (c2 ? 2u : 0u) + (c3 ? 1u : 0u);
                 part |= ((((id >> r) & 1u) << 3) | mag) << (4 * r);
                 const double ax = fabs((double)v[r]);
                 s2 += ax * ax;
